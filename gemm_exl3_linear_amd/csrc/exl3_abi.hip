@@ -1,0 +1,182 @@
+// C ABI of the EXL3 library (declared in include/exl3.h): host-side
+// validation, fail-closed on anything unsupported, then dispatch to the
+// kernels.  Nothing is enqueued when validation fails, and nothing is
+// allocated: the caller provides every buffer, including the workspace.
+#include <stdio.h>
+#include <stdlib.h>
+
+#include "../../include/exl3.h"
+#include "exl3_gemv.hpp"
+#include "exl3_internal.hpp"
+
+namespace {
+
+constexpr int kGemvMaxRows = 16;  // rows up to this use the decode GEMV
+
+bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
+bool aligned4(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 3u) == 0; }
+
+bool trace_on() {
+  static const int on = [] {
+    const char* v = getenv("EXL3_TRACE");
+    return (v && v[0] && v[0] != '0') ? 1 : 0;
+  }();
+  return on != 0;
+}
+
+void trace(const char* what, long long a, long long b, long long c, long long d) {
+  if (trace_on()) fprintf(stderr, "[exl3] %s %lld %lld %lld %lld\n", what, a, b, c, d);
+}
+
+exl3_status from_hip(hipError_t e) { return e == hipSuccess ? EXL3_OK : EXL3_E_HIP; }
+
+// Common checks of a tensor record; `mult` is the required multiple of k, n.
+exl3_status check_weight(const exl3_weight* w, int mult, bool need_signs) {
+  if (!w) return EXL3_E_INVALID;
+  if (w->bits < 1 || w->bits > 8) return EXL3_E_INVALID;
+  if (w->codebook != EXL3_CODEBOOK_MUL1) return EXL3_E_UNSUPPORTED;
+  if (w->k <= 0 || w->n <= 0 || w->k % mult || w->n % mult) return EXL3_E_INVALID;
+  if (!w->trellis || !aligned16(w->trellis)) return EXL3_E_INVALID;
+  if (need_signs) {
+    if (!w->suh || !w->svh || !aligned16(w->suh) || !aligned16(w->svh)) return EXL3_E_INVALID;
+    if (w->bias && !aligned16(w->bias)) return EXL3_E_INVALID;
+  }
+  return EXL3_OK;
+}
+
+exl3_status check_arena(const exl3_expert_weights* a, int slots) {
+  if (!a) return EXL3_E_INVALID;
+  if (a->bits < 1 || a->bits > 8) return EXL3_E_INVALID;
+  if (a->codebook != EXL3_CODEBOOK_MUL1) return EXL3_E_UNSUPPORTED;
+  if (a->slots != slots || a->experts <= 0) return EXL3_E_INVALID;
+  if (a->k <= 0 || a->n <= 0 || a->k % 128 || a->n % 128) return EXL3_E_INVALID;
+  if (!a->trellis || !a->suh || !a->svh) return EXL3_E_INVALID;
+  if (!aligned16(a->trellis) || !aligned16(a->suh) || !aligned16(a->svh)) return EXL3_E_INVALID;
+  return EXL3_OK;
+}
+
+size_t linear_ws(const exl3_weight* w, int64_t m) {
+  if (m <= kGemvMaxRows) return exl3::plan_gemv(w->k, w->n, (int)m).ws;
+  return exl3::gemm_workspace(w->k, w->n, (int)m);
+}
+
+exl3::ArenaDesc desc(const exl3_expert_weights* a) {
+  return exl3::ArenaDesc{a->trellis, a->suh, a->svh, a->experts, a->slots, a->k, a->n, a->bits};
+}
+
+exl3_status check_grouped(const exl3_expert_weights* gu, const exl3_expert_weights* dn, int64_t t,
+                          int32_t topk) {
+  exl3_status st = check_arena(gu, 2);
+  if (st != EXL3_OK) return st;
+  if ((st = check_arena(dn, 1)) != EXL3_OK) return st;
+  if (dn->experts != gu->experts || dn->k != gu->n || dn->n != gu->k) return EXL3_E_INVALID;
+  if (t < 0 || topk < 1 || topk > EXL3_MAX_TOPK) return EXL3_E_INVALID;
+  // the grouped GEMM grid holds one workgroup row per 64-row tile (< 65536)
+  if (t * topk > (int64_t)1 << 21) return EXL3_E_INVALID;
+  return EXL3_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+int32_t exl3_abi_version(void) { return EXL3_ABI_VERSION; }
+
+const char* exl3_status_str(exl3_status status) {
+  switch (status) {
+    case EXL3_OK: return "ok";
+    case EXL3_E_INVALID: return "invalid argument (size, width, pointer or alignment)";
+    case EXL3_E_UNSUPPORTED: return "unsupported codebook (only mul1 is decoded)";
+    case EXL3_E_WORKSPACE: return "workspace missing or too small";
+    case EXL3_E_HIP: return "HIP launch error";
+    default: return "unknown status";
+  }
+}
+
+exl3_status exl3_reconstruct(const exl3_weight* w, uint16_t* w_out, exl3_stream_t stream) {
+  exl3_status st = check_weight(w, 16, false);
+  if (st != EXL3_OK) return st;
+  if (!w_out || !aligned16(w_out)) return EXL3_E_INVALID;
+  trace("reconstruct k n bits", w->k, w->n, w->bits, 0);
+  return from_hip(exl3::launch_reconstruct(w->trellis, w_out, w->k, w->n, w->bits,
+                                           reinterpret_cast<hipStream_t>(stream)));
+}
+
+exl3_status exl3_hadamard(const void* in, void* out, int32_t dtype, int64_t rows, int64_t dim,
+                          int64_t ld_in, int64_t ld_out, const uint16_t* sign_before,
+                          const uint16_t* sign_after, exl3_stream_t stream) {
+  if (dtype != EXL3_F16 && dtype != EXL3_F32) return EXL3_E_INVALID;
+  if (rows < 0 || dim <= 0 || dim % 128) return EXL3_E_INVALID;
+  if (ld_in < dim || ld_out < dim || ld_in % 8 || ld_out % 8) return EXL3_E_INVALID;
+  if (rows == 0) return EXL3_OK;
+  if (!in || !out || !aligned16(in) || !aligned16(out)) return EXL3_E_INVALID;
+  if (sign_before && !aligned16(sign_before)) return EXL3_E_INVALID;
+  if (sign_after && !aligned16(sign_after)) return EXL3_E_INVALID;
+  if (in == out && ld_in != ld_out) return EXL3_E_INVALID;
+  const bool f32 = dtype == EXL3_F32;
+  trace("hadamard rows dim dtype", rows, dim, dtype, 0);
+  return from_hip(exl3::launch_hadamard(in, f32, out, f32, rows, dim, ld_in, ld_out, sign_before,
+                                        sign_after, reinterpret_cast<hipStream_t>(stream)));
+}
+
+size_t exl3_linear_workspace_size(const exl3_weight* w, int64_t m) {
+  if (check_weight(w, 128, false) != EXL3_OK || m < 0) return 0;
+  if (m == 0) return 0;
+  return linear_ws(w, m);
+}
+
+exl3_status exl3_linear(const exl3_weight* w, const void* x, int64_t m, int64_t ldx, void* y,
+                        int64_t ldy, int32_t y_dtype, void* ws, size_t ws_bytes,
+                        exl3_stream_t stream) {
+  exl3_status st = check_weight(w, 128, true);
+  if (st != EXL3_OK) return st;
+  if (m < 0 || m > ((int64_t)1 << 24)) return EXL3_E_INVALID;
+  if (y_dtype != EXL3_F16 && y_dtype != EXL3_F32) return EXL3_E_INVALID;
+  if (ldx < w->k || ldy < w->n || ldx % 8 || ldy % 8) return EXL3_E_INVALID;
+  if (m == 0) return EXL3_OK;
+  if (!x || !y || !aligned16(x) || !aligned16(y)) return EXL3_E_INVALID;
+  const size_t need = linear_ws(w, m);
+  if (need > 0 && (!ws || ws_bytes < need || !aligned16(ws))) return EXL3_E_WORKSPACE;
+  const hipStream_t s = reinterpret_cast<hipStream_t>(stream);
+  const bool f32 = y_dtype == EXL3_F32;
+  if (m <= kGemvMaxRows) {
+    const exl3::GemvPlan plan = exl3::plan_gemv(w->k, w->n, (int)m);
+    trace("linear/gemv k n m splits", w->k, w->n, m, plan.splits);
+    return from_hip(exl3::launch_gemv(w->trellis, w->suh, w->svh, w->bias, w->k, w->n, w->bits,
+                                      static_cast<const uint16_t*>(x), (int)m, ldx, y, ldy, f32,
+                                      ws, plan, s));
+  }
+  trace("linear/gemm k n m bits", w->k, w->n, m, w->bits);
+  return from_hip(exl3::launch_gemm(w->trellis, w->suh, w->svh, w->bias, w->k, w->n, w->bits,
+                                    static_cast<const uint16_t*>(x), (int)m, ldx, y, ldy, f32, ws,
+                                    s));
+}
+
+size_t exl3_grouped_experts_workspace_size(const exl3_expert_weights* gate_up,
+                                           const exl3_expert_weights* down, int64_t t,
+                                           int32_t topk) {
+  if (check_grouped(gate_up, down, t, topk) != EXL3_OK || t == 0) return 0;
+  return exl3::grouped_workspace(desc(gate_up), desc(down), t, topk);
+}
+
+exl3_status exl3_grouped_experts(const exl3_expert_weights* gate_up,
+                                 const exl3_expert_weights* down, const void* x,
+                                 const int32_t* topk_ids, const float* topk_weights, int64_t t,
+                                 int32_t topk, float* y, void* ws, size_t ws_bytes,
+                                 exl3_stream_t stream) {
+  exl3_status st = check_grouped(gate_up, down, t, topk);
+  if (st != EXL3_OK) return st;
+  if (t == 0) return EXL3_OK;
+  if (!x || !topk_ids || !topk_weights || !y) return EXL3_E_INVALID;
+  if (!aligned16(x) || !aligned16(y) || !aligned4(topk_ids) || !aligned4(topk_weights))
+    return EXL3_E_INVALID;
+  const size_t need = exl3::grouped_workspace(desc(gate_up), desc(down), t, topk);
+  if (!ws || ws_bytes < need || !aligned16(ws)) return EXL3_E_WORKSPACE;
+  trace("grouped t topk experts bits", t, topk, gate_up->experts, gate_up->bits);
+  return from_hip(exl3::launch_grouped(desc(gate_up), desc(down),
+                                       static_cast<const uint16_t*>(x), topk_ids, topk_weights, t,
+                                       topk, y, ws, ws_bytes,
+                                       reinterpret_cast<hipStream_t>(stream)));
+}
+
+}  // extern "C"

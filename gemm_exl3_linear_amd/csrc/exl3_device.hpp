@@ -1,0 +1,180 @@
+// Device-side building blocks shared by every EXL3 kernel of this library
+// (gfx950 / CDNA4, wave64).
+//
+// Format (exl3xpu README "MoE (routed experts)"; Arc 140V MoE post, section
+// 2A; TensorFold issue #832 "Description"): a tensor's 16x16 tiles are stored
+// as 16*K uint16 words, trellis[k/16][n/16][16*K].  The words of a tile, read
+// in index order and most-significant bit first, form a cyclic stream of
+// 256*K bits; state j is the 16-bit window starting at bit K*j; the mul1
+// codebook maps state S to fp16_RN((sigma - 510) * 1775 / 2^18), sigma being
+// the byte sum of (S * 0x9E3779) mod 2^32 (bounded by +-3.453125, exl3xpu
+// README "Prefill: int8 linears ..."); state j is tile row j/16, column j%16.
+//
+// Work unit of the decode: one lane owns a *row pair* of a tile (rows 2p and
+// 2p+1, p = 0..7): the 2K consecutive words 2K*p .. 2K*p+2K-1 plus the first
+// word of the next row pair (the "spill" word, taken cyclically inside the
+// tile).  Eight consecutive lanes own one tile, so a wave's loads of a run of
+// tiles are contiguous.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace exl3 {
+
+typedef _Float16 half2_t __attribute__((ext_vector_type(2)));
+typedef _Float16 half4_t __attribute__((ext_vector_type(4)));
+typedef float float4_t __attribute__((ext_vector_type(4)));
+typedef float float2_t __attribute__((ext_vector_type(2)));
+
+// Codebook constants of the mul1 reading (one definition each).
+constexpr uint32_t kMul1Multiplier = 0x9E3779u;  // < 2^24: one v_mul_u32_u24
+constexpr uint32_t kHalf1024Pair = 0x64006400u;  // fp16 bit pattern of 1024.0, both halves
+constexpr float kSigmaBiasPlus1024 = 1534.0f;    // 1024 + 510
+constexpr float kMul1Scale = 1775.0f / 262144.0f;  // 1775 * 2^-18, exact in fp16
+constexpr float kInvSqrt128 = 0.08838834764831845f;
+
+__device__ __forceinline__ uint32_t lane_id() { return __lane_id(); }
+
+// Stream-ordered dword: a little-endian dword holds w[2i] in its low half;
+// rotating by 16 puts w[2i] (the earlier word) in the high half.
+__device__ __forceinline__ uint32_t stream_dword(uint32_t le) {
+  return __builtin_amdgcn_alignbit(le, le, 16);
+}
+
+// h = S * multiplier for the state held in the high (HI = true) or low half
+// of `w`.  The half is selected by the SDWA operand selector, so no separate
+// extract instruction is needed.
+template <bool HI>
+__device__ __forceinline__ uint32_t hash_half(uint32_t w, uint32_t mult) {
+  uint32_t h;
+  if constexpr (HI)
+    asm("v_mul_u32_u24_sdwa %0, %1, %2 dst_sel:DWORD dst_unused:UNUSED_PAD src0_sel:WORD_1 "
+        "src1_sel:DWORD"
+        : "=v"(h)
+        : "v"(w), "v"(mult));
+  else
+    asm("v_mul_u32_u24_sdwa %0, %1, %2 dst_sel:DWORD dst_unused:UNUSED_PAD src0_sel:WORD_0 "
+        "src1_sel:DWORD"
+        : "=v"(h)
+        : "v"(w), "v"(mult));
+  return h;
+}
+
+// Hash of the state that starts at bit P of the row-pair stream held in the
+// stream-ordered dwords B[0..K] (B[K] carries the spill word in its high half).
+template <int K, int P>
+__device__ __forceinline__ uint32_t state_hash(const uint32_t (&B)[K + 1], uint32_t mult) {
+  constexpr int i = P / 32;
+  constexpr int o = P % 32;
+  constexpr int o16 = o & 15;
+  uint32_t w;
+  if constexpr (o16 == 0)
+    w = B[i];
+  else
+    w = __builtin_amdgcn_alignbit(B[i], B[i + 1], 32 - o16);  // bits [o16, o16+32) of the stream
+  return hash_half<(o < 16)>(w, mult);
+}
+
+// Decode one row pair.  D[0..K-1] are the lane's 2K words as little-endian
+// dwords, spill_b is the stream-ordered first dword of the next row pair.
+// Output: out[c] = half2 {W[2p][c], W[2p+1][c]} for the 16 columns c of the
+// tile, i.e. two consecutive k values of one output column.
+template <int K, int C>
+__device__ __forceinline__ void decode_column(const uint32_t (&B)[K + 1], uint32_t mult,
+                                              uint32_t (&out)[16]) {
+  const uint32_t h0 = state_hash<K, K * C>(B, mult);
+  const uint32_t h1 = state_hash<K, K * (16 + C)>(B, mult);
+  // sigma + 1024 as fp16 bit patterns, packed: low half <- row 2p, high <- 2p+1
+  const uint32_t s0 = __builtin_amdgcn_sad_u8(h0, 0u, kHalf1024Pair);
+  const uint32_t packed = __builtin_amdgcn_sad_hi_u8(h1, 0u, s0);
+  const half2_t bias = {(_Float16)kSigmaBiasPlus1024, (_Float16)kSigmaBiasPlus1024};
+  const half2_t scale = {(_Float16)kMul1Scale, (_Float16)kMul1Scale};
+  half2_t v = __builtin_bit_cast(half2_t, packed);
+  v = (v - bias) * scale;  // exact subtraction, then the single fp16 rounding
+  out[C] = __builtin_bit_cast(uint32_t, v);
+}
+
+template <int K, int C = 0>
+__device__ __forceinline__ void decode_columns(const uint32_t (&B)[K + 1], uint32_t mult,
+                                               uint32_t (&out)[16]) {
+  if constexpr (C < 16) {
+    decode_column<K, C>(B, mult, out);
+    decode_columns<K, C + 1>(B, mult, out);
+  }
+}
+
+template <int K>
+__device__ __forceinline__ void decode_rowpair(const uint32_t (&D)[K], uint32_t spill_b,
+                                               uint32_t (&out)[16]) {
+  uint32_t B[K + 1];
+#pragma unroll
+  for (int i = 0; i < K; ++i) B[i] = stream_dword(D[i]);
+  B[K] = spill_b;
+  const uint32_t mult = kMul1Multiplier;
+  decode_columns<K>(B, mult, out);
+}
+
+// Stream-ordered first dword of the next row pair in the same tile: lane
+// group of 8 (one tile), lane p reads lane (p+1) mod 8.  All 8 lanes of a tile
+// must be active together.
+__device__ __forceinline__ uint32_t spill_from_next(uint32_t my_first_le) {
+  const uint32_t l = lane_id();
+  const uint32_t src = (l & ~7u) | ((l + 1u) & 7u);
+  return (uint32_t)__builtin_amdgcn_ds_bpermute((int)(src << 2), (int)stream_dword(my_first_le));
+}
+
+// Load the lane's 2K words (4K bytes at a 4-byte aligned address).
+template <int K>
+__device__ __forceinline__ void load_rowpair(const uint32_t* __restrict__ p, uint32_t (&D)[K]) {
+  if constexpr (K % 4 == 0) {
+#pragma unroll
+    for (int i = 0; i < K; i += 4) {
+      const uint4 v = *reinterpret_cast<const uint4*>(p + i);
+      D[i] = v.x; D[i + 1] = v.y; D[i + 2] = v.z; D[i + 3] = v.w;
+    }
+  } else if constexpr (K == 2 || K == 6) {
+#pragma unroll
+    for (int i = 0; i < K; i += 2) {
+      const uint2 v = *reinterpret_cast<const uint2*>(p + i);
+      D[i] = v.x; D[i + 1] = v.y;
+    }
+  } else {
+#pragma unroll
+    for (int i = 0; i < K; ++i) D[i] = p[i];
+  }
+}
+
+// ---------------------------------------------------------------------------
+// 128-point Walsh-Hadamard transform held by one wave: lane l owns elements
+// 2l (a) and 2l+1 (b).  Butterfly (u, v) -> (u + v, u - v) with u the lower
+// index, strides 1..64, Sylvester (natural) order; no normalisation here.
+// ---------------------------------------------------------------------------
+__device__ __forceinline__ float shfl_xor_f(float v, int mask) {
+  const int src = (int)(lane_id() ^ (uint32_t)mask);
+  return __int_as_float(__builtin_amdgcn_ds_bpermute(src << 2, __float_as_int(v)));
+}
+
+__device__ __forceinline__ void fwht128_pair(float& a, float& b) {
+  const float s = a + b, d = a - b;
+  a = s;
+  b = d;
+  const uint32_t l = lane_id();
+#pragma unroll
+  for (int m = 1; m < 64; m <<= 1) {
+    const float pa = shfl_xor_f(a, m);
+    const float pb = shfl_xor_f(b, m);
+    const bool upper = (l & (uint32_t)m) != 0;
+    a = upper ? (pa - a) : (a + pa);
+    b = upper ? (pb - b) : (b + pb);
+  }
+}
+
+__device__ __forceinline__ float h2f(uint16_t h) {
+  return (float)__builtin_bit_cast(_Float16, h);
+}
+__device__ __forceinline__ uint16_t f2h(float f) {
+  return __builtin_bit_cast(uint16_t, (_Float16)f);
+}
+
+}  // namespace exl3

@@ -1,0 +1,70 @@
+// Dense prefill linear (m > 16): x' = (x .* suh) H is written once to the
+// workspace by the Hadamard kernel, then one fused decode + MFMA GEMM launch
+// computes y = (x' W~) H .* svh (+ bias).  See exl3_gemm.hpp for the kernel.
+#include "exl3_gemm.hpp"
+#include "exl3_internal.hpp"
+
+namespace exl3 {
+
+struct DenseGemmRes {
+  const uint16_t* a;
+  int64_t lda;
+  int m;
+  int bm;
+  const uint16_t* trellis;
+  const uint16_t* svh;
+  const uint16_t* bias;
+  void* y;
+  int64_t ldy;
+  bool y_f32;
+  __device__ GemmTask task(int mtile, int /*z*/) const {
+    GemmTask T;
+    const int r0 = mtile * bm;
+    T.valid = r0 < m;
+    T.a = a + (int64_t)r0 * lda;
+    T.lda = lda;
+    T.rows = (m - r0) < bm ? (m - r0) : bm;
+    T.trellis = trellis;
+    T.svh = svh;
+    T.bias = bias;
+    T.y = y_f32 ? (void*)(static_cast<float*>(y) + (int64_t)r0 * ldy)
+                : (void*)(static_cast<uint16_t*>(y) + (int64_t)r0 * ldy);
+    T.ldy = ldy;
+    return T;
+  }
+};
+
+static int choose_bm(int m) { return m >= 256 ? 256 : (m > 64 ? 128 : 64); }
+
+template <int K>
+struct DenseGemmRun {
+  static hipError_t run(const DenseGemmRes& r, int k, int n, hipStream_t s) {
+    const dim3 grid(n / 128, (r.m + r.bm - 1) / r.bm, 1);
+#define EXL3_GEMM_LAUNCH(BM)                                                                    \
+  do {                                                                                          \
+    if (r.y_f32)                                                                                \
+      hipLaunchKernelGGL((gemm_kernel<K, BM, true, DenseGemmRes>), grid, dim3(256), 0, s, r, k, n); \
+    else                                                                                        \
+      hipLaunchKernelGGL((gemm_kernel<K, BM, false, DenseGemmRes>), grid, dim3(256), 0, s, r, k, n); \
+  } while (0)
+    if (r.bm == 256) EXL3_GEMM_LAUNCH(256);
+    else if (r.bm == 128) EXL3_GEMM_LAUNCH(128);
+    else EXL3_GEMM_LAUNCH(64);
+#undef EXL3_GEMM_LAUNCH
+    return hipGetLastError();
+  }
+};
+
+size_t gemm_workspace(int k, int /*n*/, int m) { return (size_t)m * k * sizeof(uint16_t); }
+
+hipError_t launch_gemm(const uint16_t* trellis, const uint16_t* suh, const uint16_t* svh,
+                       const uint16_t* bias, int k, int n, int bits, const uint16_t* x, int m,
+                       int64_t ldx, void* y, int64_t ldy, bool y_f32, void* ws, hipStream_t s) {
+  uint16_t* xp = static_cast<uint16_t*>(ws);
+  hipError_t e = launch_hadamard(x, false, xp, false, m, k, ldx, k, suh, nullptr, s);
+  if (e != hipSuccess) return e;
+  DenseGemmRes r{xp, k, m, choose_bm(m), trellis, svh, bias, y, ldy, y_f32};
+  return dispatch_bits<DenseGemmRun>(bits, r, k, n, s);
+}
+
+}  // namespace exl3

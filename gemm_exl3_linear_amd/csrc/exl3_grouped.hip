@@ -1,0 +1,486 @@
+// Routed-expert SwiGLU MLP over packed EXL3 arenas, routed contribution only.
+//
+// exl3xpu README, "MoE (routed experts)": the contribution is computed in
+// fp32 with the routing weight applied to the down-projection output; one
+// launch per projection, routing kept on device.  Arc 140V MoE post, section 2:
+// gate+up as one launch over (expert, slot) units sharing the input row, SiLU
+// between the launches, device-side binning of tokens into contiguous
+// per-expert slices (2D), fp32 weighted gather (2D).
+//
+// Two regimes, chosen on the host from the number of (token, slot) pairs
+// P = t * topk (no device data is read back):
+//
+// Small P (decode, token-parallel verify): every pair is an independent M=1
+// unit (the README's "per-unit x stride" idea).
+//   1. gemv_kernel over units (pair, gate|up)          -> fp32 partials
+//   2. gu_unit_epilogue: reduce, output transform, svh, a = silu(g) * u, then
+//      the down projection's input transform (a .* suh_down) H   -> fp16 x'_d
+//   3. gemv_kernel over units (pair)                    -> fp32 partials
+//   4. down_unit_epilogue: per (token, 128 columns), for slots in order:
+//      reduce, transform, svh, times the routing weight, summed in fp32 -> y
+//
+// Large P (prefill): device binning, then one grouped MFMA GEMM launch per
+// projection over a device-built tile list (expert, first row, rows), so each
+// expert's weights are decoded once per 64-row tile instead of once per row.
+//   1. zero counters, count pairs per expert (integer atomics: exact)
+//   2. one thread builds offsets and the tile list
+//   3. scatter pairs into expert order (the order inside an expert is not
+//      fixed, but every row is computed independently of its position, so
+//      the output does not depend on it)
+//   4. x'_g, x'_u = (x_token .* suh_e,slot) H for each sorted row   -> fp16
+//   5. gemm_kernel over (128 cols, tile, slot)  -> g, u fp32 (transformed)
+//   6. a = silu(g) * u, x'_d = (a .* suh_down_e) H                  -> fp16
+//   7. gemm_kernel over (128 cols, tile)        -> d fp32 (transformed, svh)
+//   8. y[token] = sum over slots in order of w * d                  -> fp32
+#include "exl3_device.hpp"
+#include "exl3_gemm.hpp"
+#include "exl3_gemv.hpp"
+#include "exl3_internal.hpp"
+
+namespace exl3 {
+
+constexpr int kGroupedUnitMaxPairs = 64;  // P at or below this uses the unit path
+constexpr int kGroupedBM = 64;            // rows per tile of the grouped GEMM
+
+__device__ __forceinline__ float silu_f(float z) { return z / (1.0f + __expf(-z)); }
+
+static inline size_t align256(size_t v) { return (v + 255) & ~(size_t)255; }
+
+// ---------------------------------------------------------------------------
+// small-P path
+// ---------------------------------------------------------------------------
+struct GuUnitRes {
+  const uint16_t* trellis;
+  const uint16_t* suh;
+  int64_t tensor_dw_words;  // words of one (expert, slot) tensor
+  int k;                    // hidden
+  int n;                    // intermediate
+  const uint16_t* x;
+  int topk;
+  const int32_t* ids;
+  float* ws;
+  int splits;
+  __device__ GemvTask task(int u, int split) const {
+    GemvTask T;
+    const int pair = u >> 1, slot = u & 1;
+    const int e = ids[pair];
+    const int tok = pair / topk;
+    T.valid = true;
+    T.trellis = trellis + (int64_t)(e * 2 + slot) * tensor_dw_words;
+    T.suh = suh + (int64_t)(e * 2 + slot) * k;
+    T.x = x + (int64_t)tok * k;
+    T.ldx = k;
+    T.m = 1;
+    T.partial = ws + ((int64_t)u * splits + split) * n;
+    return T;
+  }
+};
+
+struct DnUnitRes {
+  const uint16_t* trellis;
+  int64_t tensor_words;
+  int k;  // intermediate
+  int n;  // hidden
+  const uint16_t* xd;  // fp16 [P][k], already in the Hadamard domain
+  const int32_t* ids;
+  float* ws;
+  int splits;
+  __device__ GemvTask task(int u, int split) const {
+    GemvTask T;
+    const int e = ids[u];
+    T.valid = true;
+    T.trellis = trellis + (int64_t)e * tensor_words;
+    T.suh = nullptr;
+    T.x = xd + (int64_t)u * k;
+    T.ldx = k;
+    T.m = 1;
+    T.partial = ws + ((int64_t)u * splits + split) * n;
+    return T;
+  }
+};
+
+// reduce gate and up, SiLU, then the down projection's input transform
+__global__ __launch_bounds__(256) void gu_unit_epilogue(
+    const float* __restrict__ part, int splits, int P, int inter, const int32_t* __restrict__ ids,
+    const uint16_t* __restrict__ svh_gu, const uint16_t* __restrict__ suh_dn,
+    uint16_t* __restrict__ xd) {
+  const int nblocks = inter >> 7;
+  const int task = blockIdx.x * 4 + (threadIdx.x >> 6);
+  if (task >= P * nblocks) return;
+  const int pair = task / nblocks, nb = task - pair * nblocks;
+  const int col = nb * 128 + 2 * (int)lane_id();
+  const int e = ids[pair];
+  float gv[2], uv[2];
+  for (int slot = 0; slot < 2; ++slot) {
+    float a = 0.f, b = 0.f;
+    const float* pp = part + ((int64_t)(pair * 2 + slot) * splits) * inter + col;
+    for (int s = 0; s < splits; ++s) {
+      const float2 v = *reinterpret_cast<const float2*>(pp + (int64_t)s * inter);
+      a += v.x;
+      b += v.y;
+    }
+    fwht128_pair(a, b);
+    const uint32_t sv =
+        *reinterpret_cast<const uint32_t*>(svh_gu + (int64_t)(e * 2 + slot) * inter + col);
+    a *= kInvSqrt128 * h2f((uint16_t)(sv & 0xFFFF));
+    b *= kInvSqrt128 * h2f((uint16_t)(sv >> 16));
+    if (slot == 0) { gv[0] = a; gv[1] = b; } else { uv[0] = a; uv[1] = b; }
+  }
+  float a = silu_f(gv[0]) * uv[0];
+  float b = silu_f(gv[1]) * uv[1];
+  const uint32_t su = *reinterpret_cast<const uint32_t*>(suh_dn + (int64_t)e * inter + col);
+  a *= h2f((uint16_t)(su & 0xFFFF));
+  b *= h2f((uint16_t)(su >> 16));
+  fwht128_pair(a, b);
+  a *= kInvSqrt128;
+  b *= kInvSqrt128;
+  *reinterpret_cast<uint32_t*>(xd + (int64_t)pair * inter + col) =
+      (uint32_t)f2h(a) | ((uint32_t)f2h(b) << 16);
+}
+
+// per (token, 128 columns): slots in order, reduce, transform, svh, weight, sum
+__global__ __launch_bounds__(256) void down_unit_epilogue(
+    const float* __restrict__ part, int splits, int64_t t_count, int topk, int hidden,
+    const int32_t* __restrict__ ids, const float* __restrict__ w,
+    const uint16_t* __restrict__ svh_dn, float* __restrict__ y) {
+  const int nblocks = hidden >> 7;
+  const int64_t task = (int64_t)blockIdx.x * 4 + (threadIdx.x >> 6);
+  if (task >= t_count * nblocks) return;
+  const int64_t tok = task / nblocks;
+  const int nb = (int)(task - tok * nblocks);
+  const int col = nb * 128 + 2 * (int)lane_id();
+  float ya = 0.f, yb = 0.f;
+  for (int s = 0; s < topk; ++s) {
+    const int64_t pair = tok * topk + s;
+    const int e = ids[pair];
+    float a = 0.f, b = 0.f;
+    const float* pp = part + (pair * splits) * hidden + col;
+    for (int q = 0; q < splits; ++q) {
+      const float2 v = *reinterpret_cast<const float2*>(pp + (int64_t)q * hidden);
+      a += v.x;
+      b += v.y;
+    }
+    fwht128_pair(a, b);
+    const uint32_t sv = *reinterpret_cast<const uint32_t*>(svh_dn + (int64_t)e * hidden + col);
+    const float wt = w[pair];
+    ya += wt * (a * kInvSqrt128 * h2f((uint16_t)(sv & 0xFFFF)));
+    yb += wt * (b * kInvSqrt128 * h2f((uint16_t)(sv >> 16)));
+  }
+  *reinterpret_cast<float2*>(y + tok * hidden + col) = make_float2(ya, yb);
+}
+
+template <int K>
+struct GuUnitRun {
+  static hipError_t run(const GuUnitRes& r, int k, int n, int units, int kc, size_t lds,
+                        hipStream_t s) {
+    hipLaunchKernelGGL((gemv_kernel<K, GuUnitRes>), dim3(n / 128, r.splits, units), dim3(256), lds,
+                       s, r, k, n, kc);
+    return hipGetLastError();
+  }
+};
+
+template <int K>
+struct DnUnitRun {
+  static hipError_t run(const DnUnitRes& r, int k, int n, int units, int kc, size_t lds,
+                        hipStream_t s) {
+    hipLaunchKernelGGL((gemv_kernel<K, DnUnitRes>), dim3(n / 128, r.splits, units), dim3(256), lds,
+                       s, r, k, n, kc);
+    return hipGetLastError();
+  }
+};
+
+struct UnitLayout {
+  int s_gu, s_dn;
+  size_t part_gu, xd, part_dn, total;
+};
+
+static UnitLayout unit_layout(const ArenaDesc& gu, const ArenaDesc& dn, int64_t P) {
+  UnitLayout L;
+  L.s_gu = gemv_choose_splits(gu.k, (gu.n / 128) * (int)P * 2, 1, kGemvTargetWorkgroups);
+  L.s_dn = gemv_choose_splits(dn.k, (dn.n / 128) * (int)P, 1, kGemvTargetWorkgroups);
+  size_t off = 0;
+  L.part_gu = off; off += align256((size_t)P * 2 * L.s_gu * gu.n * sizeof(float));
+  L.xd = off;      off += align256((size_t)P * gu.n * sizeof(uint16_t));
+  L.part_dn = off; off += align256((size_t)P * L.s_dn * dn.n * sizeof(float));
+  L.total = off;
+  return L;
+}
+
+// ---------------------------------------------------------------------------
+// large-P path
+// ---------------------------------------------------------------------------
+struct TileEntry {
+  int e, row0, rows, pad;
+};
+
+struct GemmLayout {
+  int max_tiles;
+  size_t counts, cursor, offsets, ntiles, tiles, pos, sorted, xg, gu, xd, d, total;
+};
+
+static GemmLayout gemm_layout(const ArenaDesc& gu, const ArenaDesc& dn, int64_t P) {
+  GemmLayout L;
+  const int E = gu.experts;
+  L.max_tiles = (int)((P + kGroupedBM - 1) / kGroupedBM) + (int)(P < E ? P : E);
+  size_t off = 0;
+  L.counts = off;  off += align256((size_t)E * 4);
+  L.cursor = off;  off += align256((size_t)E * 4);
+  L.offsets = off; off += align256((size_t)E * 4);
+  L.ntiles = off;  off += 256;
+  L.tiles = off;   off += align256((size_t)L.max_tiles * sizeof(TileEntry));
+  L.pos = off;     off += align256((size_t)P * 4);
+  L.sorted = off;  off += align256((size_t)P * 4);
+  L.xg = off;      off += align256((size_t)2 * P * gu.k * sizeof(uint16_t));
+  L.gu = off;      off += align256((size_t)2 * P * gu.n * sizeof(float));
+  L.xd = off;      off += align256((size_t)P * dn.k * sizeof(uint16_t));
+  L.d = off;       off += align256((size_t)P * dn.n * sizeof(float));
+  L.total = off;
+  return L;
+}
+
+__global__ void zero_i32(int32_t* __restrict__ p, int count) {
+  const int i = blockIdx.x * blockDim.x + threadIdx.x;
+  if (i < count) p[i] = 0;
+}
+
+__global__ void bin_count(const int32_t* __restrict__ ids, int64_t P, int32_t* __restrict__ counts) {
+  const int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+  if (i < P) atomicAdd(&counts[ids[i]], 1);
+}
+
+// one thread: exclusive scan of the counts and the list of row tiles
+__global__ void bin_plan(const int32_t* __restrict__ counts, int E, int bm,
+                         int32_t* __restrict__ offsets, int32_t* __restrict__ ntiles,
+                         TileEntry* __restrict__ tiles) {
+  if (threadIdx.x != 0 || blockIdx.x != 0) return;
+  int off = 0, nt = 0;
+  for (int e = 0; e < E; ++e) {
+    const int c = counts[e];
+    offsets[e] = off;
+    for (int r = 0; r < c; r += bm) {
+      TileEntry te;
+      te.e = e;
+      te.row0 = off + r;
+      te.rows = (c - r) < bm ? (c - r) : bm;
+      te.pad = 0;
+      tiles[nt++] = te;
+    }
+    off += c;
+  }
+  *ntiles = nt;
+}
+
+__global__ void bin_scatter(const int32_t* __restrict__ ids, int64_t P,
+                            const int32_t* __restrict__ offsets, int32_t* __restrict__ cursor,
+                            int32_t* __restrict__ pos, int32_t* __restrict__ sorted) {
+  const int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+  if (i >= P) return;
+  const int e = ids[i];
+  const int r = offsets[e] + atomicAdd(&cursor[e], 1);
+  sorted[r] = (int32_t)i;
+  pos[i] = r;
+}
+
+// x'_slot[r] = (x[token(r)] .* suh[e(r)][slot]) H, one wave per (row, slot, block)
+__global__ __launch_bounds__(256) void gu_input_transform(
+    const uint16_t* __restrict__ x, int topk, int64_t P, int hidden,
+    const int32_t* __restrict__ sorted, const int32_t* __restrict__ ids,
+    const uint16_t* __restrict__ suh_gu, uint16_t* __restrict__ xg) {
+  const int nblocks = hidden >> 7;
+  const int64_t task = (int64_t)blockIdx.x * 4 + (threadIdx.x >> 6);
+  if (task >= P * 2 * nblocks) return;
+  const int64_t r = task / (2 * nblocks);
+  const int rem = (int)(task - r * 2 * nblocks);
+  const int slot = rem / nblocks, nb = rem - slot * nblocks;
+  const int pair = sorted[r];
+  const int e = ids[pair];
+  const int64_t tok = pair / topk;
+  const int col = nb * 128 + 2 * (int)lane_id();
+  const uint32_t xv = *reinterpret_cast<const uint32_t*>(x + tok * hidden + col);
+  const uint32_t sv =
+      *reinterpret_cast<const uint32_t*>(suh_gu + (int64_t)(e * 2 + slot) * hidden + col);
+  float a = h2f((uint16_t)(xv & 0xFFFF)) * h2f((uint16_t)(sv & 0xFFFF));
+  float b = h2f((uint16_t)(xv >> 16)) * h2f((uint16_t)(sv >> 16));
+  fwht128_pair(a, b);
+  a *= kInvSqrt128;
+  b *= kInvSqrt128;
+  *reinterpret_cast<uint32_t*>(xg + ((int64_t)slot * P + r) * hidden + col) =
+      (uint32_t)f2h(a) | ((uint32_t)f2h(b) << 16);
+}
+
+// a = silu(g) * u, x'_d = (a .* suh_down_e) H, one wave per (row, block)
+__global__ __launch_bounds__(256) void silu_down_transform(
+    const float* __restrict__ gu, int64_t P, int inter, const int32_t* __restrict__ sorted,
+    const int32_t* __restrict__ ids, const uint16_t* __restrict__ suh_dn,
+    uint16_t* __restrict__ xd) {
+  const int nblocks = inter >> 7;
+  const int64_t task = (int64_t)blockIdx.x * 4 + (threadIdx.x >> 6);
+  if (task >= P * nblocks) return;
+  const int64_t r = task / nblocks;
+  const int nb = (int)(task - r * nblocks);
+  const int e = ids[sorted[r]];
+  const int col = nb * 128 + 2 * (int)lane_id();
+  const float2 g = *reinterpret_cast<const float2*>(gu + r * inter + col);
+  const float2 u = *reinterpret_cast<const float2*>(gu + (P + r) * inter + col);
+  const uint32_t su = *reinterpret_cast<const uint32_t*>(suh_dn + (int64_t)e * inter + col);
+  float a = silu_f(g.x) * u.x * h2f((uint16_t)(su & 0xFFFF));
+  float b = silu_f(g.y) * u.y * h2f((uint16_t)(su >> 16));
+  fwht128_pair(a, b);
+  a *= kInvSqrt128;
+  b *= kInvSqrt128;
+  *reinterpret_cast<uint32_t*>(xd + r * inter + col) = (uint32_t)f2h(a) | ((uint32_t)f2h(b) << 16);
+}
+
+// y[token] = sum over slots in order of w[token, slot] * d[pos(token, slot)]
+__global__ __launch_bounds__(256) void combine_rows(const float* __restrict__ d,
+                                                   const int32_t* __restrict__ pos,
+                                                   const float* __restrict__ w, int64_t t_count,
+                                                   int topk, int hidden, float* __restrict__ y) {
+  const int64_t idx = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;  // float4 index
+  const int q = hidden >> 2;
+  if (idx >= t_count * q) return;
+  const int64_t tok = idx / q;
+  const int c4 = (int)(idx - tok * q);
+  float4 acc = make_float4(0.f, 0.f, 0.f, 0.f);
+  for (int s = 0; s < topk; ++s) {
+    const int64_t pr = tok * topk + s;
+    const float wt = w[pr];
+    const float4 v = reinterpret_cast<const float4*>(d + (int64_t)pos[pr] * hidden)[c4];
+    acc.x += wt * v.x;
+    acc.y += wt * v.y;
+    acc.z += wt * v.z;
+    acc.w += wt * v.w;
+  }
+  reinterpret_cast<float4*>(y + tok * hidden)[c4] = acc;
+}
+
+struct GroupedGemmRes {
+  const TileEntry* tiles;
+  const int32_t* ntiles;
+  const uint16_t* a;       // fp16 [slots][P][k]
+  int64_t P;
+  int k, n;
+  const uint16_t* trellis;
+  const uint16_t* svh;
+  int slots;
+  int64_t tensor_words;
+  float* y;                // fp32 [slots][P][n]
+  __device__ GemmTask task(int tile, int slot) const {
+    GemmTask T;
+    T.valid = tile < *ntiles;
+    if (!T.valid) return T;
+    const TileEntry te = tiles[tile];
+    T.a = a + ((int64_t)slot * P + te.row0) * k;
+    T.lda = k;
+    T.rows = te.rows;
+    T.trellis = trellis + (int64_t)(te.e * slots + slot) * tensor_words;
+    T.svh = svh + (int64_t)(te.e * slots + slot) * n;
+    T.bias = nullptr;
+    T.y = y + ((int64_t)slot * P + te.row0) * n;
+    T.ldy = n;
+    return T;
+  }
+};
+
+template <int K>
+struct GroupedGemmRun {
+  static hipError_t run(const GroupedGemmRes& r, int max_tiles, hipStream_t s) {
+    hipLaunchKernelGGL((gemm_kernel<K, kGroupedBM, true, GroupedGemmRes>),
+                       dim3(r.n / 128, max_tiles, r.slots), dim3(256), 0, s, r, r.k, r.n);
+    return hipGetLastError();
+  }
+};
+
+// ---------------------------------------------------------------------------
+size_t grouped_workspace(const ArenaDesc& gu, const ArenaDesc& dn, int64_t t, int topk) {
+  const int64_t P = t * topk;
+  if (P <= kGroupedUnitMaxPairs) return unit_layout(gu, dn, P).total;
+  return gemm_layout(gu, dn, P).total;
+}
+
+hipError_t launch_grouped(const ArenaDesc& gu, const ArenaDesc& dn, const uint16_t* x,
+                          const int32_t* ids, const float* w, int64_t t, int topk, float* y,
+                          void* ws, size_t /*ws_bytes*/, hipStream_t s) {
+  const int64_t P = t * topk;
+  const int hidden = gu.k, inter = gu.n;
+  const int64_t words_gu = (int64_t)(gu.k / 16) * (gu.n / 16) * 16 * gu.bits;
+  const int64_t words_dn = (int64_t)(dn.k / 16) * (dn.n / 16) * 16 * dn.bits;
+  unsigned char* base = static_cast<unsigned char*>(ws);
+  hipError_t e;
+  if (P <= kGroupedUnitMaxPairs) {
+    const UnitLayout L = unit_layout(gu, dn, P);
+    float* part_gu = reinterpret_cast<float*>(base + L.part_gu);
+    uint16_t* xd = reinterpret_cast<uint16_t*>(base + L.xd);
+    float* part_dn = reinterpret_cast<float*>(base + L.part_dn);
+    GuUnitRes rg{gu.trellis, gu.suh, words_gu, hidden, inter, x, topk, ids, part_gu, L.s_gu};
+    const int kc_g = hidden / L.s_gu;
+    e = dispatch_bits<GuUnitRun>(gu.bits, rg, hidden, inter, (int)(P * 2), kc_g,
+                                 gemv_lds_bytes(kc_g, 1), s);
+    if (e != hipSuccess) return e;
+    {
+      const int tasks = (int)P * (inter / 128);
+      hipLaunchKernelGGL(gu_unit_epilogue, dim3((tasks + 3) / 4), dim3(256), 0, s, part_gu, L.s_gu,
+                         (int)P, inter, ids, gu.svh, dn.suh, xd);
+      if ((e = hipGetLastError()) != hipSuccess) return e;
+    }
+    DnUnitRes rd{dn.trellis, words_dn, inter, hidden, xd, ids, part_dn, L.s_dn};
+    const int kc_d = inter / L.s_dn;
+    e = dispatch_bits<DnUnitRun>(dn.bits, rd, inter, hidden, (int)P, kc_d, gemv_lds_bytes(kc_d, 1),
+                                 s);
+    if (e != hipSuccess) return e;
+    {
+      const int64_t tasks = t * (hidden / 128);
+      hipLaunchKernelGGL(down_unit_epilogue, dim3((unsigned)((tasks + 3) / 4)), dim3(256), 0, s,
+                         part_dn, L.s_dn, t, topk, hidden, ids, w, dn.svh, y);
+      return hipGetLastError();
+    }
+  }
+
+  const GemmLayout L = gemm_layout(gu, dn, P);
+  const int E = gu.experts;
+  int32_t* counts = reinterpret_cast<int32_t*>(base + L.counts);
+  int32_t* cursor = reinterpret_cast<int32_t*>(base + L.cursor);
+  int32_t* offsets = reinterpret_cast<int32_t*>(base + L.offsets);
+  int32_t* ntiles = reinterpret_cast<int32_t*>(base + L.ntiles);
+  TileEntry* tiles = reinterpret_cast<TileEntry*>(base + L.tiles);
+  int32_t* pos = reinterpret_cast<int32_t*>(base + L.pos);
+  int32_t* sorted = reinterpret_cast<int32_t*>(base + L.sorted);
+  uint16_t* xg = reinterpret_cast<uint16_t*>(base + L.xg);
+  float* gbuf = reinterpret_cast<float*>(base + L.gu);
+  uint16_t* xd = reinterpret_cast<uint16_t*>(base + L.xd);
+  float* dbuf = reinterpret_cast<float*>(base + L.d);
+
+  hipLaunchKernelGGL(zero_i32, dim3((E + 255) / 256), dim3(256), 0, s, counts, E);
+  hipLaunchKernelGGL(zero_i32, dim3((E + 255) / 256), dim3(256), 0, s, cursor, E);
+  hipLaunchKernelGGL(bin_count, dim3((unsigned)((P + 255) / 256)), dim3(256), 0, s, ids, P, counts);
+  hipLaunchKernelGGL(bin_plan, dim3(1), dim3(64), 0, s, counts, E, kGroupedBM, offsets, ntiles,
+                     tiles);
+  hipLaunchKernelGGL(bin_scatter, dim3((unsigned)((P + 255) / 256)), dim3(256), 0, s, ids, P,
+                     offsets, cursor, pos, sorted);
+  {
+    const int64_t tasks = P * 2 * (hidden / 128);
+    hipLaunchKernelGGL(gu_input_transform, dim3((unsigned)((tasks + 3) / 4)), dim3(256), 0, s, x,
+                       topk, P, hidden, sorted, ids, gu.suh, xg);
+  }
+  if ((e = hipGetLastError()) != hipSuccess) return e;
+  GroupedGemmRes rg{tiles, ntiles, xg, P, hidden, inter, gu.trellis, gu.svh, 2, words_gu, gbuf};
+  e = dispatch_bits<GroupedGemmRun>(gu.bits, rg, L.max_tiles, s);
+  if (e != hipSuccess) return e;
+  {
+    const int64_t tasks = P * (inter / 128);
+    hipLaunchKernelGGL(silu_down_transform, dim3((unsigned)((tasks + 3) / 4)), dim3(256), 0, s,
+                       gbuf, P, inter, sorted, ids, dn.suh, xd);
+  }
+  if ((e = hipGetLastError()) != hipSuccess) return e;
+  GroupedGemmRes rd{tiles, ntiles, xd, P, inter, hidden, dn.trellis, dn.svh, 1, words_dn, dbuf};
+  e = dispatch_bits<GroupedGemmRun>(dn.bits, rd, L.max_tiles, s);
+  if (e != hipSuccess) return e;
+  {
+    const int64_t n4 = t * (hidden / 4);
+    hipLaunchKernelGGL(combine_rows, dim3((unsigned)((n4 + 255) / 256)), dim3(256), 0, s, dbuf, pos,
+                       w, t, topk, hidden, y);
+  }
+  return hipGetLastError();
+}
+
+}  // namespace exl3

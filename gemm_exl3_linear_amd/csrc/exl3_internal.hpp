@@ -1,0 +1,69 @@
+// Host-side declarations shared by the kernel files and the C-ABI layer.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stddef.h>
+#include <stdint.h>
+
+namespace exl3 {
+
+// Dispatch a runtime width K (1..8) to a template instantiation.
+template <template <int> class F, typename... Args>
+hipError_t dispatch_bits(int bits, Args&&... args) {
+  switch (bits) {
+    case 1: return F<1>::run(args...);
+    case 2: return F<2>::run(args...);
+    case 3: return F<3>::run(args...);
+    case 4: return F<4>::run(args...);
+    case 5: return F<5>::run(args...);
+    case 6: return F<6>::run(args...);
+    case 7: return F<7>::run(args...);
+    case 8: return F<8>::run(args...);
+    default: return hipErrorInvalidValue;
+  }
+}
+
+// --- reconstruct -----------------------------------------------------------
+hipError_t launch_reconstruct(const uint16_t* trellis, uint16_t* out, int k, int n, int bits,
+                              hipStream_t s);
+
+// --- Hadamard --------------------------------------------------------------
+// out = ((in .* sign_before) H) .* sign_after, blocks of 128, fp32 arithmetic.
+// in_f32 / out_f32 select the element types.  Rows are independent.
+hipError_t launch_hadamard(const void* in, bool in_f32, void* out, bool out_f32, int64_t rows,
+                           int64_t dim, int64_t ld_in, int64_t ld_out,
+                           const uint16_t* sign_before, const uint16_t* sign_after,
+                           hipStream_t s);
+
+// --- dense linear ----------------------------------------------------------
+struct GemvPlan {
+  int splits;      // k ranges (each a multiple of 128 rows)
+  int kc;          // rows of k per workgroup
+  size_t lds;      // dynamic LDS bytes of the main kernel
+  size_t ws;       // workspace bytes (fp32 partials)
+};
+GemvPlan plan_gemv(int k, int n, int m);
+hipError_t launch_gemv(const uint16_t* trellis, const uint16_t* suh, const uint16_t* svh,
+                       const uint16_t* bias, int k, int n, int bits, const uint16_t* x,
+                       int m, int64_t ldx, void* y, int64_t ldy, bool y_f32, void* ws,
+                       const GemvPlan& plan, hipStream_t s);
+
+size_t gemm_workspace(int k, int n, int m);
+hipError_t launch_gemm(const uint16_t* trellis, const uint16_t* suh, const uint16_t* svh,
+                       const uint16_t* bias, int k, int n, int bits, const uint16_t* x,
+                       int m, int64_t ldx, void* y, int64_t ldy, bool y_f32, void* ws,
+                       hipStream_t s);
+
+// --- grouped experts -------------------------------------------------------
+struct ArenaDesc {
+  const uint16_t* trellis;
+  const uint16_t* suh;
+  const uint16_t* svh;
+  int experts, slots, k, n, bits;
+};
+size_t grouped_workspace(const ArenaDesc& gu, const ArenaDesc& dn, int64_t t, int topk);
+hipError_t launch_grouped(const ArenaDesc& gu, const ArenaDesc& dn, const uint16_t* x,
+                          const int32_t* ids, const float* w, int64_t t, int topk, float* y,
+                          void* ws, size_t ws_bytes, hipStream_t s);
+
+}  // namespace exl3

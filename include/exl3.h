@@ -1,0 +1,190 @@
+/*
+ * exl3.h - C ABI of the MI355X (gfx950) EXL3 quantized-linear library.
+ *
+ * The operation (sources: the exl3xpu README, sections "MoE (routed experts)",
+ * "Prefill: int8 linears ..." and "Adding a model"; the Arc 140V MoE post,
+ * sections 1 and 2A-2D; TensorFold issue #832, "Description"):
+ *
+ *   An EXL3 tensor of shape k x n (k = in_features, n = out_features, both
+ *   multiples of 128) stores 16x16 weight tiles as K-bit trellis codes
+ *   (K = 1..8): a uint16 array trellis[k/16][n/16][16*K], plus fp16 sign
+ *   vectors suh[k] and svh[n] and an optional fp16 bias[n].  Decoding a tile
+ *   gives the Hadamard-domain weight W~ (fp16, k x n), and the layer is
+ *
+ *       y = ((x .* suh) Hk  W~  Hn) .* svh (+ bias)
+ *
+ *   where Hd applies the orthonormal 128-point Walsh-Hadamard transform
+ *   (Sylvester order, scaled by 1/sqrt(128)) to each block of 128 consecutive
+ *   elements.
+ *
+ *   Decode of tile (a, b): its 16*K words, read in index order and each word
+ *   most-significant bit first, form a cyclic bitstream of 256*K bits.  State
+ *   j (0..255) is the 16-bit window starting at bit K*j (wrapping around).
+ *   The mul1 codebook (marker EXL3_CODEBOOK_MUL1, the pages' "cb=2") maps a
+ *   state S to fp16_RN((sigma - 510) * 1775 / 2^18), sigma being the sum of
+ *   the four bytes of (S * 0x9E3779) mod 2^32; every value lies within
+ *   +-3.453125.  State j is weight W~[16a + j/16][16b + j%16].
+ *
+ * Conventions for every entry point:
+ *   - Pointers named as device pointers must point to GPU memory of the
+ *     current HIP device; the caller allocates and owns every buffer.  The
+ *     library keeps no pointer after a call returns and allocates nothing.
+ *   - Every call only enqueues work on `stream` (NULL = the default stream):
+ *     no host synchronisation, no read-back of device data.
+ *   - Arguments are validated on the host before anything is enqueued; on any
+ *     error nothing is enqueued and a status other than EXL3_OK is returned.
+ *     There is no fallback to another code path.
+ *   - Device pointers must be 16-byte aligned unless stated otherwise.
+ *   - Calls on different streams may run concurrently; a call must not
+ *     overlap another call that writes the same output or workspace.
+ */
+#ifndef EXL3_H
+#define EXL3_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define EXL3_ABI_VERSION 1
+
+/* The only codebook this library decodes (the pages' "mul1", marker cb=2). */
+#define EXL3_CODEBOOK_MUL1 2
+
+/* Largest supported routing fan-out for exl3_grouped_experts. */
+#define EXL3_MAX_TOPK 16
+
+typedef struct ihipStream_t* exl3_stream_t; /* same type as hipStream_t */
+
+typedef enum exl3_status {
+    EXL3_OK = 0,
+    EXL3_E_INVALID = 1,     /* bad size, width, pointer or alignment */
+    EXL3_E_UNSUPPORTED = 2, /* codebook other than mul1 (fail-closed) */
+    EXL3_E_WORKSPACE = 3,   /* workspace missing or too small */
+    EXL3_E_HIP = 4          /* a HIP launch reported an error */
+} exl3_status;
+
+typedef enum exl3_dtype {
+    EXL3_F16 = 0,
+    EXL3_F32 = 1
+} exl3_dtype;
+
+/* One EXL3 tensor (all pointers are device pointers).
+ *   trellis  uint16 [k/16][n/16][16*bits], row-major, 16-byte aligned
+ *   suh      fp16 [k] (sign applied before the input transform)
+ *   svh      fp16 [n] (sign applied after the output transform)
+ *   bias     fp16 [n] or NULL (added last)
+ *   k, n     multiples of 128 (16 suffices for exl3_reconstruct)
+ *   bits     trellis width K, 1..8
+ *   codebook must be EXL3_CODEBOOK_MUL1                                   */
+typedef struct exl3_weight {
+    const uint16_t* trellis;
+    const uint16_t* suh;
+    const uint16_t* svh;
+    const uint16_t* bias;
+    int32_t k;
+    int32_t n;
+    int32_t bits;
+    int32_t codebook;
+} exl3_weight;
+
+/* A packed arena of per-expert EXL3 tensors, one allocation per tensor kind
+ * (Arc 140V MoE post, section 2A: w13 [E, 2, ...] and w2 [E, 1, ...]).
+ *   trellis  uint16 [experts][slots][k/16][n/16][16*bits]
+ *   suh      fp16 [experts][slots][k]
+ *   svh      fp16 [experts][slots][n]
+ * Width and codebook are uniform over the arena.                          */
+typedef struct exl3_expert_weights {
+    const uint16_t* trellis;
+    const uint16_t* suh;
+    const uint16_t* svh;
+    int32_t experts;
+    int32_t slots;
+    int32_t k;
+    int32_t n;
+    int32_t bits;
+    int32_t codebook;
+} exl3_expert_weights;
+
+/* Returns EXL3_ABI_VERSION of the built library. */
+int32_t exl3_abi_version(void);
+
+/* Static, NUL-terminated description of a status code (never NULL). */
+const char* exl3_status_str(exl3_status status);
+
+/* exl3_reconstruct - decode a whole tensor to W~ (Hadamard domain, no signs).
+ * The exl3xpu README ("Correctness") gates every kernel path on bit-identical
+ * dequantized weights; this entry point exposes the decode for that check.
+ *   w_out  fp16 [k][n] row-major, device pointer, 16-byte aligned.
+ * Requires k, n multiples of 16.  Output is bit-exact by definition.       */
+exl3_status exl3_reconstruct(const exl3_weight* w, uint16_t* w_out, exl3_stream_t stream);
+
+/* exl3_hadamard - out = ((in .* sign_before) Hdim) .* sign_after, row by row
+ * (the standalone randomized Hadamard transform of the exl3xpu README,
+ * "Layout": Hadamard in/out kernels; and the MoE post, section 2C).
+ *   in, out      [rows][ld_*] of `dtype` (EXL3_F16 or EXL3_F32); in-place
+ *                (in == out with equal strides) is allowed
+ *   dim          multiple of 128; transformed in blocks of 128
+ *   ld_in/ld_out row strides in elements, >= dim, multiples of 8
+ *   sign_before, sign_after  fp16 [dim] device pointers or NULL
+ * Arithmetic is fp32; an fp16 output is rounded to nearest.               */
+exl3_status exl3_hadamard(const void* in, void* out, int32_t dtype, int64_t rows, int64_t dim,
+                          int64_t ld_in, int64_t ld_out, const uint16_t* sign_before,
+                          const uint16_t* sign_after, exl3_stream_t stream);
+
+/* Bytes of device workspace exl3_linear needs for m rows of this tensor
+ * (0 if the arguments are invalid). */
+size_t exl3_linear_workspace_size(const exl3_weight* w, int64_t m);
+
+/* exl3_linear - y = ((x .* suh) Hk W~ Hn) .* svh (+ bias).
+ * (exl3xpu README "Layout": the linear op dispatches on the row count; the
+ * GEMM runs in the Hadamard domain per "Prefill: int8 linears ...";
+ * TensorFold issue #832: rows are computed independently of the batch.)
+ *   x      fp16 [m][ldx] device pointer, ldx >= k, ldx multiple of 8
+ *   y      [m][ldy] of y_dtype (EXL3_F16 or EXL3_F32; fp32 outputs are the
+ *          issue's "decodeF32/promptF32" contract), ldy >= n, multiple of 8
+ *   ws     device workspace of at least exl3_linear_workspace_size(w, m)
+ *          bytes (may be NULL when that size is 0)
+ * m == 0 returns EXL3_OK without enqueueing anything.  The kernel (decode
+ * GEMV for m <= 16, MFMA GEMM above) is chosen internally from m; each output
+ * row is computed with the same arithmetic whatever m is.                 */
+exl3_status exl3_linear(const exl3_weight* w, const void* x, int64_t m, int64_t ldx, void* y,
+                        int64_t ldy, int32_t y_dtype, void* ws, size_t ws_bytes,
+                        exl3_stream_t stream);
+
+/* Bytes of device workspace exl3_grouped_experts needs (0 if invalid). */
+size_t exl3_grouped_experts_workspace_size(const exl3_expert_weights* gate_up,
+                                           const exl3_expert_weights* down, int64_t t,
+                                           int32_t topk);
+
+/* exl3_grouped_experts - routed-expert SwiGLU MLP, routed contribution only.
+ * (exl3xpu README "MoE (routed experts)": computed in fp32 with the routing
+ * weight applied to the down-projection output, never to its input; one
+ * launch per projection with routing kept on device; MoE post section 2:
+ * SiLU between the two launches, device-side token binning, fp32 gather.)
+ *   gate_up  arena with slots == 2 (slot 0 = gate, slot 1 = up), k = hidden,
+ *            n = intermediate
+ *   down     arena with slots == 1, k = intermediate, n = hidden, same
+ *            number of experts
+ *   x             fp16 [t][hidden] device pointer (row stride = hidden)
+ *   topk_ids      int32 [t][topk] device pointer, each in [0, experts)
+ *   topk_weights  fp32 [t][topk] device pointer
+ *   y             fp32 [t][hidden] device pointer, overwritten with
+ *                 Y[i] = sum over s in slot order of w[i][s] * down_e(a),
+ *                 a = silu(gate_e(x_i)) * up_e(x_i), e = topk_ids[i][s]
+ *   ws            device workspace of at least the queried size
+ * 1 <= topk <= EXL3_MAX_TOPK.  t == 0 returns EXL3_OK without work.
+ * Out-of-range ids are a contract violation and are not checked on device. */
+exl3_status exl3_grouped_experts(const exl3_expert_weights* gate_up,
+                                 const exl3_expert_weights* down, const void* x,
+                                 const int32_t* topk_ids, const float* topk_weights, int64_t t,
+                                 int32_t topk, float* y, void* ws, size_t ws_bytes,
+                                 exl3_stream_t stream);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* EXL3_H */

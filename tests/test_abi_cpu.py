@@ -1,0 +1,107 @@
+"""C-ABI checks that need no GPU: the library loads, exports what the header
+declares, and its host-side validation and workspace queries behave.  None of
+these calls reaches a HIP API (every invalid call returns before enqueueing)."""
+import ctypes
+
+import pytest
+
+import gemm_exl3_linear_amd as X
+
+
+def _w(k=256, n=256, bits=4, cb=X.CODEBOOK_MUL1, ptr=16):
+    return X._Weight(ptr, ptr, ptr, 0, k, n, bits, cb)
+
+
+def test_library_exports_every_header_function():
+    L = X.lib()
+    names = X.header_functions()
+    assert {"exl3_linear", "exl3_grouped_experts", "exl3_hadamard", "exl3_reconstruct"} <= set(names)
+    for nm in names:
+        assert hasattr(L, nm), nm
+
+
+def test_abi_version_and_status_strings():
+    assert X.abi_version() == 1
+    for s in range(5):
+        assert X.status_str(s)
+    assert "unknown" in X.status_str(99)
+
+
+def test_workspace_queries_are_host_only():
+    L = X.lib()
+    w = _w(5120, 17408, 4)
+    for m in (1, 4, 16):
+        ws = L.exl3_linear_workspace_size(ctypes.byref(w), m)
+        assert ws > 0 and ws % 4 == 0
+    assert L.exl3_linear_workspace_size(ctypes.byref(w), 4096) == 4096 * 5120 * 2
+    assert L.exl3_linear_workspace_size(ctypes.byref(_w(bits=9)), 1) == 0
+    assert L.exl3_linear_workspace_size(ctypes.byref(_w(k=200)), 1) == 0
+    gu = X._Arena(16, 16, 16, 256, 2, 2048, 512, 3, X.CODEBOOK_MUL1)
+    dn = X._Arena(16, 16, 16, 256, 1, 512, 2048, 3, X.CODEBOOK_MUL1)
+    assert L.exl3_grouped_experts_workspace_size(ctypes.byref(gu), ctypes.byref(dn), 1, 8) > 0
+    assert L.exl3_grouped_experts_workspace_size(ctypes.byref(gu), ctypes.byref(dn), 4096, 8) > 0
+    bad = X._Arena(16, 16, 16, 256, 1, 2048, 512, 3, X.CODEBOOK_MUL1)
+    assert L.exl3_grouped_experts_workspace_size(ctypes.byref(bad), ctypes.byref(dn), 1, 8) == 0
+
+
+@pytest.mark.parametrize("kw,expect", [
+    (dict(bits=0), X.EXL3_E_INVALID),
+    (dict(bits=9), X.EXL3_E_INVALID),
+    (dict(cb=1), X.EXL3_E_UNSUPPORTED),
+    (dict(cb=3), X.EXL3_E_UNSUPPORTED),
+    (dict(k=200), X.EXL3_E_INVALID),
+    (dict(n=100), X.EXL3_E_INVALID),
+    (dict(ptr=0), X.EXL3_E_INVALID),
+    (dict(ptr=18), X.EXL3_E_INVALID),
+])
+def test_linear_rejects_before_enqueue(kw, expect):
+    L = X.lib()
+    w = _w(**kw)
+    st = L.exl3_linear(ctypes.byref(w), 16, 1, w.k, 16, w.n, X.EXL3_F16, 0, 0, 0)
+    assert st == expect
+
+
+def test_linear_other_argument_errors():
+    L = X.lib()
+    w = _w()
+    assert L.exl3_linear(ctypes.byref(w), 16, 1, 255, 16, 256, X.EXL3_F16, 0, 0, 0) == X.EXL3_E_INVALID
+    assert L.exl3_linear(ctypes.byref(w), 16, 1, 256, 16, 256, 7, 0, 0, 0) == X.EXL3_E_INVALID
+    assert L.exl3_linear(ctypes.byref(w), 16, -1, 256, 16, 256, X.EXL3_F16, 0, 0, 0) == X.EXL3_E_INVALID
+    assert L.exl3_linear(ctypes.byref(w), 0, 1, 256, 16, 256, X.EXL3_F16, 0, 0, 0) == X.EXL3_E_INVALID
+    # valid shapes but no workspace: refused with the workspace status
+    assert L.exl3_linear(ctypes.byref(w), 16, 1, 256, 16, 256, X.EXL3_F16, 0, 0, 0) == X.EXL3_E_WORKSPACE
+    need = L.exl3_linear_workspace_size(ctypes.byref(w), 1)
+    assert L.exl3_linear(ctypes.byref(w), 16, 1, 256, 16, 256, X.EXL3_F16, 16, need - 4, 0) == X.EXL3_E_WORKSPACE
+    # m == 0 is a no-op
+    assert L.exl3_linear(ctypes.byref(w), 0, 0, 256, 0, 256, X.EXL3_F16, 0, 0, 0) == X.EXL3_OK
+    assert L.exl3_linear(None, 16, 1, 256, 16, 256, X.EXL3_F16, 0, 0, 0) == X.EXL3_E_INVALID
+
+
+def test_reconstruct_and_hadamard_rejects():
+    L = X.lib()
+    assert L.exl3_reconstruct(ctypes.byref(_w(bits=0)), 16, 0) == X.EXL3_E_INVALID
+    assert L.exl3_reconstruct(ctypes.byref(_w(cb=1)), 16, 0) == X.EXL3_E_UNSUPPORTED
+    assert L.exl3_reconstruct(ctypes.byref(_w(k=24)), 16, 0) == X.EXL3_E_INVALID
+    assert L.exl3_reconstruct(ctypes.byref(_w()), 0, 0) == X.EXL3_E_INVALID
+    assert L.exl3_hadamard(16, 16, 0, 4, 100, 128, 128, 0, 0, 0) == X.EXL3_E_INVALID
+    assert L.exl3_hadamard(16, 16, 2, 4, 128, 128, 128, 0, 0, 0) == X.EXL3_E_INVALID
+    assert L.exl3_hadamard(16, 16, 0, 4, 128, 120, 128, 0, 0, 0) == X.EXL3_E_INVALID
+    assert L.exl3_hadamard(0, 16, 0, 4, 128, 128, 128, 0, 0, 0) == X.EXL3_E_INVALID
+    assert L.exl3_hadamard(16, 16, 0, 4, 128, 128, 136, 0, 0, 0) == X.EXL3_E_INVALID
+    assert L.exl3_hadamard(0, 0, 0, 0, 128, 128, 128, 0, 0, 0) == X.EXL3_OK
+
+
+def test_grouped_rejects():
+    L = X.lib()
+    gu = X._Arena(16, 16, 16, 8, 2, 256, 128, 3, X.CODEBOOK_MUL1)
+    dn = X._Arena(16, 16, 16, 8, 1, 128, 256, 3, X.CODEBOOK_MUL1)
+    args = lambda g, d, t, k, ws=0, n=0: L.exl3_grouped_experts(ctypes.byref(g), ctypes.byref(d), 16, 16, 16,
+                                                                   t, k, 16, ws, n, 0)
+    assert args(gu, dn, 1, 0) == X.EXL3_E_INVALID
+    assert args(gu, dn, 1, 17) == X.EXL3_E_INVALID
+    assert args(gu, dn, 1, 2) == X.EXL3_E_WORKSPACE
+    assert args(gu, dn, 0, 2) == X.EXL3_OK
+    dn_bad = X._Arena(16, 16, 16, 7, 1, 128, 256, 3, X.CODEBOOK_MUL1)
+    assert args(gu, dn_bad, 1, 2) == X.EXL3_E_INVALID
+    gu_cb = X._Arena(16, 16, 16, 8, 2, 256, 128, 3, 1)
+    assert args(gu_cb, dn, 1, 2) == X.EXL3_E_UNSUPPORTED

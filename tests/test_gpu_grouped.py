@@ -1,0 +1,100 @@
+"""GPU parity of exl3_grouped_experts against the float64 oracle across
+routing patterns, both regimes (per-pair units and grouped GEMM)."""
+import numpy as np
+import pytest
+
+import synth
+from oracle import exl3_oracle as O
+from tests import _gpu as G
+
+pytestmark = pytest.mark.gpu
+TOL = 2e-3
+
+
+def _run(m, ids=None, w=None):
+    import torch
+    import gemm_exl3_linear_amd as X
+    ids = m["ids"] if ids is None else ids
+    w = m["weights"] if w is None else w
+    gu = X.Exl3Arena.from_numpy(m["gate_up"], G.dev())
+    dn = X.Exl3Arena.from_numpy(m["down"], G.dev())
+    y = X.exl3_grouped_experts(G.to_dev(m["x"]), G.to_dev(ids.astype(np.int32)),
+                               G.to_dev(w.astype(np.float32)), gu, dn)
+    torch.cuda.synchronize()
+    return y.double().cpu().numpy()
+
+
+def _ref(m, ids=None, w=None, tokens=None):
+    ids = m["ids"] if ids is None else ids
+    w = m["weights"] if w is None else w
+    x = m["x"]
+    if tokens is not None:
+        x, ids, w = x[tokens], ids[tokens], w[tokens]
+    return O.grouped_experts(x, ids, w, m["gate_up"], m["down"])
+
+
+def _small(t, experts=16, topk=4, hidden=256, inter=128, bits=3, seed=40):
+    return synth.moe_inputs(seed + t, t, experts=experts, topk=topk, hidden=hidden, inter=inter, bits=bits)
+
+
+@pytest.mark.parametrize("t", [1, 2, 4, 16, 64])
+def test_random_routing(t):
+    m = _small(t)
+    err = O.rel_frobenius(_run(m), _ref(m))
+    assert err < TOL, err
+
+
+@pytest.mark.parametrize("t", [3, 40])
+def test_all_tokens_same_experts(t):
+    m = _small(t)
+    ids = np.tile(np.array([5, 1, 9, 0], np.int32), (t, 1))
+    err = O.rel_frobenius(_run(m, ids=ids), _ref(m, ids=ids))
+    assert err < TOL, err
+
+
+@pytest.mark.parametrize("t", [2, 33])
+def test_top1_unit_weight(t):
+    m = _small(t, topk=1)
+    w = np.ones((t, 1), np.float32)
+    err = O.rel_frobenius(_run(m, w=w), _ref(m, w=w))
+    assert err < TOL, err
+
+
+@pytest.mark.parametrize("t", [2, 40])
+def test_zero_weights_exact_zero(t):
+    m = _small(t)
+    w = np.zeros_like(m["weights"])
+    assert (_run(m, w=w) == 0).all()
+
+
+def test_unused_expert_has_no_effect():
+    m = _small(24)
+    used = set(np.unique(m["ids"]).tolist())
+    unused = [e for e in range(16) if e not in used]
+    y = _run(m)
+    if unused:
+        m2 = dict(m); m2["gate_up"] = dict(m["gate_up"]); m2["gate_up"]["trellis"] = m["gate_up"]["trellis"].copy()
+        m2["gate_up"]["trellis"][unused[0]] ^= 0x3C3C
+        np.testing.assert_array_equal(_run(m2), y)
+
+
+@pytest.mark.parametrize("t", [1, 50])
+def test_max_topk(t):
+    m = _small(t, experts=32, topk=16)
+    err = O.rel_frobenius(_run(m), _ref(m))
+    assert err < TOL, err
+
+
+@pytest.mark.parametrize("t", [1, 4])
+def test_moe_256x2048x512_k3_small_t(t):
+    m = synth.moe_inputs(synth.SEED_MOE_256x2048x512, t)
+    err = O.rel_frobenius(_run(m), _ref(m))
+    assert err < TOL, err
+
+
+def test_moe_256x2048x512_k3_t4096_sampled_tokens():
+    m = synth.moe_inputs(synth.SEED_MOE_256x2048x512, 4096)
+    y = _run(m)
+    tokens = np.sort(np.random.default_rng(1).choice(4096, 12, replace=False))
+    err = O.rel_frobenius(y[tokens], _ref(m, tokens=tokens))
+    assert err < TOL, err

@@ -1,0 +1,144 @@
+"""GPU parity of exl3_linear against the float64 oracle (relative Frobenius
+error <= 2e-3 over the whole output), plus the invariants the arithmetic makes
+bit-exact on the GPU."""
+import numpy as np
+import pytest
+
+import synth
+from oracle import exl3_oracle as O
+from tests import _gpu as G
+
+pytestmark = pytest.mark.gpu
+TOL = 2e-3
+
+
+def _run(d, m=None, out_dtype=None, bias=None):
+    import torch
+    import gemm_exl3_linear_amd as X
+    x = d["x"] if m is None else d["x"][:m]
+    y = X.exl3_linear(G.to_dev(x), G.weight(d, bias=bias), out_dtype=out_dtype or torch.float16)
+    torch.cuda.synchronize()
+    return y
+
+
+def _ref(d, m=None, bias=None, W=None):
+    x = d["x"] if m is None else d["x"][:m]
+    return O.linear(x, d["trellis"], d["suh"], d["svh"], d["bits"], bias=bias, w_decoded=W)
+
+
+def test_single_tensor_2048x512_k4_m1():
+    d = G.linear_case(synth.SEED_SINGLE_2048x512, 1, 2048, 512, 4)
+    y = _run(d)
+    err = O.rel_frobenius(y.double().cpu().numpy(), _ref(d, W=G.decoded(synth.SEED_SINGLE_2048x512, 1, 2048, 512, 4)))
+    assert err < TOL, err
+
+
+@pytest.mark.parametrize("bits", range(1, 9))
+@pytest.mark.parametrize("m", [1, 3, 16])
+def test_gemv_all_widths(bits, m):
+    d = synth.linear_inputs(200 + bits, m, 1024, 384, bits)
+    y = _run(d)
+    err = O.rel_frobenius(y.double().cpu().numpy(), _ref(d))
+    assert err < TOL, err
+
+
+@pytest.mark.parametrize("bits", [2, 3, 4, 8])
+@pytest.mark.parametrize("m", [17, 64, 100, 300])
+def test_gemm_ragged_rows(bits, m):
+    d = synth.linear_inputs(300 + bits, m, 512, 256, bits)
+    y = _run(d)
+    err = O.rel_frobenius(y.double().cpu().numpy(), _ref(d))
+    assert err < TOL, err
+
+
+@pytest.mark.parametrize("m", [1, 5, 40])
+def test_fp32_output_and_bias(m):
+    import torch
+    d = synth.linear_inputs(400 + m, m, 256, 512, 4)
+    bias = np.linspace(-2, 2, 512).astype(np.float16)
+    y = _run(d, out_dtype=torch.float32, bias=bias)
+    assert y.dtype == torch.float32
+    err = O.rel_frobenius(y.double().cpu().numpy(), _ref(d, bias=bias))
+    assert err < TOL, err
+
+
+def test_empty_batch_is_noop():
+    import torch
+    import gemm_exl3_linear_amd as X
+    d = synth.linear_inputs(1, 1, 128, 128, 4)
+    y = torch.full((0, 128), 7.0, dtype=torch.float16, device=G.dev())
+    X.exl3_linear(G.to_dev(d["x"][:0]), G.weight(d), out=y)
+    torch.cuda.synchronize()
+
+
+@pytest.mark.parametrize("m", [1, 16, 40])
+def test_sign_invariances_bit_exact(m):
+    import torch
+    d = synth.linear_inputs(500 + m, m, 512, 384, 4)
+    y = _run(d)
+    d2 = dict(d)
+    d2["x"] = d["x"].copy(); d2["suh"] = d["suh"].copy()
+    d2["x"][:, 11] = -d2["x"][:, 11]; d2["suh"][11] = -d2["suh"][11]
+    np.testing.assert_array_equal(G.f16_bits(_run(d2)), G.f16_bits(y))
+    d3 = dict(d); d3["svh"] = d["svh"].copy(); d3["svh"][5] = -d3["svh"][5]
+    y3 = _run(d3)
+    assert torch.equal(y3[:, 5], -y[:, 5])
+    keep = [c for c in range(384) if c != 5]
+    assert torch.equal(y3[:, keep], y[:, keep])
+    d4 = dict(d); d4["x"] = -d["x"]
+    assert torch.equal(_run(d4), -y)
+
+
+@pytest.mark.parametrize("m", [1, 7, 33])
+def test_constant_trellis_exact_zeros(m):
+    d = synth.linear_inputs(600 + m, m, 384, 256, 4)
+    d = dict(d); d["trellis"] = np.zeros_like(d["trellis"])
+    y = _run(d).float().cpu().numpy()
+    mask = np.ones(256, bool); mask[::128] = False
+    assert (y[:, mask] == 0).all()
+    err = O.rel_frobenius(y, _ref(d))
+    assert err < TOL, err
+
+
+def test_row_invariance_gemv():
+    # every row of an m <= 16 call equals the same row computed alone, bit for bit
+    d = synth.linear_inputs(700, 16, 1024, 512, 4)
+    y16 = G.f16_bits(_run(d))
+    for m in (1, 4, 9):
+        ym = G.f16_bits(_run(d, m=m))
+        np.testing.assert_array_equal(ym, y16[:m])
+
+
+def test_row_invariance_gemm():
+    d = synth.linear_inputs(701, 300, 512, 256, 3)
+    y = G.f16_bits(_run(d))
+    ys = G.f16_bits(_run(d, m=20))
+    np.testing.assert_array_equal(ys, y[:20])
+
+
+def test_repeat_bit_identical():
+    d = synth.linear_inputs(702, 4, 2048, 1024, 4)
+    a = G.f16_bits(_run(d))
+    for _ in range(5):
+        np.testing.assert_array_equal(G.f16_bits(_run(d)), a)
+
+
+# --- full-size workloads, in the launch configuration the benchmark times ---
+@pytest.mark.parametrize("m", [1, 4, 16])
+def test_dense_decode_5120x17408_k4(m):
+    d = G.linear_case(synth.SEED_DENSE_5120x17408, 16, 5120, 17408, 4)
+    y = _run(d, m=m)
+    W = G.decoded(synth.SEED_DENSE_5120x17408, 16, 5120, 17408, 4)
+    err = O.rel_frobenius(y.double().cpu().numpy(), _ref(d, m=m, W=W))
+    assert err < TOL, err
+
+
+def test_dense_prefill_4096x5120x17408_k4_sampled_rows():
+    d = G.linear_case(synth.SEED_PREFILL_4096x5120x17408, 4096, 5120, 17408, 4)
+    y = _run(d)
+    rows = np.random.default_rng(0).choice(4096, 64, replace=False)
+    rows.sort()
+    W = O.decode_tensor(d["trellis"], 4)
+    sub = dict(d); sub["x"] = d["x"][rows]
+    err = O.rel_frobenius(y[rows].double().cpu().numpy(), _ref(sub, W=W))
+    assert err < TOL, err
