@@ -1,0 +1,227 @@
+"""Benchmark of the EXL3 linear layer on one MI355X.
+
+Headline workload: the dense decode GEMV of a k=5120 x n=17408 EXL3 tensor at
+K=4 bits with one activation row (M=1): one step is one exl3_linear call
+(input sign + transform, trellis stream and decode, contraction, split-k sum,
+output transform + svh, cast).  24 copies of the trellis (1.07 GB) are used
+in rotation so that successive steps read HBM, not the 256 MB last-level
+cache.  `value` is the whole-job rate of the metric (algorithmic bytes of the
+call per second); `roofline` reports the single kernel the call launches,
+timed per launch with HIP events on the launch stream.  The float64 oracle is
+timed on the host on the same workload as the CPU baseline.
+
+python bench.py [--gpus 1] [--steps K] [--warmup W] [--no-cpu-baseline]
+                [--no-secondary] [--profile-pass]
+"""
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+HBM_PEAK_GBS = 8000.0          # MI355X HBM3E, published
+MFMA_F16_PEAK_TFLOPS = 2500.0  # MI355X dense fp16 matrix, published
+METRIC = "EXL3 GEMV HBM GB/s (% of 8 TB/s) at M=1; prefill GEMM TFLOPS (% MFMA)"
+GEMV_SOURCES = ["gemm_exl3_linear_amd/csrc/exl3_device.hpp", "gemm_exl3_linear_amd/csrc/exl3_gemv.hpp",
+                "gemm_exl3_linear_amd/csrc/exl3_gemv.hip"]
+TRAFFIC_FILE = os.path.join(ROOT, "profiles", "gemv_dense_5120x17408_k4_m1_traffic.json")
+
+
+def gemv_source_hash() -> str:
+    h = hashlib.sha256()
+    for p in GEMV_SOURCES:
+        with open(os.path.join(ROOT, p), "rb") as f:
+            h.update(f.read())
+    return h.hexdigest()[:16]
+
+
+def linear_bytes(k, n, bits, m, out_bytes=2):
+    """Algorithmic bytes of one call: trellis + suh + svh + x + y, each once."""
+    return k * n * bits // 8 + 2 * k + 2 * n + 2 * m * k + out_bytes * m * n
+
+
+def measured_traffic():
+    """HBM bytes per launch from the committed rocprofv3 counter summary, or
+    None when the GEMV sources changed after the counters were taken."""
+    try:
+        with open(TRAFFIC_FILE) as f:
+            t = json.load(f)
+    except (OSError, ValueError):
+        return None
+    if t.get("gemv_source_hash") != gemv_source_hash():
+        return None
+    return t.get("hbm_bytes_per_launch")
+
+
+def time_calls(fn, steps, warmup, stream):
+    """Returns (mean per-launch time from per-call event pairs, whole-loop time)."""
+    import torch
+    for i in range(warmup):
+        fn(i)
+    torch.cuda.synchronize()
+    starts = [torch.cuda.Event(enable_timing=True) for _ in range(steps)]
+    ends = [torch.cuda.Event(enable_timing=True) for _ in range(steps)]
+    t0 = torch.cuda.Event(enable_timing=True)
+    t1 = torch.cuda.Event(enable_timing=True)
+    t0.record(stream)
+    for i in range(steps):
+        starts[i].record(stream)
+        fn(warmup + i)
+        ends[i].record(stream)
+    t1.record(stream)
+    torch.cuda.synchronize()
+    per = sum(s.elapsed_time(e) for s, e in zip(starts, ends)) / steps
+    return per * 1e-3, t0.elapsed_time(t1) * 1e-3
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=1000)
+    ap.add_argument("--warmup", type=int, default=100)
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-secondary", action="store_true")
+    ap.add_argument("--profile-pass", action="store_true",
+                    help="short run for counter collection: a plain copy of known size, then 50 GEMV calls")
+    args = ap.parse_args()
+    world = int(os.environ.get("WORLD_SIZE", "1"))
+    if args.gpus != 1 or world != 1:
+        print(f"bench.py measures one GPU: this build has no multi-GPU path (asked for --gpus {args.gpus}, "
+              f"WORLD_SIZE {world}).", file=sys.stderr)
+        sys.exit(2)
+
+    import numpy as np
+    import torch
+
+    import gemm_exl3_linear_amd as X
+    import synth
+
+    assert torch.cuda.is_available(), "bench.py needs a GPU"
+    X.lib()  # fail loudly if the library is missing
+    dev = torch.device("cuda:0")
+    stream = torch.cuda.current_stream()
+    k, n, bits = 5120, 17408, 4
+    d = synth.linear_inputs(synth.SEED_DENSE_5120x17408, 16, k, n, bits)
+    trellis_bytes = k * n * bits // 8
+    copies = -(-(1 << 30) // trellis_bytes)
+    t_host = torch.from_numpy(d["trellis"].view(np.int16).copy())
+    trellis = [t_host.to(dev) for _ in range(copies)]
+    suh = torch.from_numpy(d["suh"]).to(dev)
+    svh = torch.from_numpy(d["svh"]).to(dev)
+    xs = torch.from_numpy(d["x"]).to(dev)
+    weights = [X.Exl3Weight(t, suh, svh, bits) for t in trellis]
+    ws = torch.zeros(max(X.exl3_linear_workspace_size(weights[0], m) for m in (1, 4, 16)),
+                     dtype=torch.uint8, device=dev)
+    y = torch.empty((16, n), dtype=torch.float16, device=dev)
+
+    def gemv(m):
+        def call(i):
+            X.exl3_linear(xs[:m], weights[i % copies], out=y[:m], workspace=ws, stream=stream)
+        return call
+
+    if args.profile_pass:
+        a = torch.empty(256 << 20, dtype=torch.uint8, device=dev)
+        b = torch.empty_like(a)
+        for _ in range(5):
+            b.copy_(a)
+        for i in range(50):
+            gemv(1)(i)
+        torch.cuda.synchronize()
+        print(json.dumps({"profile_pass": True, "copy_bytes": a.numel(), "gemv_calls": 50,
+                          "gemv_source_hash": gemv_source_hash()}))
+        return
+
+    per_launch, total = time_calls(gemv(1), args.steps, args.warmup, stream)
+    nbytes = linear_bytes(k, n, bits, 1)
+    value = nbytes * args.steps / total / 1e9
+    achieved = nbytes / per_launch / 1e9
+
+    secondary = {}
+    if not args.no_secondary:
+        for m in (4, 16):
+            pl, _ = time_calls(gemv(m), 200, 20, stream)
+            gb = linear_bytes(k, n, bits, m) / pl / 1e9
+            secondary[f"gemv_m{m}"] = {"GB/s": round(gb, 1), "frac_hbm": round(gb / HBM_PEAK_GBS, 4),
+                                       "us_per_call": round(pl * 1e6, 2)}
+        # prefill: M=4096 (input transform kernel + fused decode/MFMA GEMM kernel)
+        dp = synth.linear_inputs(synth.SEED_PREFILL_4096x5120x17408, 4096, k, n, bits)
+        wp = X.Exl3Weight.from_numpy(dp["trellis"], dp["suh"], dp["svh"], bits, device=dev)
+        xp = torch.from_numpy(dp["x"]).to(dev)
+        wsp = torch.zeros(X.exl3_linear_workspace_size(wp, 4096), dtype=torch.uint8, device=dev)
+        yp = torch.empty((4096, n), dtype=torch.float16, device=dev)
+        pl, _ = time_calls(lambda i: X.exl3_linear(xp, wp, out=yp, workspace=wsp, stream=stream), 20, 3, stream)
+        tf = 2.0 * 4096 * k * n / pl / 1e12
+        secondary["prefill_m4096"] = {"TFLOP/s": round(tf, 1), "frac_mfma_f16": round(tf / MFMA_F16_PEAK_TFLOPS, 4),
+                                      "ms_per_call": round(pl * 1e3, 3)}
+        del wp, xp, wsp, yp
+        # routed experts: 256 experts, top-8, hidden 2048, intermediate 512, K=3
+        for t in (1, 4096):
+            mo = synth.moe_inputs(synth.SEED_MOE_256x2048x512, t)
+            gu = X.Exl3Arena.from_numpy(mo["gate_up"], dev)
+            dn = X.Exl3Arena.from_numpy(mo["down"], dev)
+            xm = torch.from_numpy(mo["x"]).to(dev)
+            ids = torch.from_numpy(mo["ids"]).to(dev)
+            wt = torch.from_numpy(mo["weights"]).to(dev)
+            wsm = torch.zeros(X.exl3_grouped_experts_workspace_size(gu, dn, t, 8), dtype=torch.uint8, device=dev)
+            ym = torch.empty((t, 2048), dtype=torch.float32, device=dev)
+            reps = 200 if t == 1 else 10
+            pl, _ = time_calls(lambda i: X.exl3_grouped_experts(xm, ids, wt, gu, dn, out=ym, workspace=wsm,
+                                                                stream=stream), reps, 3, stream)
+            flops = 2.0 * t * 8 * 3 * 2048 * 512
+            secondary[f"moe_t{t}"] = {"us_per_call": round(pl * 1e6, 2),
+                                      "TFLOP/s": round(flops / pl / 1e12, 2)}
+            del gu, dn, xm, ids, wt, wsm, ym
+
+    cpu = None
+    if not args.no_cpu_baseline:
+        import threadpoolctl
+        from oracle import exl3_oracle as O
+        x1 = d["x"][:1]
+        reps, t_cpu = 0, 0.0
+        while reps < 3 and (reps == 0 or t_cpu < 10.0):
+            t0 = time.perf_counter()
+            O.linear(x1, d["trellis"], d["suh"], d["svh"], bits)
+            t_cpu += time.perf_counter() - t0
+            reps += 1
+        info = threadpoolctl.threadpool_info()
+        threads = max([i.get("num_threads", 1) for i in info] + [1])
+        cpu = {"value": round(nbytes * reps / t_cpu / 1e9, 4), "unit": "GB/s", "cores": threads,
+               "kind": "oracle",
+               "sample": f"full workload (k=5120, n=17408, K=4, M=1), {reps} pass(es) of the float64 oracle "
+                         f"(vectorised decode single-threaded, matrix product on {threads} BLAS threads), "
+                         f"{t_cpu:.1f} s, host os.cpu_count()={os.cpu_count()}"}
+
+    traffic = measured_traffic()
+    out = {
+        "metric": METRIC,
+        "value": round(value, 1),
+        "unit": "GB/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(total / args.steps * 1e3, 5),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "f16",
+        "data": "synthetic",
+        "config": {"workload": "dense decode GEMV, EXL3 k=5120 n=17408 K=4, M=1, fp16 in/out",
+                   "k": k, "n": n, "bits": bits, "m": 1, "weight_copies_rotated": copies,
+                   "algorithmic_bytes_per_call": nbytes},
+        "roofline": {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                     "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": traffic,
+                     "kernel": "gemv_kernel<4, DenseGemvRes>", "us_per_launch": round(per_launch * 1e6, 3)},
+        "cpu_baseline": cpu,
+        "secondary": secondary,
+    }
+    print(json.dumps(out))
+
+
+if __name__ == "__main__":
+    main()

@@ -224,7 +224,7 @@ def exl3_linear(x, w: Exl3Weight, out_dtype=None, out=None, workspace=None, stre
     ydt = {torch.float16: EXL3_F16, torch.float32: EXL3_F32}[out.dtype]
     need = exl3_linear_workspace_size(w, m)
     if workspace is None and need:
-        workspace = torch.empty(need, dtype=torch.uint8, device=x.device)
+        workspace = torch.zeros(need, dtype=torch.uint8, device=x.device)
     wsb = 0 if workspace is None else workspace.numel() * workspace.element_size()
     cw = w._c()
     _check(lib().exl3_linear(ctypes.byref(cw), _ptr(x), m, x.stride(0), _ptr(out), out.stride(0), ydt,
@@ -248,7 +248,7 @@ def exl3_grouped_experts(x, topk_ids, topk_weights, gate_up: Exl3Arena, down: Ex
         out = torch.empty((t, down.n), dtype=torch.float32, device=x.device)
     need = exl3_grouped_experts_workspace_size(gate_up, down, t, topk)
     if workspace is None and need:
-        workspace = torch.empty(need, dtype=torch.uint8, device=x.device)
+        workspace = torch.zeros(need, dtype=torch.uint8, device=x.device)
     wsb = 0 if workspace is None else workspace.numel() * workspace.element_size()
     a, b = gate_up._c(), down._c()
     _check(lib().exl3_grouped_experts(ctypes.byref(a), ctypes.byref(b), _ptr(x), _ptr(topk_ids),

@@ -5,7 +5,7 @@
 #include <stdio.h>
 #include <stdlib.h>
 
-#include "../../include/exl3.h"
+#include "exl3.h"
 #include "exl3_gemv.hpp"
 #include "exl3_internal.hpp"
 

@@ -55,12 +55,18 @@ struct DenseGemmRun {
   }
 };
 
-size_t gemm_workspace(int k, int /*n*/, int m) { return (size_t)m * k * sizeof(uint16_t); }
+// The workspace starts with the same arrival-counter region as the decode
+// GEMV's (left untouched here, so it stays zero), followed by x' (fp16 [m][k]).
+static size_t counter_region(int n) { return ((size_t)(n / 128) * 4 + 255) & ~(size_t)255; }
+
+size_t gemm_workspace(int k, int n, int m) {
+  return counter_region(n) + (size_t)m * k * sizeof(uint16_t);
+}
 
 hipError_t launch_gemm(const uint16_t* trellis, const uint16_t* suh, const uint16_t* svh,
                        const uint16_t* bias, int k, int n, int bits, const uint16_t* x, int m,
                        int64_t ldx, void* y, int64_t ldy, bool y_f32, void* ws, hipStream_t s) {
-  uint16_t* xp = static_cast<uint16_t*>(ws);
+  uint16_t* xp = reinterpret_cast<uint16_t*>(static_cast<unsigned char*>(ws) + counter_region(n));
   hipError_t e = launch_hadamard(x, false, xp, false, m, k, ldx, k, suh, nullptr, s);
   if (e != hipSuccess) return e;
   DenseGemmRes r{xp, k, m, choose_bm(m), trellis, svh, bias, y, ldy, y_f32};

@@ -1,7 +1,8 @@
 // Decode-GEMV kernel template shared by the dense linear and the grouped
-// experts (see exl3_gemv.hip for the design).  A resolver R maps
-// (blockIdx.z, blockIdx.y) to the tensor, activations and workspace slice of
-// one workgroup.
+// experts (design notes in exl3_gemv.hip).  A resolver R supplies, per
+// workgroup, the tensor, the activations and the partial-sum slice, and
+// implements the finishing step that the last-arriving workgroup of an
+// output group runs (split-k sum in a fixed order, output transform, ...).
 #pragma once
 
 #include "exl3_device.hpp"
@@ -23,9 +24,7 @@ constexpr int kGemvTargetWorkgroups = 1024;
 
 size_t gemv_lds_bytes(int kc, int m);
 int gemv_choose_splits(int k, int groups, int m, int target_wgs);
-hipError_t launch_gemv_epilogue(const float* partial, int splits, int m, int n,
-                                const uint16_t* svh, const uint16_t* bias, void* y, int64_t ldy,
-                                bool y_f32, hipStream_t s);
+int gemv_prefetch(int kc);
 
 // ---------------------------------------------------------------------------
 // prologue: x' = (x .* suh) H over the workgroup's k range into LDS, layout
@@ -56,83 +55,105 @@ __device__ __forceinline__ void gemv_prologue(const GemvTask& T, int k0, int kc,
   }
 }
 
-template <int K, class R>
+// Sum of the fp32 partial slices s = 0..splits-1 (fixed order) for the two
+// columns col, col+1 of one row; slices are `stride` floats apart.
+__device__ __forceinline__ void sum_partials(const float* p, int splits, int64_t stride, float& a,
+                                             float& b) {
+  a = 0.f;
+  b = 0.f;
+  for (int s = 0; s < splits; ++s) {
+    const float2 v = *reinterpret_cast<const float2*>(p + (int64_t)s * stride);
+    a += v.x;
+    b += v.y;
+  }
+}
+
+// One k tile of one wave: decode the lane's row pair, hand the k-pairs to the
+// matrix cores through the wave's LDS transpose region, accumulate.
+template <int K>
+__device__ __forceinline__ void gemv_tile(const uint32_t (&D)[K], int kt, int m, const uint16_t* xs,
+                                          uint32_t* tr, uint32_t* my, int g, int j,
+                                          float4_t (&acc)[8]) {
+  const uint32_t spill = spill_from_next(D[0]);
+  uint32_t wp[16];
+  decode_rowpair<K>(D, spill, wp);
+  uint4* my4 = reinterpret_cast<uint4*>(my);
+  my4[0] = make_uint4(wp[0], wp[1], wp[2], wp[3]);
+  my4[1] = make_uint4(wp[4], wp[5], wp[6], wp[7]);
+  my4[2] = make_uint4(wp[8], wp[9], wp[10], wp[11]);
+  my4[3] = make_uint4(wp[12], wp[13], wp[14], wp[15]);
+  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+  __builtin_amdgcn_wave_barrier();
+  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+  half4_t av = {0, 0, 0, 0};
+  if (j < m) av = *reinterpret_cast<const half4_t*>(xs + ((kt * m + j) << 4) + 4 * g);
+#pragma unroll
+  for (int q = 0; q < 8; ++q) {
+    const uint32_t b0 = tr[(q * 8 + 2 * g) * 20 + j];
+    const uint32_t b1 = tr[(q * 8 + 2 * g + 1) * 20 + j];
+    const uint2 bb = make_uint2(b0, b1);
+    const half4_t bv = __builtin_bit_cast(half4_t, bb);
+    acc[q] = __builtin_amdgcn_mfma_f32_16x16x16f16(av, bv, acc[q], 0, 0, 0);
+  }
+  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+  __builtin_amdgcn_wave_barrier();
+  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+}
+
+// PF = loads kept in flight per lane; the per-wave trip count kc/64 must be a
+// multiple of PF (the planner guarantees it), so the loop has no tail and no
+// branch around its loads.
+template <int K, int PF, class R>
 __global__ __launch_bounds__(256) void gemv_kernel(R r, int k, int n, int kc) {
   extern __shared__ __align__(16) unsigned char smem[];
+  __shared__ int last_flag;
   const GemvTask T = r.task(blockIdx.z, blockIdx.y);
   if (!T.valid) return;  // uniform over the workgroup
   const int m = T.m;
   const int nb = blockIdx.x;
   const int k0 = blockIdx.y * kc;
-  const int ktiles = kc >> 4;
   const int nt = n >> 4;
   uint16_t* xs = reinterpret_cast<uint16_t*>(smem);
   const size_t xs_bytes = ((size_t)kc * m * 2 + 15) & ~(size_t)15;
   uint32_t* tr_all = reinterpret_cast<uint32_t*>(smem + xs_bytes);
   float* red = reinterpret_cast<float*>(smem + xs_bytes);
 
-  gemv_prologue(T, k0, kc, xs);
-  __syncthreads();
-
-  const int wave = threadIdx.x >> 6;
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int lane = threadIdx.x & 63;
   const int t = lane >> 3, p = lane & 7;    // decode role: n-tile, row pair
   const int g = lane >> 4, j = lane & 15;   // MFMA role: k group, row/column
   uint32_t* tr = tr_all + wave * (64 * 20);
   uint32_t* my = tr + (t * 8 + p) * 20;
 
-  // lane's row pair in k tile kt: dword offset ((k0/16 + kt) * nt + nb*8 + t) * 8K + K p
+  // wave w handles k tiles w, w+4, w+8, ... of the range; iteration it -> tile w + 4 it
   const uint32_t* tbase = reinterpret_cast<const uint32_t*>(T.trellis) +
-                          ((int64_t)(k0 >> 4) * nt + nb * 8 + t) * (8 * K) + K * p;
-  const int64_t kt_stride = (int64_t)nt * (8 * K);
+                          ((int64_t)((k0 >> 4) + wave) * nt + nb * 8 + t) * (8 * K) + K * p;
+  const int64_t it_stride = (int64_t)4 * nt * (8 * K);
+  const int cnt = kc >> 6;
+
+  // the first PF trellis loads go out before the prologue so that their
+  // latency overlaps the input transform
+  uint32_t ring[PF][K];
+#pragma unroll
+  for (int s = 0; s < PF; ++s) load_rowpair<K>(tbase + s * it_stride, ring[s]);
+
+  gemv_prologue(T, k0, kc, xs);
+  __syncthreads();
 
   float4_t acc[8];
 #pragma unroll
   for (int q = 0; q < 8; ++q) acc[q] = float4_t{0.f, 0.f, 0.f, 0.f};
 
-  const int cnt = (ktiles - wave + 3) >> 2;  // k tiles wave, wave+4, ...
-  constexpr int PF = (K <= 4) ? 8 : 4;
-  uint32_t ring[PF][K];
-#pragma unroll
-  for (int s = 0; s < PF; ++s)
-    if (s < cnt) load_rowpair<K>(tbase + (int64_t)(wave + 4 * s) * kt_stride, ring[s]);
-
   for (int base = 0; base < cnt; base += PF) {
 #pragma unroll
     for (int s = 0; s < PF; ++s) {
       const int it = base + s;
-      if (it < cnt) {
-        uint32_t D[K];
-#pragma unroll
-        for (int q = 0; q < K; ++q) D[q] = ring[s][q];
-        if (it + PF < cnt)
-          load_rowpair<K>(tbase + (int64_t)(wave + 4 * (it + PF)) * kt_stride, ring[s]);
-        const int kt = wave + 4 * it;
-        const uint32_t spill = spill_from_next(D[0]);
-        uint32_t wp[16];
-        decode_rowpair<K>(D, spill, wp);
-        uint4* my4 = reinterpret_cast<uint4*>(my);
-        my4[0] = make_uint4(wp[0], wp[1], wp[2], wp[3]);
-        my4[1] = make_uint4(wp[4], wp[5], wp[6], wp[7]);
-        my4[2] = make_uint4(wp[8], wp[9], wp[10], wp[11]);
-        my4[3] = make_uint4(wp[12], wp[13], wp[14], wp[15]);
-        __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
-        __builtin_amdgcn_wave_barrier();
-        __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
-        half4_t av = {0, 0, 0, 0};
-        if (j < m) av = *reinterpret_cast<const half4_t*>(xs + ((kt * m + j) << 4) + 4 * g);
-#pragma unroll
-        for (int q = 0; q < 8; ++q) {
-          const uint32_t b0 = tr[(q * 8 + 2 * g) * 20 + j];
-          const uint32_t b1 = tr[(q * 8 + 2 * g + 1) * 20 + j];
-          const uint2 bb = make_uint2(b0, b1);
-          const half4_t bv = __builtin_bit_cast(half4_t, bb);
-          acc[q] = __builtin_amdgcn_mfma_f32_16x16x16f16(av, bv, acc[q], 0, 0, 0);
-        }
-        __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
-        __builtin_amdgcn_wave_barrier();
-        __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
-      }
+      gemv_tile<K>(ring[s], wave + 4 * it, m, xs, tr, my, g, j, acc);
+      // refill the slot just consumed (same registers, so no copy and no wait
+      // at the loop edge); the last block re-reads the final tile, a cache
+      // hit, instead of branching
+      const int nxt = (it + PF < cnt) ? (it + PF) : (cnt - 1);
+      load_rowpair<K>(tbase + nxt * it_stride, ring[s]);
     }
   }
 
@@ -155,6 +176,32 @@ __global__ __launch_bounds__(256) void gemv_kernel(R r, int k, int n, int kc) {
     s += red[(3 * m + i) * 128 + c];
     T.partial[(int64_t)i * n + nb * 128 + c] = s;
   }
+
+  // arrival: the last workgroup of the output group finishes it
+  __syncthreads();
+  if (threadIdx.x == 0) {
+    __threadfence();  // make this workgroup's partials visible device-wide
+    unsigned int* ctr = r.counter(blockIdx.z, nb);
+    const unsigned int old = atomicAdd(ctr, 1u);
+    last_flag = (old + 1u == r.arrivals(blockIdx.z)) ? 1 : 0;
+  }
+  __syncthreads();
+  if (!last_flag) return;
+  __threadfence();  // see every other workgroup's partials
+  r.finish(blockIdx.z, nb, n);
+  if (threadIdx.x == 0) *r.counter(blockIdx.z, nb) = 0u;  // ready for the next call
+}
+
+// Launch with the prefetch depth the k range allows.
+template <int K, class R>
+hipError_t launch_gemv_kernel(const R& r, dim3 grid, size_t lds, hipStream_t s, int k, int n,
+                              int kc) {
+  switch (gemv_prefetch(kc)) {
+    case 8: hipLaunchKernelGGL((gemv_kernel<K, 8, R>), grid, dim3(256), lds, s, r, k, n, kc); break;
+    case 4: hipLaunchKernelGGL((gemv_kernel<K, 4, R>), grid, dim3(256), lds, s, r, k, n, kc); break;
+    default: hipLaunchKernelGGL((gemv_kernel<K, 2, R>), grid, dim3(256), lds, s, r, k, n, kc); break;
+  }
+  return hipGetLastError();
 }
 
 }  // namespace exl3

@@ -12,12 +12,13 @@
 //
 // Small P (decode, token-parallel verify): every pair is an independent M=1
 // unit (the README's "per-unit x stride" idea).
-//   1. gemv_kernel over units (pair, gate|up)          -> fp32 partials
-//   2. gu_unit_epilogue: reduce, output transform, svh, a = silu(g) * u, then
-//      the down projection's input transform (a .* suh_down) H   -> fp16 x'_d
-//   3. gemv_kernel over units (pair)                    -> fp32 partials
-//   4. down_unit_epilogue: per (token, 128 columns), for slots in order:
-//      reduce, transform, svh, times the routing weight, summed in fp32 -> y
+//   1. gemv_kernel over units (pair, gate|up); the last workgroup to arrive on
+//      a (pair, 128 columns) group sums the k slices of gate and up, applies
+//      the output transform and svh, forms a = silu(g) * u and writes the
+//      down projection's input (a .* suh_down) H as fp16
+//   2. gemv_kernel over units (pair); the last workgroup to arrive on a
+//      (token, 128 columns) group adds, for slots in order, the transformed
+//      down output times the routing weight in fp32 and writes y
 //
 // Large P (prefill): device binning, then one grouped MFMA GEMM launch per
 // projection over a device-built tile list (expert, first row, rows), so each
@@ -52,39 +53,79 @@ static inline size_t align256(size_t v) { return (v + 255) & ~(size_t)255; }
 struct GuUnitRes {
   const uint16_t* trellis;
   const uint16_t* suh;
-  int64_t tensor_dw_words;  // words of one (expert, slot) tensor
-  int k;                    // hidden
-  int n;                    // intermediate
+  const uint16_t* svh;
+  int64_t tensor_words;  // words of one (expert, slot) tensor
+  int k;                 // hidden
+  int n;                 // intermediate
   const uint16_t* x;
   int topk;
   const int32_t* ids;
-  float* ws;
+  float* part;           // fp32 [P][2][splits][n]
   int splits;
+  unsigned int* ctr;     // [P][n/128]
+  const uint16_t* suh_dn;
+  uint16_t* xd;          // fp16 [P][n]: input of the down projection, Hadamard domain
   __device__ GemvTask task(int u, int split) const {
     GemvTask T;
     const int pair = u >> 1, slot = u & 1;
     const int e = ids[pair];
     const int tok = pair / topk;
     T.valid = true;
-    T.trellis = trellis + (int64_t)(e * 2 + slot) * tensor_dw_words;
+    T.trellis = trellis + (int64_t)(e * 2 + slot) * tensor_words;
     T.suh = suh + (int64_t)(e * 2 + slot) * k;
     T.x = x + (int64_t)tok * k;
     T.ldx = k;
     T.m = 1;
-    T.partial = ws + ((int64_t)u * splits + split) * n;
+    T.partial = part + ((int64_t)u * splits + split) * n;
     return T;
+  }
+  __device__ unsigned int* counter(int u, int nb) const { return ctr + (u >> 1) * (n >> 7) + nb; }
+  __device__ unsigned int arrivals(int) const { return 2u * (unsigned int)splits; }
+  // gate and up of one pair: sum, output transform, svh; a = silu(g) * u;
+  // then the down projection's input transform (a .* suh_down) H
+  __device__ void finish(int u, int nb, int) const {
+    if ((threadIdx.x >> 6) != 0) return;
+    const int pair = u >> 1;
+    const int e = ids[pair];
+    const int col = nb * 128 + 2 * (int)lane_id();
+    float gv[2], uv[2];
+    for (int slot = 0; slot < 2; ++slot) {
+      float a, b;
+      sum_partials(part + ((int64_t)(pair * 2 + slot) * splits) * n + col, splits, n, a, b);
+      fwht128_pair(a, b);
+      const uint32_t sv =
+          *reinterpret_cast<const uint32_t*>(svh + (int64_t)(e * 2 + slot) * n + col);
+      a *= kInvSqrt128 * h2f((uint16_t)(sv & 0xFFFF));
+      b *= kInvSqrt128 * h2f((uint16_t)(sv >> 16));
+      if (slot == 0) { gv[0] = a; gv[1] = b; } else { uv[0] = a; uv[1] = b; }
+    }
+    float a = silu_f(gv[0]) * uv[0];
+    float b = silu_f(gv[1]) * uv[1];
+    const uint32_t su = *reinterpret_cast<const uint32_t*>(suh_dn + (int64_t)e * n + col);
+    a *= h2f((uint16_t)(su & 0xFFFF));
+    b *= h2f((uint16_t)(su >> 16));
+    fwht128_pair(a, b);
+    a *= kInvSqrt128;
+    b *= kInvSqrt128;
+    *reinterpret_cast<uint32_t*>(xd + (int64_t)pair * n + col) =
+        (uint32_t)f2h(a) | ((uint32_t)f2h(b) << 16);
   }
 };
 
 struct DnUnitRes {
   const uint16_t* trellis;
+  const uint16_t* svh;
   int64_t tensor_words;
-  int k;  // intermediate
-  int n;  // hidden
+  int k;               // intermediate
+  int n;               // hidden
   const uint16_t* xd;  // fp16 [P][k], already in the Hadamard domain
   const int32_t* ids;
-  float* ws;
+  const float* w;
+  int topk;
+  float* part;         // fp32 [P][splits][n]
   int splits;
+  unsigned int* ctr;   // [t][n/128]
+  float* y;            // fp32 [t][n]
   __device__ GemvTask task(int u, int split) const {
     GemvTask T;
     const int e = ids[u];
@@ -94,88 +135,37 @@ struct DnUnitRes {
     T.x = xd + (int64_t)u * k;
     T.ldx = k;
     T.m = 1;
-    T.partial = ws + ((int64_t)u * splits + split) * n;
+    T.partial = part + ((int64_t)u * splits + split) * n;
     return T;
   }
+  __device__ unsigned int* counter(int u, int nb) const { return ctr + (u / topk) * (n >> 7) + nb; }
+  __device__ unsigned int arrivals(int) const { return (unsigned int)(topk * splits); }
+  // y[token, block] = sum over slots in order of w * ((sum_s partial) H .* svh)
+  __device__ void finish(int u, int nb, int) const {
+    if ((threadIdx.x >> 6) != 0) return;
+    const int tok = u / topk;
+    const int col = nb * 128 + 2 * (int)lane_id();
+    float ya = 0.f, yb = 0.f;
+    for (int s = 0; s < topk; ++s) {
+      const int pair = tok * topk + s;
+      const int e = ids[pair];
+      float a, b;
+      sum_partials(part + ((int64_t)pair * splits) * n + col, splits, n, a, b);
+      fwht128_pair(a, b);
+      const uint32_t sv = *reinterpret_cast<const uint32_t*>(svh + (int64_t)e * n + col);
+      const float wt = w[pair];
+      ya += wt * (a * kInvSqrt128 * h2f((uint16_t)(sv & 0xFFFF)));
+      yb += wt * (b * kInvSqrt128 * h2f((uint16_t)(sv >> 16)));
+    }
+    *reinterpret_cast<float2*>(y + (int64_t)tok * n + col) = make_float2(ya, yb);
+  }
 };
-
-// reduce gate and up, SiLU, then the down projection's input transform
-__global__ __launch_bounds__(256) void gu_unit_epilogue(
-    const float* __restrict__ part, int splits, int P, int inter, const int32_t* __restrict__ ids,
-    const uint16_t* __restrict__ svh_gu, const uint16_t* __restrict__ suh_dn,
-    uint16_t* __restrict__ xd) {
-  const int nblocks = inter >> 7;
-  const int task = blockIdx.x * 4 + (threadIdx.x >> 6);
-  if (task >= P * nblocks) return;
-  const int pair = task / nblocks, nb = task - pair * nblocks;
-  const int col = nb * 128 + 2 * (int)lane_id();
-  const int e = ids[pair];
-  float gv[2], uv[2];
-  for (int slot = 0; slot < 2; ++slot) {
-    float a = 0.f, b = 0.f;
-    const float* pp = part + ((int64_t)(pair * 2 + slot) * splits) * inter + col;
-    for (int s = 0; s < splits; ++s) {
-      const float2 v = *reinterpret_cast<const float2*>(pp + (int64_t)s * inter);
-      a += v.x;
-      b += v.y;
-    }
-    fwht128_pair(a, b);
-    const uint32_t sv =
-        *reinterpret_cast<const uint32_t*>(svh_gu + (int64_t)(e * 2 + slot) * inter + col);
-    a *= kInvSqrt128 * h2f((uint16_t)(sv & 0xFFFF));
-    b *= kInvSqrt128 * h2f((uint16_t)(sv >> 16));
-    if (slot == 0) { gv[0] = a; gv[1] = b; } else { uv[0] = a; uv[1] = b; }
-  }
-  float a = silu_f(gv[0]) * uv[0];
-  float b = silu_f(gv[1]) * uv[1];
-  const uint32_t su = *reinterpret_cast<const uint32_t*>(suh_dn + (int64_t)e * inter + col);
-  a *= h2f((uint16_t)(su & 0xFFFF));
-  b *= h2f((uint16_t)(su >> 16));
-  fwht128_pair(a, b);
-  a *= kInvSqrt128;
-  b *= kInvSqrt128;
-  *reinterpret_cast<uint32_t*>(xd + (int64_t)pair * inter + col) =
-      (uint32_t)f2h(a) | ((uint32_t)f2h(b) << 16);
-}
-
-// per (token, 128 columns): slots in order, reduce, transform, svh, weight, sum
-__global__ __launch_bounds__(256) void down_unit_epilogue(
-    const float* __restrict__ part, int splits, int64_t t_count, int topk, int hidden,
-    const int32_t* __restrict__ ids, const float* __restrict__ w,
-    const uint16_t* __restrict__ svh_dn, float* __restrict__ y) {
-  const int nblocks = hidden >> 7;
-  const int64_t task = (int64_t)blockIdx.x * 4 + (threadIdx.x >> 6);
-  if (task >= t_count * nblocks) return;
-  const int64_t tok = task / nblocks;
-  const int nb = (int)(task - tok * nblocks);
-  const int col = nb * 128 + 2 * (int)lane_id();
-  float ya = 0.f, yb = 0.f;
-  for (int s = 0; s < topk; ++s) {
-    const int64_t pair = tok * topk + s;
-    const int e = ids[pair];
-    float a = 0.f, b = 0.f;
-    const float* pp = part + (pair * splits) * hidden + col;
-    for (int q = 0; q < splits; ++q) {
-      const float2 v = *reinterpret_cast<const float2*>(pp + (int64_t)q * hidden);
-      a += v.x;
-      b += v.y;
-    }
-    fwht128_pair(a, b);
-    const uint32_t sv = *reinterpret_cast<const uint32_t*>(svh_dn + (int64_t)e * hidden + col);
-    const float wt = w[pair];
-    ya += wt * (a * kInvSqrt128 * h2f((uint16_t)(sv & 0xFFFF)));
-    yb += wt * (b * kInvSqrt128 * h2f((uint16_t)(sv >> 16)));
-  }
-  *reinterpret_cast<float2*>(y + tok * hidden + col) = make_float2(ya, yb);
-}
 
 template <int K>
 struct GuUnitRun {
   static hipError_t run(const GuUnitRes& r, int k, int n, int units, int kc, size_t lds,
                         hipStream_t s) {
-    hipLaunchKernelGGL((gemv_kernel<K, GuUnitRes>), dim3(n / 128, r.splits, units), dim3(256), lds,
-                       s, r, k, n, kc);
-    return hipGetLastError();
+    return launch_gemv_kernel<K>(r, dim3(n / 128, r.splits, units), lds, s, k, n, kc);
   }
 };
 
@@ -183,22 +173,32 @@ template <int K>
 struct DnUnitRun {
   static hipError_t run(const DnUnitRes& r, int k, int n, int units, int kc, size_t lds,
                         hipStream_t s) {
-    hipLaunchKernelGGL((gemv_kernel<K, DnUnitRes>), dim3(n / 128, r.splits, units), dim3(256), lds,
-                       s, r, k, n, kc);
-    return hipGetLastError();
+    return launch_gemv_kernel<K>(r, dim3(n / 128, r.splits, units), lds, s, k, n, kc);
   }
 };
 
+// Arrival counters of the unit path live at the start of the workspace, in a
+// region whose size depends only on the arena shapes (enough for the largest
+// unit-path call).  Both regimes leave this region zero when a call ends, so
+// one workspace can serve calls of any size.
+static size_t counter_region(const ArenaDesc& gu, const ArenaDesc& dn) {
+  const size_t c = (size_t)kGroupedUnitMaxPairs * (gu.n / 128) +
+                   (size_t)kGroupedUnitMaxPairs * (dn.n / 128);
+  return align256(c * 4);
+}
+
 struct UnitLayout {
   int s_gu, s_dn;
-  size_t part_gu, xd, part_dn, total;
+  size_t ctr_gu, ctr_dn, part_gu, xd, part_dn, total;
 };
 
 static UnitLayout unit_layout(const ArenaDesc& gu, const ArenaDesc& dn, int64_t P) {
   UnitLayout L;
   L.s_gu = gemv_choose_splits(gu.k, (gu.n / 128) * (int)P * 2, 1, kGemvTargetWorkgroups);
   L.s_dn = gemv_choose_splits(dn.k, (dn.n / 128) * (int)P, 1, kGemvTargetWorkgroups);
-  size_t off = 0;
+  L.ctr_gu = 0;
+  L.ctr_dn = (size_t)kGroupedUnitMaxPairs * (gu.n / 128) * 4;
+  size_t off = counter_region(gu, dn);
   L.part_gu = off; off += align256((size_t)P * 2 * L.s_gu * gu.n * sizeof(float));
   L.xd = off;      off += align256((size_t)P * gu.n * sizeof(uint16_t));
   L.part_dn = off; off += align256((size_t)P * L.s_dn * dn.n * sizeof(float));
@@ -222,7 +222,7 @@ static GemmLayout gemm_layout(const ArenaDesc& gu, const ArenaDesc& dn, int64_t 
   GemmLayout L;
   const int E = gu.experts;
   L.max_tiles = (int)((P + kGroupedBM - 1) / kGroupedBM) + (int)(P < E ? P : E);
-  size_t off = 0;
+  size_t off = counter_region(gu, dn);
   L.counts = off;  off += align256((size_t)E * 4);
   L.cursor = off;  off += align256((size_t)E * 4);
   L.offsets = off; off += align256((size_t)E * 4);
@@ -409,31 +409,22 @@ hipError_t launch_grouped(const ArenaDesc& gu, const ArenaDesc& dn, const uint16
   hipError_t e;
   if (P <= kGroupedUnitMaxPairs) {
     const UnitLayout L = unit_layout(gu, dn, P);
+    unsigned int* ctr_gu = reinterpret_cast<unsigned int*>(base + L.ctr_gu);
+    unsigned int* ctr_dn = reinterpret_cast<unsigned int*>(base + L.ctr_dn);
     float* part_gu = reinterpret_cast<float*>(base + L.part_gu);
     uint16_t* xd = reinterpret_cast<uint16_t*>(base + L.xd);
     float* part_dn = reinterpret_cast<float*>(base + L.part_dn);
-    GuUnitRes rg{gu.trellis, gu.suh, words_gu, hidden, inter, x, topk, ids, part_gu, L.s_gu};
+    GuUnitRes rg{gu.trellis, gu.suh, gu.svh, words_gu, hidden, inter, x, topk, ids,
+                 part_gu, L.s_gu, ctr_gu, dn.suh, xd};
     const int kc_g = hidden / L.s_gu;
     e = dispatch_bits<GuUnitRun>(gu.bits, rg, hidden, inter, (int)(P * 2), kc_g,
                                  gemv_lds_bytes(kc_g, 1), s);
     if (e != hipSuccess) return e;
-    {
-      const int tasks = (int)P * (inter / 128);
-      hipLaunchKernelGGL(gu_unit_epilogue, dim3((tasks + 3) / 4), dim3(256), 0, s, part_gu, L.s_gu,
-                         (int)P, inter, ids, gu.svh, dn.suh, xd);
-      if ((e = hipGetLastError()) != hipSuccess) return e;
-    }
-    DnUnitRes rd{dn.trellis, words_dn, inter, hidden, xd, ids, part_dn, L.s_dn};
+    DnUnitRes rd{dn.trellis, dn.svh, words_dn, inter, hidden, xd, ids, w, topk,
+                 part_dn, L.s_dn, ctr_dn, y};
     const int kc_d = inter / L.s_dn;
-    e = dispatch_bits<DnUnitRun>(dn.bits, rd, inter, hidden, (int)P, kc_d, gemv_lds_bytes(kc_d, 1),
-                                 s);
-    if (e != hipSuccess) return e;
-    {
-      const int64_t tasks = t * (hidden / 128);
-      hipLaunchKernelGGL(down_unit_epilogue, dim3((unsigned)((tasks + 3) / 4)), dim3(256), 0, s,
-                         part_dn, L.s_dn, t, topk, hidden, ids, w, dn.svh, y);
-      return hipGetLastError();
-    }
+    return dispatch_bits<DnUnitRun>(dn.bits, rd, inter, hidden, (int)P, kc_d,
+                                    gemv_lds_bytes(kc_d, 1), s);
   }
 
   const GemmLayout L = gemm_layout(gu, dn, P);

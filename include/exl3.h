@@ -146,10 +146,15 @@ size_t exl3_linear_workspace_size(const exl3_weight* w, int64_t m);
  *   y      [m][ldy] of y_dtype (EXL3_F16 or EXL3_F32; fp32 outputs are the
  *          issue's "decodeF32/promptF32" contract), ldy >= n, multiple of 8
  *   ws     device workspace of at least exl3_linear_workspace_size(w, m)
- *          bytes (may be NULL when that size is 0)
+ *          bytes (may be NULL when that size is 0).  It must be zero-filled
+ *          before its first use: it holds arrival counters that every call
+ *          leaves at zero again, so a workspace can be reused by later calls
+ *          (of any size, on the same stream) without clearing it.
  * m == 0 returns EXL3_OK without enqueueing anything.  The kernel (decode
- * GEMV for m <= 16, MFMA GEMM above) is chosen internally from m; each output
- * row is computed with the same arithmetic whatever m is.                 */
+ * GEMV for m <= 16, MFMA GEMM above) is chosen internally from m.  Within
+ * each of the two ranges a row's result does not depend on m or on the other
+ * rows (bit for bit); across them the summation order differs, so results
+ * agree to rounding.                                                      */
 exl3_status exl3_linear(const exl3_weight* w, const void* x, int64_t m, int64_t ldx, void* y,
                         int64_t ldy, int32_t y_dtype, void* ws, size_t ws_bytes,
                         exl3_stream_t stream);
@@ -174,7 +179,8 @@ size_t exl3_grouped_experts_workspace_size(const exl3_expert_weights* gate_up,
  *   y             fp32 [t][hidden] device pointer, overwritten with
  *                 Y[i] = sum over s in slot order of w[i][s] * down_e(a),
  *                 a = silu(gate_e(x_i)) * up_e(x_i), e = topk_ids[i][s]
- *   ws            device workspace of at least the queried size
+ *   ws            device workspace of at least the queried size, zero-filled
+ *                 before its first use (same counter rule as exl3_linear)
  * 1 <= topk <= EXL3_MAX_TOPK.  t == 0 returns EXL3_OK without work.
  * Out-of-range ids are a contract violation and are not checked on device. */
 exl3_status exl3_grouped_experts(const exl3_expert_weights* gate_up,
