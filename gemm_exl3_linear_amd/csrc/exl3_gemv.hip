@@ -5,20 +5,10 @@
 // int8 linears ...": the product runs in the Hadamard domain; "Layout": the
 // Hadamard-in and Hadamard-out kernels around the vector GEMV).
 //
-// gemv_kernel, one workgroup per (128-column block, k range[, unit]):
-//   prologue  x' = (x .* suh) H for the workgroup's k range, fp16, into LDS
-//   main loop each wave walks k tiles; lane (t, p) streams the row pair p of
-//             n-tile t with one coalesced load, decodes 32 weights in
-//             registers into k-pairs, and hands them to the matrix cores
-//             through a small per-wave LDS transpose (MFMA 16x16x16 f16, the
-//             activation rows padded to 16, fp32 accumulation)
-//   end       the four waves' partial sums are added in a fixed order and
-//             written to the fp32 workspace, one slice per k range; the
-//             workgroup then counts itself in on its 128-column block, and
-//             the last one to arrive adds the slices in k order, applies the
-//             output transform, svh and bias, casts, and resets the counter.
-// One launch per call.  The sums never depend on arrival order, so results
-// are bit-reproducible, and every row is computed the same way whatever m is.
+// Dense tensors run the persistent stream-k kernel of exl3_gemv_sk.hpp
+// followed by its finishing launch.  The workgroup-per-(block, k range)
+// gemv_kernel of exl3_gemv.hpp serves the grouped experts' small-batch path;
+// its planning helpers live here.
 #include "exl3_device.hpp"
 #include "exl3_gemv.hpp"
 #include "exl3_gemv_sk.hpp"
@@ -58,30 +48,26 @@ int gemv_choose_splits(int k, int groups, int m, int target_wgs) {
   return best > 0 ? best : kb;
 }
 
-// Stream-k plan of the dense decode GEMV: G workgroups (kGemvSkWorkgroups =
-// two per CU of the 256-CU MI355X, fewer for small tensors, enough that a run
-// spans at most 48 units), the number of partial slots an n block can
-// receive, LDS and workspace sizes.  The plan depends on (k, n) only, so every
-// m <= 16 sees the same summation order, and it needs no device query.
+// Plan of the dense decode GEMV: W waves (kGemvSkWaves = eight per CU of the
+// 256-CU MI355X; more when runs would exceed 48 row steps, fewer for small
+// tensors), the number of partial slots a block can receive, and the
+// workspace (fp32 partials, then the transformed activations when m > 1).
+// The plan depends on (k, n) only, so every m <= 16 sees the same summation
+// order, and it needs no device query.
 GemvPlan plan_gemv(int k, int n, int m) {
   GemvPlan p;
-  const int64_t KB = k / 128, NB = n / 128, U = KB * NB;
-  int64_t G = kGemvSkWorkgroups;
-  if (G > U) G = U;
-  if (G < (U + 47) / 48) G = (U + 47) / 48;
-  // at most kSkMaxSlots runs may meet one n block: runs of >= KB / (slots - 2) units
-  {
-    const int64_t min_run = (KB + kSkMaxSlots - 3) / (kSkMaxSlots - 2);
-    if (U / G < min_run) G = U / min_run > 0 ? U / min_run : 1;
-  }
-  const int64_t run_min = U / G, run_max = (U + G - 1) / G;
-  p.splits = (int)G;
-  p.kc = (int)run_max;  // units per workgroup at most
-  p.slots = (int)((KB - 1 + run_min - 1) / run_min + 1);
-  p.lds = (((size_t)run_max * m * 256 + 15) & ~(size_t)15) + (size_t)4 * m * 512 +
-          (m > 1 ? (size_t)4 * 64 * 20 * 4 : 0);
-  p.ctr_bytes = ((size_t)NB * 4 + 255) & ~(size_t)255;
-  p.xprep_off = p.ctr_bytes + (((size_t)NB * p.slots * m * 128 * sizeof(float) + 255) & ~(size_t)255);
+  const int64_t KT = k / 16, NB = n / 128, R = KT * NB;
+  int64_t W = kGemvSkWaves;
+  if (W < (R + 47) / 48) W = (R + 47) / 48;
+  W = (W + 3) / 4 * 4;
+  if (W > R) W = (R + 3) / 4 * 4;  // runs of at least one row step (extra waves idle)
+  const int64_t run_min = R / W > 0 ? R / W : 1;
+  p.splits = (int)W;
+  p.kc = (int)((R + W - 1) / W);
+  p.slots = (int)((KT - 1 + run_min - 1) / run_min + 1);
+  p.lds = 0;
+  p.ctr_bytes = 0;
+  p.xprep_off = (((size_t)NB * p.slots * m * 128 * sizeof(float) + 255) & ~(size_t)255);
   p.ws = p.xprep_off + (m > 1 ? (size_t)m * k * sizeof(uint16_t) : 0);
   return p;
 }
@@ -89,11 +75,15 @@ GemvPlan plan_gemv(int k, int n, int m) {
 template <int K>
 struct SkRun {
   static hipError_t run(const SkArgs& a, const GemvPlan& plan, hipStream_t s) {
-    const dim3 grid((unsigned)a.G);
+    const dim3 grid((unsigned)(a.W / 4));
     if (a.m == 1)
-      hipLaunchKernelGGL((gemv_sk_kernel<K, true, 8>), grid, dim3(256), plan.lds, s, a);
+      hipLaunchKernelGGL((gemv_sk_kernel<K, true, 8>), grid, dim3(256), 0, s, a);
     else
-      hipLaunchKernelGGL((gemv_sk_kernel<K, false, 8>), grid, dim3(256), plan.lds, s, a);
+      hipLaunchKernelGGL((gemv_sk_kernel<K, false, 8>), grid, dim3(256), 0, s, a);
+    const hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return e;
+    const int tasks = (a.n / 128) * a.m;
+    hipLaunchKernelGGL(gemv_sk_finish, dim3((unsigned)((tasks + 3) / 4)), dim3(256), 0, s, a);
     return hipGetLastError();
   }
 };
@@ -120,13 +110,11 @@ hipError_t launch_gemv(const uint16_t* trellis, const uint16_t* suh, const uint1
   a.m = m;
   a.k = k;
   a.n = n;
-  a.KB = k / 128;
-  a.NB = n / 128;
-  a.U = (int64_t)a.KB * a.NB;
-  a.G = plan.splits;
+  a.KT = k / 16;
+  a.R = (int64_t)a.KT * (n / 128);
+  a.W = plan.splits;
   a.slots = plan.slots;
   a.part = reinterpret_cast<float*>(base + plan.ctr_bytes);
-  a.ctr = reinterpret_cast<unsigned int*>(base);
   a.svh = svh;
   a.bias = bias;
   a.y = y;

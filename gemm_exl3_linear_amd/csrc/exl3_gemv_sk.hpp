@@ -1,57 +1,57 @@
 // Persistent decode GEMV for 1..16 activation rows (dense EXL3 linear).
 //
-// Work decomposition ("stream-k"): the product is cut into units of one
-// 128-column block (nb) by one 128-row block of k (kb); units are ordered
-// nb-major and every workgroup takes one contiguous run of them, so the
-// number of trellis bytes per workgroup differs by at most one unit.  The
-// grid holds two workgroups per CU, all resident at once: each wave keeps PF
-// row-pair loads in flight across the whole run, including across n-block
-// boundaries, and the only drain is at the end of the run.
+// Work decomposition ("stream-k" at wave granularity).  A row step is one k
+// tile (16 rows of k) of one 128-column block (8 n tiles of 16 columns): the
+// R = (n/128) * (k/16) row steps are ordered block-major and every wave of the
+// persistent grid takes one contiguous run of them, so runs differ by at most
+// one row step.  Waves never wait for each other: each keeps PF row-pair loads
+// in flight from the start to the end of its run, across block boundaries.
 //
-// Per workgroup:
-//   1. x' = (x .* suh) H for the k blocks of its units (fp16, LDS); these
-//      loads go out first, the trellis loads right after.
-//   2. Main loop.  Iteration `it` of wave w covers k tile 8 kb + w + 4 (it&1)
-//      of unit it/2 over the 8 n tiles of the block: lane (t, p) loads row
-//      pair p of n tile t (one coalesced 4K-byte load per lane), decodes 32
-//      weights into k-pairs, and contracts them:
+// gemv_sk_kernel, per wave:
+//   1. m == 1: x' = (x .* suh) H for the (at most a few) k blocks its run
+//      touches, computed in the wave after the first trellis loads went out;
+//      m > 1: x' comes from one input-transform launch and each row step's
+//      A fragment travels with the trellis loads.
+//   2. Row step: lane (t, p) loads row pair p of n tile t (one coalesced
+//      4K-byte load per lane), decodes 32 weights into k-pairs and contracts:
 //        m == 1 : v_dot2_f32_f16 with the x' pair of its two rows, 16 column
-//                 accumulators per lane (no LDS traffic);
-//        m >= 2 : the k-pairs go through a per-wave LDS transpose into MFMA
+//                 accumulators per lane, no LDS traffic;
+//        m >= 2 : k-pairs through a per-wave LDS transpose into MFMA
 //                 16x16x16 f16 (rows padded to 16).
-//   3. At the end of each n-block segment of the run, the waves' sums are
-//      reduced in a fixed order and stored to the segment's partial slot with
-//      agent-coherent stores (they write through to the device coherence
-//      point; no cache write-back of the whole L2 is needed).
-//   4. After the run: one wait for those stores, one relaxed agent-scope
-//      atomic increment per segment; the workgroup that completes an n block
-//      sums its slots in slot order (agent-coherent loads), applies the
-//      output transform, svh and bias, casts, stores y and resets the counter.
-// The sums never depend on timing, so results are bit-reproducible; a row's
-// arithmetic does not depend on m within the MFMA range.
+//   3. Segment end (block changes or run ends): the wave's column sums go to
+//      the segment's partial slot in the fp32 workspace.
+// gemv_sk_finish, one wave per (activation row, 128-column block): adds the
+// block's slots in slot order, applies the output transform, svh and bias,
+// casts and stores y.  The hand-off between the two is the kernel boundary:
+// no wave waits on another and no cache maintenance runs inside a kernel
+// (the L2 of one XCD does not see another XCD's writes before a device-scope
+// release, which at kernel granularity costs nothing extra).
+// The sums never depend on timing, so results are bit-reproducible; the plan
+// depends on (k, n) only, so a row's arithmetic does not depend on m within
+// the MFMA range (2..16).
 #pragma once
 
 #include "exl3_device.hpp"
 
 namespace exl3 {
 
-constexpr int kGemvSkWorkgroups = 512;
-constexpr int kSkMaxSlots = 16;  // partial slots per n block (the planner keeps below this)
+constexpr int kGemvSkWaves = 2048;  // 8 waves per CU of the 256-CU MI355X
+constexpr int kSkSlotBatch = 16;    // partial slots loaded per batch in the finish
+constexpr int kSkMaxXBlocks = 8;    // k blocks a run may touch (m == 1)
 
 struct SkArgs {
   const uint16_t* trellis;  // [k/16][n/16][16K]
   const uint16_t* suh;      // fp16 [k]
   const uint16_t* x;        // fp16 [m][ldx]
   int64_t ldx;
-  const uint16_t* xprep;    // fp16 [m][k] already transformed, or nullptr (m == 1)
+  const uint16_t* xprep;    // fp16 [m][k] already transformed (m > 1), else nullptr
   int m;
   int k, n;
-  int KB, NB;               // k/128, n/128
-  int64_t U;                // units = NB * KB
-  int G;                    // workgroups (grid)
-  int slots;                // partial slots per n block
-  float* part;              // fp32 [NB][slots][m][128]
-  unsigned int* ctr;        // [NB] arrival counters (zero between calls)
+  int KT;                   // k / 16
+  int64_t R;                // row steps = (n / 128) * KT
+  int W;                    // waves of the grid
+  int slots;                // partial slots per block
+  float* part;              // fp32 [n/128][slots][m][128]
   const uint16_t* svh;
   const uint16_t* bias;
   void* y;
@@ -59,26 +59,13 @@ struct SkArgs {
   int y_f32;
 };
 
-// workgroup whose run contains unit u (runs are [w U / G, (w+1) U / G))
-__device__ __forceinline__ int sk_owner(int64_t u, int64_t U, int G) {
-  return (int)(((u + 1) * G - 1) / U);
+// wave whose run contains row step r (runs are [w R / W, (w+1) R / W))
+__device__ __forceinline__ int sk_owner(int64_t r, int64_t R, int W) {
+  return (int)(((r + 1) * W - 1) / R);
 }
 
-__device__ __forceinline__ void lds_barrier() {
-  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup", "local");
-  __builtin_amdgcn_s_barrier();
-  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup", "local");
-}
-
-__device__ __forceinline__ void store_coherent(float* p, float v) {
-  __hip_atomic_store(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-}
-__device__ __forceinline__ float load_coherent(const float* p) {
-  return __hip_atomic_load(p, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-}
-
-// dot2 reduction over the 8 row-pair lanes of a tile: lane p ends with the
-// sums of columns 2p and 2p+1 of its n tile
+// dot2 accumulators: sum over the 8 row-pair lanes of a tile; lane p ends with
+// the sums of columns 2p and 2p+1 of its n tile
 __device__ __forceinline__ void reduce_rowpairs(float (&acc)[16], float& c0, float& c1) {
   const uint32_t l = lane_id();
   float v8[8];
@@ -98,106 +85,114 @@ __device__ __forceinline__ void reduce_rowpairs(float (&acc)[16], float& c0, flo
     v4[c] = keep + shfl_xor_f(send, 2);
   }
   const bool up1 = (l & 1u) != 0;
-#pragma unroll
-  for (int c = 0; c < 2; ++c) {
-    const float send = up1 ? v4[c] : v4[c + 2];
-    const float keep = up1 ? v4[c + 2] : v4[c];
-    (c == 0 ? c0 : c1) = keep + shfl_xor_f(send, 1);
+  {
+    const float send = up1 ? v4[0] : v4[2];
+    const float keep = up1 ? v4[2] : v4[0];
+    c0 = keep + shfl_xor_f(send, 1);
+  }
+  {
+    const float send = up1 ? v4[1] : v4[3];
+    const float keep = up1 ? v4[3] : v4[1];
+    c1 = keep + shfl_xor_f(send, 1);
   }
 }
 
+// LDS per wave: m == 1: x' blocks [kSkMaxXBlocks][128] fp16 (2 KB);
+// m >= 2: transpose region [8 n tiles][8 row pairs][20] dwords (5 KB)
+constexpr int kSkWaveLdsDot = kSkMaxXBlocks * 128 * 2;
+constexpr int kSkWaveLdsMfma = 64 * 20 * 4;
+
 template <int K, bool DOT, int PF>
 __global__ __launch_bounds__(256) void gemv_sk_kernel(SkArgs a) {
-  extern __shared__ __align__(16) unsigned char smem[];
-  __shared__ int last_flags[64];
-
-  const int w = blockIdx.x;
-  const int64_t u0 = (int64_t)w * a.U / a.G;
-  const int64_t u1 = (int64_t)(w + 1) * a.U / a.G;
-  const int nu = (int)(u1 - u0);
-  if (nu <= 0) return;
-  const int m = a.m;
-  const int nt = a.n >> 4;
-  const int KB = a.KB;
-
-  uint16_t* xs = reinterpret_cast<uint16_t*>(smem);  // [nu][m][128]
-  const size_t xs_bytes = ((size_t)nu * m * 256 + 15) & ~(size_t)15;
-  float* red = reinterpret_cast<float*>(smem + xs_bytes);                 // [4][m][128]
-  uint32_t* tr_all = reinterpret_cast<uint32_t*>(smem + xs_bytes + (size_t)4 * m * 512);
+  constexpr int WAVE_LDS = DOT ? kSkWaveLdsDot : kSkWaveLdsMfma;
+  __shared__ __align__(16) unsigned char smem[4 * WAVE_LDS];
 
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int wid = blockIdx.x * 4 + wave;
+  const int64_t r0 = (int64_t)wid * a.R / a.W;
+  const int64_t r1 = (int64_t)(wid + 1) * a.R / a.W;
+  const int len = (int)(r1 - r0);
+  if (len <= 0) return;
+  const int m = a.m;
+  const int nt = a.n >> 4;
+  const int KT = a.KT;
   const int lane = threadIdx.x & 63;
   const int t = lane >> 3, p = lane & 7;   // decode role
   const int g = lane >> 4, j = lane & 15;  // MFMA role
+  unsigned char* wl = smem + wave * WAVE_LDS;
 
-  // ---- 1. input transform, first batch of loads before the trellis loads
-  const int tasks = nu * m;
-  constexpr int XB = 4;  // tasks per wave per batch
-  uint32_t xv[XB], sv[XB];
-  auto load_tasks = [&](int first) {
-#pragma unroll
-    for (int q = 0; q < XB; ++q) {
-      const int task = first + 4 * q;
-      if (task < tasks) {
-        const int ui = task / m, i = task - ui * m;
-        const int kb = (int)((u0 + ui) % KB);
-        const int kk = kb * 128 + 2 * lane;
-        xv[q] = *reinterpret_cast<const uint32_t*>(a.x + (int64_t)i * a.ldx + kk);
-        sv[q] = *reinterpret_cast<const uint32_t*>(a.suh + kk);
-      }
-    }
+  // Row-step cursors are uniform: (nb, kt) advance by one k tile per step and
+  // wrap to the next block at k/16, so no division happens inside the loop.
+  const int64_t nb0 = r0 / KT;
+  const int kt0 = (int)(r0 - nb0 * KT);
+  const int64_t tile_dw = 8 * K;                 // dwords per 16x16 tile
+  const int64_t kt_dw = (int64_t)nt * tile_dw;   // dwords per k tile row
+  const uint32_t* tr_lane = reinterpret_cast<const uint32_t*>(a.trellis) + K * p + t * tile_dw;
+  // prefetch cursor
+  int64_t pf_nb = nb0;
+  int pf_kt = kt0;
+  int pf_left = len;  // row steps the prefetch cursor may still visit
+  auto pf_ptr = [&]() -> const uint32_t* {
+    return tr_lane + (int64_t)pf_kt * kt_dw + pf_nb * 8 * tile_dw;
   };
-  auto transform_tasks = [&](int first) {
-#pragma unroll
-    for (int q = 0; q < XB; ++q) {
-      const int task = first + 4 * q;
-      if (task < tasks) {
-        float x0 = h2f((uint16_t)(xv[q] & 0xFFFF)) * h2f((uint16_t)(sv[q] & 0xFFFF));
-        float x1 = h2f((uint16_t)(xv[q] >> 16)) * h2f((uint16_t)(sv[q] >> 16));
-        fwht128_pair(x0, x1);
-        x0 *= kInvSqrt128;
-        x1 *= kInvSqrt128;
-        *reinterpret_cast<uint32_t*>(xs + (size_t)task * 128 + 2 * lane) =
-            (uint32_t)f2h(x0) | ((uint32_t)f2h(x1) << 16);
-      }
-    }
+  auto pf_afrag = [&]() -> const uint2* {
+    const int row = j < m ? j : 0;
+    return reinterpret_cast<const uint2*>(a.xprep + (int64_t)row * a.k + pf_kt * 16 + 4 * g);
   };
-  if (!a.xprep) load_tasks(wave);
+  auto pf_advance = [&]() {  // stays on the last row step once the run is exhausted
+    const int adv = pf_left > 1 ? 1 : 0;  // selects, not branches: the loads
+    pf_left -= adv;                       // around stay unconditional
+    pf_kt += adv;
+    const int wrap = pf_kt == KT ? 1 : 0;
+    pf_kt = wrap ? 0 : pf_kt;
+    pf_nb += wrap;
+  };
 
-  // ---- trellis ring: iteration it -> unit it/2, k tile w + 4 (it & 1)
-  const int iters = 2 * nu;
-  const uint32_t* tr_base = reinterpret_cast<const uint32_t*>(a.trellis) + K * p;
-  auto tile_ptr = [&](int it) -> const uint32_t* {
-    const int64_t u = u0 + (it >> 1);
-    const int64_t nb = u / KB;
-    const int64_t kt = (u - nb * KB) * 8 + wave + 4 * (it & 1);
-    return tr_base + ((kt * nt + nb * 8 + t) * (8 * K));
-  };
-  uint32_t ring[PF][K];
+  // ---- m == 1: x' for the k blocks of the run; block b of the run is k block
+  // (kt0 / 8 + b) mod k/128.  These loads go out first (a fixed number of them,
+  // so the wait below counts only the trellis loads issued after them).
+  const int kb0 = kt0 >> 3;
+  const int KBn = KT >> 3;
+  uint32_t xv[DOT ? kSkMaxXBlocks : 1], sv[DOT ? kSkMaxXBlocks : 1];
+  const int nblk = ((kt0 & 7) + len + 7) >> 3;
+  if constexpr (DOT) {
 #pragma unroll
-  for (int s = 0; s < PF; ++s) load_rowpair<K>(tile_ptr(s < iters ? s : iters - 1), ring[s]);
-
-  if (!a.xprep) {
-    transform_tasks(wave);
-    for (int first = wave + 4 * XB; first < tasks; first += 4 * XB) {
-      load_tasks(first);
-      transform_tasks(first);
-    }
-  } else {
-    // x' was prepared by the input-transform kernel: copy the run's blocks
-    const int chunks = tasks * 16;  // 16-byte chunks
-#pragma unroll 4
-    for (int idx = threadIdx.x; idx < chunks; idx += 256) {
-      const int task = idx >> 4, ofs = (idx & 15) * 8;
-      const int ui = task / m, i = task - ui * m;
-      const int kb = (int)((u0 + ui) % KB);
-      *reinterpret_cast<uint4*>(xs + (size_t)task * 128 + ofs) =
-          *reinterpret_cast<const uint4*>(a.xprep + (int64_t)i * a.k + kb * 128 + ofs);
+    for (int b = 0; b < kSkMaxXBlocks; ++b) {
+      const int bb = b < nblk ? b : nblk - 1;
+      const int kb = (kb0 + bb) % KBn;
+      const int kk = kb * 128 + 2 * lane;
+      xv[b] = *reinterpret_cast<const uint32_t*>(a.x + kk);
+      sv[b] = *reinterpret_cast<const uint32_t*>(a.suh + kk);
     }
   }
-  lds_barrier();
 
-  // ---- 2. main loop
+  uint32_t ring[PF][K];
+  uint2 aring[DOT ? 1 : PF];
+#pragma unroll
+  for (int s = 0; s < PF; ++s) {
+    load_rowpair<K>(pf_ptr(), ring[s]);
+    if constexpr (!DOT) aring[s] = *pf_afrag();
+    pf_advance();
+  }
+
+  if constexpr (DOT) {
+    uint16_t* xs = reinterpret_cast<uint16_t*>(wl);
+#pragma unroll
+    for (int b = 0; b < kSkMaxXBlocks; ++b) {
+      if (b < nblk) {
+        float x0 = h2f((uint16_t)(xv[b] & 0xFFFF)) * h2f((uint16_t)(sv[b] & 0xFFFF));
+        float x1 = h2f((uint16_t)(xv[b] >> 16)) * h2f((uint16_t)(sv[b] >> 16));
+        fwht128_pair(x0, x1);
+        *reinterpret_cast<uint32_t*>(xs + b * 128 + 2 * lane) =
+            (uint32_t)f2h(x0 * kInvSqrt128) | ((uint32_t)f2h(x1 * kInvSqrt128) << 16);
+      }
+    }
+    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront", "local");
+    __builtin_amdgcn_wave_barrier();
+    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront", "local");
+  }
+
+  // ---- main loop
   float dacc[16];
   float4_t macc[8];
   auto clear_acc = [&]() {
@@ -210,51 +205,45 @@ __global__ __launch_bounds__(256) void gemv_sk_kernel(SkArgs a) {
     }
   };
   clear_acc();
-  uint32_t* tr = tr_all + wave * (64 * 20);
+  uint32_t* tr = reinterpret_cast<uint32_t*>(wl);
   uint32_t* my = tr + (t * 8 + p) * 20;
-  const int64_t nb_first = u0 / KB;
 
-  // end of an n-block segment: fixed-order sum over the waves, coherent store
+  // segment end: the wave's column sums to the segment's slot (no wait)
   auto flush = [&](int64_t nb) {
+    const int slot = wid - sk_owner(nb * KT, a.R, a.W);
+    float* dst = a.part + ((int64_t)nb * a.slots + slot) * m * 128;
     if constexpr (DOT) {
       float c0, c1;
       reduce_rowpairs(dacc, c0, c1);
-      *reinterpret_cast<float2*>(red + wave * 128 + 16 * t + 2 * p) = make_float2(c0, c1);
+      *reinterpret_cast<float2*>(dst + 16 * t + 2 * p) = make_float2(c0, c1);
     } else {
 #pragma unroll
       for (int q = 0; q < 8; ++q)
 #pragma unroll
         for (int rr = 0; rr < 4; ++rr) {
           const int i = 4 * g + rr;
-          if (i < m) red[(wave * m + i) * 128 + q * 16 + j] = macc[q][rr];
+          if (i < m) dst[i * 128 + 16 * q + j] = macc[q][rr];
         }
     }
-    lds_barrier();
-    const int slot = w - sk_owner(nb * KB, a.U, a.G);
-    float* dst = a.part + ((int64_t)nb * a.slots + slot) * m * 128;
-    for (int idx = threadIdx.x; idx < m * 128; idx += 256) {
-      float s = red[idx];
-      s += red[m * 128 + idx];
-      s += red[2 * m * 128 + idx];
-      s += red[3 * m * 128 + idx];
-      store_coherent(dst + idx, s);
-    }
-    lds_barrier();
     clear_acc();
   };
 
-  for (int base = 0; base < iters; base += PF) {
+  // consumption cursor
+  int64_t c_nb = nb0;
+  int c_kt = kt0;
+  int c_b = 0;  // x' block of the run (m == 1)
+  for (int base = 0; base < len; base += PF) {
 #pragma unroll
     for (int s = 0; s < PF; ++s) {
       const int it = base + s;
-      if (it < iters) {
-        const int ui = it >> 1;
-        const int ktl = wave + 4 * (it & 1);
+      if (it < len) {
         const uint32_t spill = spill_from_next(ring[s][0]);
         uint32_t wp[16];
         decode_rowpair<K>(ring[s], spill, wp);
         if constexpr (DOT) {
-          const half2_t xp = *reinterpret_cast<const half2_t*>(xs + (size_t)ui * 128 + ktl * 16 + 2 * p);
+          const uint16_t* xs = reinterpret_cast<const uint16_t*>(wl);
+          const half2_t xp =
+              *reinterpret_cast<const half2_t*>(xs + c_b * 128 + (c_kt & 7) * 16 + 2 * p);
 #pragma unroll
           for (int c = 0; c < 16; ++c)
             dacc[c] = __builtin_amdgcn_fdot2(__builtin_bit_cast(half2_t, wp[c]), xp, dacc[c], false);
@@ -268,8 +257,7 @@ __global__ __launch_bounds__(256) void gemv_sk_kernel(SkArgs a) {
           __builtin_amdgcn_wave_barrier();
           __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront", "local");
           half4_t av = {0, 0, 0, 0};
-          if (j < m)
-            av = *reinterpret_cast<const half4_t*>(xs + ((size_t)ui * m + j) * 128 + ktl * 16 + 4 * g);
+          if (j < m) av = __builtin_bit_cast(half4_t, aring[DOT ? 0 : s]);
 #pragma unroll
           for (int q = 0; q < 8; ++q) {
             const uint32_t b0 = tr[(q * 8 + 2 * g) * 20 + j];
@@ -281,76 +269,70 @@ __global__ __launch_bounds__(256) void gemv_sk_kernel(SkArgs a) {
           __builtin_amdgcn_wave_barrier();
           __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront", "local");
         }
-        // segment end: last k tile pair of the last unit of an n block in the run
-        if (it & 1) {
-          const int64_t u = u0 + ui;
-          if (u + 1 == u1 || (u + 1) % KB == 0) flush(u / KB);
-        }
+        // advance the consumption cursor; segment end at a block end or run end
+        const bool block_end = (c_kt + 1 == KT);
+        if (block_end || it + 1 == len) flush(c_nb);
+        c_kt = block_end ? 0 : c_kt + 1;
+        c_nb += block_end ? 1 : 0;
+        c_b += (c_kt & 7) == 0 ? 1 : 0;
       }
-      // refill the slot (unconditionally, so every step issues exactly one
-      // load and the wait counts stay static); past the end, re-read the last
-      // tile, a cache hit
-      const int nxt = (it + PF < iters) ? it + PF : iters - 1;
-      load_rowpair<K>(tile_ptr(nxt), ring[s]);
+      // refill the slot (unconditionally: every step issues the same loads, so
+      // the wait counts stay static); past the end, re-read the last step
+      load_rowpair<K>(pf_ptr(), ring[s]);
+      if constexpr (!DOT) aring[s] = *pf_afrag();
+      pf_advance();
     }
   }
+}
 
-  // ---- 4. arrivals, then the finishing step of completed n blocks
-  __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0): the coherent stores are done
-  __syncthreads();
-  const int64_t nb_last = (u1 - 1) / KB;
-  const int nseg = (int)(nb_last - nb_first + 1);
-  if (threadIdx.x < nseg) {
-    const int64_t nb = nb_first + threadIdx.x;
-    const int arrivals = sk_owner((nb + 1) * KB - 1, a.U, a.G) - sk_owner(nb * KB, a.U, a.G) + 1;
-    const unsigned int old =
-        __hip_atomic_fetch_add(a.ctr + nb, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-    last_flags[threadIdx.x] = (old + 1u == (unsigned int)arrivals) ? arrivals : 0;
-  }
-  __syncthreads();
-  for (int sg = 0; sg < nseg; ++sg) {
-    const int arrivals = last_flags[sg];
-    if (!arrivals) continue;
-    const int64_t nb = nb_first + sg;
-    const int col = (int)nb * 128 + 2 * lane;
-    const float* src = a.part + (int64_t)nb * a.slots * m * 128;
-    for (int i = wave; i < m; i += 4) {
-      // all slot loads first (they go to the coherence point), then the sum
-      // in slot order
-      float v0[kSkMaxSlots], v1[kSkMaxSlots];
+// Slots of block nb: the waves whose runs intersect it, in run order.
+__device__ __forceinline__ int sk_arrivals(int64_t nb, int64_t KT, int64_t R, int W) {
+  return sk_owner((nb + 1) * KT - 1, R, W) - sk_owner(nb * KT, R, W) + 1;
+}
+
+// One wave per (activation row i, 128-column block nb); lane l owns columns
+// 2l, 2l+1 of the block.
+__global__ __launch_bounds__(256) void gemv_sk_finish(SkArgs a) {
+  const int NB = a.n >> 7;
+  const int task = blockIdx.x * 4 + __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  if (task >= NB * a.m) return;
+  const int m = a.m;
+  const int i = task / NB, nb = task - i * NB;
+  const int lane = threadIdx.x & 63;
+  const int col = nb * 128 + 2 * lane;
+  const int arrivals = sk_arrivals(nb, a.KT, a.R, a.W);
+  const float* src = a.part + ((int64_t)nb * a.slots * m + i) * 128 + 2 * lane;
+  const uint32_t svv = *reinterpret_cast<const uint32_t*>(a.svh + col);
+  uint32_t bv = 0;
+  if (a.bias) bv = *reinterpret_cast<const uint32_t*>(a.bias + col);
+  // slots in order, up to kSkSlotBatch loads in flight
+  float x0 = 0.f, x1 = 0.f;
+  for (int s0 = 0; s0 < arrivals; s0 += kSkSlotBatch) {
+    float2 v[kSkSlotBatch];
 #pragma unroll
-      for (int s = 0; s < kSkMaxSlots; ++s) {
-        if (s < arrivals) {
-          v0[s] = load_coherent(src + ((int64_t)s * m + i) * 128 + 2 * lane);
-          v1[s] = load_coherent(src + ((int64_t)s * m + i) * 128 + 2 * lane + 1);
-        }
-      }
-      float x0 = 0.f, x1 = 0.f;
+    for (int q = 0; q < kSkSlotBatch; ++q)
+      if (s0 + q < arrivals)
+        v[q] = *reinterpret_cast<const float2*>(src + (int64_t)(s0 + q) * m * 128);
 #pragma unroll
-      for (int s = 0; s < kSkMaxSlots; ++s) {
-        if (s < arrivals) {
-          x0 += v0[s];
-          x1 += v1[s];
-        }
+    for (int q = 0; q < kSkSlotBatch; ++q)
+      if (s0 + q < arrivals) {
+        x0 += v[q].x;
+        x1 += v[q].y;
       }
-      fwht128_pair(x0, x1);
-      const uint32_t svv = *reinterpret_cast<const uint32_t*>(a.svh + col);
-      x0 *= kInvSqrt128 * h2f((uint16_t)(svv & 0xFFFF));
-      x1 *= kInvSqrt128 * h2f((uint16_t)(svv >> 16));
-      if (a.bias) {
-        const uint32_t bv = *reinterpret_cast<const uint32_t*>(a.bias + col);
-        x0 += h2f((uint16_t)(bv & 0xFFFF));
-        x1 += h2f((uint16_t)(bv >> 16));
-      }
-      if (a.y_f32)
-        *reinterpret_cast<float2*>(static_cast<float*>(a.y) + (int64_t)i * a.ldy + col) =
-            make_float2(x0, x1);
-      else
-        *reinterpret_cast<uint32_t*>(static_cast<uint16_t*>(a.y) + (int64_t)i * a.ldy + col) =
-            (uint32_t)f2h(x0) | ((uint32_t)f2h(x1) << 16);
-    }
-    if (threadIdx.x == 0) a.ctr[nb] = 0u;  // every arrival is in: ready for the next call
   }
+  fwht128_pair(x0, x1);
+  x0 *= kInvSqrt128 * h2f((uint16_t)(svv & 0xFFFF));
+  x1 *= kInvSqrt128 * h2f((uint16_t)(svv >> 16));
+  if (a.bias) {
+    x0 += h2f((uint16_t)(bv & 0xFFFF));
+    x1 += h2f((uint16_t)(bv >> 16));
+  }
+  if (a.y_f32)
+    *reinterpret_cast<float2*>(static_cast<float*>(a.y) + (int64_t)i * a.ldy + col) =
+        make_float2(x0, x1);
+  else
+    *reinterpret_cast<uint32_t*>(static_cast<uint16_t*>(a.y) + (int64_t)i * a.ldy + col) =
+        (uint32_t)f2h(x0) | ((uint32_t)f2h(x1) << 16);
 }
 
 }  // namespace exl3

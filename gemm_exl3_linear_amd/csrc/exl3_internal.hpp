@@ -37,13 +37,13 @@ hipError_t launch_hadamard(const void* in, bool in_f32, void* out, bool out_f32,
 
 // --- dense linear ----------------------------------------------------------
 struct GemvPlan {
-  int splits;      // workgroups of the persistent grid
-  int kc;          // largest number of (128 x 128) units per workgroup
-  int slots;       // partial-sum slots per 128-column block
+  int splits;        // waves of the persistent grid
+  int kc;            // longest run of row steps per wave
+  int slots;         // partial-sum slots per 128-column block
   size_t lds;        // dynamic LDS bytes of the kernel
-  size_t ctr_bytes;  // arrival counters at the start of the workspace
+  size_t ctr_bytes;  // bytes before the fp32 partials (0: no arrival counters)
   size_t xprep_off;  // offset of the transformed rows x' (m > 1)
-  size_t ws;         // workspace bytes (counters + fp32 partials)
+  size_t ws;         // workspace bytes (partials + x')
 };
 GemvPlan plan_gemv(int k, int n, int m);
 hipError_t launch_gemv(const uint16_t* trellis, const uint16_t* suh, const uint16_t* svh,

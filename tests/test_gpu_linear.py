@@ -165,3 +165,30 @@ def test_workspace_reused_across_sizes():
         torch.cuda.synchronize()
         np.testing.assert_array_equal(G.f16_bits(y), ref[m])
     assert X.exl3_linear_workspace_size(w, 1) <= need
+
+
+@pytest.mark.parametrize("m", [1, 16, 40])
+def test_back_to_back_calls_changing_weights(m):
+    # Calls share one workspace and run back to back with no host sync while
+    # the weights change every call: a result that picked up a partial sum
+    # left by the previous call (stale cache line) would differ from the same
+    # call run alone.  5120 x 17408 spreads every block over many waves, so
+    # the slots of one block come from several XCDs.
+    import torch
+    import gemm_exl3_linear_amd as X
+    k, n, bits, copies, calls = 5120, 17408, 4, 4, 24
+    ds = [synth.linear_inputs(900 + c, m, k, n, bits) for c in range(copies)]
+    ws_ = [G.weight(d) for d in ds]
+    x = G.to_dev(ds[0]["x"])
+    alone = []
+    for w in ws_:
+        alone.append(G.f16_bits(X.exl3_linear(x, w)))
+        torch.cuda.synchronize()
+    ws = torch.zeros(X.exl3_linear_workspace_size(ws_[0], m), dtype=torch.uint8, device=G.dev())
+    ys = torch.empty((calls, m, n), dtype=torch.float16, device=G.dev())
+    for i in range(calls):
+        X.exl3_linear(x, ws_[i % copies], out=ys[i], workspace=ws)
+    torch.cuda.synchronize()
+    got = G.f16_bits(ys)
+    for i in range(calls):
+        np.testing.assert_array_equal(got[i], alone[i % copies], err_msg=f"call {i}")
