@@ -62,24 +62,32 @@ def measured_traffic():
 
 
 def time_calls(fn, steps, warmup, stream):
-    """Returns (mean per-launch time from per-call event pairs, whole-loop time)."""
+    """Returns (mean per-launch time from per-call event pairs, whole-loop time).
+
+    Two timed passes over the same `steps` calls: the whole-loop time comes
+    from one event pair around back-to-back calls (nothing recorded between
+    them), the per-launch time from an event pair around each call."""
     import torch
     for i in range(warmup):
         fn(i)
     torch.cuda.synchronize()
-    starts = [torch.cuda.Event(enable_timing=True) for _ in range(steps)]
-    ends = [torch.cuda.Event(enable_timing=True) for _ in range(steps)]
     t0 = torch.cuda.Event(enable_timing=True)
     t1 = torch.cuda.Event(enable_timing=True)
     t0.record(stream)
     for i in range(steps):
+        fn(warmup + i)
+    t1.record(stream)
+    torch.cuda.synchronize()
+    total = t0.elapsed_time(t1) * 1e-3
+    starts = [torch.cuda.Event(enable_timing=True) for _ in range(steps)]
+    ends = [torch.cuda.Event(enable_timing=True) for _ in range(steps)]
+    for i in range(steps):
         starts[i].record(stream)
         fn(warmup + i)
         ends[i].record(stream)
-    t1.record(stream)
     torch.cuda.synchronize()
     per = sum(s.elapsed_time(e) for s, e in zip(starts, ends)) / steps
-    return per * 1e-3, t0.elapsed_time(t1) * 1e-3
+    return per * 1e-3, total
 
 
 def main():

@@ -80,7 +80,15 @@ __device__ __forceinline__ uint32_t state_hash(const uint32_t (&B)[K + 1], uint3
 // dwords, spill_b is the stream-ordered first dword of the next row pair.
 // Output: out[c] = half2 {W[2p][c], W[2p+1][c]} for the 16 columns c of the
 // tile, i.e. two consecutive k values of one output column.
-template <int K, int C>
+//
+// BIASED = true stops before the codebook's affine step and returns the
+// biased codes b = 1024 + sigma (exact fp16 integers 1024..2044) instead:
+// W = (b - 1534) * 1775 / 2^18 holds exactly before W's own fp16 rounding, so
+// a contraction sum_r b_r x_r - 1534 sum_r x_r, scaled once by 1775 / 2^18,
+// is the product with the unrounded codebook values (relative difference to
+// the fp16-rounded weights at most 2^-12 per weight).  That saves the packed
+// subtract and multiply per weight pair, a quarter of the decode's VALU work.
+template <int K, int C, bool BIASED>
 __device__ __forceinline__ void decode_column(const uint32_t (&B)[K + 1], uint32_t mult,
                                               uint32_t (&out)[16]) {
   const uint32_t h0 = state_hash<K, K * C>(B, mult);
@@ -88,23 +96,27 @@ __device__ __forceinline__ void decode_column(const uint32_t (&B)[K + 1], uint32
   // sigma + 1024 as fp16 bit patterns, packed: low half <- row 2p, high <- 2p+1
   const uint32_t s0 = __builtin_amdgcn_sad_u8(h0, 0u, kHalf1024Pair);
   const uint32_t packed = __builtin_amdgcn_sad_hi_u8(h1, 0u, s0);
-  const half2_t bias = {(_Float16)kSigmaBiasPlus1024, (_Float16)kSigmaBiasPlus1024};
-  const half2_t scale = {(_Float16)kMul1Scale, (_Float16)kMul1Scale};
-  half2_t v = __builtin_bit_cast(half2_t, packed);
-  v = (v - bias) * scale;  // exact subtraction, then the single fp16 rounding
-  out[C] = __builtin_bit_cast(uint32_t, v);
-}
-
-template <int K, int C = 0>
-__device__ __forceinline__ void decode_columns(const uint32_t (&B)[K + 1], uint32_t mult,
-                                               uint32_t (&out)[16]) {
-  if constexpr (C < 16) {
-    decode_column<K, C>(B, mult, out);
-    decode_columns<K, C + 1>(B, mult, out);
+  if constexpr (BIASED) {
+    out[C] = packed;
+  } else {
+    const half2_t bias = {(_Float16)kSigmaBiasPlus1024, (_Float16)kSigmaBiasPlus1024};
+    const half2_t scale = {(_Float16)kMul1Scale, (_Float16)kMul1Scale};
+    half2_t v = __builtin_bit_cast(half2_t, packed);
+    v = (v - bias) * scale;  // exact subtraction, then the single fp16 rounding
+    out[C] = __builtin_bit_cast(uint32_t, v);
   }
 }
 
-template <int K>
+template <int K, bool BIASED, int C = 0>
+__device__ __forceinline__ void decode_columns(const uint32_t (&B)[K + 1], uint32_t mult,
+                                               uint32_t (&out)[16]) {
+  if constexpr (C < 16) {
+    decode_column<K, C, BIASED>(B, mult, out);
+    decode_columns<K, BIASED, C + 1>(B, mult, out);
+  }
+}
+
+template <int K, bool BIASED = false>
 __device__ __forceinline__ void decode_rowpair(const uint32_t (&D)[K], uint32_t spill_b,
                                                uint32_t (&out)[16]) {
   uint32_t B[K + 1];
@@ -112,7 +124,7 @@ __device__ __forceinline__ void decode_rowpair(const uint32_t (&D)[K], uint32_t 
   for (int i = 0; i < K; ++i) B[i] = stream_dword(D[i]);
   B[K] = spill_b;
   const uint32_t mult = kMul1Multiplier;
-  decode_columns<K>(B, mult, out);
+  decode_columns<K, BIASED>(B, mult, out);
 }
 
 // Stream-ordered first dword of the next row pair in the same tile: lane

@@ -13,13 +13,17 @@
 //      m > 1: x' comes from one input-transform launch and each row step's
 //      A fragment travels with the trellis loads.
 //   2. Row step: lane (t, p) loads row pair p of n tile t (one coalesced
-//      4K-byte load per lane), decodes 32 weights into k-pairs and contracts:
+//      4K-byte load per lane), decodes 32 weights into k-pairs of biased
+//      codes b = 1024 + sigma (decode_rowpair<K, true>) and contracts:
 //        m == 1 : v_dot2_f32_f16 with the x' pair of its two rows, 16 column
 //                 accumulators per lane, no LDS traffic;
 //        m >= 2 : k-pairs through a per-wave LDS transpose into MFMA
 //                 16x16x16 f16 (rows padded to 16).
-//   3. Segment end (block changes or run ends): the wave's column sums go to
-//      the segment's partial slot in the fp32 workspace.
+//      alongside, the sum of the segment's x' (a dot with ones at m == 1, a
+//      ninth MFMA against an all-ones B at m >= 2).
+//   3. Segment end (block changes or run ends): sum b x' - 1534 sum x' for
+//      each column goes to the segment's partial slot in the fp32 workspace
+//      (the codebook scale 1775 / 2^18 is applied once, in the finish).
 // gemv_sk_finish, one wave per (activation row, 128-column block): adds the
 // block's slots in slot order, applies the output transform, svh and bias,
 // casts and stores y.  The hand-off between the two is the kernel boundary:
@@ -36,7 +40,7 @@
 namespace exl3 {
 
 constexpr int kGemvSkWaves = 2048;  // 8 waves per CU of the 256-CU MI355X
-constexpr int kSkSlotBatch = 16;    // partial slots loaded per batch in the finish
+constexpr int kSkSlotBatch = 32;    // partial slots loaded per batch in the finish
 constexpr int kSkMaxXBlocks = 8;    // k blocks a run may touch (m == 1)
 
 struct SkArgs {
@@ -194,14 +198,18 @@ __global__ __launch_bounds__(256) void gemv_sk_kernel(SkArgs a) {
 
   // ---- main loop
   float dacc[16];
+  float dxs;        // m == 1: sum of the lane's x' pairs over the segment
   float4_t macc[8];
+  float4_t mxs;     // m >= 2: sum of x' over the segment, per row (any column)
   auto clear_acc = [&]() {
     if constexpr (DOT) {
 #pragma unroll
       for (int c = 0; c < 16; ++c) dacc[c] = 0.f;
+      dxs = 0.f;
     } else {
 #pragma unroll
       for (int q = 0; q < 8; ++q) macc[q] = float4_t{0.f, 0.f, 0.f, 0.f};
+      mxs = float4_t{0.f, 0.f, 0.f, 0.f};
     }
   };
   clear_acc();
@@ -213,6 +221,8 @@ __global__ __launch_bounds__(256) void gemv_sk_kernel(SkArgs a) {
     const int slot = wid - sk_owner(nb * KT, a.R, a.W);
     float* dst = a.part + ((int64_t)nb * a.slots + slot) * m * 128;
     if constexpr (DOT) {
+#pragma unroll
+      for (int c = 0; c < 16; ++c) dacc[c] = __builtin_fmaf(-kSigmaBiasPlus1024, dxs, dacc[c]);
       float c0, c1;
       reduce_rowpairs(dacc, c0, c1);
       *reinterpret_cast<float2*>(dst + 16 * t + 2 * p) = make_float2(c0, c1);
@@ -222,7 +232,7 @@ __global__ __launch_bounds__(256) void gemv_sk_kernel(SkArgs a) {
 #pragma unroll
         for (int rr = 0; rr < 4; ++rr) {
           const int i = 4 * g + rr;
-          if (i < m) dst[i * 128 + 16 * q + j] = macc[q][rr];
+          if (i < m) dst[i * 128 + 16 * q + j] = __builtin_fmaf(-kSigmaBiasPlus1024, mxs[rr], macc[q][rr]);
         }
     }
     clear_acc();
@@ -239,11 +249,13 @@ __global__ __launch_bounds__(256) void gemv_sk_kernel(SkArgs a) {
       if (it < len) {
         const uint32_t spill = spill_from_next(ring[s][0]);
         uint32_t wp[16];
-        decode_rowpair<K>(ring[s], spill, wp);
+        decode_rowpair<K, true>(ring[s], spill, wp);
         if constexpr (DOT) {
           const uint16_t* xs = reinterpret_cast<const uint16_t*>(wl);
           const half2_t xp =
               *reinterpret_cast<const half2_t*>(xs + c_b * 128 + (c_kt & 7) * 16 + 2 * p);
+          const half2_t ones = {(_Float16)1.0f, (_Float16)1.0f};
+          dxs = __builtin_amdgcn_fdot2(xp, ones, dxs, false);
 #pragma unroll
           for (int c = 0; c < 16; ++c)
             dacc[c] = __builtin_amdgcn_fdot2(__builtin_bit_cast(half2_t, wp[c]), xp, dacc[c], false);
@@ -265,6 +277,8 @@ __global__ __launch_bounds__(256) void gemv_sk_kernel(SkArgs a) {
             const half4_t bv = __builtin_bit_cast(half4_t, make_uint2(b0, b1));
             macc[q] = __builtin_amdgcn_mfma_f32_16x16x16f16(av, bv, macc[q], 0, 0, 0);
           }
+          const half4_t ones4 = {(_Float16)1.0f, (_Float16)1.0f, (_Float16)1.0f, (_Float16)1.0f};
+          mxs = __builtin_amdgcn_mfma_f32_16x16x16f16(av, ones4, mxs, 0, 0, 0);
           __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront", "local");
           __builtin_amdgcn_wave_barrier();
           __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront", "local");
@@ -321,8 +335,10 @@ __global__ __launch_bounds__(256) void gemv_sk_finish(SkArgs a) {
       }
   }
   fwht128_pair(x0, x1);
-  x0 *= kInvSqrt128 * h2f((uint16_t)(svv & 0xFFFF));
-  x1 *= kInvSqrt128 * h2f((uint16_t)(svv >> 16));
+  // codebook scale and the transform's normalisation as one constant
+  constexpr float kOut = kMul1Scale * kInvSqrt128;
+  x0 *= kOut * h2f((uint16_t)(svv & 0xFFFF));
+  x1 *= kOut * h2f((uint16_t)(svv >> 16));
   if (a.bias) {
     x0 += h2f((uint16_t)(bv & 0xFFFF));
     x1 += h2f((uint16_t)(bv >> 16));
