@@ -36,6 +36,8 @@ exl3_status check_weight(const exl3_weight* w, int mult, bool need_signs) {
   if (w->bits < 1 || w->bits > 8) return EXL3_E_INVALID;
   if (w->codebook != EXL3_CODEBOOK_MUL1) return EXL3_E_UNSUPPORTED;
   if (w->k <= 0 || w->n <= 0 || w->k % mult || w->n % mult) return EXL3_E_INVALID;
+  // tile counts index the kernels' 32-bit work plans
+  if ((int64_t)(w->k / 16) * (w->n / 16) >= ((int64_t)1 << 31)) return EXL3_E_INVALID;
   if (!w->trellis || !aligned16(w->trellis)) return EXL3_E_INVALID;
   if (need_signs) {
     if (!w->suh || !w->svh || !aligned16(w->suh) || !aligned16(w->svh)) return EXL3_E_INVALID;
@@ -133,6 +135,8 @@ exl3_status exl3_linear(const exl3_weight* w, const void* x, int64_t m, int64_t 
   if (m < 0 || m > ((int64_t)1 << 24)) return EXL3_E_INVALID;
   if (y_dtype != EXL3_F16 && y_dtype != EXL3_F32) return EXL3_E_INVALID;
   if (ldx < w->k || ldy < w->n || ldx % 8 || ldy % 8) return EXL3_E_INVALID;
+  // the kernels address a tensor's trellis with 32-bit byte offsets
+  if ((int64_t)w->k * w->n / 8 * w->bits >= ((int64_t)1 << 32)) return EXL3_E_INVALID;
   if (m == 0) return EXL3_OK;
   if (!x || !y || !aligned16(x) || !aligned16(y)) return EXL3_E_INVALID;
   const size_t need = linear_ws(w, m);

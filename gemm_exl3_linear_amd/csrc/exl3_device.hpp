@@ -157,6 +157,41 @@ __device__ __forceinline__ void load_rowpair(const uint32_t* __restrict__ p, uin
   }
 }
 
+// Buffer-descriptor word 3 of a raw (unformatted, stride 0) buffer on gfx9
+// parts: 32-bit data format, no swizzle.
+constexpr int kBufferRsrcWord3 = 0x00020000;
+
+// Raw buffer descriptor over [base, base + bytes): out-of-range loads return 0.
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void* base, uint32_t bytes) {
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), (short)0, (int)bytes,
+                                           kBufferRsrcWord3);
+}
+
+// The lane's 2K words through a buffer descriptor: byte offset voff + soff
+// (soff uniform), K dwords in the widest loads K allows.
+template <int K, int N>
+__device__ __forceinline__ void load_rowpair_buf(__amdgpu_buffer_rsrc_t rs, uint32_t voff,
+                                                 uint32_t soff, uint32_t (&D)[N]) {
+  static_assert(N >= K, "destination too small");
+  typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
+  typedef uint32_t u32x3 __attribute__((ext_vector_type(3)));
+  typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+#pragma unroll
+  for (int i = 0; i + 4 <= K; i += 4) {
+    const u32x4 v = __builtin_amdgcn_raw_buffer_load_b128(rs, (int)voff + 4 * i, (int)soff, 0);
+    D[i] = v.x; D[i + 1] = v.y; D[i + 2] = v.z; D[i + 3] = v.w;
+  }
+  if constexpr (K % 4 == 3) {
+    const u32x3 v = __builtin_amdgcn_raw_buffer_load_b96(rs, (int)voff + 4 * (K - 3), (int)soff, 0);
+    D[K - 3] = v.x; D[K - 2] = v.y; D[K - 1] = v.z;
+  } else if constexpr (K % 4 == 2) {
+    const u32x2 v = __builtin_amdgcn_raw_buffer_load_b64(rs, (int)voff + 4 * (K - 2), (int)soff, 0);
+    D[K - 2] = v.x; D[K - 1] = v.y;
+  } else if constexpr (K % 4 == 1) {
+    D[K - 1] = __builtin_amdgcn_raw_buffer_load_b32(rs, (int)voff + 4 * (K - 1), (int)soff, 0);
+  }
+}
+
 // ---------------------------------------------------------------------------
 // 128-point Walsh-Hadamard transform held by one wave: lane l owns elements
 // 2l (a) and 2l+1 (b).  Butterfly (u, v) -> (u + v, u - v) with u the lower

@@ -111,8 +111,10 @@ hipError_t launch_gemv(const uint16_t* trellis, const uint16_t* suh, const uint1
   a.k = k;
   a.n = n;
   a.KT = k / 16;
-  a.R = (int64_t)a.KT * (n / 128);
+  a.R = a.KT * (n / 128);
   a.W = plan.splits;
+  a.q = a.R / a.W;
+  a.rem = a.R - a.q * a.W;
   a.slots = plan.slots;
   a.part = reinterpret_cast<float*>(base + plan.ctr_bytes);
   a.svh = svh;

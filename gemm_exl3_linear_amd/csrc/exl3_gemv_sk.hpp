@@ -3,20 +3,22 @@
 // Work decomposition ("stream-k" at wave granularity).  A row step is one k
 // tile (16 rows of k) of one 128-column block (8 n tiles of 16 columns): the
 // R = (n/128) * (k/16) row steps are ordered block-major and every wave of the
-// persistent grid takes one contiguous run of them, so runs differ by at most
-// one row step.  Waves never wait for each other: each keeps PF row-pair loads
-// in flight from the start to the end of its run, across block boundaries.
+// persistent grid takes one contiguous run of them (q = R / W steps, one more
+// for the first R % W waves).  Waves never wait for each other: each keeps PF
+// row-pair loads in flight from the start to the end of its run, across block
+// boundaries.
 //
 // gemv_sk_kernel, per wave:
-//   1. m == 1: x' = (x .* suh) H for the (at most a few) k blocks its run
-//      touches, computed in the wave after the first trellis loads went out;
+//   1. m == 1: x' = (x .* suh) H for the (at most eight) k blocks its run
+//      touches, four blocks at a time, after the first trellis loads went out;
 //      m > 1: x' comes from one input-transform launch and each row step's
 //      A fragment travels with the trellis loads.
 //   2. Row step: lane (t, p) loads row pair p of n tile t (one coalesced
-//      4K-byte load per lane), decodes 32 weights into k-pairs of biased
-//      codes b = 1024 + sigma (decode_rowpair<K, true>) and contracts:
+//      4K-byte load per lane) and the first dword of the next row pair (its
+//      spill word), decodes 32 weights into k-pairs of biased codes
+//      b = 1024 + sigma (decode_rowpair<K, true>) and contracts:
 //        m == 1 : v_dot2_f32_f16 with the x' pair of its two rows, 16 column
-//                 accumulators per lane, no LDS traffic;
+//                 accumulators per lane;
 //        m >= 2 : k-pairs through a per-wave LDS transpose into MFMA
 //                 16x16x16 f16 (rows padded to 16).
 //      alongside, the sum of the segment's x' (a dot with ones at m == 1, a
@@ -52,8 +54,9 @@ struct SkArgs {
   int m;
   int k, n;
   int KT;                   // k / 16
-  int64_t R;                // row steps = (n / 128) * KT
+  int R;                    // row steps = (n / 128) * KT
   int W;                    // waves of the grid
+  int q, rem;               // run lengths: q + 1 for waves < rem, q for the rest
   int slots;                // partial slots per block
   float* part;              // fp32 [n/128][slots][m][128]
   const uint16_t* svh;
@@ -63,9 +66,15 @@ struct SkArgs {
   int y_f32;
 };
 
-// wave whose run contains row step r (runs are [w R / W, (w+1) R / W))
-__device__ __forceinline__ int sk_owner(int64_t r, int64_t R, int W) {
-  return (int)(((r + 1) * W - 1) / R);
+// first row step of wave w's run
+__device__ __forceinline__ int sk_start(int w, int q, int rem) {
+  return w * q + (w < rem ? w : rem);
+}
+
+// wave whose run contains row step r
+__device__ __forceinline__ int sk_owner(int r, int q, int rem) {
+  const int big = rem * (q + 1);  // steps covered by the longer runs
+  return r < big ? r / (q + 1) : rem + (r - big) / q;
 }
 
 // dot2 accumulators: sum over the 8 row-pair lanes of a tile; lane p ends with
@@ -106,6 +115,43 @@ __device__ __forceinline__ void reduce_rowpairs(float (&acc)[16], float& c0, flo
 constexpr int kSkWaveLdsDot = kSkMaxXBlocks * 128 * 2;
 constexpr int kSkWaveLdsMfma = 64 * 20 * 4;
 
+// Input transform of up to four 128-element k blocks at once (m == 1): lane
+// l holds elements 8 (l % 16) .. 8 (l % 16) + 7 of block l / 16, so the three
+// lowest butterfly strides stay inside the lane and the other four pair
+// lanes l ^ 1, 2, 4, 8 of the same 16-lane group (ds_swizzle, no LDS
+// memory).  v[e] = x * suh on entry, the unnormalised transform on exit.
+template <int MASK>
+__device__ __forceinline__ float swizzle_xor_f(float v) {
+  // bitmask mode: source lane = (lane & 0x1F) ^ MASK inside each 32 lanes
+  return __int_as_float(__builtin_amdgcn_ds_swizzle(__float_as_int(v), (MASK << 10) | 0x1F));
+}
+
+template <int MASK>
+__device__ __forceinline__ void fwht_lane_stage(float (&v)[8]) {
+  float pv[8];
+#pragma unroll
+  for (int e = 0; e < 8; ++e) pv[e] = swizzle_xor_f<MASK>(v[e]);
+  const bool upper = (lane_id() & (uint32_t)MASK) != 0;
+#pragma unroll
+  for (int e = 0; e < 8; ++e) v[e] = upper ? (pv[e] - v[e]) : (v[e] + pv[e]);
+}
+
+__device__ __forceinline__ void fwht128_x8(float (&v)[8]) {
+#pragma unroll
+  for (int h = 1; h < 8; h <<= 1)
+#pragma unroll
+    for (int e = 0; e < 8; ++e)
+      if ((e & h) == 0) {
+        const float u = v[e], w = v[e + h];
+        v[e] = u + w;
+        v[e + h] = u - w;
+      }
+  fwht_lane_stage<1>(v);
+  fwht_lane_stage<2>(v);
+  fwht_lane_stage<4>(v);
+  fwht_lane_stage<8>(v);
+}
+
 template <int K, bool DOT, int PF>
 __global__ __launch_bounds__(256) void gemv_sk_kernel(SkArgs a) {
   constexpr int WAVE_LDS = DOT ? kSkWaveLdsDot : kSkWaveLdsMfma;
@@ -113,82 +159,107 @@ __global__ __launch_bounds__(256) void gemv_sk_kernel(SkArgs a) {
 
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int wid = blockIdx.x * 4 + wave;
-  const int64_t r0 = (int64_t)wid * a.R / a.W;
-  const int64_t r1 = (int64_t)(wid + 1) * a.R / a.W;
-  const int len = (int)(r1 - r0);
+  const int len = a.q + (wid < a.rem ? 1 : 0);
   if (len <= 0) return;
+  const int r0 = sk_start(wid, a.q, a.rem);
   const int m = a.m;
-  const int nt = a.n >> 4;
   const int KT = a.KT;
   const int lane = threadIdx.x & 63;
   const int t = lane >> 3, p = lane & 7;   // decode role
   const int g = lane >> 4, j = lane & 15;  // MFMA role
   unsigned char* wl = smem + wave * WAVE_LDS;
 
-  // Row-step cursors are uniform: (nb, kt) advance by one k tile per step and
-  // wrap to the next block at k/16, so no division happens inside the loop.
-  const int64_t nb0 = r0 / KT;
-  const int kt0 = (int)(r0 - nb0 * KT);
-  const int64_t tile_dw = 8 * K;                 // dwords per 16x16 tile
-  const int64_t kt_dw = (int64_t)nt * tile_dw;   // dwords per k tile row
-  const uint32_t* tr_lane = reinterpret_cast<const uint32_t*>(a.trellis) + K * p + t * tile_dw;
-  // prefetch cursor
-  int64_t pf_nb = nb0;
-  int pf_kt = kt0;
-  int pf_left = len;  // row steps the prefetch cursor may still visit
-  auto pf_ptr = [&]() -> const uint32_t* {
-    return tr_lane + (int64_t)pf_kt * kt_dw + pf_nb * 8 * tile_dw;
-  };
-  auto pf_afrag = [&]() -> const uint2* {
-    const int row = j < m ? j : 0;
-    return reinterpret_cast<const uint2*>(a.xprep + (int64_t)row * a.k + pf_kt * 16 + 4 * g);
+  // The run starts at k tile kt0 of block nb0; the wave is partial slot
+  // slot0 of that block and slot 0 of every later one.
+  const int nb0 = r0 / KT;
+  const int kt0 = r0 - nb0 * KT;
+  const int slot0 = wid - sk_owner(nb0 * KT, a.q, a.rem);
+
+  // Trellis addressing.  One buffer descriptor per 128-column block covers
+  // its k range; a row step is a uniform offset (kt * bytes of a k-tile row),
+  // a lane adds its row pair and the first dword of the next row pair of the
+  // same tile (the spill word, cyclic inside the tile).
+  constexpr int kTileBytes = 32 * K;
+  constexpr int kBlkBytes = 8 * kTileBytes;
+  const uint32_t kt_bytes = (uint32_t)(a.n >> 4) * kTileBytes;  // whole tensor < 2^32 B
+  const uint32_t col_bytes = (uint32_t)(KT - 1) * kt_bytes + kBlkBytes;
+  const uint32_t lane_off = (uint32_t)(t * kTileBytes + 4 * K * p);
+  const uint32_t spill_off = (uint32_t)(t * kTileBytes + 4 * K * ((p + 1) & 7));
+  const unsigned char* tr0 = reinterpret_cast<const unsigned char*>(a.trellis);
+  int pf_nb = nb0, pf_kt = kt0, pf_left = len;
+  uint32_t pf_soff = (uint32_t)kt0 * kt_bytes;
+  __amdgpu_buffer_rsrc_t pf_rs = make_rsrc(tr0 + (int64_t)pf_nb * kBlkBytes, col_bytes);
+  // m >= 2: the A fragment of a row step, x'[j][16 kt + 4 g .. + 3]
+  __amdgpu_buffer_rsrc_t x_rs = make_rsrc(a.xprep, DOT ? 0u : (uint32_t)m * a.k * 2);
+  const uint32_t x_voff = (uint32_t)(((j < m ? j : 0) * a.k + 4 * g) * 2);
+  auto pf_load = [&](uint32_t (&D)[K + 1], uint2& A) {
+    load_rowpair_buf<K>(pf_rs, lane_off, pf_soff, D);
+    D[K] = __builtin_amdgcn_raw_buffer_load_b32(pf_rs, (int)spill_off, (int)pf_soff, 0);
+    if constexpr (!DOT) {
+      typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
+      const u32x2 v = __builtin_amdgcn_raw_buffer_load_b64(x_rs, (int)x_voff, pf_kt * 32, 0);
+      A = make_uint2(v.x, v.y);
+    }
   };
   auto pf_advance = [&]() {  // stays on the last row step once the run is exhausted
-    const int adv = pf_left > 1 ? 1 : 0;  // selects, not branches: the loads
-    pf_left -= adv;                       // around stay unconditional
-    pf_kt += adv;
-    const int wrap = pf_kt == KT ? 1 : 0;
-    pf_kt = wrap ? 0 : pf_kt;
-    pf_nb += wrap;
+    if (pf_left > 1) {
+      --pf_left;
+      ++pf_kt;
+      pf_soff += kt_bytes;
+      if (pf_kt == KT) {
+        pf_kt = 0;
+        pf_soff = 0;
+        ++pf_nb;
+        pf_rs = make_rsrc(tr0 + (int64_t)pf_nb * kBlkBytes, col_bytes);
+      }
+    }
   };
 
-  // ---- m == 1: x' for the k blocks of the run; block b of the run is k block
-  // (kt0 / 8 + b) mod k/128.  These loads go out first (a fixed number of them,
-  // so the wait below counts only the trellis loads issued after them).
-  const int kb0 = kt0 >> 3;
-  const int KBn = KT >> 3;
-  uint32_t xv[DOT ? kSkMaxXBlocks : 1], sv[DOT ? kSkMaxXBlocks : 1];
+  // ---- m == 1: x and suh of the k blocks the run touches go out first: k
+  // block b of the run is (kt0 / 8 + b) mod k/128; lane l loads 8 elements of
+  // run block l / 16 (first round) and 4 + l / 16 (second round).
   const int nblk = ((kt0 & 7) + len + 7) >> 3;
+  uint4 xv[DOT ? 2 : 1], sv[DOT ? 2 : 1];
   if constexpr (DOT) {
+    const int kb0 = kt0 >> 3, KBn = KT >> 3;
 #pragma unroll
-    for (int b = 0; b < kSkMaxXBlocks; ++b) {
+    for (int rd = 0; rd < 2; ++rd) {
+      const int b = 4 * rd + g;
       const int bb = b < nblk ? b : nblk - 1;
-      const int kb = (kb0 + bb) % KBn;
-      const int kk = kb * 128 + 2 * lane;
-      xv[b] = *reinterpret_cast<const uint32_t*>(a.x + kk);
-      sv[b] = *reinterpret_cast<const uint32_t*>(a.suh + kk);
+      const int kk = ((kb0 + bb) % KBn) * 128 + 8 * j;
+      xv[rd] = *reinterpret_cast<const uint4*>(a.x + kk);
+      sv[rd] = *reinterpret_cast<const uint4*>(a.suh + kk);
     }
   }
 
-  uint32_t ring[PF][K];
-  uint2 aring[DOT ? 1 : PF];
+  uint32_t ring[PF][K + 1];
+  uint2 aring[PF];
 #pragma unroll
   for (int s = 0; s < PF; ++s) {
-    load_rowpair<K>(pf_ptr(), ring[s]);
-    if constexpr (!DOT) aring[s] = *pf_afrag();
+    pf_load(ring[s], aring[s]);
     pf_advance();
   }
 
   if constexpr (DOT) {
     uint16_t* xs = reinterpret_cast<uint16_t*>(wl);
 #pragma unroll
-    for (int b = 0; b < kSkMaxXBlocks; ++b) {
-      if (b < nblk) {
-        float x0 = h2f((uint16_t)(xv[b] & 0xFFFF)) * h2f((uint16_t)(sv[b] & 0xFFFF));
-        float x1 = h2f((uint16_t)(xv[b] >> 16)) * h2f((uint16_t)(sv[b] >> 16));
-        fwht128_pair(x0, x1);
-        *reinterpret_cast<uint32_t*>(xs + b * 128 + 2 * lane) =
-            (uint32_t)f2h(x0 * kInvSqrt128) | ((uint32_t)f2h(x1 * kInvSqrt128) << 16);
+    for (int rd = 0; rd < 2; ++rd) {
+      if (4 * rd < nblk) {
+        const uint32_t xw[4] = {xv[rd].x, xv[rd].y, xv[rd].z, xv[rd].w};
+        const uint32_t sw[4] = {sv[rd].x, sv[rd].y, sv[rd].z, sv[rd].w};
+        float v[8];
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          v[2 * e] = h2f((uint16_t)(xw[e] & 0xFFFF)) * h2f((uint16_t)(sw[e] & 0xFFFF));
+          v[2 * e + 1] = h2f((uint16_t)(xw[e] >> 16)) * h2f((uint16_t)(sw[e] >> 16));
+        }
+        fwht128_x8(v);
+        uint32_t o[4];
+#pragma unroll
+        for (int e = 0; e < 4; ++e)
+          o[e] = (uint32_t)f2h(v[2 * e] * kInvSqrt128) | ((uint32_t)f2h(v[2 * e + 1] * kInvSqrt128) << 16);
+        if (4 * rd + g < nblk)
+          *reinterpret_cast<uint4*>(xs + (4 * rd + g) * 128 + 8 * j) = make_uint4(o[0], o[1], o[2], o[3]);
       }
     }
     __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront", "local");
@@ -217,8 +288,7 @@ __global__ __launch_bounds__(256) void gemv_sk_kernel(SkArgs a) {
   uint32_t* my = tr + (t * 8 + p) * 20;
 
   // segment end: the wave's column sums to the segment's slot (no wait)
-  auto flush = [&](int64_t nb) {
-    const int slot = wid - sk_owner(nb * KT, a.R, a.W);
+  auto flush = [&](int nb, int slot) {
     float* dst = a.part + ((int64_t)nb * a.slots + slot) * m * 128;
     if constexpr (DOT) {
 #pragma unroll
@@ -238,27 +308,33 @@ __global__ __launch_bounds__(256) void gemv_sk_kernel(SkArgs a) {
     clear_acc();
   };
 
-  // consumption cursor
-  int64_t c_nb = nb0;
-  int c_kt = kt0;
-  int c_b = 0;  // x' block of the run (m == 1)
+  // The x' pair of step `it` is at byte 32 (it + kt0 % 8) + 4 p of the wave's
+  // region: one k tile is 32 bytes of x', and k blocks of the run follow each
+  // other (a block column ends at a k-block boundary).  It is read one step
+  // ahead; the read after the last step stays inside the region
+  // (runs are at most 48 steps: 32 (48 + 8) + 32 <= 2048 bytes).
+  const unsigned char* xlane = wl + 32 * (kt0 & 7) + 4 * p;
+  half2_t xp = {0, 0};
+  if constexpr (DOT) xp = *reinterpret_cast<const half2_t*>(xlane);
+  int c_nb = nb0, c_slot = slot0;
+  int to_end = KT - kt0;  // row steps left in the current block
   for (int base = 0; base < len; base += PF) {
+    const unsigned char* xg = xlane + 32 * base;
 #pragma unroll
     for (int s = 0; s < PF; ++s) {
       const int it = base + s;
       if (it < len) {
-        const uint32_t spill = spill_from_next(ring[s][0]);
         uint32_t wp[16];
-        decode_rowpair<K, true>(ring[s], spill, wp);
+        decode_rowpair<K, true>(*reinterpret_cast<const uint32_t(*)[K]>(ring[s]),
+                                stream_dword(ring[s][K]), wp);
         if constexpr (DOT) {
-          const uint16_t* xs = reinterpret_cast<const uint16_t*>(wl);
-          const half2_t xp =
-              *reinterpret_cast<const half2_t*>(xs + c_b * 128 + (c_kt & 7) * 16 + 2 * p);
+          const half2_t xc = xp;
+          xp = *reinterpret_cast<const half2_t*>(xg + 32 * (s + 1));
           const half2_t ones = {(_Float16)1.0f, (_Float16)1.0f};
-          dxs = __builtin_amdgcn_fdot2(xp, ones, dxs, false);
+          dxs = __builtin_amdgcn_fdot2(xc, ones, dxs, false);
 #pragma unroll
           for (int c = 0; c < 16; ++c)
-            dacc[c] = __builtin_amdgcn_fdot2(__builtin_bit_cast(half2_t, wp[c]), xp, dacc[c], false);
+            dacc[c] = __builtin_amdgcn_fdot2(__builtin_bit_cast(half2_t, wp[c]), xc, dacc[c], false);
         } else {
           uint4* my4 = reinterpret_cast<uint4*>(my);
           my4[0] = make_uint4(wp[0], wp[1], wp[2], wp[3]);
@@ -269,7 +345,7 @@ __global__ __launch_bounds__(256) void gemv_sk_kernel(SkArgs a) {
           __builtin_amdgcn_wave_barrier();
           __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront", "local");
           half4_t av = {0, 0, 0, 0};
-          if (j < m) av = __builtin_bit_cast(half4_t, aring[DOT ? 0 : s]);
+          if (j < m) av = __builtin_bit_cast(half4_t, aring[s]);
 #pragma unroll
           for (int q = 0; q < 8; ++q) {
             const uint32_t b0 = tr[(q * 8 + 2 * g) * 20 + j];
@@ -283,25 +359,28 @@ __global__ __launch_bounds__(256) void gemv_sk_kernel(SkArgs a) {
           __builtin_amdgcn_wave_barrier();
           __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront", "local");
         }
-        // advance the consumption cursor; segment end at a block end or run end
-        const bool block_end = (c_kt + 1 == KT);
-        if (block_end || it + 1 == len) flush(c_nb);
-        c_kt = block_end ? 0 : c_kt + 1;
-        c_nb += block_end ? 1 : 0;
-        c_b += (c_kt & 7) == 0 ? 1 : 0;
+        // segment end at a block end or the run's end
+        --to_end;
+        if (to_end == 0 || it + 1 == len) {
+          flush(c_nb, c_slot);
+          c_slot = 0;
+          if (to_end == 0) {
+            ++c_nb;
+            to_end = KT;
+          }
+        }
       }
       // refill the slot (unconditionally: every step issues the same loads, so
       // the wait counts stay static); past the end, re-read the last step
-      load_rowpair<K>(pf_ptr(), ring[s]);
-      if constexpr (!DOT) aring[s] = *pf_afrag();
+      pf_load(ring[s], aring[s]);
       pf_advance();
     }
   }
 }
 
 // Slots of block nb: the waves whose runs intersect it, in run order.
-__device__ __forceinline__ int sk_arrivals(int64_t nb, int64_t KT, int64_t R, int W) {
-  return sk_owner((nb + 1) * KT - 1, R, W) - sk_owner(nb * KT, R, W) + 1;
+__device__ __forceinline__ int sk_arrivals(int nb, int KT, int q, int rem) {
+  return sk_owner((nb + 1) * KT - 1, q, rem) - sk_owner(nb * KT, q, rem) + 1;
 }
 
 // One wave per (activation row i, 128-column block nb); lane l owns columns
@@ -314,7 +393,7 @@ __global__ __launch_bounds__(256) void gemv_sk_finish(SkArgs a) {
   const int i = task / NB, nb = task - i * NB;
   const int lane = threadIdx.x & 63;
   const int col = nb * 128 + 2 * lane;
-  const int arrivals = sk_arrivals(nb, a.KT, a.R, a.W);
+  const int arrivals = sk_arrivals(nb, a.KT, a.q, a.rem);
   const float* src = a.part + ((int64_t)nb * a.slots * m + i) * 128 + 2 * lane;
   const uint32_t svv = *reinterpret_cast<const uint32_t*>(a.svh + col);
   uint32_t bv = 0;
