@@ -77,13 +77,13 @@ struct SkRun {
   static hipError_t run(const SkArgs& a, const GemvPlan& plan, hipStream_t s) {
     const dim3 grid((unsigned)(a.W / 4));
     if (a.m == 1)
-      hipLaunchKernelGGL((gemv_sk_kernel<K, true, 8>), grid, dim3(256), 0, s, a);
+      hipLaunchKernelGGL((gemv_sk_kernel<K, true, 4>), grid, dim3(256), 0, s, a);
     else
       hipLaunchKernelGGL((gemv_sk_kernel<K, false, 8>), grid, dim3(256), 0, s, a);
     const hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
-    const int tasks = (a.n / 128) * a.m;
-    hipLaunchKernelGGL(gemv_sk_finish, dim3((unsigned)((tasks + 3) / 4)), dim3(256), 0, s, a);
+    const int tasks = (a.n / 128) * a.m;  // one 64-thread workgroup each
+    hipLaunchKernelGGL(gemv_sk_finish, dim3((unsigned)tasks), dim3(64), 0, s, a);
     return hipGetLastError();
   }
 };

@@ -42,7 +42,7 @@
 namespace exl3 {
 
 constexpr int kGemvSkWaves = 2048;  // 8 waves per CU of the 256-CU MI355X
-constexpr int kSkSlotBatch = 32;    // partial slots loaded per batch in the finish
+constexpr int kSkSlotBatch = 8;     // partial slots per lane loaded per batch in the finish
 constexpr int kSkMaxXBlocks = 8;    // k blocks a run may touch (m == 1)
 
 struct SkArgs {
@@ -383,51 +383,75 @@ __device__ __forceinline__ int sk_arrivals(int nb, int KT, int q, int rem) {
   return sk_owner((nb + 1) * KT - 1, q, rem) - sk_owner(nb * KT, q, rem) + 1;
 }
 
-// One wave per (activation row i, 128-column block nb); lane l owns columns
-// 2l, 2l+1 of the block.
-__global__ __launch_bounds__(256) void gemv_sk_finish(SkArgs a) {
+// One wave (a 64-thread workgroup, so the tasks spread over the CUs) per
+// (activation row i, 128-column block nb).  Lane l owns columns
+// 8 (l % 16) .. 8 (l % 16) + 7 of the block and sums the block's slots
+// l / 16, l / 16 + 4, l / 16 + 8, ... in that order; the four slot groups are
+// then combined as (g0 + g1) + (g2 + g3) (fp32 addition commutes, so every
+// lane ends with the same total whichever of a pair it holds).  The output
+// transform is three in-lane butterfly stages and four lane swizzles inside
+// each group of 16 lanes; lanes 0..15 store.
+__global__ __launch_bounds__(64) void gemv_sk_finish(SkArgs a) {
   const int NB = a.n >> 7;
-  const int task = blockIdx.x * 4 + __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
-  if (task >= NB * a.m) return;
   const int m = a.m;
+  const int task = (int)blockIdx.x;
   const int i = task / NB, nb = task - i * NB;
-  const int lane = threadIdx.x & 63;
-  const int col = nb * 128 + 2 * lane;
+  const int lane = (int)threadIdx.x;
+  const int c8 = 8 * (lane & 15);
+  const int sg = lane >> 4;
+  const int col = nb * 128 + c8;
   const int arrivals = sk_arrivals(nb, a.KT, a.q, a.rem);
-  const float* src = a.part + ((int64_t)nb * a.slots * m + i) * 128 + 2 * lane;
-  const uint32_t svv = *reinterpret_cast<const uint32_t*>(a.svh + col);
-  uint32_t bv = 0;
-  if (a.bias) bv = *reinterpret_cast<const uint32_t*>(a.bias + col);
-  // slots in order, up to kSkSlotBatch loads in flight
-  float x0 = 0.f, x1 = 0.f;
-  for (int s0 = 0; s0 < arrivals; s0 += kSkSlotBatch) {
-    float2 v[kSkSlotBatch];
+  const float* src = a.part + ((int64_t)nb * a.slots * m + i) * 128 + c8;
+  const uint4 svv = *reinterpret_cast<const uint4*>(a.svh + col);
+  uint4 bv = make_uint4(0, 0, 0, 0);
+  if (a.bias) bv = *reinterpret_cast<const uint4*>(a.bias + col);
+  float v[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
+  for (int s0 = sg; s0 < arrivals; s0 += 4 * kSkSlotBatch) {
+    float4 lo[kSkSlotBatch], hi[kSkSlotBatch];
 #pragma unroll
     for (int q = 0; q < kSkSlotBatch; ++q)
-      if (s0 + q < arrivals)
-        v[q] = *reinterpret_cast<const float2*>(src + (int64_t)(s0 + q) * m * 128);
+      if (s0 + 4 * q < arrivals) {
+        const float4* p4 = reinterpret_cast<const float4*>(src + (int64_t)(s0 + 4 * q) * m * 128);
+        lo[q] = p4[0];
+        hi[q] = p4[1];
+      }
 #pragma unroll
     for (int q = 0; q < kSkSlotBatch; ++q)
-      if (s0 + q < arrivals) {
-        x0 += v[q].x;
-        x1 += v[q].y;
+      if (s0 + 4 * q < arrivals) {
+        v[0] += lo[q].x; v[1] += lo[q].y; v[2] += lo[q].z; v[3] += lo[q].w;
+        v[4] += hi[q].x; v[5] += hi[q].y; v[6] += hi[q].z; v[7] += hi[q].w;
       }
   }
-  fwht128_pair(x0, x1);
+#pragma unroll
+  for (int e = 0; e < 8; ++e) v[e] += swizzle_xor_f<16>(v[e]);
+#pragma unroll
+  for (int e = 0; e < 8; ++e) v[e] += shfl_xor_f(v[e], 32);
+  fwht128_x8(v);
   // codebook scale and the transform's normalisation as one constant
   constexpr float kOut = kMul1Scale * kInvSqrt128;
-  x0 *= kOut * h2f((uint16_t)(svv & 0xFFFF));
-  x1 *= kOut * h2f((uint16_t)(svv >> 16));
-  if (a.bias) {
-    x0 += h2f((uint16_t)(bv & 0xFFFF));
-    x1 += h2f((uint16_t)(bv >> 16));
+  const uint32_t sw[4] = {svv.x, svv.y, svv.z, svv.w};
+  const uint32_t bw[4] = {bv.x, bv.y, bv.z, bv.w};
+#pragma unroll
+  for (int e = 0; e < 4; ++e) {
+    v[2 * e] *= kOut * h2f((uint16_t)(sw[e] & 0xFFFF));
+    v[2 * e + 1] *= kOut * h2f((uint16_t)(sw[e] >> 16));
+    if (a.bias) {
+      v[2 * e] += h2f((uint16_t)(bw[e] & 0xFFFF));
+      v[2 * e + 1] += h2f((uint16_t)(bw[e] >> 16));
+    }
   }
-  if (a.y_f32)
-    *reinterpret_cast<float2*>(static_cast<float*>(a.y) + (int64_t)i * a.ldy + col) =
-        make_float2(x0, x1);
-  else
-    *reinterpret_cast<uint32_t*>(static_cast<uint16_t*>(a.y) + (int64_t)i * a.ldy + col) =
-        (uint32_t)f2h(x0) | ((uint32_t)f2h(x1) << 16);
+  if (sg != 0) return;
+  if (a.y_f32) {
+    float4* yp = reinterpret_cast<float4*>(static_cast<float*>(a.y) + (int64_t)i * a.ldy + col);
+    yp[0] = make_float4(v[0], v[1], v[2], v[3]);
+    yp[1] = make_float4(v[4], v[5], v[6], v[7]);
+  } else {
+    uint32_t o[4];
+#pragma unroll
+    for (int e = 0; e < 4; ++e) o[e] = (uint32_t)f2h(v[2 * e]) | ((uint32_t)f2h(v[2 * e + 1]) << 16);
+    *reinterpret_cast<uint4*>(static_cast<uint16_t*>(a.y) + (int64_t)i * a.ldy + col) =
+        make_uint4(o[0], o[1], o[2], o[3]);
+  }
 }
 
 }  // namespace exl3
