@@ -11,14 +11,31 @@ struct DenseGemmRes {
   int64_t lda;
   int m;
   int bm;
+  int mt;   // row tiles
+  int nbt;  // 256-column tiles
   const uint16_t* trellis;
   const uint16_t* svh;
   const uint16_t* bias;
   void* y;
   int64_t ldy;
   bool y_f32;
-  __device__ GemmTask task(int mtile, int /*z*/) const {
+  // Workgroup -> (row tile, column tile).  Workgroups are dispatched to the
+  // eight XCDs round robin, so when the tile count is a multiple of eight the
+  // workgroups of one XCD are given one contiguous range of the tile order.
+  // The order walks groups of two row tiles across all column tiles, so the
+  // workgroups resident on one XCD at a time share two row panels of x' (in
+  // that XCD's L2) and each trellis column panel between two of them.
+  __device__ GemmTask task() const {
+    const int total = mt * nbt;
+    const int bid = (int)blockIdx.x;
+    const int u = (total % 8 == 0) ? (bid % 8) * (total / 8) + bid / 8 : bid;
+    constexpr int G = 2;
+    const int grp = u / (G * nbt), within = u - grp * (G * nbt);
+    const int g0 = grp * G;
+    const int gs = (mt - g0) < G ? (mt - g0) : G;
+    const int mtile = g0 + within % gs;
     GemmTask T;
+    T.nb = within / gs;
     const int r0 = mtile * bm;
     T.valid = r0 < m;
     T.a = a + (int64_t)r0 * lda;
@@ -34,18 +51,18 @@ struct DenseGemmRes {
   }
 };
 
-static int choose_bm(int m) { return m >= 256 ? 256 : (m > 64 ? 128 : 64); }
+static int choose_bm(int m) { return m > 128 ? 256 : (m > 64 ? 128 : 64); }
 
 template <int K>
 struct DenseGemmRun {
   static hipError_t run(const DenseGemmRes& r, int k, int n, hipStream_t s) {
-    const dim3 grid(n / 128, (r.m + r.bm - 1) / r.bm, 1);
+    const dim3 grid(r.mt * r.nbt);
 #define EXL3_GEMM_LAUNCH(BM)                                                                    \
   do {                                                                                          \
     if (r.y_f32)                                                                                \
-      hipLaunchKernelGGL((gemm_kernel<K, BM, true, DenseGemmRes>), grid, dim3(256), 0, s, r, k, n); \
+      hipLaunchKernelGGL((gemm_kernel<K, BM, true, DenseGemmRes>), grid, dim3(kGemmThreads), 0, s, r, k, n); \
     else                                                                                        \
-      hipLaunchKernelGGL((gemm_kernel<K, BM, false, DenseGemmRes>), grid, dim3(256), 0, s, r, k, n); \
+      hipLaunchKernelGGL((gemm_kernel<K, BM, false, DenseGemmRes>), grid, dim3(kGemmThreads), 0, s, r, k, n); \
   } while (0)
     if (r.bm == 256) EXL3_GEMM_LAUNCH(256);
     else if (r.bm == 128) EXL3_GEMM_LAUNCH(128);
@@ -69,7 +86,9 @@ hipError_t launch_gemm(const uint16_t* trellis, const uint16_t* suh, const uint1
   uint16_t* xp = reinterpret_cast<uint16_t*>(static_cast<unsigned char*>(ws) + counter_region(n));
   hipError_t e = launch_hadamard(x, false, xp, false, m, k, ldx, k, suh, nullptr, s);
   if (e != hipSuccess) return e;
-  DenseGemmRes r{xp, k, m, choose_bm(m), trellis, svh, bias, y, ldy, y_f32};
+  const int bm = choose_bm(m);
+  DenseGemmRes r{xp, k, m, bm, (m + bm - 1) / bm, (n + kGemmBN - 1) / kGemmBN, trellis, svh, bias,
+                 y, ldy, y_f32};
   return dispatch_bits<DenseGemmRun>(bits, r, k, n, s);
 }
 

@@ -1,28 +1,39 @@
 // Fused decode + MFMA GEMM kernel template (the prefill regime, m > 16),
 // shared by the dense linear and the grouped experts.
 //
-// One workgroup computes a BM x 128 output tile over the full k range:
-//   per k step of 64 rows  - the A panel (activations already in the
-//                            Hadamard domain, fp16) is staged into LDS;
-//                          - the 4 x 8 trellis tiles of the step are decoded
-//                            in registers (one row pair per thread, the same
-//                            routine as every other kernel) and written to LDS
-//                            as k-contiguous fp16 columns;
-//                          - four waves run MFMA 16x16x16 f16 with fp32
-//                            accumulation on their BM/4 x 128 slice.
-//   epilogue               - the 128 output columns are exactly one Hadamard
-//                            block: the output transform runs on the
-//                            accumulators (3 stages in registers, 4 across
-//                            lanes), then svh, bias and the cast.
-// The next step's global loads are issued before the current step's MFMAs.
+// One workgroup (four waves) computes a BM x 128 output tile over the full k
+// range: wave w owns rows w BM/4 .. (w+1) BM/4 - 1 and all 128 columns, one
+// whole Hadamard block.  Two workgroups share each CU (two waves per SIMD: a
+// single wave cannot issue v_mfma_f32_16x16x32_f16 back to back), and being
+// independent they fill each other's barrier and memory stalls.
+//   per k step of 32 rows  - each wave loads its A fragments (activations
+//                            already in the Hadamard domain, fp16) straight
+//                            from global memory into registers, in the MFMA
+//                            operand layout (no LDS for A);
+//                          - the 2 x 8 trellis tiles of the next step are
+//                            decoded in registers, half a row pair per thread
+//                            (the routine every other kernel uses), and
+//                            written to the other LDS stage column-major (k
+//                            contiguous), so each B fragment is one 16-byte
+//                            LDS read;
+//                          - v_mfma_f32_16x16x32_f16 (gfx950's full-rate fp16
+//                            contraction) with fp32 accumulation, the decode
+//                            interleaved with the MFMAs.
+//   epilogue               - the output transform runs on the accumulators
+//                            (3 stages in registers, 4 across lanes), then
+//                            svh, bias and the cast.
+// One barrier per step; the loads of the next steps are in flight meanwhile.
 #pragma once
 
 #include "exl3_device.hpp"
 
 namespace exl3 {
 
+typedef _Float16 half8_t __attribute__((ext_vector_type(8)));
+
 struct GemmTask {
   bool valid;
+  int nb;                   // 256-column tile
   const uint16_t* a;        // fp16 rows of x' for this tile, row 0
   int64_t lda;
   int rows;                 // valid rows in this tile (<= BM)
@@ -33,30 +44,81 @@ struct GemmTask {
   int64_t ldy;
 };
 
-constexpr int kGemmBK = 64;                    // k rows per step (4 tiles)
-constexpr int kGemmRowDw = 36;                 // LDS row stride in dwords (64 halves + pad)
-constexpr int kGemmBTileDw = 16 * kGemmRowDw + 8;  // per n-tile block of B (bank spread)
+constexpr int kGemmBN = 128;        // columns per workgroup tile (one Hadamard block)
+constexpr int kGemmBK = 32;         // k rows per step (two trellis tiles)
+constexpr int kGemmThreads = 256;   // four waves, each BM/4 rows x 128 columns
+
+// Decoded-weight stage: 128 columns x 32 k (fp16) as 512 chunks of 16 bytes
+// (four k-pairs of one column each).  Each group of four columns G = col / 4
+// owns 16 consecutive chunks (256 bytes, one pass over 64 LDS banks); inside
+// it, chunk gc of column cl = col % 4 sits at 4 (cl ^ (G / 4 % 4)) +
+// (gc ^ (G % 4)).  The MFMA fragment reads (16 lanes: sixteen consecutive
+// columns, one chunk each) and the decoder's 4-byte writes (64 lanes: eight
+// k-pairs of two k tiles and four n tiles, one column each) then each touch
+// distinct banks.
+__device__ __forceinline__ int gemm_b_chunk(int col, int gc) {
+  const int G = col >> 2, cl = col & 3;
+  return 16 * G + 4 * (cl ^ ((G >> 2) & 3)) + (gc ^ (G & 3));
+}
+
+// __builtin_amdgcn_sched_group_barrier instruction classes
+constexpr int kSchedValu = 0x002, kSchedMfma = 0x008, kSchedVmemRead = 0x020,
+              kSchedDsRead = 0x100, kSchedDsWrite = 0x200;
+
+template <int V>
+struct IntC {
+  static constexpr int value = V;
+};
+
+template <int I, int N, class F>
+__device__ __forceinline__ void static_for(F&& f) {
+  if constexpr (I < N) {
+    f(IntC<I>{});
+    static_for<I + 1, N>(f);
+  }
+}
 
 template <int K, int BM, bool Y_F32, class R>
-__global__ __launch_bounds__(256) void gemm_kernel(R r, int k, int n) {
-  constexpr int MI = BM / 64;          // 16-row subtiles per wave
-  constexpr int AQ = BM / 32;          // uint4 A chunks per thread per step
-  __shared__ __align__(16) uint32_t As[BM * kGemmRowDw];
-  __shared__ __align__(16) uint32_t Bs[8 * kGemmBTileDw];
+__global__ __launch_bounds__(kGemmThreads, 2) void gemm_kernel(R r, int k, int n) {
+  constexpr int WM = BM / 4;           // rows per wave tile
+  constexpr int MI = WM / 16;          // 16-row MFMA tiles per wave
+  static_assert(MI >= 1, "BM must be a multiple of 64");
+  __shared__ uint4 bst0[kGemmBN * 4], bst1[kGemmBN * 4];
 
-  const GemmTask T = r.task(blockIdx.y, blockIdx.z);
+  const GemmTask T = r.task();
   if (!T.valid) return;
-  const int nb = blockIdx.x;
-  const int nt = n >> 4;
+  const int nt16 = n >> 4;
   const int tid = threadIdx.x;
   const int wave = tid >> 6, lane = tid & 63;
   const int g = lane >> 4, j = lane & 15;
+  const int wm = wave, wn = 0;
+  const int col0 = T.nb * kGemmBN;
 
-  // decode role of this thread: k tile ktl of the step, n tile t, row pair p
-  const int ktl = tid >> 6, t = (tid >> 3) & 7, p = tid & 7;
-  const uint32_t* tb = reinterpret_cast<const uint32_t*>(T.trellis) +
-                       ((int64_t)ktl * nt + nb * 8 + t) * (8 * K) + K * p;
-  const int64_t step_dw = (int64_t)4 * nt * (8 * K);
+  // decode role: row pair p, k tile kt of the step, n tile t of the workgroup
+  // tile, column half h (uniform per wave: waves 0-1 decode columns 0-7 of
+  // each n tile, waves 2-3 columns 8-15)
+  const int p = tid & 7, kt = (tid >> 3) & 1, t = (tid >> 4) & 7, h = tid >> 7;
+  constexpr uint32_t kTileBytes = 32 * K;
+  const __amdgpu_buffer_rsrc_t t_rs =
+      make_rsrc(T.trellis, (uint32_t)((uint64_t)(k >> 4) * nt16 * kTileBytes));
+  const uint32_t t_voff = (uint32_t)(kt * nt16 + T.nb * 8 + t) * kTileBytes + 4 * K * p;
+  const uint32_t t_step = 2u * (uint32_t)nt16 * kTileBytes;
+  // LDS dword of each decoded k-pair this thread writes (k-pair 8 kt + p of
+  // columns 16 t + 8 h + c)
+  const int kp = 8 * kt + p;
+  int bw_dw[8];
+#pragma unroll
+  for (int c = 0; c < 8; ++c) bw_dw[c] = gemm_b_chunk(16 * t + 8 * h + c, kp >> 2) * 4 + (kp & 3);
+  // A fragment rows; rows at or past T.rows read as zero (outside the range)
+  const __amdgpu_buffer_rsrc_t a_rs = make_rsrc(T.a, (uint32_t)((uint64_t)T.rows * T.lda * 2));
+  uint32_t a_voff[MI];
+#pragma unroll
+  for (int mi = 0; mi < MI; ++mi)
+    a_voff[mi] = (uint32_t)(((int64_t)(wm * WM + 16 * mi + j) * T.lda + 8 * g) * 2);
+  // B fragment chunks this lane reads (column 128 wn + 16 q + j, chunk g)
+  int br_ch[8];
+#pragma unroll
+  for (int q = 0; q < 8; ++q) br_ch[q] = gemm_b_chunk(128 * wn + 16 * q + j, g);
 
   float4_t acc[MI][8];
 #pragma unroll
@@ -64,62 +126,113 @@ __global__ __launch_bounds__(256) void gemm_kernel(R r, int k, int n) {
 #pragma unroll
     for (int q = 0; q < 8; ++q) acc[mi][q] = float4_t{0.f, 0.f, 0.f, 0.f};
 
-  uint4 ra[AQ];
-  uint32_t rt[K];
-  auto load_step = [&](int ks) {
+  const int nsteps = k / kGemmBK;  // k is a multiple of 128: nsteps is a multiple of 4
+  typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+  // two register sets: A fragments of step s and trellis words of step s live in set s % 2
+  half8_t ra[2][MI];
+  uint32_t rt[2][K];
+  auto load_a = [&](int set, int ks) {
+    ks = ks < nsteps ? ks : nsteps - 1;  // past the end: re-read the last step (unused)
 #pragma unroll
-    for (int q = 0; q < AQ; ++q) {
-      const int idx = tid + 256 * q;
-      const int row = idx >> 3, ch = idx & 7;
-      if (row < T.rows)
-        ra[q] = *reinterpret_cast<const uint4*>(T.a + (int64_t)row * T.lda + ks * kGemmBK + ch * 8);
-      else
-        ra[q] = make_uint4(0, 0, 0, 0);
-    }
-    load_rowpair<K>(tb + ks * step_dw, rt);
+    for (int mi = 0; mi < MI; ++mi)
+      ra[set][mi] = __builtin_bit_cast(
+          half8_t, __builtin_amdgcn_raw_buffer_load_b128(a_rs, (int)a_voff[mi], ks * kGemmBK * 2, 0));
+  };
+  auto load_t = [&](int set, int ks) {
+    ks = ks < nsteps ? ks : nsteps - 1;
+    load_rowpair_buf<K>(t_rs, t_voff, (uint32_t)ks * t_step, rt[set]);
+  };
+  // decode the eight columns 8 H .. 8 H + 7 of this thread's row pair from
+  // the stream dwords B (the register set of the next step)
+  auto decode8 = [&](const uint32_t (&B)[K + 1], uint32_t (&wv)[8], auto hc) {
+    constexpr int H = decltype(hc)::value;
+    uint32_t wp[16];
+    static_for<0, 8>([&](auto cc) {
+      constexpr int c = decltype(cc)::value;
+      decode_column<K, 8 * H + c, false>(B, kMul1Multiplier, wp);
+      wv[c] = wp[8 * H + c];
+    });
+  };
+  auto stream_of = [&](int tset, uint32_t (&B)[K + 1]) {
+#pragma unroll
+    for (int i = 0; i < K; ++i) B[i] = stream_dword(rt[tset][i]);
+    B[K] = spill_from_next(rt[tset][0]);
+  };
+  // One step: the MFMAs on stage `cur` with the A fragments of register set
+  // `aset`, and the decode of the next step's trellis (register set `tset`)
+  // into stage `nxt`.  The schedule is fixed explicitly: the B fragment reads
+  // first, then each MFMA followed by two decode instructions (the matrix
+  // core runs while the wave decodes), then the decoded stores.
+  auto step = [&](const uint4* cur, uint4* nxt, int aset, int tset, auto hc) {
+    uint32_t B[K + 1];
+    stream_of(tset, B);
+    half8_t bv[8];
+#pragma unroll
+    for (int q = 0; q < 8; ++q) bv[q] = __builtin_bit_cast(half8_t, cur[br_ch[q]]);
+    uint32_t wv[8];
+    decode8(B, wv, hc);
+#pragma unroll
+    for (int q = 0; q < 8; ++q)
+#pragma unroll
+      for (int mi = 0; mi < MI; ++mi)
+        acc[mi][q] = __builtin_amdgcn_mfma_f32_16x16x32_f16(ra[aset][mi], bv[q], acc[mi][q], 0, 0, 0);
+    uint32_t* nd = reinterpret_cast<uint32_t*>(nxt);
+#pragma unroll
+    for (int c = 0; c < 8; ++c) nd[bw_dw[c]] = wv[c];
+    __builtin_amdgcn_sched_group_barrier(kSchedDsRead, 9, 0);
+    static_for<0, 8 * MI>([&](auto) {
+      __builtin_amdgcn_sched_group_barrier(kSchedMfma, 1, 0);
+      __builtin_amdgcn_sched_group_barrier(kSchedValu, 64 / (8 * MI) + 1, 0);
+    });
+    __builtin_amdgcn_sched_group_barrier(kSchedDsWrite, 8, 0);
+    __builtin_amdgcn_sched_group_barrier(kSchedVmemRead, MI + (K + 3) / 4, 0);
   };
 
-  const int nsteps = k / kGemmBK;
-  load_step(0);
-  for (int ks = 0; ks < nsteps; ++ks) {
-#pragma unroll
-    for (int q = 0; q < AQ; ++q) {
-      const int idx = tid + 256 * q;
-      const int row = idx >> 3, ch = idx & 7;
-      *reinterpret_cast<uint4*>(As + row * kGemmRowDw + ch * 4) = ra[q];
-    }
+  auto run = [&](auto hc) {
+    // prologue: step 0 decoded into stage 0; A of steps 0, 1 and trellis of
+    // steps 1, 2 in flight
+    load_t(0, 0);
+    load_a(0, 0);
+    load_t(1, 1);
+    load_a(1, 1);
     {
-      const uint32_t spill = spill_from_next(rt[0]);
-      uint32_t wp[16];
-      decode_rowpair<K>(rt, spill, wp);
-      uint32_t* bdst = Bs + t * kGemmBTileDw + 8 * ktl + p;
+      uint32_t B[K + 1], wv[8];
+      stream_of(0, B);
+      decode8(B, wv, hc);
+      uint32_t* nd = reinterpret_cast<uint32_t*>(bst0);
 #pragma unroll
-      for (int c = 0; c < 16; ++c) bdst[c * kGemmRowDw] = wp[c];
+      for (int c = 0; c < 8; ++c) nd[bw_dw[c]] = wv[c];
     }
+    load_t(0, 2);
     __syncthreads();
-    if (ks + 1 < nsteps) load_step(ks + 1);
-#pragma unroll
-    for (int kk = 0; kk < 4; ++kk) {
-      half4_t av[MI];
-#pragma unroll
-      for (int mi = 0; mi < MI; ++mi) {
-        const int row = wave * (BM / 4) + 16 * mi + j;
-        av[mi] = *reinterpret_cast<const half4_t*>(As + row * kGemmRowDw + 8 * kk + 2 * g);
-      }
-#pragma unroll
-      for (int q = 0; q < 8; ++q) {
-        const half4_t bv =
-            *reinterpret_cast<const half4_t*>(Bs + q * kGemmBTileDw + j * kGemmRowDw + 8 * kk + 2 * g);
-#pragma unroll
-        for (int mi = 0; mi < MI; ++mi)
-          acc[mi][q] = __builtin_amdgcn_mfma_f32_16x16x16f16(av[mi], bv, acc[mi][q], 0, 0, 0);
-      }
+    // Step s: MFMAs on stage s % 2 with A set s % 2; decode of step s + 1
+    // (trellis set (s + 1) % 2) into the other stage; then A set s % 2 is
+    // refilled with step s + 2 and trellis set (s + 1) % 2 with step s + 3.
+    // Past the last step the decode and loads repeat valid data that is unused.
+    for (int ks = 0; ks < nsteps; ks += 2) {
+      step(bst0, bst1, 0, 1, hc);
+      load_a(0, ks + 2);
+      load_t(1, ks + 3);
+      __syncthreads();
+      step(bst1, bst0, 1, 0, hc);
+      load_a(1, ks + 3);
+      load_t(0, ks + 4);
+      __syncthreads();
     }
-    __syncthreads();
-  }
+  };
+  if (h == 0)
+    run(IntC<0>{});
+  else
+    run(IntC<1>{});
 
-  // epilogue: output Hadamard over the 128 columns, svh, bias, cast
-  const int col0 = nb * 128;
+  // epilogue: output Hadamard over each wave's 128 columns, svh, bias, cast
+  const int cb = col0 + 128 * wn;
+  float sv[8], bv[8];
+#pragma unroll
+  for (int q = 0; q < 8; ++q) {
+    sv[q] = kInvSqrt128 * h2f(T.svh[cb + 16 * q + j]);
+    bv[q] = T.bias ? h2f(T.bias[cb + 16 * q + j]) : 0.f;
+  }
 #pragma unroll
   for (int mi = 0; mi < MI; ++mi) {
 #pragma unroll
@@ -128,13 +241,13 @@ __global__ __launch_bounds__(256) void gemm_kernel(R r, int k, int n) {
 #pragma unroll
       for (int q = 0; q < 8; ++q) v[q] = acc[mi][q][rr];
 #pragma unroll
-      for (int h = 1; h < 8; h <<= 1)
+      for (int sd = 1; sd < 8; sd <<= 1)
 #pragma unroll
         for (int q = 0; q < 8; ++q)
-          if ((q & h) == 0) {
-            const float u0 = v[q], u1 = v[q + h];
+          if ((q & sd) == 0) {
+            const float u0 = v[q], u1 = v[q + sd];
             v[q] = u0 + u1;
-            v[q + h] = u0 - u1;
+            v[q + sd] = u0 - u1;
           }
 #pragma unroll
       for (int msk = 1; msk < 16; msk <<= 1) {
@@ -145,13 +258,13 @@ __global__ __launch_bounds__(256) void gemm_kernel(R r, int k, int n) {
           v[q] = upper ? (pv - v[q]) : (v[q] + pv);
         }
       }
-      const int row = wave * (BM / 4) + 16 * mi + 4 * g + rr;
+      const int row = wm * WM + 16 * mi + 4 * g + rr;
       if (row < T.rows) {
 #pragma unroll
         for (int q = 0; q < 8; ++q) {
-          const int col = col0 + 16 * q + j;
-          float o = v[q] * kInvSqrt128 * h2f(T.svh[col]);
-          if (T.bias) o += h2f(T.bias[col]);
+          const int col = cb + 16 * q + j;
+          float o = v[q] * sv[q];
+          if (T.bias) o += bv[q];
           if constexpr (Y_F32)
             static_cast<float*>(T.y)[(int64_t)row * T.ldy + col] = o;
           else

@@ -22,7 +22,7 @@
 //
 // Large P (prefill): device binning, then one grouped MFMA GEMM launch per
 // projection over a device-built tile list (expert, first row, rows), so each
-// expert's weights are decoded once per 64-row tile instead of once per row.
+// expert's weights are decoded once per 128-row tile instead of once per row.
 //   1. zero counters, count pairs per expert (integer atomics: exact)
 //   2. one thread builds offsets and the tile list
 //   3. scatter pairs into expert order (the order inside an expert is not
@@ -41,7 +41,7 @@
 namespace exl3 {
 
 constexpr int kGroupedUnitMaxPairs = 64;  // P at or below this uses the unit path
-constexpr int kGroupedBM = 64;            // rows per tile of the grouped GEMM
+constexpr int kGroupedBM = 128;           // rows per tile of the grouped GEMM
 
 __device__ __forceinline__ float silu_f(float z) { return z / (1.0f + __expf(-z)); }
 
@@ -365,8 +365,10 @@ struct GroupedGemmRes {
   int slots;
   int64_t tensor_words;
   float* y;                // fp32 [slots][P][n]
-  __device__ GemmTask task(int tile, int slot) const {
+  __device__ GemmTask task() const {
+    const int tile = (int)blockIdx.y, slot = (int)blockIdx.z;
     GemmTask T;
+    T.nb = (int)blockIdx.x;
     T.valid = tile < *ntiles;
     if (!T.valid) return T;
     const TileEntry te = tiles[tile];
@@ -386,7 +388,8 @@ template <int K>
 struct GroupedGemmRun {
   static hipError_t run(const GroupedGemmRes& r, int max_tiles, hipStream_t s) {
     hipLaunchKernelGGL((gemm_kernel<K, kGroupedBM, true, GroupedGemmRes>),
-                       dim3(r.n / 128, max_tiles, r.slots), dim3(256), 0, s, r, r.k, r.n);
+                       dim3((r.n + kGemmBN - 1) / kGemmBN, max_tiles, r.slots), dim3(kGemmThreads), 0, s, r,
+                       r.k, r.n);
     return hipGetLastError();
   }
 };
