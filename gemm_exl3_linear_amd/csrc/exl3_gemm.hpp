@@ -205,19 +205,25 @@ __global__ __launch_bounds__(kGemmThreads, 2) void gemm_kernel(R r, int k, int n
     }
     load_t(0, 2);
     __syncthreads();
+    __builtin_amdgcn_sched_barrier(0);
     // Step s: MFMAs on stage s % 2 with A set s % 2; decode of step s + 1
     // (trellis set (s + 1) % 2) into the other stage; then A set s % 2 is
     // refilled with step s + 2 and trellis set (s + 1) % 2 with step s + 3.
     // Past the last step the decode and loads repeat valid data that is unused.
+    // (sched_barrier: the compiler would otherwise hoist the next step's
+    // register-only decode above the barrier, which forces a wait on the
+    // loads issued one step earlier)
     for (int ks = 0; ks < nsteps; ks += 2) {
       step(bst0, bst1, 0, 1, hc);
       load_a(0, ks + 2);
       load_t(1, ks + 3);
       __syncthreads();
+      __builtin_amdgcn_sched_barrier(0);
       step(bst1, bst0, 1, 0, hc);
       load_a(1, ks + 3);
       load_t(0, ks + 4);
       __syncthreads();
+      __builtin_amdgcn_sched_barrier(0);
     }
   };
   if (h == 0)
