@@ -90,6 +90,69 @@ def time_calls(fn, steps, warmup, stream):
     return per * 1e-3, total
 
 
+def mixed_layer_leg(X, torch, synth, dev, stream, reps=50):
+    """The mixed-width decoder layer: q, k, v, o (5120 x 5120), gate, up
+    (5120 x 17408), down (17408 x 5120) with per-tensor widths drawn from 2..8.
+    M = 1: the seven projections run in layer order, repeatedly, each call
+    timed with its own event pair (between two calls of one tensor the other
+    six stream about 220 MB, so each call reads mostly HBM); M = 4096: each
+    projection timed alone (the MFMA-bound prefill)."""
+    out = {"bits": {}, "m1": {}, "m4096": {}}
+    d1 = synth.mixed_layer_inputs(synth.SEED_MIXED_LAYER, 1)
+    names = [nm for nm, _, _ in synth.MIXED_LAYER_SHAPES]
+    ws, xs, ys = {}, {}, {}
+    for nm in names:
+        d = d1[nm]
+        out["bits"][nm] = d["bits"]
+        ws[nm] = X.Exl3Weight.from_numpy(d["trellis"], d["suh"], d["svh"], d["bits"], device=dev)
+        xs[nm] = torch.from_numpy(d["x"]).to(dev)
+        ys[nm] = torch.empty((1, d["n"]), dtype=torch.float16, device=dev)
+    wsp = torch.zeros(max(X.exl3_linear_workspace_size(ws[nm], 4096) for nm in names),
+                      dtype=torch.uint8, device=dev)
+    for _ in range(3):
+        for nm in names:
+            X.exl3_linear(xs[nm], ws[nm], out=ys[nm], workspace=wsp, stream=stream)
+    torch.cuda.synchronize()
+    ev = [[(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in names]
+          for _ in range(reps)]
+    for r in range(reps):
+        for i, nm in enumerate(names):
+            ev[r][i][0].record(stream)
+            X.exl3_linear(xs[nm], ws[nm], out=ys[nm], workspace=wsp, stream=stream)
+            ev[r][i][1].record(stream)
+    torch.cuda.synchronize()
+    tot_b = tot_t = 0.0
+    for i, nm in enumerate(names):
+        d = d1[nm]
+        t = sum(ev[r][i][0].elapsed_time(ev[r][i][1]) for r in range(reps)) / reps * 1e-3
+        b = linear_bytes(d["k"], d["n"], d["bits"], 1)
+        tot_b += b
+        tot_t += t
+        out["m1"][nm] = {"us": round(t * 1e6, 2), "GB/s": round(b / t / 1e9, 1),
+                         "frac_hbm": round(b / t / 1e9 / HBM_PEAK_GBS, 4)}
+    out["m1"]["layer"] = {"us": round(tot_t * 1e6, 2), "GB/s": round(tot_b / tot_t / 1e9, 1),
+                          "frac_hbm": round(tot_b / tot_t / 1e9 / HBM_PEAK_GBS, 4)}
+    del xs, ys
+    d4 = synth.mixed_layer_inputs(synth.SEED_MIXED_LAYER, 4096)
+    tot_f = tot_t = 0.0
+    for nm in names:
+        d = d4[nm]
+        x4 = torch.from_numpy(d["x"]).to(dev)
+        y4 = torch.empty((4096, d["n"]), dtype=torch.float16, device=dev)
+        pl, _ = time_calls(lambda i: X.exl3_linear(x4, ws[nm], out=y4, workspace=wsp, stream=stream),
+                           10, 2, stream)
+        f = 2.0 * 4096 * d["k"] * d["n"]
+        tot_f += f
+        tot_t += pl
+        out["m4096"][nm] = {"ms": round(pl * 1e3, 3), "TFLOP/s": round(f / pl / 1e12, 1),
+                            "frac_mfma_f16": round(f / pl / 1e12 / MFMA_F16_PEAK_TFLOPS, 4)}
+        del x4, y4
+    out["m4096"]["layer"] = {"ms": round(tot_t * 1e3, 3), "TFLOP/s": round(tot_f / tot_t / 1e12, 1),
+                             "frac_mfma_f16": round(tot_f / tot_t / 1e12 / MFMA_F16_PEAK_TFLOPS, 4)}
+    del ws, wsp, d1, d4
+    return out
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -170,6 +233,7 @@ def main():
         secondary["prefill_m4096"] = {"TFLOP/s": round(tf, 1), "frac_mfma_f16": round(tf / MFMA_F16_PEAK_TFLOPS, 4),
                                       "ms_per_call": round(pl * 1e3, 3)}
         del wp, xp, wsp, yp
+        secondary["mixed_layer"] = mixed_layer_leg(X, torch, synth, dev, stream)
         # routed experts: 256 experts, top-8, hidden 2048, intermediate 512, K=3
         for t in (1, 4096):
             mo = synth.moe_inputs(synth.SEED_MOE_256x2048x512, t)

@@ -66,6 +66,29 @@ def mixed_layer_bits(seed: int, names=("q", "k", "v", "o", "gate", "up", "down")
     return g, {nm: int(g.integers(2, 9)) for nm in names}
 
 
+# One decoder layer's seven projections (in_features, out_features): four
+# 5120 x 5120 attention projections, then the gated MLP 5120 -> 17408 -> 5120.
+MIXED_LAYER_SHAPES = (("q", 5120, 5120), ("k", 5120, 5120), ("v", 5120, 5120), ("o", 5120, 5120),
+                      ("gate", 5120, 17408), ("up", 5120, 17408), ("down", 17408, 5120))
+
+
+def mixed_layer_inputs(seed: int, m: int, shapes=MIXED_LAYER_SHAPES):
+    """The mixed-width layer: per-tensor widths first (mixed_layer_bits), then
+    each tensor's trellis, suh and svh in the order q, k, v, o, gate, up,
+    down, then each projection's activations x ~ N(0, 1) [m, in_features] in
+    the same order."""
+    g, bits = mixed_layer_bits(seed, tuple(nm for nm, _, _ in shapes))
+    out = {}
+    for nm, k, n in shapes:
+        t = trellis(g, k, n, bits[nm])
+        suh = signs(g, k)
+        svh = signs(g, n)
+        out[nm] = dict(trellis=t, suh=suh, svh=svh, k=k, n=n, bits=bits[nm])
+    for nm, k, n in shapes:
+        out[nm]["x"] = activations(g, m, k)
+    return out
+
+
 def expert_arena(g: np.random.Generator, experts: int, slots: int, k: int, n: int, bits: int):
     """Packed expert arena: trellis [E, slots, k/16, n/16, 16*bits], suh [E, slots, k],
     svh [E, slots, n]."""

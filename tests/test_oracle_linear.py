@@ -101,3 +101,23 @@ def test_bias_added_last():
     y = O.linear(d["x"], d["trellis"], d["suh"], d["svh"], 4)
     yb = O.linear(d["x"], d["trellis"], d["suh"], d["svh"], 4, bias=bias)
     np.testing.assert_allclose(yb - y, np.broadcast_to(bias.astype(np.float64), y.shape), atol=1e-12)
+
+
+def test_mixed_layer_generator_order_and_widths():
+    # widths come first and do not depend on the activation count; tensors are
+    # drawn before activations, so m changes only x
+    a = synth.mixed_layer_inputs(synth.SEED_MIXED_LAYER, 1,
+                                 shapes=(("q", 256, 128), ("k", 128, 256), ("down", 384, 128)))
+    b = synth.mixed_layer_inputs(synth.SEED_MIXED_LAYER, 3,
+                                 shapes=(("q", 256, 128), ("k", 128, 256), ("down", 384, 128)))
+    _, bits = synth.mixed_layer_bits(synth.SEED_MIXED_LAYER, ("q", "k", "down"))
+    for nm in ("q", "k", "down"):
+        assert a[nm]["bits"] == b[nm]["bits"] == bits[nm]
+        assert 2 <= bits[nm] <= 8
+        assert np.array_equal(a[nm]["trellis"], b[nm]["trellis"])
+        assert a[nm]["trellis"].shape == (a[nm]["k"] // 16, a[nm]["n"] // 16, 16 * bits[nm])
+        assert a[nm]["x"].shape == (1, a[nm]["k"]) and b[nm]["x"].shape == (3, b[nm]["k"])
+    # bits-per-weight accounting of the full layer: trellis bytes = sum k n K / 8
+    _, full = synth.mixed_layer_bits(synth.SEED_MIXED_LAYER)
+    nbytes = sum(k * n * full[nm] // 8 for nm, k, n in synth.MIXED_LAYER_SHAPES)
+    assert 93_061_120 <= nbytes <= 372_244_480
