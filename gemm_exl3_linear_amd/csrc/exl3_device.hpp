@@ -217,6 +217,43 @@ __device__ __forceinline__ void fwht128_pair(float& a, float& b) {
   }
 }
 
+// Transform of up to four 128-element blocks at once by one wave: lane
+// l holds elements 8 (l % 16) .. 8 (l % 16) + 7 of block l / 16, so the three
+// lowest butterfly strides stay inside the lane and the other four pair
+// lanes l ^ 1, 2, 4, 8 of the same 16-lane group (ds_swizzle, no LDS
+// memory).  v[e] = x * suh on entry, the unnormalised transform on exit.
+template <int MASK>
+__device__ __forceinline__ float swizzle_xor_f(float v) {
+  // bitmask mode: source lane = (lane & 0x1F) ^ MASK inside each 32 lanes
+  return __int_as_float(__builtin_amdgcn_ds_swizzle(__float_as_int(v), (MASK << 10) | 0x1F));
+}
+
+template <int MASK>
+__device__ __forceinline__ void fwht_lane_stage(float (&v)[8]) {
+  float pv[8];
+#pragma unroll
+  for (int e = 0; e < 8; ++e) pv[e] = swizzle_xor_f<MASK>(v[e]);
+  const bool upper = (lane_id() & (uint32_t)MASK) != 0;
+#pragma unroll
+  for (int e = 0; e < 8; ++e) v[e] = upper ? (pv[e] - v[e]) : (v[e] + pv[e]);
+}
+
+__device__ __forceinline__ void fwht128_x8(float (&v)[8]) {
+#pragma unroll
+  for (int h = 1; h < 8; h <<= 1)
+#pragma unroll
+    for (int e = 0; e < 8; ++e)
+      if ((e & h) == 0) {
+        const float u = v[e], w = v[e + h];
+        v[e] = u + w;
+        v[e + h] = u - w;
+      }
+  fwht_lane_stage<1>(v);
+  fwht_lane_stage<2>(v);
+  fwht_lane_stage<4>(v);
+  fwht_lane_stage<8>(v);
+}
+
 __device__ __forceinline__ float h2f(uint16_t h) {
   return (float)__builtin_bit_cast(_Float16, h);
 }

@@ -115,43 +115,6 @@ __device__ __forceinline__ void reduce_rowpairs(float (&acc)[16], float& c0, flo
 constexpr int kSkWaveLdsDot = kSkMaxXBlocks * 128 * 2;
 constexpr int kSkWaveLdsMfma = 64 * 20 * 4;
 
-// Input transform of up to four 128-element k blocks at once (m == 1): lane
-// l holds elements 8 (l % 16) .. 8 (l % 16) + 7 of block l / 16, so the three
-// lowest butterfly strides stay inside the lane and the other four pair
-// lanes l ^ 1, 2, 4, 8 of the same 16-lane group (ds_swizzle, no LDS
-// memory).  v[e] = x * suh on entry, the unnormalised transform on exit.
-template <int MASK>
-__device__ __forceinline__ float swizzle_xor_f(float v) {
-  // bitmask mode: source lane = (lane & 0x1F) ^ MASK inside each 32 lanes
-  return __int_as_float(__builtin_amdgcn_ds_swizzle(__float_as_int(v), (MASK << 10) | 0x1F));
-}
-
-template <int MASK>
-__device__ __forceinline__ void fwht_lane_stage(float (&v)[8]) {
-  float pv[8];
-#pragma unroll
-  for (int e = 0; e < 8; ++e) pv[e] = swizzle_xor_f<MASK>(v[e]);
-  const bool upper = (lane_id() & (uint32_t)MASK) != 0;
-#pragma unroll
-  for (int e = 0; e < 8; ++e) v[e] = upper ? (pv[e] - v[e]) : (v[e] + pv[e]);
-}
-
-__device__ __forceinline__ void fwht128_x8(float (&v)[8]) {
-#pragma unroll
-  for (int h = 1; h < 8; h <<= 1)
-#pragma unroll
-    for (int e = 0; e < 8; ++e)
-      if ((e & h) == 0) {
-        const float u = v[e], w = v[e + h];
-        v[e] = u + w;
-        v[e + h] = u - w;
-      }
-  fwht_lane_stage<1>(v);
-  fwht_lane_stage<2>(v);
-  fwht_lane_stage<4>(v);
-  fwht_lane_stage<8>(v);
-}
-
 template <int K, bool DOT, int PF>
 __global__ __launch_bounds__(256) void gemv_sk_kernel(SkArgs a) {
   constexpr int WAVE_LDS = DOT ? kSkWaveLdsDot : kSkWaveLdsMfma;

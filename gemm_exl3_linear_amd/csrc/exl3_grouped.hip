@@ -24,7 +24,7 @@
 // projection over a device-built tile list (expert, first row, rows), so each
 // expert's weights are decoded once per 128-row tile instead of once per row.
 //   1. zero counters, count pairs per expert (integer atomics: exact)
-//   2. one thread builds offsets and the tile list
+//   2. one workgroup scans the counts into offsets and the tile list
 //   3. scatter pairs into expert order (the order inside an expert is not
 //      fixed, but every row is computed independently of its position, so
 //      the output does not depend on it)
@@ -248,26 +248,55 @@ __global__ void bin_count(const int32_t* __restrict__ ids, int64_t P, int32_t* _
   if (i < P) atomicAdd(&counts[ids[i]], 1);
 }
 
-// one thread: exclusive scan of the counts and the list of row tiles
-__global__ void bin_plan(const int32_t* __restrict__ counts, int E, int bm,
-                         int32_t* __restrict__ offsets, int32_t* __restrict__ ntiles,
-                         TileEntry* __restrict__ tiles) {
-  if (threadIdx.x != 0 || blockIdx.x != 0) return;
-  int off = 0, nt = 0;
-  for (int e = 0; e < E; ++e) {
-    const int c = counts[e];
-    offsets[e] = off;
-    for (int r = 0; r < c; r += bm) {
-      TileEntry te;
-      te.e = e;
-      te.row0 = off + r;
-      te.rows = (c - r) < bm ? (c - r) : bm;
-      te.pad = 0;
-      tiles[nt++] = te;
-    }
-    off += c;
+// One workgroup: exclusive scans of the per-expert row counts and of their
+// tile counts (ceil(count / bm)), in chunks of kPlanThreads experts, then
+// every expert writes its offset and its row tiles.
+constexpr int kPlanThreads = 1024;
+
+__device__ __forceinline__ int block_exclusive_scan(int v, int* sh, int& total) {
+  const int tid = threadIdx.x;
+  sh[tid] = v;
+  __syncthreads();
+  for (int d = 1; d < kPlanThreads; d <<= 1) {
+    const int add = tid >= d ? sh[tid - d] : 0;
+    __syncthreads();
+    sh[tid] += add;
+    __syncthreads();
   }
-  *ntiles = nt;
+  const int incl = sh[tid];
+  total = sh[kPlanThreads - 1];
+  __syncthreads();
+  return incl - v;
+}
+
+__global__ __launch_bounds__(kPlanThreads) void bin_plan(const int32_t* __restrict__ counts, int E, int bm,
+                                                         int32_t* __restrict__ offsets,
+                                                         int32_t* __restrict__ ntiles,
+                                                         TileEntry* __restrict__ tiles) {
+  __shared__ int sh[kPlanThreads];
+  int row_base = 0, tile_base = 0;
+  for (int e0 = 0; e0 < E; e0 += kPlanThreads) {
+    const int e = e0 + (int)threadIdx.x;
+    const int c = e < E ? counts[e] : 0;
+    const int nt = (c + bm - 1) / bm;
+    int rows_total, tiles_total;
+    const int off = row_base + block_exclusive_scan(c, sh, rows_total);
+    const int toff = tile_base + block_exclusive_scan(nt, sh, tiles_total);
+    if (e < E) {
+      offsets[e] = off;
+      for (int t = 0; t < nt; ++t) {
+        TileEntry te;
+        te.e = e;
+        te.row0 = off + t * bm;
+        te.rows = (c - t * bm) < bm ? (c - t * bm) : bm;
+        te.pad = 0;
+        tiles[toff + t] = te;
+      }
+    }
+    row_base += rows_total;
+    tile_base += tiles_total;
+  }
+  if (threadIdx.x == 0) *ntiles = tile_base;
 }
 
 __global__ void bin_scatter(const int32_t* __restrict__ ids, int64_t P,
@@ -281,54 +310,87 @@ __global__ void bin_scatter(const int32_t* __restrict__ ids, int64_t P,
   pos[i] = r;
 }
 
-// x'_slot[r] = (x[token(r)] .* suh[e(r)][slot]) H, one wave per (row, slot, block)
+// x'_slot[r] = (x[token(r)] .* suh[e(r)][slot]) H, one wave per (sorted row,
+// slot), four 128-element blocks at a time (fwht128_x8 layout: lane l holds 8
+// elements of block 4 round + l / 16)
 __global__ __launch_bounds__(256) void gu_input_transform(
     const uint16_t* __restrict__ x, int topk, int64_t P, int hidden,
     const int32_t* __restrict__ sorted, const int32_t* __restrict__ ids,
     const uint16_t* __restrict__ suh_gu, uint16_t* __restrict__ xg) {
-  const int nblocks = hidden >> 7;
   const int64_t task = (int64_t)blockIdx.x * 4 + (threadIdx.x >> 6);
-  if (task >= P * 2 * nblocks) return;
-  const int64_t r = task / (2 * nblocks);
-  const int rem = (int)(task - r * 2 * nblocks);
-  const int slot = rem / nblocks, nb = rem - slot * nblocks;
+  if (task >= P * 2) return;
+  const int64_t r = task >> 1;
+  const int slot = (int)(task & 1);
   const int pair = sorted[r];
   const int e = ids[pair];
   const int64_t tok = pair / topk;
-  const int col = nb * 128 + 2 * (int)lane_id();
-  const uint32_t xv = *reinterpret_cast<const uint32_t*>(x + tok * hidden + col);
-  const uint32_t sv =
-      *reinterpret_cast<const uint32_t*>(suh_gu + (int64_t)(e * 2 + slot) * hidden + col);
-  float a = h2f((uint16_t)(xv & 0xFFFF)) * h2f((uint16_t)(sv & 0xFFFF));
-  float b = h2f((uint16_t)(xv >> 16)) * h2f((uint16_t)(sv >> 16));
-  fwht128_pair(a, b);
-  a *= kInvSqrt128;
-  b *= kInvSqrt128;
-  *reinterpret_cast<uint32_t*>(xg + ((int64_t)slot * P + r) * hidden + col) =
-      (uint32_t)f2h(a) | ((uint32_t)f2h(b) << 16);
+  const int lane = (int)lane_id();
+  const int g = lane >> 4, j = lane & 15;
+  const int nblk = hidden >> 7;
+  const uint16_t* xr = x + tok * hidden;
+  const uint16_t* sr = suh_gu + (int64_t)(e * 2 + slot) * hidden;
+  uint16_t* dst = xg + ((int64_t)slot * P + r) * hidden;
+  for (int b0 = 0; b0 < nblk; b0 += 4) {
+    const int b = b0 + g;
+    const int kk = (b < nblk ? b : nblk - 1) * 128 + 8 * j;
+    const uint4 xv = *reinterpret_cast<const uint4*>(xr + kk);
+    const uint4 sv = *reinterpret_cast<const uint4*>(sr + kk);
+    const uint32_t xw[4] = {xv.x, xv.y, xv.z, xv.w};
+    const uint32_t sw[4] = {sv.x, sv.y, sv.z, sv.w};
+    float v[8];
+#pragma unroll
+    for (int q = 0; q < 4; ++q) {
+      v[2 * q] = h2f((uint16_t)(xw[q] & 0xFFFF)) * h2f((uint16_t)(sw[q] & 0xFFFF));
+      v[2 * q + 1] = h2f((uint16_t)(xw[q] >> 16)) * h2f((uint16_t)(sw[q] >> 16));
+    }
+    fwht128_x8(v);
+    uint32_t o[4];
+#pragma unroll
+    for (int q = 0; q < 4; ++q)
+      o[q] = (uint32_t)f2h(v[2 * q] * kInvSqrt128) | ((uint32_t)f2h(v[2 * q + 1] * kInvSqrt128) << 16);
+    if (b < nblk) *reinterpret_cast<uint4*>(dst + kk) = make_uint4(o[0], o[1], o[2], o[3]);
+  }
 }
 
-// a = silu(g) * u, x'_d = (a .* suh_down_e) H, one wave per (row, block)
+// a = silu(g) * u, x'_d = (a .* suh_down_e) H, one wave per sorted row, four
+// 128-element blocks at a time
 __global__ __launch_bounds__(256) void silu_down_transform(
     const float* __restrict__ gu, int64_t P, int inter, const int32_t* __restrict__ sorted,
     const int32_t* __restrict__ ids, const uint16_t* __restrict__ suh_dn,
     uint16_t* __restrict__ xd) {
-  const int nblocks = inter >> 7;
-  const int64_t task = (int64_t)blockIdx.x * 4 + (threadIdx.x >> 6);
-  if (task >= P * nblocks) return;
-  const int64_t r = task / nblocks;
-  const int nb = (int)(task - r * nblocks);
+  const int64_t r = (int64_t)blockIdx.x * 4 + (threadIdx.x >> 6);
+  if (r >= P) return;
   const int e = ids[sorted[r]];
-  const int col = nb * 128 + 2 * (int)lane_id();
-  const float2 g = *reinterpret_cast<const float2*>(gu + r * inter + col);
-  const float2 u = *reinterpret_cast<const float2*>(gu + (P + r) * inter + col);
-  const uint32_t su = *reinterpret_cast<const uint32_t*>(suh_dn + (int64_t)e * inter + col);
-  float a = silu_f(g.x) * u.x * h2f((uint16_t)(su & 0xFFFF));
-  float b = silu_f(g.y) * u.y * h2f((uint16_t)(su >> 16));
-  fwht128_pair(a, b);
-  a *= kInvSqrt128;
-  b *= kInvSqrt128;
-  *reinterpret_cast<uint32_t*>(xd + r * inter + col) = (uint32_t)f2h(a) | ((uint32_t)f2h(b) << 16);
+  const int lane = (int)lane_id();
+  const int g = lane >> 4, j = lane & 15;
+  const int nblk = inter >> 7;
+  const float* gr = gu + r * inter;
+  const float* ur = gu + (P + r) * inter;
+  const uint16_t* sr = suh_dn + (int64_t)e * inter;
+  for (int b0 = 0; b0 < nblk; b0 += 4) {
+    const int b = b0 + g;
+    const int kk = (b < nblk ? b : nblk - 1) * 128 + 8 * j;
+    const float4 g0 = *reinterpret_cast<const float4*>(gr + kk);
+    const float4 g1 = *reinterpret_cast<const float4*>(gr + kk + 4);
+    const float4 u0 = *reinterpret_cast<const float4*>(ur + kk);
+    const float4 u1 = *reinterpret_cast<const float4*>(ur + kk + 4);
+    const uint4 sv = *reinterpret_cast<const uint4*>(sr + kk);
+    const float gv[8] = {g0.x, g0.y, g0.z, g0.w, g1.x, g1.y, g1.z, g1.w};
+    const float uv[8] = {u0.x, u0.y, u0.z, u0.w, u1.x, u1.y, u1.z, u1.w};
+    const uint32_t sw[4] = {sv.x, sv.y, sv.z, sv.w};
+    float v[8];
+#pragma unroll
+    for (int q = 0; q < 4; ++q) {
+      v[2 * q] = silu_f(gv[2 * q]) * uv[2 * q] * h2f((uint16_t)(sw[q] & 0xFFFF));
+      v[2 * q + 1] = silu_f(gv[2 * q + 1]) * uv[2 * q + 1] * h2f((uint16_t)(sw[q] >> 16));
+    }
+    fwht128_x8(v);
+    uint32_t o[4];
+#pragma unroll
+    for (int q = 0; q < 4; ++q)
+      o[q] = (uint32_t)f2h(v[2 * q] * kInvSqrt128) | ((uint32_t)f2h(v[2 * q + 1] * kInvSqrt128) << 16);
+    if (b < nblk) *reinterpret_cast<uint4*>(xd + r * inter + kk) = make_uint4(o[0], o[1], o[2], o[3]);
+  }
 }
 
 // y[token] = sum over slots in order of w[token, slot] * d[pos(token, slot)]
@@ -447,12 +509,12 @@ hipError_t launch_grouped(const ArenaDesc& gu, const ArenaDesc& dn, const uint16
   hipLaunchKernelGGL(zero_i32, dim3((E + 255) / 256), dim3(256), 0, s, counts, E);
   hipLaunchKernelGGL(zero_i32, dim3((E + 255) / 256), dim3(256), 0, s, cursor, E);
   hipLaunchKernelGGL(bin_count, dim3((unsigned)((P + 255) / 256)), dim3(256), 0, s, ids, P, counts);
-  hipLaunchKernelGGL(bin_plan, dim3(1), dim3(64), 0, s, counts, E, kGroupedBM, offsets, ntiles,
-                     tiles);
+  hipLaunchKernelGGL(bin_plan, dim3(1), dim3(kPlanThreads), 0, s, counts, E, kGroupedBM, offsets,
+                     ntiles, tiles);
   hipLaunchKernelGGL(bin_scatter, dim3((unsigned)((P + 255) / 256)), dim3(256), 0, s, ids, P,
                      offsets, cursor, pos, sorted);
   {
-    const int64_t tasks = P * 2 * (hidden / 128);
+    const int64_t tasks = P * 2;  // one wave each
     hipLaunchKernelGGL(gu_input_transform, dim3((unsigned)((tasks + 3) / 4)), dim3(256), 0, s, x,
                        topk, P, hidden, sorted, ids, gu.suh, xg);
   }
@@ -461,7 +523,7 @@ hipError_t launch_grouped(const ArenaDesc& gu, const ArenaDesc& dn, const uint16
   e = dispatch_bits<GroupedGemmRun>(gu.bits, rg, L.max_tiles, s);
   if (e != hipSuccess) return e;
   {
-    const int64_t tasks = P * (inter / 128);
+    const int64_t tasks = P;  // one wave each
     hipLaunchKernelGGL(silu_down_transform, dim3((unsigned)((tasks + 3) / 4)), dim3(256), 0, s,
                        gbuf, P, inter, sorted, ids, dn.suh, xd);
   }
