@@ -56,16 +56,37 @@ __device__ __forceinline__ void gemv_prologue(const GemvTask& T, int k0, int kc,
 }
 
 // Sum of the fp32 partial slices s = 0..splits-1 (fixed order) for the two
-// columns col, col+1 of one row; slices are `stride` floats apart.
+// columns col, col+1 of one row; slices are `stride` floats apart.  The
+// slices were written by other workgroups of the same kernel on the same XCD
+// (see gemv_kernel), so the loads are device scope: past this CU's L1, from
+// the XCD's L2.
 __device__ __forceinline__ void sum_partials(const float* p, int splits, int64_t stride, float& a,
                                              float& b) {
   a = 0.f;
   b = 0.f;
   for (int s = 0; s < splits; ++s) {
-    const float2 v = *reinterpret_cast<const float2*>(p + (int64_t)s * stride);
-    a += v.x;
-    b += v.y;
+    const float* q = p + (int64_t)s * stride;
+    a += __hip_atomic_load(q, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    b += __hip_atomic_load(q + 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
   }
+}
+
+// Workgroups are dispatched to the eight XCDs of MI355X round robin
+// (workgroup b runs on XCD b % 8; verified by reading the XCC_ID hardware
+// register of every workgroup).  An output group's workgroups (all k ranges
+// of all units that one finish reads) are given indices congruent mod 8, so
+// the group's partial sums pass through one XCD's L2 and the hand-off needs no
+// L2 write-back or invalidate.  Index b: XCD x = b % 8, position i = b / 8;
+// group 8 (i / members) + x, member i % members.
+constexpr int kGemvXcds = 8;
+__device__ __forceinline__ bool gemv_place(int b, int groups, int members, int& group, int& member) {
+  const int x = b % kGemvXcds, i = b / kGemvXcds;
+  group = (i / members) * kGemvXcds + x;
+  member = i - (i / members) * members;
+  return group < groups;
+}
+inline int gemv_grid(int groups, int members) {
+  return (groups + kGemvXcds - 1) / kGemvXcds * kGemvXcds * members;
 }
 
 // One k tile of one wave: decode the lane's row pair, hand the k-pairs to the
@@ -107,11 +128,12 @@ template <int K, int PF, class R>
 __global__ __launch_bounds__(256) void gemv_kernel(R r, int k, int n, int kc) {
   extern __shared__ __align__(16) unsigned char smem[];
   __shared__ int last_flag;
-  const GemvTask T = r.task(blockIdx.z, blockIdx.y);
-  if (!T.valid) return;  // uniform over the workgroup
+  int unit, split, nb;
+  if (!r.place((int)blockIdx.x, unit, split, nb)) return;  // uniform over the workgroup
+  const GemvTask T = r.task(unit, split);
+  if (!T.valid) return;
   const int m = T.m;
-  const int nb = blockIdx.x;
-  const int k0 = blockIdx.y * kc;
+  const int k0 = split * kc;
   const int nt = n >> 4;
   uint16_t* xs = reinterpret_cast<uint16_t*>(smem);
   const size_t xs_bytes = ((size_t)kc * m * 2 + 15) & ~(size_t)15;
@@ -177,19 +199,23 @@ __global__ __launch_bounds__(256) void gemv_kernel(R r, int k, int n, int kc) {
     T.partial[(int64_t)i * n + nb * 128 + c] = s;
   }
 
-  // arrival: the last workgroup of the output group finishes it
+  // arrival: the last workgroup of the output group finishes it.  Every
+  // thread's partial stores are complete in the XCD's L2 (vmcnt(0)) before
+  // the workgroup barrier, and the counter moves after it.
+  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup");
+  __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0)
   __syncthreads();
   if (threadIdx.x == 0) {
-    __threadfence();  // make this workgroup's partials visible device-wide
-    unsigned int* ctr = r.counter(blockIdx.z, nb);
-    const unsigned int old = atomicAdd(ctr, 1u);
-    last_flag = (old + 1u == r.arrivals(blockIdx.z)) ? 1 : 0;
+    unsigned int* ctr = r.counter(unit, nb);
+    const unsigned int old = __hip_atomic_fetch_add(ctr, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    last_flag = (old + 1u == r.arrivals(unit)) ? 1 : 0;
   }
   __syncthreads();
   if (!last_flag) return;
-  __threadfence();  // see every other workgroup's partials
-  r.finish(blockIdx.z, nb, n);
-  if (threadIdx.x == 0) *r.counter(blockIdx.z, nb) = 0u;  // ready for the next call
+  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup");
+  r.finish(unit, nb, n);
+  if (threadIdx.x == 0)  // ready for the next call
+    __hip_atomic_store(r.counter(unit, nb), 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
 
 // Launch with the prefetch depth the k range allows.

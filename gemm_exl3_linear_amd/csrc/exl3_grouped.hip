@@ -10,7 +10,7 @@
 // Two regimes, chosen on the host from the number of (token, slot) pairs
 // P = t * topk (no device data is read back):
 //
-// Small P (decode, token-parallel verify): every pair is an independent M=1
+// Small P (P <= 512: decode, token-parallel verify, short prompts): every pair is an independent M=1
 // unit (the README's "per-unit x stride" idea).
 //   1. gemv_kernel over units (pair, gate|up); the last workgroup to arrive on
 //      a (pair, 128 columns) group sums the k slices of gate and up, applies
@@ -40,7 +40,11 @@
 
 namespace exl3 {
 
-constexpr int kGroupedUnitMaxPairs = 64;  // P at or below this uses the unit path
+// P at or below this uses the unit path: measured on MI355X for 256 experts x
+// (2048 -> 2 x 512 -> 2048), K=3, top-8, the unit path is faster up to T = 64
+// (P = 512: 248 us against 261 us for the binned path) and slower from T = 128
+// (478 against 299 us).
+constexpr int kGroupedUnitMaxPairs = 512;
 constexpr int kGroupedBM = 128;           // rows per tile of the grouped GEMM
 
 __device__ __forceinline__ float silu_f(float z) { return z / (1.0f + __expf(-z)); }
@@ -65,6 +69,17 @@ struct GuUnitRes {
   unsigned int* ctr;     // [P][n/128]
   const uint16_t* suh_dn;
   uint16_t* xd;          // fp16 [P][n]: input of the down projection, Hadamard domain
+  int pairs;             // P
+  // output group (pair, 128 columns); members (gate|up, k range)
+  __device__ bool place(int b, int& u, int& split, int& nb) const {
+    int grp, mem;
+    if (!gemv_place(b, pairs * (n >> 7), 2 * splits, grp, mem)) return false;
+    const int pair = grp / (n >> 7);
+    nb = grp - pair * (n >> 7);
+    u = 2 * pair + mem / splits;
+    split = mem - (mem / splits) * splits;
+    return true;
+  }
   __device__ GemvTask task(int u, int split) const {
     GemvTask T;
     const int pair = u >> 1, slot = u & 1;
@@ -126,6 +141,17 @@ struct DnUnitRes {
   int splits;
   unsigned int* ctr;   // [t][n/128]
   float* y;            // fp32 [t][n]
+  int tokens;          // t
+  // output group (token, 128 columns); members (slot, k range)
+  __device__ bool place(int b, int& u, int& split, int& nb) const {
+    int grp, mem;
+    if (!gemv_place(b, tokens * (n >> 7), topk * splits, grp, mem)) return false;
+    const int tok = grp / (n >> 7);
+    nb = grp - tok * (n >> 7);
+    u = tok * topk + mem / splits;
+    split = mem - (mem / splits) * splits;
+    return true;
+  }
   __device__ GemvTask task(int u, int split) const {
     GemvTask T;
     const int e = ids[u];
@@ -163,17 +189,19 @@ struct DnUnitRes {
 
 template <int K>
 struct GuUnitRun {
-  static hipError_t run(const GuUnitRes& r, int k, int n, int units, int kc, size_t lds,
+  static hipError_t run(const GuUnitRes& r, int k, int n, int /*units*/, int kc, size_t lds,
                         hipStream_t s) {
-    return launch_gemv_kernel<K>(r, dim3(n / 128, r.splits, units), lds, s, k, n, kc);
+    const int grid = gemv_grid(r.pairs * (n / 128), 2 * r.splits);
+    return launch_gemv_kernel<K>(r, dim3(grid), lds, s, k, n, kc);
   }
 };
 
 template <int K>
 struct DnUnitRun {
-  static hipError_t run(const DnUnitRes& r, int k, int n, int units, int kc, size_t lds,
+  static hipError_t run(const DnUnitRes& r, int k, int n, int /*units*/, int kc, size_t lds,
                         hipStream_t s) {
-    return launch_gemv_kernel<K>(r, dim3(n / 128, r.splits, units), lds, s, k, n, kc);
+    const int grid = gemv_grid(r.tokens * (n / 128), r.topk * r.splits);
+    return launch_gemv_kernel<K>(r, dim3(grid), lds, s, k, n, kc);
   }
 };
 
@@ -480,13 +508,13 @@ hipError_t launch_grouped(const ArenaDesc& gu, const ArenaDesc& dn, const uint16
     uint16_t* xd = reinterpret_cast<uint16_t*>(base + L.xd);
     float* part_dn = reinterpret_cast<float*>(base + L.part_dn);
     GuUnitRes rg{gu.trellis, gu.suh, gu.svh, words_gu, hidden, inter, x, topk, ids,
-                 part_gu, L.s_gu, ctr_gu, dn.suh, xd};
+                 part_gu, L.s_gu, ctr_gu, dn.suh, xd, (int)P};
     const int kc_g = hidden / L.s_gu;
     e = dispatch_bits<GuUnitRun>(gu.bits, rg, hidden, inter, (int)(P * 2), kc_g,
                                  gemv_lds_bytes(kc_g, 1), s);
     if (e != hipSuccess) return e;
     DnUnitRes rd{dn.trellis, dn.svh, words_dn, inter, hidden, xd, ids, w, topk,
-                 part_dn, L.s_dn, ctr_dn, y};
+                 part_dn, L.s_dn, ctr_dn, y, (int)t};
     const int kc_d = inter / L.s_dn;
     return dispatch_bits<DnUnitRun>(dn.bits, rd, inter, hidden, (int)P, kc_d,
                                     gemv_lds_bytes(kc_d, 1), s);

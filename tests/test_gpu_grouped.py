@@ -37,14 +37,16 @@ def _small(t, experts=16, topk=4, hidden=256, inter=128, bits=3, seed=40):
     return synth.moe_inputs(seed + t, t, experts=experts, topk=topk, hidden=hidden, inter=inter, bits=bits)
 
 
-@pytest.mark.parametrize("t", [1, 2, 4, 16, 64])
+# The unit path serves t * topk <= 512 (token, slot) pairs, the binned grouped
+# GEMM path larger calls; sizes on both sides of the threshold (topk = 4 here).
+@pytest.mark.parametrize("t", [1, 2, 4, 16, 64, 128, 129, 300])
 def test_random_routing(t):
     m = _small(t)
     err = O.rel_frobenius(_run(m), _ref(m))
     assert err < TOL, err
 
 
-@pytest.mark.parametrize("t", [3, 40])
+@pytest.mark.parametrize("t", [3, 40, 200])
 def test_all_tokens_same_experts(t):
     m = _small(t)
     ids = np.tile(np.array([5, 1, 9, 0], np.int32), (t, 1))
@@ -52,7 +54,7 @@ def test_all_tokens_same_experts(t):
     assert err < TOL, err
 
 
-@pytest.mark.parametrize("t", [2, 33])
+@pytest.mark.parametrize("t", [2, 33, 600])
 def test_top1_unit_weight(t):
     m = _small(t, topk=1)
     w = np.ones((t, 1), np.float32)
@@ -60,17 +62,18 @@ def test_top1_unit_weight(t):
     assert err < TOL, err
 
 
-@pytest.mark.parametrize("t", [2, 40])
+@pytest.mark.parametrize("t", [2, 40, 200])
 def test_zero_weights_exact_zero(t):
     m = _small(t)
     w = np.zeros_like(m["weights"])
     assert (_run(m, w=w) == 0).all()
 
 
-def test_unused_expert_has_no_effect():
-    m = _small(24)
+@pytest.mark.parametrize("t", [24, 200])
+def test_unused_expert_has_no_effect(t):
+    m = _small(t, experts=64) if t > 100 else _small(t)
     used = set(np.unique(m["ids"]).tolist())
-    unused = [e for e in range(16) if e not in used]
+    unused = [e for e in range(m["gate_up"]["experts"]) if e not in used]
     y = _run(m)
     if unused:
         m2 = dict(m); m2["gate_up"] = dict(m["gate_up"]); m2["gate_up"]["trellis"] = m["gate_up"]["trellis"].copy()
@@ -85,7 +88,7 @@ def test_max_topk(t):
     assert err < TOL, err
 
 
-@pytest.mark.parametrize("t", [1, 4])
+@pytest.mark.parametrize("t", [1, 4, 64, 65])
 def test_moe_256x2048x512_k3_small_t(t):
     m = synth.moe_inputs(synth.SEED_MOE_256x2048x512, t)
     err = O.rel_frobenius(_run(m), _ref(m))
