@@ -95,8 +95,10 @@ def mixed_layer_leg(X, torch, synth, dev, stream, reps=50):
     (5120 x 17408), down (17408 x 5120) with per-tensor widths drawn from 2..8.
     M = 1: the seven projections run in layer order, repeatedly, each call
     timed with its own event pair (between two calls of one tensor the other
-    six stream about 220 MB, so each call reads mostly HBM); M = 4096: each
-    projection timed alone (the MFMA-bound prefill)."""
+    six stream about 220 MB, so each call reads mostly HBM), then again with
+    the projections that read one input fused into one exl3_linear_multi call
+    each ((q, k, v), o, (gate, up), down); M = 4096: each projection timed
+    alone (the MFMA-bound prefill)."""
     out = {"bits": {}, "m1": {}, "m4096": {}}
     d1 = synth.mixed_layer_inputs(synth.SEED_MIXED_LAYER, 1)
     names = [nm for nm, _, _ in synth.MIXED_LAYER_SHAPES]
@@ -132,6 +134,38 @@ def mixed_layer_leg(X, torch, synth, dev, stream, reps=50):
                          "frac_hbm": round(b / t / 1e9 / HBM_PEAK_GBS, 4)}
     out["m1"]["layer"] = {"us": round(tot_t * 1e6, 2), "GB/s": round(tot_b / tot_t / 1e9, 1),
                           "frac_hbm": round(tot_b / tot_t / 1e9 / HBM_PEAK_GBS, 4)}
+    # the same layer with the projections that share an input fused into one
+    # exl3_linear_multi call each: (q, k, v), o, (gate, up), down
+    groups = [("q", "k", "v"), ("o",), ("gate", "up"), ("down",)]
+    gouts = {g: [ys[nm] for nm in g] for g in groups}
+    gws = {g: [ws[nm] for nm in g] for g in groups}
+    wsm = torch.zeros(max(X.exl3_linear_multi_workspace_size(gws[g], 1) for g in groups), dtype=torch.uint8,
+                      device=dev)
+    def gcall(g):
+        X.exl3_linear_multi(xs[g[0]], gws[g], outs=gouts[g], workspace=wsm, stream=stream)
+    for _ in range(3):
+        for g in groups:
+            gcall(g)
+    torch.cuda.synchronize()
+    evg = [[(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in groups]
+           for _ in range(reps)]
+    for r in range(reps):
+        for i, g in enumerate(groups):
+            evg[r][i][0].record(stream)
+            gcall(g)
+            evg[r][i][1].record(stream)
+    torch.cuda.synchronize()
+    out["m1_fused"] = {}
+    tot_t = 0.0
+    for i, g in enumerate(groups):
+        t = sum(evg[r][i][0].elapsed_time(evg[r][i][1]) for r in range(reps)) / reps * 1e-3
+        b = sum(linear_bytes(d1[nm]["k"], d1[nm]["n"], d1[nm]["bits"], 1) for nm in g)
+        tot_t += t
+        out["m1_fused"]["+".join(g)] = {"us": round(t * 1e6, 2), "GB/s": round(b / t / 1e9, 1),
+                                        "frac_hbm": round(b / t / 1e9 / HBM_PEAK_GBS, 4)}
+    out["m1_fused"]["layer"] = {"us": round(tot_t * 1e6, 2), "GB/s": round(tot_b / tot_t / 1e9, 1),
+                                "frac_hbm": round(tot_b / tot_t / 1e9 / HBM_PEAK_GBS, 4)}
+    del wsm
     del xs, ys
     d4 = synth.mixed_layer_inputs(synth.SEED_MIXED_LAYER, 4096)
     tot_f = tot_t = 0.0

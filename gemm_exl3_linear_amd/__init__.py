@@ -28,6 +28,7 @@ EXL3_F16 = 0
 EXL3_F32 = 1
 CODEBOOK_MUL1 = 2
 MAX_TOPK = 16
+MAX_MULTI = 8
 
 
 class Exl3Error(RuntimeError):
@@ -79,6 +80,11 @@ def lib() -> ctypes.CDLL:
     L.exl3_linear_workspace_size.argtypes = [ctypes.POINTER(_Weight), i64]
     L.exl3_linear.restype = i32
     L.exl3_linear.argtypes = [ctypes.POINTER(_Weight), vp, i64, i64, vp, i64, i32, vp, sz, vp]
+    L.exl3_linear_multi_workspace_size.restype = sz
+    L.exl3_linear_multi_workspace_size.argtypes = [ctypes.POINTER(ctypes.POINTER(_Weight)), i32, i64]
+    L.exl3_linear_multi.restype = i32
+    L.exl3_linear_multi.argtypes = [ctypes.POINTER(ctypes.POINTER(_Weight)), i32, vp, i64, i64,
+                                    ctypes.POINTER(vp), ctypes.POINTER(i64), i32, vp, sz, vp]
     L.exl3_grouped_experts_workspace_size.restype = sz
     L.exl3_grouped_experts_workspace_size.argtypes = [ctypes.POINTER(_Arena), ctypes.POINTER(_Arena), i64, i32]
     L.exl3_grouped_experts.restype = i32
@@ -230,6 +236,38 @@ def exl3_linear(x, w: Exl3Weight, out_dtype=None, out=None, workspace=None, stre
     _check(lib().exl3_linear(ctypes.byref(cw), _ptr(x), m, x.stride(0), _ptr(out), out.stride(0), ydt,
                              _ptr(workspace), wsb, _stream(stream)), "exl3_linear")
     return out
+
+
+def _weight_array(ws):
+    """ctypes array of pointers to the tensors' C records (records kept alive)."""
+    recs = [w._c() for w in ws]
+    arr = (ctypes.POINTER(_Weight) * len(recs))(*[ctypes.pointer(r) for r in recs])
+    return arr, recs
+
+
+def exl3_linear_multi_workspace_size(ws, m: int) -> int:
+    arr, _recs = _weight_array(ws)
+    return int(lib().exl3_linear_multi_workspace_size(arr, len(ws), int(m)))
+
+
+def exl3_linear_multi(x, ws, out_dtype=None, outs=None, workspace=None, stream=None):
+    """y[i] = exl3_linear(x, ws[i]) for tensors that share the input x (same k)."""
+    import torch
+    assert x.dim() == 2 and x.dtype == torch.float16 and x.stride(1) == 1
+    m = x.shape[0]
+    if outs is None:
+        outs = [torch.empty((m, w.n), dtype=out_dtype or torch.float16, device=x.device) for w in ws]
+    ydt = {torch.float16: EXL3_F16, torch.float32: EXL3_F32}[outs[0].dtype]
+    need = exl3_linear_multi_workspace_size(ws, m)
+    if workspace is None and need:
+        workspace = torch.zeros(need, dtype=torch.uint8, device=x.device)
+    wsb = 0 if workspace is None else workspace.numel() * workspace.element_size()
+    arr, _recs = _weight_array(ws)
+    yp = (ctypes.c_void_p * len(outs))(*[_ptr(o) for o in outs])
+    ld = (ctypes.c_int64 * len(outs))(*[o.stride(0) for o in outs])
+    _check(lib().exl3_linear_multi(arr, len(ws), _ptr(x), m, x.stride(0), yp, ld, ydt, _ptr(workspace), wsb,
+                                   _stream(stream)), "exl3_linear_multi")
+    return outs
 
 
 def exl3_grouped_experts_workspace_size(gate_up: Exl3Arena, down: Exl3Arena, t: int, topk: int) -> int:

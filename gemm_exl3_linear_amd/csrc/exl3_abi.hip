@@ -62,6 +62,33 @@ size_t linear_ws(const exl3_weight* w, int64_t m) {
   return exl3::gemm_workspace(w->k, w->n, (int)m);
 }
 
+// Common checks of a multi-tensor call: 1..EXL3_MAX_MULTI valid records that
+// share k.
+exl3_status check_multi(const exl3_weight* const* w, int32_t count) {
+  if (!w || count < 1 || count > EXL3_MAX_MULTI) return EXL3_E_INVALID;
+  for (int i = 0; i < count; ++i) {
+    const exl3_status st = check_weight(w[i], 128, true);
+    if (st != EXL3_OK) return st;
+    if (w[i]->k != w[0]->k) return EXL3_E_INVALID;
+    if ((int64_t)w[i]->k * w[i]->n / 8 * w[i]->bits >= ((int64_t)1 << 32)) return EXL3_E_INVALID;
+  }
+  return EXL3_OK;
+}
+
+size_t multi_ws(const exl3_weight* const* w, int32_t count, int64_t m) {
+  if (m == 1) {
+    exl3::MultiTensor t[EXL3_MAX_MULTI];
+    for (int i = 0; i < count; ++i) t[i] = {w[i]->trellis, w[i]->suh, w[i]->svh, w[i]->bias, w[i]->n, w[i]->bits};
+    return exl3::plan_gemv_multi(t, count, w[0]->k).ws;
+  }
+  size_t need = 0;
+  for (int i = 0; i < count; ++i) {
+    const size_t s = linear_ws(w[i], m);
+    if (s > need) need = s;
+  }
+  return need;
+}
+
 exl3::ArenaDesc desc(const exl3_expert_weights* a) {
   return exl3::ArenaDesc{a->trellis, a->suh, a->svh, a->experts, a->slots, a->k, a->n, a->bits};
 }
@@ -73,7 +100,7 @@ exl3_status check_grouped(const exl3_expert_weights* gu, const exl3_expert_weigh
   if ((st = check_arena(dn, 1)) != EXL3_OK) return st;
   if (dn->experts != gu->experts || dn->k != gu->n || dn->n != gu->k) return EXL3_E_INVALID;
   if (t < 0 || topk < 1 || topk > EXL3_MAX_TOPK) return EXL3_E_INVALID;
-  // the grouped GEMM grid holds one workgroup row per 64-row tile (< 65536)
+  // the grouped GEMM grid holds one workgroup row per 128-row tile (< 65536)
   if (t * topk > (int64_t)1 << 21) return EXL3_E_INVALID;
   return EXL3_OK;
 }
@@ -154,6 +181,46 @@ exl3_status exl3_linear(const exl3_weight* w, const void* x, int64_t m, int64_t 
   return from_hip(exl3::launch_gemm(w->trellis, w->suh, w->svh, w->bias, w->k, w->n, w->bits,
                                     static_cast<const uint16_t*>(x), (int)m, ldx, y, ldy, f32, ws,
                                     s));
+}
+
+size_t exl3_linear_multi_workspace_size(const exl3_weight* const* w, int32_t count, int64_t m) {
+  if (check_multi(w, count) != EXL3_OK || m <= 0) return 0;
+  return multi_ws(w, count, m);
+}
+
+exl3_status exl3_linear_multi(const exl3_weight* const* w, int32_t count, const void* x, int64_t m,
+                              int64_t ldx, void* const* y, const int64_t* ldy, int32_t y_dtype,
+                              void* ws, size_t ws_bytes, exl3_stream_t stream) {
+  exl3_status st = check_multi(w, count);
+  if (st != EXL3_OK) return st;
+  if (m < 0 || m > ((int64_t)1 << 24)) return EXL3_E_INVALID;
+  if (y_dtype != EXL3_F16 && y_dtype != EXL3_F32) return EXL3_E_INVALID;
+  if (!y || !ldy || ldx < w[0]->k || ldx % 8) return EXL3_E_INVALID;
+  for (int i = 0; i < count; ++i)
+    if (ldy[i] < w[i]->n || ldy[i] % 8) return EXL3_E_INVALID;
+  if (m == 0) return EXL3_OK;
+  if (!x || !aligned16(x)) return EXL3_E_INVALID;
+  for (int i = 0; i < count; ++i)
+    if (!y[i] || !aligned16(y[i])) return EXL3_E_INVALID;
+  const size_t need = multi_ws(w, count, m);
+  if (need > 0 && (!ws || ws_bytes < need || !aligned16(ws))) return EXL3_E_WORKSPACE;
+  const hipStream_t s = reinterpret_cast<hipStream_t>(stream);
+  if (m == 1) {
+    exl3::MultiTensor t[EXL3_MAX_MULTI];
+    for (int i = 0; i < count; ++i) t[i] = {w[i]->trellis, w[i]->suh, w[i]->svh, w[i]->bias, w[i]->n, w[i]->bits};
+    const exl3::MultiPlan mp = exl3::plan_gemv_multi(t, count, w[0]->k);
+    trace("linear_multi/gemv count k waves tasks", count, w[0]->k, mp.wbase[count], mp.fbase[count]);
+    // x has one row; its stride does not matter
+    return from_hip(exl3::launch_gemv_multi(t, count, w[0]->k, static_cast<const uint16_t*>(x), y,
+                                            ldy, y_dtype == EXL3_F32, ws, mp, s));
+  }
+  // several rows: each tensor in turn on the single-tensor path (the same
+  // kernels and results as separate exl3_linear calls), sharing the workspace
+  for (int i = 0; i < count; ++i) {
+    st = exl3_linear(w[i], x, m, ldx, y[i], ldy[i], y_dtype, ws, ws_bytes, stream);
+    if (st != EXL3_OK) return st;
+  }
+  return EXL3_OK;
 }
 
 size_t exl3_grouped_experts_workspace_size(const exl3_expert_weights* gate_up,

@@ -125,4 +125,85 @@ hipError_t launch_gemv(const uint16_t* trellis, const uint16_t* suh, const uint1
   return dispatch_bits<SkRun>(bits, a, plan, s);
 }
 
+// ---------------------------------------------------------------------------
+// several tensors sharing one activation row (m == 1), one launch pair
+// ---------------------------------------------------------------------------
+// Waves per tensor: kGemvSkWaves in proportion to the tensors' trellis bytes,
+// each at least ceil(R_i / 48) (runs of at most 48 row steps) and at most R_i,
+// rounded up to a multiple of 4.  Partials of tensor i follow those of i - 1.
+static_assert(kMultiMax == kSkMaxMulti, "multi-tensor limits differ");
+
+MultiPlan plan_gemv_multi(const MultiTensor* t, int count, int k) {
+  MultiPlan mp;
+  mp.count = count;
+  double total = 0;
+  for (int i = 0; i < count; ++i) total += (double)t[i].n * t[i].bits;
+  const int64_t KT = k / 16;
+  size_t off = 0;
+  int64_t wsum = 0, tasks = 0;
+  for (int i = 0; i < count; ++i) {
+    const int64_t NB = t[i].n / 128, R = KT * NB;
+    int64_t W = (int64_t)((double)kGemvSkWaves * t[i].n * t[i].bits / total + 0.5);
+    if (W < (R + 47) / 48) W = (R + 47) / 48;
+    W = (W + 3) / 4 * 4;
+    if (W > R) W = (R + 3) / 4 * 4;
+    if (W < 4) W = 4;
+    const int64_t run_min = R / W > 0 ? R / W : 1;
+    mp.waves[i] = (int)W;
+    mp.slots[i] = (int)((KT - 1 + run_min - 1) / run_min + 1);
+    mp.part_off[i] = off;
+    off += ((size_t)NB * mp.slots[i] * 128 * sizeof(float) + 255) & ~(size_t)255;
+    mp.wbase[i] = (int)wsum;
+    mp.fbase[i] = (int)tasks;
+    wsum += W;
+    tasks += NB;
+  }
+  mp.wbase[count] = (int)wsum;
+  mp.fbase[count] = (int)tasks;
+  mp.ws = off;
+  return mp;
+}
+
+hipError_t launch_gemv_multi(const MultiTensor* t, int count, int k, const uint16_t* x, void* const* y,
+                             const int64_t* ldy, bool y_f32, void* ws, const MultiPlan& mp,
+                             hipStream_t s) {
+  SkMulti ma;
+  ma.count = count;
+  unsigned char* base = static_cast<unsigned char*>(ws);
+  for (int i = 0; i <= count; ++i) {
+    ma.wbase[i] = mp.wbase[i];
+    ma.fbase[i] = mp.fbase[i];
+  }
+  for (int i = 0; i < count; ++i) {
+    SkArgs& a = ma.t[i];
+    a.trellis = t[i].trellis;
+    a.suh = t[i].suh;
+    a.x = x;
+    a.ldx = k;
+    a.xprep = nullptr;
+    a.m = 1;
+    a.k = k;
+    a.n = t[i].n;
+    a.KT = k / 16;
+    a.R = a.KT * (a.n / 128);
+    a.W = mp.waves[i];
+    a.q = a.R / a.W;
+    a.rem = a.R - a.q * a.W;
+    a.slots = mp.slots[i];
+    a.part = reinterpret_cast<float*>(base + mp.part_off[i]);
+    a.svh = t[i].svh;
+    a.bias = t[i].bias;
+    a.y = y[i];
+    a.ldy = ldy[i];
+    a.y_f32 = y_f32 ? 1 : 0;
+    ma.bits[i] = t[i].bits;
+  }
+  hipLaunchKernelGGL((gemv_sk_multi_kernel<4>), dim3((unsigned)(mp.wbase[count] / 4)), dim3(256), 0, s,
+                     ma);
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  hipLaunchKernelGGL(gemv_sk_multi_finish, dim3((unsigned)mp.fbase[count]), dim3(64), 0, s, ma);
+  return hipGetLastError();
+}
+
 }  // namespace exl3

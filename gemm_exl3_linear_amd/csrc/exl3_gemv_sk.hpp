@@ -115,13 +115,9 @@ __device__ __forceinline__ void reduce_rowpairs(float (&acc)[16], float& c0, flo
 constexpr int kSkWaveLdsDot = kSkMaxXBlocks * 128 * 2;
 constexpr int kSkWaveLdsMfma = 64 * 20 * 4;
 
+// The work of wave `wid` of a tensor's grid; wl is the wave's LDS region.
 template <int K, bool DOT, int PF>
-__global__ __launch_bounds__(256) void gemv_sk_kernel(SkArgs a) {
-  constexpr int WAVE_LDS = DOT ? kSkWaveLdsDot : kSkWaveLdsMfma;
-  __shared__ __align__(16) unsigned char smem[4 * WAVE_LDS];
-
-  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
-  const int wid = blockIdx.x * 4 + wave;
+__device__ __forceinline__ void sk_run(const SkArgs& a, int wid, unsigned char* wl) {
   const int len = a.q + (wid < a.rem ? 1 : 0);
   if (len <= 0) return;
   const int r0 = sk_start(wid, a.q, a.rem);
@@ -130,7 +126,6 @@ __global__ __launch_bounds__(256) void gemv_sk_kernel(SkArgs a) {
   const int lane = threadIdx.x & 63;
   const int t = lane >> 3, p = lane & 7;   // decode role
   const int g = lane >> 4, j = lane & 15;  // MFMA role
-  unsigned char* wl = smem + wave * WAVE_LDS;
 
   // The run starts at k tile kt0 of block nb0; the wave is partial slot
   // slot0 of that block and slot 0 of every later one.
@@ -346,20 +341,16 @@ __device__ __forceinline__ int sk_arrivals(int nb, int KT, int q, int rem) {
   return sk_owner((nb + 1) * KT - 1, q, rem) - sk_owner(nb * KT, q, rem) + 1;
 }
 
-// One wave (a 64-thread workgroup, so the tasks spread over the CUs) per
-// (activation row i, 128-column block nb).  Lane l owns columns
-// 8 (l % 16) .. 8 (l % 16) + 7 of the block and sums the block's slots
-// l / 16, l / 16 + 4, l / 16 + 8, ... in that order; the four slot groups are
-// then combined as (g0 + g1) + (g2 + g3) (fp32 addition commutes, so every
-// lane ends with the same total whichever of a pair it holds).  The output
-// transform is three in-lane butterfly stages and four lane swizzles inside
-// each group of 16 lanes; lanes 0..15 store.
-__global__ __launch_bounds__(64) void gemv_sk_finish(SkArgs a) {
-  const int NB = a.n >> 7;
+// Finish of (activation row i, 128-column block nb), by one wave.  Lane l
+// owns columns 8 (l % 16) .. 8 (l % 16) + 7 of the block and sums the block's
+// slots l / 16, l / 16 + 4, l / 16 + 8, ... in that order; the four slot
+// groups are then combined as (g0 + g1) + (g2 + g3) (fp32 addition commutes,
+// so every lane ends with the same total whichever of a pair it holds).  The
+// output transform is three in-lane butterfly stages and four lane swizzles
+// inside each group of 16 lanes; lanes 0..15 store.
+__device__ __forceinline__ void sk_finish(const SkArgs& a, int i, int nb) {
   const int m = a.m;
-  const int task = (int)blockIdx.x;
-  const int i = task / NB, nb = task - i * NB;
-  const int lane = (int)threadIdx.x;
+  const int lane = (int)(threadIdx.x & 63);
   const int c8 = 8 * (lane & 15);
   const int sg = lane >> 4;
   const int col = nb * 128 + c8;
@@ -415,6 +406,72 @@ __global__ __launch_bounds__(64) void gemv_sk_finish(SkArgs a) {
     *reinterpret_cast<uint4*>(static_cast<uint16_t*>(a.y) + (int64_t)i * a.ldy + col) =
         make_uint4(o[0], o[1], o[2], o[3]);
   }
+}
+
+
+template <int K, bool DOT, int PF>
+__global__ __launch_bounds__(256) void gemv_sk_kernel(SkArgs a) {
+  constexpr int WAVE_LDS = DOT ? kSkWaveLdsDot : kSkWaveLdsMfma;
+  __shared__ __align__(16) unsigned char smem[4 * WAVE_LDS];
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  sk_run<K, DOT, PF>(a, (int)blockIdx.x * 4 + wave, smem + wave * WAVE_LDS);
+}
+
+// One wave (a 64-thread workgroup, so the tasks spread over the CUs) per
+// (activation row i, 128-column block nb).
+__global__ __launch_bounds__(64) void gemv_sk_finish(SkArgs a) {
+  const int NB = a.n >> 7;
+  const int task = (int)blockIdx.x;
+  const int i = task / NB;
+  sk_finish(a, i, task - i * NB);
+}
+
+// ---------------------------------------------------------------------------
+// Several tensors that share one activation row (m == 1) in one launch pair:
+// the projections that read the same input (q, k, v; gate and up), each with
+// its own width K, shape and signs (TensorFold issue #832, "Description":
+// widths are mixed per tensor).  Every tensor keeps its own stream-k plan over
+// W_i waves (W_i in proportion to its trellis bytes); the waves of the grid
+// are the tensors' waves one after the other, and a wave dispatches on its
+// tensor's K.  One finishing launch covers all tensors' blocks.
+// ---------------------------------------------------------------------------
+constexpr int kSkMaxMulti = 8;
+
+struct SkMulti {
+  int count;
+  int wbase[kSkMaxMulti + 1];  // first wave of tensor i; wbase[count] = all waves
+  int fbase[kSkMaxMulti + 1];  // first finishing task of tensor i
+  int bits[kSkMaxMulti];
+  SkArgs t[kSkMaxMulti];
+};
+
+template <int PF, int K = 1>
+__device__ __forceinline__ void sk_run_bits(int bits, const SkArgs& a, int wid, unsigned char* wl) {
+  if constexpr (K <= 8) {
+    if (bits == K)
+      sk_run<K, true, PF>(a, wid, wl);
+    else
+      sk_run_bits<PF, K + 1>(bits, a, wid, wl);
+  }
+}
+
+template <int PF>
+__global__ __launch_bounds__(256) void gemv_sk_multi_kernel(SkMulti ma) {
+  __shared__ __align__(16) unsigned char smem[4 * kSkWaveLdsDot];
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int gw = (int)blockIdx.x * 4 + wave;
+  int i = 0;
+  while (i + 1 < ma.count && gw >= ma.wbase[i + 1]) ++i;
+  if (gw >= ma.wbase[i + 1]) return;
+  sk_run_bits<PF>(ma.bits[i], ma.t[i], gw - ma.wbase[i], smem + wave * kSkWaveLdsDot);
+}
+
+__global__ __launch_bounds__(64) void gemv_sk_multi_finish(SkMulti ma) {
+  const int task = (int)blockIdx.x;
+  int i = 0;
+  while (i + 1 < ma.count && task >= ma.fbase[i + 1]) ++i;
+  if (task >= ma.fbase[i + 1]) return;
+  sk_finish(ma.t[i], 0, task - ma.fbase[i]);
 }
 
 }  // namespace exl3

@@ -51,6 +51,29 @@ hipError_t launch_gemv(const uint16_t* trellis, const uint16_t* suh, const uint1
                        int m, int64_t ldx, void* y, int64_t ldy, bool y_f32, void* ws,
                        const GemvPlan& plan, hipStream_t s);
 
+// several tensors sharing one activation row (m == 1), one launch pair
+constexpr int kMultiMax = 8;
+struct MultiTensor {
+  const uint16_t* trellis;
+  const uint16_t* suh;
+  const uint16_t* svh;
+  const uint16_t* bias;
+  int n, bits;
+};
+struct MultiPlan {
+  int count;
+  int waves[kMultiMax];
+  int slots[kMultiMax];
+  size_t part_off[kMultiMax];
+  int wbase[kMultiMax + 1];
+  int fbase[kMultiMax + 1];
+  size_t ws;
+};
+MultiPlan plan_gemv_multi(const MultiTensor* t, int count, int k);
+hipError_t launch_gemv_multi(const MultiTensor* t, int count, int k, const uint16_t* x, void* const* y,
+                             const int64_t* ldy, bool y_f32, void* ws, const MultiPlan& mp,
+                             hipStream_t s);
+
 size_t gemm_workspace(int k, int n, int m);
 hipError_t launch_gemm(const uint16_t* trellis, const uint16_t* suh, const uint16_t* svh,
                        const uint16_t* bias, int k, int n, int bits, const uint16_t* x,

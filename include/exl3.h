@@ -57,6 +57,9 @@ extern "C" {
 /* Largest supported routing fan-out for exl3_grouped_experts. */
 #define EXL3_MAX_TOPK 16
 
+/* Largest number of tensors in one exl3_linear_multi call. */
+#define EXL3_MAX_MULTI 8
+
 typedef struct ihipStream_t* exl3_stream_t; /* same type as hipStream_t */
 
 typedef enum exl3_status {
@@ -161,6 +164,32 @@ size_t exl3_linear_workspace_size(const exl3_weight* w, int64_t m);
 exl3_status exl3_linear(const exl3_weight* w, const void* x, int64_t m, int64_t ldx, void* y,
                         int64_t ldy, int32_t y_dtype, void* ws, size_t ws_bytes,
                         exl3_stream_t stream);
+
+/* Bytes of device workspace exl3_linear_multi needs for m rows of these
+ * tensors (0 if the arguments are invalid). */
+size_t exl3_linear_multi_workspace_size(const exl3_weight* const* w, int32_t count, int64_t m);
+
+/* exl3_linear_multi - y[i] = exl3_linear(w[i], x) for i < count, for the
+ * projections that read one input (q, k and v; gate and up), each tensor with
+ * its own width, shape, signs and bias (TensorFold issue #832,
+ * "Description": widths are mixed per tensor; the fused multi-tensor launch
+ * is the issue's "fused-shard" idea).
+ *   w      host array of count tensor records, 1 <= count <= EXL3_MAX_MULTI,
+ *          all with the same k (the records' buffers are device pointers)
+ *   x      fp16 [m][ldx] device pointer, as for exl3_linear
+ *   y      host array of count device pointers, y[i] is [m][ldy[i]] of
+ *          y_dtype with ldy[i] >= w[i]->n, multiple of 8
+ *   ws     device workspace of at least exl3_linear_multi_workspace_size
+ *          bytes, zero-filled before its first use (same rule as exl3_linear)
+ * m == 1 runs all tensors in one decode-GEMV launch and one finishing
+ * launch (each tensor keeps its own split over a share of the waves, in
+ * proportion to its trellis bytes, so its results agree with exl3_linear to
+ * rounding); m >= 2 runs the tensors one after another through exl3_linear
+ * (bit-identical to separate calls).  m == 0 returns EXL3_OK.  Validation of
+ * every tensor happens before anything is enqueued.                       */
+exl3_status exl3_linear_multi(const exl3_weight* const* w, int32_t count, const void* x, int64_t m,
+                              int64_t ldx, void* const* y, const int64_t* ldy, int32_t y_dtype,
+                              void* ws, size_t ws_bytes, exl3_stream_t stream);
 
 /* Bytes of device workspace exl3_grouped_experts needs (0 if invalid). */
 size_t exl3_grouped_experts_workspace_size(const exl3_expert_weights* gate_up,

@@ -105,3 +105,38 @@ def test_grouped_rejects():
     assert args(gu, dn_bad, 1, 2) == X.EXL3_E_INVALID
     gu_cb = X._Arena(16, 16, 16, 8, 2, 256, 128, 3, 1)
     assert args(gu_cb, dn, 1, 2) == X.EXL3_E_UNSUPPORTED
+
+
+def _multi(ws):
+    recs = list(ws)
+    arr = (ctypes.POINTER(X._Weight) * len(recs))(*[ctypes.pointer(r) for r in recs])
+    return arr, recs
+
+
+def test_linear_multi_workspace_and_rejects():
+    # host-only checks: nothing reaches a device for any of these
+    L = X.lib()
+    q, k_, v = _w(5120, 5120, 7), _w(5120, 1024, 2), _w(5120, 1024, 3)
+    arr, _r = _multi([q, k_, v])
+    ws1 = L.exl3_linear_multi_workspace_size(arr, 3, 1)
+    assert ws1 > 0 and ws1 % 256 == 0
+    # m >= 2: the largest single-tensor workspace (tensors run one after another)
+    ws4 = L.exl3_linear_multi_workspace_size(arr, 3, 4)
+    assert ws4 == max(L.exl3_linear_workspace_size(ctypes.byref(w), 4) for w in (q, k_, v))
+    y = (ctypes.c_void_p * 3)(16, 16, 16)
+    ld = (ctypes.c_int64 * 3)(5120, 1024, 1024)
+    f16 = X.EXL3_F16
+    assert L.exl3_linear_multi(arr, 0, 16, 1, 5120, y, ld, f16, 0, 0, 0) == X.EXL3_E_INVALID
+    assert L.exl3_linear_multi(arr, X.MAX_MULTI + 1, 16, 1, 5120, y, ld, f16, 0, 0, 0) == X.EXL3_E_INVALID
+    assert L.exl3_linear_multi(None, 3, 16, 1, 5120, y, ld, f16, 0, 0, 0) == X.EXL3_E_INVALID
+    # a tensor with another k, an unsupported codebook, a too-small ldy
+    arr2, _r2 = _multi([q, _w(1024, 1024, 2)])
+    assert L.exl3_linear_multi(arr2, 2, 16, 1, 5120, y, ld, f16, 0, 0, 0) == X.EXL3_E_INVALID
+    assert L.exl3_linear_multi_workspace_size(arr2, 2, 1) == 0
+    arr3, _r3 = _multi([q, _w(5120, 1024, 3, cb=1)])
+    assert L.exl3_linear_multi(arr3, 2, 16, 1, 5120, y, ld, f16, 0, 0, 0) == X.EXL3_E_UNSUPPORTED
+    ld_bad = (ctypes.c_int64 * 3)(5120, 1000, 1024)
+    assert L.exl3_linear_multi(arr, 3, 16, 1, 5120, y, ld_bad, f16, 0, 0, 0) == X.EXL3_E_INVALID
+    # missing workspace, then the empty call
+    assert L.exl3_linear_multi(arr, 3, 16, 1, 5120, y, ld, f16, 0, 0, 0) == X.EXL3_E_WORKSPACE
+    assert L.exl3_linear_multi(arr, 3, 16, 0, 5120, y, ld, f16, 0, 0, 0) == X.EXL3_OK
