@@ -48,23 +48,73 @@ int gemv_choose_splits(int k, int groups, int m, int target_wgs) {
   return best > 0 ? best : kb;
 }
 
+// Runs of R row steps over W waves, the first H of which (the first-round
+// waves) take runs kSkTierWeight1 / kSkTierWeight2 times longer than the
+// others.  Falls back to equal runs (H = W) when the weighted split would
+// leave a wave without a step or exceed kSkMaxRun.
+SkSplit make_sk_split(int64_t R, int64_t W, int64_t H) {
+  SkSplit s;
+  int64_t B1 = R;
+  if (H > 0 && H < W) {
+    const int64_t den = H * kSkTierWeight1 + (W - H) * kSkTierWeight2;
+    B1 = (R * H * kSkTierWeight1 + den / 2) / den;
+    if (B1 < H || R - B1 < W - H || (B1 + H - 1) / H > kSkMaxRun) {
+      H = W;
+      B1 = R;
+    }
+  } else if (H <= 0 && W > 0) {
+    H = 0;
+    B1 = 0;
+  } else {
+    H = W;
+  }
+  s.H = (int)H;
+  s.B1 = (int)B1;
+  s.q = H > 0 ? (int)(B1 / H) : 0;
+  s.rem = H > 0 ? (int)(B1 - (int64_t)s.q * H) : 0;
+  s.q2 = W > H ? (int)((R - B1) / (W - H)) : 0;
+  s.rem2 = W > H ? (int)((R - B1) - (int64_t)s.q2 * (W - H)) : 0;
+  return s;
+}
+
+// first-tier waves of a grid whose waves [first, first + W) are part of a
+// launch: those dispatched in the first round, when the launch has a second
+// round at all
+int sk_first_round(int64_t first, int64_t W, int64_t total) {
+  if (total <= kGemvRoundWaves || total > 2 * kGemvRoundWaves) return (int)W;
+  const int64_t h = kGemvRoundWaves - first;
+  return (int)(h < 0 ? 0 : h > W ? W : h);
+}
+
+// most partial slots any block receives, and the longest run
+static void sk_split_extent(const SkSplit& s, int64_t KT, int64_t NB, int64_t W, int& slots, int& longest) {
+  slots = 1;
+  for (int64_t nb = 0; nb < NB; ++nb) {
+    const int a = sk_arrivals(s, (int)nb, (int)KT);
+    if (a > slots) slots = a;
+  }
+  longest = 0;
+  if (s.H > 0) longest = s.q + (s.rem > 0 ? 1 : 0);
+  if (W > s.H && s.q2 + (s.rem2 > 0 ? 1 : 0) > longest) longest = s.q2 + (s.rem2 > 0 ? 1 : 0);
+}
+
 // Plan of the dense decode GEMV: W waves (kGemvSkWaves = eight per CU of the
-// 256-CU MI355X; more when runs would exceed 48 row steps, fewer for small
-// tensors), the number of partial slots a block can receive, and the
-// workspace (fp32 partials, then the transformed activations when m > 1).
-// The plan depends on (k, n) only, so every m <= 16 sees the same summation
-// order, and it needs no device query.
+// 256-CU MI355X; more when runs would exceed kSkMaxRun row steps, fewer for
+// small tensors), their runs, the number of partial slots a block can
+// receive, and the workspace (fp32 partials, then the transformed activations
+// when m > 1).  For 2 <= m <= 16 the plan depends on (k, n) only, so all of
+// them see the same summation order; m == 1 (v_dot2, whose rounding order
+// differs anyway) takes the two-tier runs.  No device query.
 GemvPlan plan_gemv(int k, int n, int m) {
   GemvPlan p;
   const int64_t KT = k / 16, NB = n / 128, R = KT * NB;
   int64_t W = kGemvSkWaves;
-  if (W < (R + 47) / 48) W = (R + 47) / 48;
+  if (W < (R + kSkMaxRun - 1) / kSkMaxRun) W = (R + kSkMaxRun - 1) / kSkMaxRun;
   W = (W + 3) / 4 * 4;
   if (W > R) W = (R + 3) / 4 * 4;  // runs of at least one row step (extra waves idle)
-  const int64_t run_min = R / W > 0 ? R / W : 1;
+  p.split = make_sk_split(R, W, m == 1 ? sk_first_round(0, W, W) : W);
   p.splits = (int)W;
-  p.kc = (int)((R + W - 1) / W);
-  p.slots = (int)((KT - 1 + run_min - 1) / run_min + 1);
+  sk_split_extent(p.split, KT, NB, W, p.slots, p.kc);
   p.lds = 0;
   p.ctr_bytes = 0;
   p.xprep_off = (((size_t)NB * p.slots * m * 128 * sizeof(float) + 255) & ~(size_t)255);
@@ -113,8 +163,7 @@ hipError_t launch_gemv(const uint16_t* trellis, const uint16_t* suh, const uint1
   a.KT = k / 16;
   a.R = a.KT * (n / 128);
   a.W = plan.splits;
-  a.q = a.R / a.W;
-  a.rem = a.R - a.q * a.W;
+  a.sp = plan.split;
   a.slots = plan.slots;
   a.part = reinterpret_cast<float*>(base + plan.ctr_bytes);
   a.svh = svh;
@@ -129,8 +178,9 @@ hipError_t launch_gemv(const uint16_t* trellis, const uint16_t* suh, const uint1
 // several tensors sharing one activation row (m == 1), one launch pair
 // ---------------------------------------------------------------------------
 // Waves per tensor: kGemvSkWaves in proportion to the tensors' trellis bytes,
-// each at least ceil(R_i / 48) (runs of at most 48 row steps) and at most R_i,
-// rounded up to a multiple of 4.  Partials of tensor i follow those of i - 1.
+// each at least ceil(R_i / kSkMaxRun) and at most R_i, rounded up to a
+// multiple of 4; each tensor's waves split their runs in two tiers by the
+// launch's first round.  Partials of tensor i follow those of i - 1.
 static_assert(kMultiMax == kSkMaxMulti, "multi-tensor limits differ");
 
 MultiPlan plan_gemv_multi(const MultiTensor* t, int count, int k) {
@@ -139,20 +189,15 @@ MultiPlan plan_gemv_multi(const MultiTensor* t, int count, int k) {
   double total = 0;
   for (int i = 0; i < count; ++i) total += (double)t[i].n * t[i].bits;
   const int64_t KT = k / 16;
-  size_t off = 0;
   int64_t wsum = 0, tasks = 0;
   for (int i = 0; i < count; ++i) {
     const int64_t NB = t[i].n / 128, R = KT * NB;
     int64_t W = (int64_t)((double)kGemvSkWaves * t[i].n * t[i].bits / total + 0.5);
-    if (W < (R + 47) / 48) W = (R + 47) / 48;
+    if (W < (R + kSkMaxRun - 1) / kSkMaxRun) W = (R + kSkMaxRun - 1) / kSkMaxRun;
     W = (W + 3) / 4 * 4;
     if (W > R) W = (R + 3) / 4 * 4;
     if (W < 4) W = 4;
-    const int64_t run_min = R / W > 0 ? R / W : 1;
     mp.waves[i] = (int)W;
-    mp.slots[i] = (int)((KT - 1 + run_min - 1) / run_min + 1);
-    mp.part_off[i] = off;
-    off += ((size_t)NB * mp.slots[i] * 128 * sizeof(float) + 255) & ~(size_t)255;
     mp.wbase[i] = (int)wsum;
     mp.fbase[i] = (int)tasks;
     wsum += W;
@@ -160,6 +205,16 @@ MultiPlan plan_gemv_multi(const MultiTensor* t, int count, int k) {
   }
   mp.wbase[count] = (int)wsum;
   mp.fbase[count] = (int)tasks;
+  // runs once the whole grid is known (the first round spans tensors)
+  size_t off = 0;
+  for (int i = 0; i < count; ++i) {
+    const int64_t NB = t[i].n / 128, R = KT * NB, W = mp.waves[i];
+    mp.split[i] = make_sk_split(R, W, sk_first_round(mp.wbase[i], W, wsum));
+    int longest;
+    sk_split_extent(mp.split[i], KT, NB, W, mp.slots[i], longest);
+    mp.part_off[i] = off;
+    off += ((size_t)NB * mp.slots[i] * 128 * sizeof(float) + 255) & ~(size_t)255;
+  }
   mp.ws = off;
   return mp;
 }
@@ -187,8 +242,7 @@ hipError_t launch_gemv_multi(const MultiTensor* t, int count, int k, const uint1
     a.KT = k / 16;
     a.R = a.KT * (a.n / 128);
     a.W = mp.waves[i];
-    a.q = a.R / a.W;
-    a.rem = a.R - a.q * a.W;
+    a.sp = mp.split[i];
     a.slots = mp.slots[i];
     a.part = reinterpret_cast<float*>(base + mp.part_off[i]);
     a.svh = t[i].svh;

@@ -3,10 +3,20 @@
 // Work decomposition ("stream-k" at wave granularity).  A row step is one k
 // tile (16 rows of k) of one 128-column block (8 n tiles of 16 columns): the
 // R = (n/128) * (k/16) row steps are ordered block-major and every wave of the
-// persistent grid takes one contiguous run of them (q = R / W steps, one more
-// for the first R % W waves).  Waves never wait for each other: each keeps PF
-// row-pair loads in flight from the start to the end of its run, across block
-// boundaries.
+// persistent grid takes one contiguous run of them.  Waves never wait for each
+// other: each keeps PF row-pair loads in flight from the start to the end of
+// its run, across block boundaries.
+//
+// At m == 1 run lengths come in two tiers (SkSplit).  With two waves per
+// SIMD, the wave dispatched in the first round (one per SIMD, the lower wave
+// ids) is the older one and wins the instruction arbiter whenever both are
+// ready; measured on MI355X at 5120 x 17408, it completes about 1.9 times the
+// row steps of its younger partner in the same time, so equal runs leave the
+// younger waves finishing alone.  The first-round waves therefore take runs
+// kSkTierWeight1 / kSkTierWeight2 times longer than the rest (1 to 9 % less
+// time per call at 5120 x 17408 across K = 1..8, most at K = 3..6).  The MFMA kernel (m >= 2) gained nothing from
+// it and keeps equal runs.  The split is part of the plan (a function of k, n,
+// m == 1 and the grid only), never of timing.
 //
 // gemv_sk_kernel, per wave:
 //   1. m == 1: x' = (x .* suh) H for the (at most eight) k blocks its run
@@ -38,10 +48,15 @@
 #pragma once
 
 #include "exl3_device.hpp"
+#include "exl3_sk_split.hpp"
 
 namespace exl3 {
 
-constexpr int kGemvSkWaves = 2048;  // 8 waves per CU of the 256-CU MI355X
+constexpr int kGemvSkWaves = 2048;    // 8 waves per CU of the 256-CU MI355X
+constexpr int kGemvRoundWaves = 1024; // one wave per SIMD: 256 CUs x 4 SIMDs
+constexpr int kSkTierWeight1 = 13;    // relative run length, first-round waves
+constexpr int kSkTierWeight2 = 7;     // relative run length, the others
+constexpr int kSkMaxRun = 48;         // longest run (the x' region of a wave)
 constexpr int kSkSlotBatch = 8;     // partial slots per lane loaded per batch in the finish
 constexpr int kSkMaxXBlocks = 8;    // k blocks a run may touch (m == 1)
 
@@ -56,7 +71,7 @@ struct SkArgs {
   int KT;                   // k / 16
   int R;                    // row steps = (n / 128) * KT
   int W;                    // waves of the grid
-  int q, rem;               // run lengths: q + 1 for waves < rem, q for the rest
+  SkSplit sp;               // run of every wave
   int slots;                // partial slots per block
   float* part;              // fp32 [n/128][slots][m][128]
   const uint16_t* svh;
@@ -65,17 +80,6 @@ struct SkArgs {
   int64_t ldy;
   int y_f32;
 };
-
-// first row step of wave w's run
-__device__ __forceinline__ int sk_start(int w, int q, int rem) {
-  return w * q + (w < rem ? w : rem);
-}
-
-// wave whose run contains row step r
-__device__ __forceinline__ int sk_owner(int r, int q, int rem) {
-  const int big = rem * (q + 1);  // steps covered by the longer runs
-  return r < big ? r / (q + 1) : rem + (r - big) / q;
-}
 
 // dot2 accumulators: sum over the 8 row-pair lanes of a tile; lane p ends with
 // the sums of columns 2p and 2p+1 of its n tile
@@ -114,13 +118,16 @@ __device__ __forceinline__ void reduce_rowpairs(float (&acc)[16], float& c0, flo
 // m >= 2: transpose region [8 n tiles][8 row pairs][20] dwords (5 KB)
 constexpr int kSkWaveLdsDot = kSkMaxXBlocks * 128 * 2;
 constexpr int kSkWaveLdsMfma = 64 * 20 * 4;
+// a run of kSkMaxRun steps starting anywhere in a k block fits the x' region
+static_assert(32 * (kSkMaxRun + 8) + 32 <= kSkWaveLdsDot, "x' region too small");
+static_assert((7 + kSkMaxRun + 7) / 8 <= kSkMaxXBlocks, "run touches too many k blocks");
 
 // The work of wave `wid` of a tensor's grid; wl is the wave's LDS region.
 template <int K, bool DOT, int PF>
 __device__ __forceinline__ void sk_run(const SkArgs& a, int wid, unsigned char* wl) {
-  const int len = a.q + (wid < a.rem ? 1 : 0);
+  const int len = sk_run_len(a.sp, wid);
   if (len <= 0) return;
-  const int r0 = sk_start(wid, a.q, a.rem);
+  const int r0 = sk_run_start(a.sp, wid);
   const int m = a.m;
   const int KT = a.KT;
   const int lane = threadIdx.x & 63;
@@ -131,7 +138,7 @@ __device__ __forceinline__ void sk_run(const SkArgs& a, int wid, unsigned char* 
   // slot0 of that block and slot 0 of every later one.
   const int nb0 = r0 / KT;
   const int kt0 = r0 - nb0 * KT;
-  const int slot0 = wid - sk_owner(nb0 * KT, a.q, a.rem);
+  const int slot0 = wid - sk_run_owner(a.sp, nb0 * KT);
 
   // Trellis addressing.  One buffer descriptor per 128-column block covers
   // its k range; a row step is a uniform offset (kt * bytes of a k-tile row),
@@ -270,7 +277,7 @@ __device__ __forceinline__ void sk_run(const SkArgs& a, int wid, unsigned char* 
   // region: one k tile is 32 bytes of x', and k blocks of the run follow each
   // other (a block column ends at a k-block boundary).  It is read one step
   // ahead; the read after the last step stays inside the region
-  // (runs are at most 48 steps: 32 (48 + 8) + 32 <= 2048 bytes).
+  // (runs are at most kSkMaxRun steps).
   const unsigned char* xlane = wl + 32 * (kt0 & 7) + 4 * p;
   half2_t xp = {0, 0};
   if constexpr (DOT) xp = *reinterpret_cast<const half2_t*>(xlane);
@@ -336,11 +343,6 @@ __device__ __forceinline__ void sk_run(const SkArgs& a, int wid, unsigned char* 
   }
 }
 
-// Slots of block nb: the waves whose runs intersect it, in run order.
-__device__ __forceinline__ int sk_arrivals(int nb, int KT, int q, int rem) {
-  return sk_owner((nb + 1) * KT - 1, q, rem) - sk_owner(nb * KT, q, rem) + 1;
-}
-
 // Finish of (activation row i, 128-column block nb), by one wave.  Lane l
 // owns columns 8 (l % 16) .. 8 (l % 16) + 7 of the block and sums the block's
 // slots l / 16, l / 16 + 4, l / 16 + 8, ... in that order; the four slot
@@ -354,7 +356,7 @@ __device__ __forceinline__ void sk_finish(const SkArgs& a, int i, int nb) {
   const int c8 = 8 * (lane & 15);
   const int sg = lane >> 4;
   const int col = nb * 128 + c8;
-  const int arrivals = sk_arrivals(nb, a.KT, a.q, a.rem);
+  const int arrivals = sk_arrivals(a.sp, nb, a.KT);
   const float* src = a.part + ((int64_t)nb * a.slots * m + i) * 128 + c8;
   const uint4 svv = *reinterpret_cast<const uint4*>(a.svh + col);
   uint4 bv = make_uint4(0, 0, 0, 0);

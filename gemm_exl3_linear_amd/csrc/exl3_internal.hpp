@@ -5,6 +5,8 @@
 #include <stddef.h>
 #include <stdint.h>
 
+#include "exl3_sk_split.hpp"
+
 namespace exl3 {
 
 // Dispatch a runtime width K (1..8) to a template instantiation.
@@ -37,6 +39,7 @@ hipError_t launch_hadamard(const void* in, bool in_f32, void* out, bool out_f32,
 
 // --- dense linear ----------------------------------------------------------
 struct GemvPlan {
+  SkSplit split;     // runs of the waves
   int splits;        // waves of the persistent grid
   int kc;            // longest run of row steps per wave
   int slots;         // partial-sum slots per 128-column block
@@ -62,6 +65,7 @@ struct MultiTensor {
 };
 struct MultiPlan {
   int count;
+  SkSplit split[kMultiMax];
   int waves[kMultiMax];
   int slots[kMultiMax];
   size_t part_off[kMultiMax];

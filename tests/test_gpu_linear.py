@@ -147,6 +147,26 @@ def test_dense_decode_5120x17408_k4(m):
     assert err < TOL, err
 
 
+@pytest.mark.parametrize("k,n,bits", [(4096, 8192, 3), (3072, 12288, 5)])
+def test_single_row_two_tier_runs(k, n, bits):
+    # At m == 1 a grid of more than one wave per SIMD gives the first-round
+    # waves longer runs than the rest; these shapes put the tier boundary and
+    # the run ends at other places in the 128-column blocks than the
+    # 5120 x 17408 workload does.  Row 0 of the same call at m == 4 (equal
+    # runs, matrix cores) sums the same fp32 products in another order: the
+    # two agree to one fp16 ulp of the value plus 2^-11 of the row's rms,
+    # while a partial slot lost or counted twice would move a whole 128-column
+    # block by several percent of the rms.
+    d = synth.linear_inputs(710 + bits, 4, k, n, bits)
+    y1 = _run(d, m=1)
+    err = O.rel_frobenius(y1.double().cpu().numpy(), _ref(d, m=1))
+    assert err < TOL, err
+    ref = _run(d)[:1].float()
+    rms = ref.pow(2).mean().sqrt()
+    tol = ref.abs() * 2.0 ** -10 + rms * 2.0 ** -11
+    assert ((y1.float() - ref).abs() <= tol).all()
+
+
 def test_dense_prefill_4096x5120x17408_k4_sampled_rows():
     d = G.linear_case(synth.SEED_PREFILL_4096x5120x17408, 4096, 5120, 17408, 4)
     y = _run(d)
