@@ -34,6 +34,17 @@ constant or a single function below):
   L   y = ((x * suh) H_k  W  H_n) * svh (+ bias).
   G   grouped experts: for every (token, slot): g = L_gate(x), u = L_up(x),
       a = silu(g) * u, d = L_down(a), Y[token] += w[token, slot] * d.
+  I8  int8 prefill (exl3xpu README, "Prefill: int8 linears ..."): activations
+      get one int8 scale per row, taken after the input transform; weights
+      one static scale, 127 / 3.453125, applied inside the decode.
+      I8W: W_q = RNE((sigma - 510) * 1775 / 2**18 * 127 / 3.453125), from the
+           codebook value before its fp16 rounding (the static scale joins
+           the codebook's own affine step, so the weight is rounded once, to
+           int8); |W_q| <= 127 and no value is a tie.
+      I8X: per row of x' = (x * suh) H_k: a = max |x'|, x_q = RNE(127 x' / a)
+           (|x_q| <= 127), scale a / 127; an all-zero row gives x_q = 0.
+      I8L: y' = (x_q W_q) * (a / 127) * (3.453125 / 127), the integer product
+           exact; y = (y' H_n) * svh (+ bias).
 
 Parity with real EXL3 checkpoints is not claimed: the pages do not define the
 trellis or codebook constants, so D1-D4 define this project's own format.
@@ -59,6 +70,8 @@ MUL1_SCALE_SHIFT = 18
 MUL1_BOUND = 3.453125           # printed bound of the mul1 codebook
 HADAMARD_BLOCK = 128            # linear dims are multiples of 128
 CODEBOOK_MUL1 = 2               # the pages' codebook marker for mul1 ("cb=2")
+INT8_MAX = 127                  # symmetric int8 range of the int8 prefill
+INT8_WEIGHT_SCALE = INT8_MAX / MUL1_BOUND  # static weight scale, 127 / 3.453125
 
 
 # ---------------------------------------------------------------------------
@@ -239,6 +252,67 @@ def effective_weight(trellis, suh, svh, bits) -> np.ndarray:
 def linear_weff(x, trellis, suh, svh, bits, bias=None) -> np.ndarray:
     """Second route to the same layer: y = x W_eff (+ bias)."""
     y = np.asarray(x, dtype=np.float64) @ effective_weight(trellis, suh, svh, bits)
+    if bias is not None:
+        y = y + np.asarray(bias, dtype=np.float64)
+    return y
+
+
+# ---------------------------------------------------------------------------
+# I8: int8 prefill
+# ---------------------------------------------------------------------------
+def mul1_int8_from_sigma(sig: np.ndarray) -> np.ndarray:
+    """I8W on byte sums: RNE((sigma - 510) * 1775 / 2**18 * 127 / 3.453125).
+
+    The codebook value before rounding is exact in float64; the product with
+    the static scale is within 1e-14 of exact, far from the nearest tie
+    (0.0015 away over sigma in [0, 1020]), so np.rint decides as exact
+    arithmetic would.
+    """
+    exact = (np.asarray(sig, dtype=np.int64) - MUL1_BIAS).astype(np.float64) * (
+        MUL1_SCALE_NUM / float(1 << MUL1_SCALE_SHIFT))
+    return np.rint(exact * INT8_WEIGHT_SCALE).astype(np.int8)
+
+
+def mul1_int8(states: np.ndarray) -> np.ndarray:
+    """I8W: int8 weight of each trellis state."""
+    return mul1_int8_from_sigma(mul1_sigma(states))
+
+
+def decode_tensor_int8(trellis: np.ndarray, bits: int) -> np.ndarray:
+    """int8 weight W_q [k, n], placed as decode_tensor places W~ (D4)."""
+    kt, nt, _ = trellis.shape
+    q = mul1_int8(tensor_states(trellis, bits)).reshape(kt, nt, TILE, TILE)
+    return q.transpose(0, 2, 1, 3).reshape(kt * TILE, nt * TILE)
+
+
+def quantize_rows(xp: np.ndarray):
+    """I8X: per-row symmetric int8 of x' (float64 in): (x_q int8 [m, k], scale [m]).
+
+    scale = max |x'| / 127 and x_q = RNE(127 x' / max |x'|); a row of zeros
+    gives x_q = 0 and scale 0.
+    """
+    xp = np.asarray(xp, dtype=np.float64)
+    a = np.abs(xp).max(axis=1)
+    safe = np.where(a > 0, a, 1.0)
+    q = np.rint(xp * INT8_MAX / safe[:, None])
+    q[a == 0] = 0
+    return q.astype(np.int8), a / INT8_MAX
+
+
+def linear_int8(x, trellis, suh, svh, bits, bias=None, wq=None) -> np.ndarray:
+    """I8L: the int8 prefill layer in float64.
+
+    The integer product x_q W_q runs as a float64 matrix product, which is
+    exact here: every term is an integer of magnitude <= 127**2 and every
+    partial sum stays below 2**53 for k < 5e11.  ``wq`` lets a caller that
+    holds decode_tensor_int8(trellis) skip decoding.
+    """
+    Wq = decode_tensor_int8(trellis, bits) if wq is None else wq
+    xp = hadamard(np.asarray(x, dtype=np.float64), sign_before=suh)
+    xq, sx = quantize_rows(xp)
+    acc = xq.astype(np.float64) @ Wq.astype(np.float64)
+    yp = acc * sx[:, None] / INT8_WEIGHT_SCALE
+    y = hadamard(yp, sign_after=svh)
     if bias is not None:
         y = y + np.asarray(bias, dtype=np.float64)
     return y
