@@ -80,6 +80,12 @@ def lib() -> ctypes.CDLL:
     L.exl3_linear_workspace_size.argtypes = [ctypes.POINTER(_Weight), i64]
     L.exl3_linear.restype = i32
     L.exl3_linear.argtypes = [ctypes.POINTER(_Weight), vp, i64, i64, vp, i64, i32, vp, sz, vp]
+    L.exl3_reconstruct_int8.restype = i32
+    L.exl3_reconstruct_int8.argtypes = [ctypes.POINTER(_Weight), vp, vp]
+    L.exl3_linear_int8_workspace_size.restype = sz
+    L.exl3_linear_int8_workspace_size.argtypes = [ctypes.POINTER(_Weight), i64]
+    L.exl3_linear_int8.restype = i32
+    L.exl3_linear_int8.argtypes = [ctypes.POINTER(_Weight), vp, i64, i64, vp, i64, i32, vp, sz, vp]
     L.exl3_linear_multi_workspace_size.restype = sz
     L.exl3_linear_multi_workspace_size.argtypes = [ctypes.POINTER(ctypes.POINTER(_Weight)), i32, i64]
     L.exl3_linear_multi.restype = i32
@@ -235,6 +241,40 @@ def exl3_linear(x, w: Exl3Weight, out_dtype=None, out=None, workspace=None, stre
     cw = w._c()
     _check(lib().exl3_linear(ctypes.byref(cw), _ptr(x), m, x.stride(0), _ptr(out), out.stride(0), ydt,
                              _ptr(workspace), wsb, _stream(stream)), "exl3_linear")
+    return out
+
+
+def exl3_reconstruct_int8(w: Exl3Weight, out=None, stream=None):
+    """int8 weights W_q [k, n] of the int8 prefill (exl3_reconstruct_int8)."""
+    import torch
+    if out is None:
+        out = torch.empty((w.k, w.n), dtype=torch.int8, device=w.trellis.device)
+    cw = w._c()
+    _check(lib().exl3_reconstruct_int8(ctypes.byref(cw), _ptr(out), _stream(stream)),
+           "exl3_reconstruct_int8")
+    return out
+
+
+def exl3_linear_int8_workspace_size(w: Exl3Weight, m: int) -> int:
+    cw = w._c()
+    return int(lib().exl3_linear_int8_workspace_size(ctypes.byref(cw), int(m)))
+
+
+def exl3_linear_int8(x, w: Exl3Weight, out_dtype=None, out=None, workspace=None, stream=None):
+    """The int8 prefill linear (exl3_linear_int8): x fp16 [m, k] -> y [m, n]."""
+    import torch
+    assert x.dim() == 2 and x.dtype == torch.float16 and x.stride(1) == 1
+    m = x.shape[0]
+    if out is None:
+        out = torch.empty((m, w.n), dtype=out_dtype or torch.float16, device=x.device)
+    ydt = {torch.float16: EXL3_F16, torch.float32: EXL3_F32}[out.dtype]
+    need = exl3_linear_int8_workspace_size(w, m)
+    if workspace is None and need:
+        workspace = torch.empty(need, dtype=torch.uint8, device=x.device)
+    wsb = 0 if workspace is None else workspace.numel() * workspace.element_size()
+    cw = w._c()
+    _check(lib().exl3_linear_int8(ctypes.byref(cw), _ptr(x), m, x.stride(0), _ptr(out), out.stride(0),
+                                  ydt, _ptr(workspace), wsb, _stream(stream)), "exl3_linear_int8")
     return out
 
 

@@ -183,6 +183,42 @@ exl3_status exl3_linear(const exl3_weight* w, const void* x, int64_t m, int64_t 
                                     s));
 }
 
+size_t exl3_linear_int8_workspace_size(const exl3_weight* w, int64_t m) {
+  if (check_weight(w, 128, false) != EXL3_OK || m <= 0 || m > ((int64_t)1 << 24)) return 0;
+  return exl3::linear_int8_workspace(w->k, m);
+}
+
+exl3_status exl3_linear_int8(const exl3_weight* w, const void* x, int64_t m, int64_t ldx, void* y,
+                             int64_t ldy, int32_t y_dtype, void* ws, size_t ws_bytes,
+                             exl3_stream_t stream) {
+  exl3_status st = check_weight(w, 128, true);
+  if (st != EXL3_OK) return st;
+  if (m < 0 || m > ((int64_t)1 << 24)) return EXL3_E_INVALID;
+  if (y_dtype != EXL3_F16 && y_dtype != EXL3_F32) return EXL3_E_INVALID;
+  if (ldx < w->k || ldy < w->n || ldx % 8 || ldy % 8) return EXL3_E_INVALID;
+  if ((int64_t)w->k * w->n / 8 * w->bits >= ((int64_t)1 << 32)) return EXL3_E_INVALID;
+  // the GEMM addresses a 256-row tile of int8 activations with 32-bit offsets
+  if ((int64_t)w->k * 256 >= ((int64_t)1 << 31)) return EXL3_E_INVALID;
+  if (m == 0) return EXL3_OK;
+  if (!x || !y || !aligned16(x) || !aligned16(y)) return EXL3_E_INVALID;
+  const size_t need = exl3::linear_int8_workspace(w->k, m);
+  if (!ws || ws_bytes < need || !aligned16(ws)) return EXL3_E_WORKSPACE;
+  trace("linear_int8 k n m bits", w->k, w->n, m, w->bits);
+  return from_hip(exl3::launch_linear_int8(w->trellis, w->suh, w->svh, w->bias, w->k, w->n, w->bits,
+                                           static_cast<const uint16_t*>(x), m, ldx, y, ldy,
+                                           y_dtype == EXL3_F32, ws,
+                                           reinterpret_cast<hipStream_t>(stream)));
+}
+
+exl3_status exl3_reconstruct_int8(const exl3_weight* w, int8_t* w_out, exl3_stream_t stream) {
+  exl3_status st = check_weight(w, 16, false);
+  if (st != EXL3_OK) return st;
+  if (!w_out || !aligned16(w_out)) return EXL3_E_INVALID;
+  trace("reconstruct_int8 k n bits", w->k, w->n, w->bits, 0);
+  return from_hip(exl3::launch_reconstruct_int8(w->trellis, w_out, w->k, w->n, w->bits,
+                                                reinterpret_cast<hipStream_t>(stream)));
+}
+
 size_t exl3_linear_multi_workspace_size(const exl3_weight* const* w, int32_t count, int64_t m) {
   if (check_multi(w, count) != EXL3_OK || m <= 0) return 0;
   return multi_ws(w, count, m);

@@ -107,6 +107,34 @@ __device__ __forceinline__ void decode_column(const uint32_t (&B)[K + 1], uint32
   }
 }
 
+// int8 weight of the state that starts at bit P (exl3xpu README, "Prefill:
+// int8 linears ...": weights take one static scale, 127 / 3.453125, inside
+// the decode).  W_q = RNE((sigma - 510) * 1775 / 2^18 * 127 / 3.453125),
+// with |W_q| <= 127, is the top byte (two's complement) of
+// sigma * kI8Mul + kI8Add mod 2^32 for every sigma in [0, 1020]:
+// floor(((sigma - 510) * kI8Mul + 8388607) / 2^24), where
+// kI8Mul / 2^24 = 0.2490313... approximates the slope
+// 1775 * 127 * 64 / (2^18 * 221) closely enough that no sigma changes side
+// of a rounding boundary (the nearest is 0.0015 away), and the sum stays in
+// (-2^31, 2^31).  sigma * kI8Mul < 2^32 and kI8Mul < 2^24, so the product
+// is one v_mad_u32_u24.  Returned with W_q in byte 3 and the rest junk.
+constexpr uint32_t kI8Mul = 4178012u;
+constexpr uint32_t kI8Add = 0x817EC8B7u;  // 8388607 - 510 * kI8Mul mod 2^32
+
+template <int K, int P>
+__device__ __forceinline__ uint32_t state_i8(const uint32_t (&B)[K + 1]) {
+  const uint32_t h = state_hash<K, P>(B, kMul1Multiplier);
+  const uint32_t sigma = __builtin_amdgcn_sad_u8(h, 0u, 0u);
+  return __umul24(sigma, kI8Mul) + kI8Add;
+}
+
+// Four int8 weights (byte 3 of each) packed little-endian: a in byte 0.
+__device__ __forceinline__ uint32_t pack_i8x4(uint32_t a, uint32_t b, uint32_t c, uint32_t d) {
+  const uint32_t lo = __builtin_amdgcn_perm(b, a, 0x0C0C0703u);  // a.b3, b.b3, 0, 0
+  const uint32_t hi = __builtin_amdgcn_perm(d, c, 0x07030C0Cu);  // 0, 0, c.b3, d.b3
+  return lo | hi;
+}
+
 template <int K, bool BIASED, int C = 0>
 __device__ __forceinline__ void decode_columns(const uint32_t (&B)[K + 1], uint32_t mult,
                                                uint32_t (&out)[16]) {

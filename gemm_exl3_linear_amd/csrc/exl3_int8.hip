@@ -1,0 +1,231 @@
+// int8 prefill linear (exl3xpu README, "Prefill: int8 linears and oneDNN
+// fused attention": activations take one int8 scale per row inside the input
+// Hadamard, weights one static scale inside the decode, the product runs in
+// int8 with both scales applied and writes fp16).
+//
+//   quant_rows_kernel  x' = (x .* suh) H_k in fp32 per row, a = max |x'|,
+//                      x_q = RNE(127 x' / a) (int8 [m][k]) and a / 127.
+//   gemm_i8_kernel     decode to int8 + v_mfma_i32_16x16x64_i8, epilogue with
+//                      both scales, the output transform, svh, bias, cast.
+//   reconstruct_i8_kernel  the int8 weights W_q [k][n], for the bit-exact
+//                      decode check.
+#include "exl3_gemm_i8.hpp"
+#include "exl3_internal.hpp"
+
+namespace exl3 {
+
+// ---------------------------------------------------------------------------
+// input transform with per-row int8 quantization
+// ---------------------------------------------------------------------------
+// One workgroup of four waves per row.  A wave transforms four 128-element
+// blocks at a time (lane l holds elements 8 (l % 16) .. + 7 of block l / 16,
+// the layout of fwht128_x8).  The row is transformed twice, once for its
+// maximum and once to quantize, instead of being held: k has no upper bound
+// here and the second pass reads the row from L2.
+constexpr int kQuantThreads = 256;
+
+__device__ __forceinline__ void quant_block4(const uint16_t* __restrict__ xr,
+                                            const uint16_t* __restrict__ suh, int nb, int b,
+                                            float (&v)[8]) {
+  const int j = (int)(threadIdx.x & 15);
+  if (b < nb) {
+    const uint4 xv = *reinterpret_cast<const uint4*>(xr + b * 128 + 8 * j);
+    const uint4 sv = *reinterpret_cast<const uint4*>(suh + b * 128 + 8 * j);
+    const uint32_t xw[4] = {xv.x, xv.y, xv.z, xv.w};
+    const uint32_t sw[4] = {sv.x, sv.y, sv.z, sv.w};
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      v[2 * e] = h2f((uint16_t)(xw[e] & 0xFFFF)) * h2f((uint16_t)(sw[e] & 0xFFFF));
+      v[2 * e + 1] = h2f((uint16_t)(xw[e] >> 16)) * h2f((uint16_t)(sw[e] >> 16));
+    }
+  } else {
+#pragma unroll
+    for (int e = 0; e < 8; ++e) v[e] = 0.f;
+  }
+  fwht128_x8(v);
+#pragma unroll
+  for (int e = 0; e < 8; ++e) v[e] *= kInvSqrt128;
+}
+
+__global__ __launch_bounds__(kQuantThreads) void quant_rows_kernel(
+    const uint16_t* __restrict__ x, int64_t ldx, const uint16_t* __restrict__ suh, int k,
+    int8_t* __restrict__ xq, float* __restrict__ scale) {
+  __shared__ float wmax[kQuantThreads / 64];
+  const int64_t row = blockIdx.x;
+  const int wave = (int)(threadIdx.x >> 6), lane = (int)(threadIdx.x & 63);
+  const int nb = k / 128;
+  const uint16_t* xr = x + row * ldx;
+  float amax = 0.f;
+  for (int b0 = 4 * wave; b0 < nb; b0 += 16) {
+    float v[8];
+    quant_block4(xr, suh, nb, b0 + (lane >> 4), v);
+#pragma unroll
+    for (int e = 0; e < 8; ++e) amax = fmaxf(amax, fabsf(v[e]));
+  }
+#pragma unroll
+  for (int msk = 32; msk >= 1; msk >>= 1) amax = fmaxf(amax, shfl_xor_f(amax, msk));
+  if (lane == 0) wmax[wave] = amax;
+  __syncthreads();
+  const float a = fmaxf(fmaxf(wmax[0], wmax[1]), fmaxf(wmax[2], wmax[3]));
+  const float inv = a > 0.f ? 127.0f / a : 0.f;
+  int8_t* qr = xq + row * k;
+  for (int b0 = 4 * wave; b0 < nb; b0 += 16) {
+    const int b = b0 + (lane >> 4);
+    float v[8];
+    quant_block4(xr, suh, nb, b, v);
+    uint32_t w[2] = {0u, 0u};
+#pragma unroll
+    for (int e = 0; e < 8; ++e) {
+      const float qf = fminf(fmaxf(rintf(v[e] * inv), -127.f), 127.f);
+      w[e >> 2] |= ((uint32_t)(int32_t)qf & 0xFFu) << (8 * (e & 3));
+    }
+    if (b < nb) *reinterpret_cast<uint2*>(qr + b * 128 + 8 * (lane & 15)) = make_uint2(w[0], w[1]);
+  }
+  if (threadIdx.x == 0) scale[row] = a / 127.0f;
+}
+
+// ---------------------------------------------------------------------------
+// int8 GEMM dispatch (dense tensor)
+// ---------------------------------------------------------------------------
+struct DenseGemmI8Res {
+  const int8_t* a;
+  const float* ascale;
+  int64_t lda;
+  int m;
+  int bm;
+  int mt;   // row tiles
+  int nbt;  // 128-column tiles
+  const uint16_t* trellis;
+  const uint16_t* svh;
+  const uint16_t* bias;
+  void* y;
+  int64_t ldy;
+  bool y_f32;
+  // Workgroup -> (row tile, column tile), the XCD-aware order of the fp16
+  // prefill GEMM: with a tile count that is a multiple of eight, the
+  // workgroups of one XCD take one contiguous range of the tile order, which
+  // walks pairs of row tiles across all column tiles.
+  __device__ GemmI8Task task() const {
+    const int total = mt * nbt;
+    const int bid = (int)blockIdx.x;
+    const int u = (total % 8 == 0) ? (bid % 8) * (total / 8) + bid / 8 : bid;
+    constexpr int G = 2;
+    const int grp = u / (G * nbt), within = u - grp * (G * nbt);
+    const int g0 = grp * G;
+    const int gs = (mt - g0) < G ? (mt - g0) : G;
+    const int mtile = g0 + within % gs;
+    GemmI8Task T;
+    T.nb = within / gs;
+    const int r0 = mtile * bm;
+    T.valid = r0 < m;
+    T.a = a + (int64_t)r0 * lda;
+    T.ascale = ascale + r0;
+    T.lda = lda;
+    T.rows = (m - r0) < bm ? (m - r0) : bm;
+    T.trellis = trellis;
+    T.svh = svh;
+    T.bias = bias;
+    T.y = y_f32 ? (void*)(static_cast<float*>(y) + (int64_t)r0 * ldy)
+                : (void*)(static_cast<uint16_t*>(y) + (int64_t)r0 * ldy);
+    T.ldy = ldy;
+    return T;
+  }
+};
+
+static int choose_bm_i8(int64_t m) { return m > 128 ? 256 : (m > 64 ? 128 : 64); }
+
+template <int K>
+struct DenseGemmI8Run {
+  static hipError_t run(const DenseGemmI8Res& r, int k, int n, hipStream_t s) {
+    const dim3 grid(r.mt * r.nbt);
+#define EXL3_GEMM_I8_LAUNCH(BM)                                                                     \
+  do {                                                                                              \
+    if (r.y_f32)                                                                                    \
+      hipLaunchKernelGGL((gemm_i8_kernel<K, BM, true, DenseGemmI8Res>), grid, dim3(kGemmThreads), 0, s, r, k, n); \
+    else                                                                                            \
+      hipLaunchKernelGGL((gemm_i8_kernel<K, BM, false, DenseGemmI8Res>), grid, dim3(kGemmThreads), 0, s, r, k, n); \
+  } while (0)
+    if (r.bm == 256) EXL3_GEMM_I8_LAUNCH(256);
+    else if (r.bm == 128) EXL3_GEMM_I8_LAUNCH(128);
+    else EXL3_GEMM_I8_LAUNCH(64);
+#undef EXL3_GEMM_I8_LAUNCH
+    return hipGetLastError();
+  }
+};
+
+// Workspace: x_q (int8 [m][k]) then the row scales (fp32 [m]), each on a
+// 256-byte boundary.
+static size_t i8_scale_offset(int k, int64_t m) { return ((size_t)m * k + 255) & ~(size_t)255; }
+
+size_t linear_int8_workspace(int k, int64_t m) {
+  return i8_scale_offset(k, m) + (((size_t)m * sizeof(float) + 255) & ~(size_t)255);
+}
+
+hipError_t launch_linear_int8(const uint16_t* trellis, const uint16_t* suh, const uint16_t* svh,
+                              const uint16_t* bias, int k, int n, int bits, const uint16_t* x,
+                              int64_t m, int64_t ldx, void* y, int64_t ldy, bool y_f32, void* ws,
+                              hipStream_t s) {
+  unsigned char* base = static_cast<unsigned char*>(ws);
+  int8_t* xq = reinterpret_cast<int8_t*>(base);
+  float* sc = reinterpret_cast<float*>(base + i8_scale_offset(k, m));
+  hipLaunchKernelGGL(quant_rows_kernel, dim3((unsigned)m), dim3(kQuantThreads), 0, s, x, ldx, suh, k,
+                     xq, sc);
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  const int bm = choose_bm_i8(m);
+  DenseGemmI8Res r{xq, sc, k, (int)m, bm, (int)((m + bm - 1) / bm), n / kGemmBN, trellis, svh, bias,
+                   y, ldy, y_f32};
+  return dispatch_bits<DenseGemmI8Run>(bits, r, k, n, s);
+}
+
+// ---------------------------------------------------------------------------
+// int8 weights of a whole tensor
+// ---------------------------------------------------------------------------
+template <int K>
+__global__ __launch_bounds__(256) void reconstruct_i8_kernel(const uint16_t* __restrict__ trellis,
+                                                             int8_t* __restrict__ out, int nt,
+                                                             int64_t tiles, int n) {
+  const int64_t gid = (int64_t)blockIdx.x * 256 + threadIdx.x;
+  const int64_t tile = gid >> 3;
+  const int p = (int)(gid & 7);
+  if (tile >= tiles) return;  // whole 8-lane groups leave together
+  const int64_t a = tile / nt, b = tile % nt;
+  const uint32_t* src =
+      reinterpret_cast<const uint32_t*>(trellis + tile * (16 * K)) + (int64_t)K * p;
+  uint32_t D[K];
+  load_rowpair<K>(src, D);
+  uint32_t B[K + 1];
+#pragma unroll
+  for (int i = 0; i < K; ++i) B[i] = stream_dword(D[i]);
+  B[K] = spill_from_next(D[0]);
+  uint32_t r0[4], r1[4];  // rows 2p and 2p + 1, four columns per dword
+  static_for<0, 4>([&](auto cc) {
+    constexpr int c = 4 * decltype(cc)::value;
+    r0[decltype(cc)::value] = pack_i8x4(state_i8<K, K * c>(B), state_i8<K, K * (c + 1)>(B),
+                                        state_i8<K, K * (c + 2)>(B), state_i8<K, K * (c + 3)>(B));
+    r1[decltype(cc)::value] =
+        pack_i8x4(state_i8<K, K * (16 + c)>(B), state_i8<K, K * (17 + c)>(B),
+                  state_i8<K, K * (18 + c)>(B), state_i8<K, K * (19 + c)>(B));
+  });
+  int8_t* o0 = out + (16 * a + 2 * p) * (int64_t)n + 16 * b;
+  *reinterpret_cast<uint4*>(o0) = make_uint4(r0[0], r0[1], r0[2], r0[3]);
+  *reinterpret_cast<uint4*>(o0 + n) = make_uint4(r1[0], r1[1], r1[2], r1[3]);
+}
+
+template <int K>
+struct ReconstructI8Run {
+  static hipError_t run(const uint16_t* trellis, int8_t* out, int k, int n, hipStream_t s) {
+    const int64_t tiles = (int64_t)(k / 16) * (n / 16);
+    const unsigned blocks = (unsigned)((tiles * 8 + 255) / 256);
+    hipLaunchKernelGGL(reconstruct_i8_kernel<K>, dim3(blocks), dim3(256), 0, s, trellis, out, n / 16,
+                       tiles, n);
+    return hipGetLastError();
+  }
+};
+
+hipError_t launch_reconstruct_int8(const uint16_t* trellis, int8_t* out, int k, int n, int bits,
+                                   hipStream_t s) {
+  return dispatch_bits<ReconstructI8Run>(bits, trellis, out, k, n, s);
+}
+
+}  // namespace exl3

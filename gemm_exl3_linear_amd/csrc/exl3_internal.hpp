@@ -84,6 +84,16 @@ hipError_t launch_gemm(const uint16_t* trellis, const uint16_t* suh, const uint1
                        int m, int64_t ldx, void* y, int64_t ldy, bool y_f32, void* ws,
                        hipStream_t s);
 
+// --- int8 prefill ------------------------------------------------------------
+// workspace: x_q (int8 [m][k]) and the row scales (fp32 [m])
+size_t linear_int8_workspace(int k, int64_t m);
+hipError_t launch_linear_int8(const uint16_t* trellis, const uint16_t* suh, const uint16_t* svh,
+                              const uint16_t* bias, int k, int n, int bits, const uint16_t* x,
+                              int64_t m, int64_t ldx, void* y, int64_t ldy, bool y_f32, void* ws,
+                              hipStream_t s);
+hipError_t launch_reconstruct_int8(const uint16_t* trellis, int8_t* out, int k, int n, int bits,
+                                   hipStream_t s);
+
 // --- grouped experts -------------------------------------------------------
 struct ArenaDesc {
   const uint16_t* trellis;

@@ -191,6 +191,38 @@ exl3_status exl3_linear_multi(const exl3_weight* const* w, int32_t count, const 
                               int64_t ldx, void* const* y, const int64_t* ldy, int32_t y_dtype,
                               void* ws, size_t ws_bytes, exl3_stream_t stream);
 
+/* exl3_reconstruct_int8 - the int8 weights W_q of the int8 prefill (exl3xpu
+ * README, "Prefill: int8 linears ...": one static weight scale fused into
+ * reconstruct).  W_q = RNE((sigma - 510) * 1775 / 2^18 * 127 / 3.453125) for
+ * each state's byte sum sigma, taken from the codebook value before its fp16
+ * rounding; |W_q| <= 127.
+ *   w_out  int8 [k][n] row-major, device pointer, 16-byte aligned.
+ * Requires k, n multiples of 16.  Output is bit-exact by definition.       */
+exl3_status exl3_reconstruct_int8(const exl3_weight* w, int8_t* w_out, exl3_stream_t stream);
+
+/* Bytes of device workspace exl3_linear_int8 needs for m rows of this tensor
+ * (0 if the arguments are invalid or m == 0). */
+size_t exl3_linear_int8_workspace_size(const exl3_weight* w, int64_t m);
+
+/* exl3_linear_int8 - the int8 prefill linear (exl3xpu README, "Prefill: int8
+ * linears ..."): activations get one int8 scale per row inside the input
+ * transform, weights the static scale of exl3_reconstruct_int8, and the
+ * product runs on int8 matrix cores with both scales applied:
+ *   x' = (x .* suh) Hk;  a_r = max |x'_r|;  x_q = RNE(127 x' / a_r)
+ *   y  = ((x_q W_q) * (a_r / 127) * (3.453125 / 127)) Hn .* svh (+ bias)
+ * The integer product is exact; x' and the scales are fp32.
+ *   x, y, ldx, ldy, y_dtype  as for exl3_linear
+ *   ws     device workspace of at least exl3_linear_int8_workspace_size(w, m)
+ *          bytes (x_q and the row scales; no state is kept between calls)
+ * Any m >= 1 is accepted (the pages use it for prefill, more than 128 rows);
+ * rows are independent, so a row's result does not depend on m or on the
+ * other rows, bit for bit.  An all-zero row gives y = bias.  m == 0 returns
+ * EXL3_OK.  Compared with exl3_linear the outputs differ by the int8
+ * rounding of activations and weights (about 1e-2 relative).              */
+exl3_status exl3_linear_int8(const exl3_weight* w, const void* x, int64_t m, int64_t ldx, void* y,
+                             int64_t ldy, int32_t y_dtype, void* ws, size_t ws_bytes,
+                             exl3_stream_t stream);
+
 /* Bytes of device workspace exl3_grouped_experts needs (0 if invalid). */
 size_t exl3_grouped_experts_workspace_size(const exl3_expert_weights* gate_up,
                                            const exl3_expert_weights* down, int64_t t,

@@ -140,3 +140,29 @@ def test_linear_multi_workspace_and_rejects():
     # missing workspace, then the empty call
     assert L.exl3_linear_multi(arr, 3, 16, 1, 5120, y, ld, f16, 0, 0, 0) == X.EXL3_E_WORKSPACE
     assert L.exl3_linear_multi(arr, 3, 16, 0, 5120, y, ld, f16, 0, 0, 0) == X.EXL3_OK
+
+
+def test_linear_int8_validation_host_only():
+    L = X.lib()
+    w = _w(512, 256, 4)
+    ws = L.exl3_linear_int8_workspace_size(ctypes.byref(w), 300)
+    assert ws >= 300 * 512 + 300 * 4 and ws % 256 == 0
+    assert L.exl3_linear_int8_workspace_size(ctypes.byref(w), 0) == 0
+    assert L.exl3_linear_int8_workspace_size(ctypes.byref(_w(bits=9)), 4) == 0
+    f16 = X.EXL3_F16
+    call = lambda ww, m, ws_=0, n=0, ldx=512, ldy=256, dt=f16: L.exl3_linear_int8(
+        ctypes.byref(ww), 16, m, ldx, 16, ldy, dt, ws_, n, 0)
+    assert call(_w(512, 256, 0), 4) == X.EXL3_E_INVALID
+    assert call(_w(512, 256, 4, cb=1), 4) == X.EXL3_E_UNSUPPORTED
+    assert call(_w(200, 256, 4), 4, ldx=200) == X.EXL3_E_INVALID
+    assert call(w, 4, ldx=500) == X.EXL3_E_INVALID
+    assert call(w, 4, dt=7) == X.EXL3_E_INVALID
+    assert call(w, -1) == X.EXL3_E_INVALID
+    assert call(w, 4) == X.EXL3_E_WORKSPACE
+    need = L.exl3_linear_int8_workspace_size(ctypes.byref(w), 4)
+    assert call(w, 4, 16, need - 16) == X.EXL3_E_WORKSPACE
+    assert call(w, 0) == X.EXL3_OK
+    assert L.exl3_reconstruct_int8(ctypes.byref(_w(bits=0)), 16, 0) == X.EXL3_E_INVALID
+    assert L.exl3_reconstruct_int8(ctypes.byref(_w(cb=1)), 16, 0) == X.EXL3_E_UNSUPPORTED
+    assert L.exl3_reconstruct_int8(ctypes.byref(_w()), 0, 0) == X.EXL3_E_INVALID
+    assert L.exl3_reconstruct_int8(ctypes.byref(_w()), 17, 0) == X.EXL3_E_INVALID

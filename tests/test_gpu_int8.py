@@ -1,0 +1,139 @@
+"""GPU parity of the int8 prefill path (exl3_linear_int8, exl3_reconstruct_int8)
+against the float64 oracle's int8 readings.
+
+Tolerances: the int8 weights are integers from integers, so they must match
+bit for bit.  The layer output differs from the oracle's int8 layer only by
+fp32 arithmetic (x' and the scales), the rare activation code that fp32 puts
+on the other side of a rounding boundary, and the output cast: relative
+Frobenius error <= 1e-3 (TOL8).  Against the fp16-weight layer the int8
+rounding itself costs about 1e-2 (the oracle's own pin bounds it by 2e-2).
+"""
+import functools
+
+import numpy as np
+import pytest
+
+import synth
+from oracle import exl3_oracle as O
+from tests import _gpu as G
+
+pytestmark = pytest.mark.gpu
+TOL8 = 1e-3
+TOL_VS_FP16 = 2e-2
+
+
+def _run8(d, m=None, out_dtype=None, bias=None, x=None):
+    import torch
+    import gemm_exl3_linear_amd as X
+    if x is None:
+        x = d["x"] if m is None else d["x"][:m]
+    y = X.exl3_linear_int8(G.to_dev(x), G.weight(d, bias=bias), out_dtype=out_dtype or torch.float16)
+    torch.cuda.synchronize()
+    return y
+
+
+@functools.lru_cache(maxsize=4)
+def _wq(seed, m, k, n, bits):
+    d = G.linear_case(seed, m, k, n, bits)
+    return O.decode_tensor_int8(d["trellis"], bits)
+
+
+@pytest.mark.parametrize("bits", range(1, 9))
+def test_reconstruct_int8_bit_exact(bits):
+    import torch
+    import gemm_exl3_linear_amd as X
+    d = synth.linear_inputs(800 + bits, 1, 64, 96, bits)
+    q = X.exl3_reconstruct_int8(G.weight(d))
+    torch.cuda.synchronize()
+    np.testing.assert_array_equal(q.cpu().numpy(), O.decode_tensor_int8(d["trellis"], bits))
+
+
+@pytest.mark.parametrize("bits", [1, 2, 3, 4, 5, 6, 7, 8])
+@pytest.mark.parametrize("m", [1, 70, 300])
+def test_linear_int8_parity(bits, m):
+    # several 128-column blocks, k of several 64-row steps, ragged row tiles
+    d = G.linear_case(810 + bits, 300, 512, 384, bits)
+    y = _run8(d, m=m).double().cpu().numpy()
+    ref = O.linear_int8(d["x"][:m], d["trellis"], d["suh"], d["svh"], bits, wq=_wq(810 + bits, 300, 512, 384, bits))
+    assert O.rel_frobenius(y, ref) < TOL8
+    ref16 = O.linear(d["x"][:m], d["trellis"], d["suh"], d["svh"], bits)
+    assert O.rel_frobenius(y, ref16) < TOL_VS_FP16
+
+
+def test_linear_int8_fp32_output_and_bias():
+    import torch
+    d = G.linear_case(820, 130, 384, 256, 4)
+    bias = (np.arange(256) % 11 - 5).astype(np.float16) * np.float16(0.25)
+    y = _run8(d, out_dtype=torch.float32, bias=bias).double().cpu().numpy()
+    ref = O.linear_int8(d["x"], d["trellis"], d["suh"], d["svh"], 4, bias=bias)
+    assert O.rel_frobenius(y, ref) < TOL8
+
+
+def test_linear_int8_rows_independent_bit_exact():
+    # each row is quantized and contracted on its own: any prefix of the
+    # batch gives the same rows, and m = 1 equals the row of a full batch
+    d = G.linear_case(821, 300, 512, 256, 3)
+    full = G.f16_bits(_run8(d))
+    for m in (1, 20, 129):
+        np.testing.assert_array_equal(G.f16_bits(_run8(d, m=m)), full[:m])
+
+
+def test_linear_int8_sign_and_zero_rows():
+    import torch
+    d = G.linear_case(822, 96, 256, 384, 5)
+    x = d["x"].copy()
+    x[7] = 0
+    y = _run8(d, x=x)
+    yn = _run8(d, x=-x)
+    # x -> -x negates every code and keeps every scale: y(-x) = -y(x) exactly
+    # (compared as values: an exact zero stays +0 on both sides)
+    np.testing.assert_array_equal(yn.float().cpu().numpy(), -y.float().cpu().numpy())
+    assert (y[7].float() == 0).all()
+    # an all-zero row gives exactly the bias
+    bias = (np.arange(384) % 5 - 2).astype(np.float16)
+    yb = _run8(d, x=x, out_dtype=torch.float32, bias=bias)
+    np.testing.assert_array_equal(yb[7].cpu().numpy(), bias.astype(np.float32))
+
+
+@pytest.mark.parametrize("fill", [0x0000, 0xFFFF])
+def test_linear_int8_constant_trellis_exact_zeros(fill):
+    # W_q is one value everywhere, so every column of a 128-column block gets
+    # the same int32 sum and the output transform leaves exact zeros off the
+    # block's first column (closed form of the oracle's pin)
+    d = dict(G.linear_case(823, 70, 256, 256, 4))
+    d["trellis"] = np.full_like(d["trellis"], fill)
+    y = _run8(d).float().cpu().numpy()
+    mask = np.ones(256, bool)
+    mask[::128] = False
+    assert (y[:, mask] == 0).all()
+    ref = O.linear_int8(d["x"], d["trellis"], d["suh"], d["svh"], 4)
+    assert O.rel_frobenius(y, ref) < TOL8
+
+
+def test_linear_int8_workspace_reused_across_sizes():
+    import torch
+    import gemm_exl3_linear_amd as X
+    d = G.linear_case(824, 300, 384, 256, 2)
+    w = G.weight(d)
+    ws = torch.empty(X.exl3_linear_int8_workspace_size(w, 300), dtype=torch.uint8, device=G.dev())
+    a = X.exl3_linear_int8(G.to_dev(d["x"]), w, workspace=ws)
+    b = X.exl3_linear_int8(G.to_dev(d["x"][:33]), w, workspace=ws)
+    c = X.exl3_linear_int8(G.to_dev(d["x"]), w, workspace=ws)
+    torch.cuda.synchronize()
+    np.testing.assert_array_equal(G.f16_bits(b), G.f16_bits(a)[:33])
+    np.testing.assert_array_equal(G.f16_bits(c), G.f16_bits(a))
+
+
+# --- the full-size prefill workload, in the launch configuration the benchmark times ---
+def test_int8_prefill_4096x5120x17408_k4_sampled_rows():
+    # all 4096 rows on the GPU; the oracle on a seeded sample of 24 rows (rows
+    # are independent: quantization and contraction are per row)
+    d = G.linear_case(synth.SEED_PREFILL_4096x5120x17408, 4096, 5120, 17408, 4)
+    y = _run8(d).double().cpu().numpy()
+    rows = np.sort(np.random.default_rng(825).choice(4096, 24, replace=False))
+    wq = _wq(synth.SEED_PREFILL_4096x5120x17408, 4096, 5120, 17408, 4)
+    ref = O.linear_int8(d["x"][rows], d["trellis"], d["suh"], d["svh"], 4, wq=wq)
+    assert O.rel_frobenius(y[rows], ref) < TOL8
+    W = G.decoded(synth.SEED_PREFILL_4096x5120x17408, 4096, 5120, 17408, 4)
+    ref16 = O.linear(d["x"][rows], d["trellis"], d["suh"], d["svh"], 4, w_decoded=W)
+    assert O.rel_frobenius(y[rows], ref16) < TOL_VS_FP16
