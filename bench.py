@@ -28,6 +28,7 @@ sys.path.insert(0, ROOT)
 
 HBM_PEAK_GBS = 8000.0          # MI355X HBM3E, published
 MFMA_F16_PEAK_TFLOPS = 2500.0  # MI355X dense fp16 matrix, published
+MFMA_I8_PEAK_TOPS = 5000.0     # MI355X dense int8 matrix, published
 METRIC = "EXL3 GEMV HBM GB/s (% of 8 TB/s) at M=1; prefill GEMM TFLOPS (% MFMA)"
 GEMV_SOURCES = ["gemm_exl3_linear_amd/csrc/exl3_device.hpp", "gemm_exl3_linear_amd/csrc/exl3_gemv_sk.hpp",
                 "gemm_exl3_linear_amd/csrc/exl3_gemv.hip"]
@@ -98,8 +99,8 @@ def mixed_layer_leg(X, torch, synth, dev, stream, reps=50):
     six stream about 220 MB, so each call reads mostly HBM), then again with
     the projections that read one input fused into one exl3_linear_multi call
     each ((q, k, v), o, (gate, up), down); M = 4096: each projection timed
-    alone (the MFMA-bound prefill)."""
-    out = {"bits": {}, "m1": {}, "m4096": {}}
+    alone (the MFMA-bound prefill), through the fp16 and the int8 path."""
+    out = {"bits": {}, "m1": {}, "m4096": {}, "m4096_int8": {}}
     d1 = synth.mixed_layer_inputs(synth.SEED_MIXED_LAYER, 1)
     names = [nm for nm, _, _ in synth.MIXED_LAYER_SHAPES]
     ws, xs, ys = {}, {}, {}
@@ -168,22 +169,31 @@ def mixed_layer_leg(X, torch, synth, dev, stream, reps=50):
     del wsm
     del xs, ys
     d4 = synth.mixed_layer_inputs(synth.SEED_MIXED_LAYER, 4096)
-    tot_f = tot_t = 0.0
+    ws8 = torch.empty(max(X.exl3_linear_int8_workspace_size(ws[nm], 4096) for nm in names), dtype=torch.uint8,
+                      device=dev)
+    tot_f = tot_t = tot_t8 = 0.0
     for nm in names:
         d = d4[nm]
         x4 = torch.from_numpy(d["x"]).to(dev)
         y4 = torch.empty((4096, d["n"]), dtype=torch.float16, device=dev)
         pl, _ = time_calls(lambda i: X.exl3_linear(x4, ws[nm], out=y4, workspace=wsp, stream=stream),
                            10, 2, stream)
+        pl8, _ = time_calls(lambda i: X.exl3_linear_int8(x4, ws[nm], out=y4, workspace=ws8, stream=stream),
+                            10, 2, stream)
         f = 2.0 * 4096 * d["k"] * d["n"]
         tot_f += f
         tot_t += pl
+        tot_t8 += pl8
         out["m4096"][nm] = {"ms": round(pl * 1e3, 3), "TFLOP/s": round(f / pl / 1e12, 1),
                             "frac_mfma_f16": round(f / pl / 1e12 / MFMA_F16_PEAK_TFLOPS, 4)}
+        out["m4096_int8"][nm] = {"ms": round(pl8 * 1e3, 3), "TOP/s": round(f / pl8 / 1e12, 1),
+                                 "frac_mfma_i8": round(f / pl8 / 1e12 / MFMA_I8_PEAK_TOPS, 4)}
         del x4, y4
     out["m4096"]["layer"] = {"ms": round(tot_t * 1e3, 3), "TFLOP/s": round(tot_f / tot_t / 1e12, 1),
                              "frac_mfma_f16": round(tot_f / tot_t / 1e12 / MFMA_F16_PEAK_TFLOPS, 4)}
-    del ws, wsp, d1, d4
+    out["m4096_int8"]["layer"] = {"ms": round(tot_t8 * 1e3, 3), "TOP/s": round(tot_f / tot_t8 / 1e12, 1),
+                                  "frac_mfma_i8": round(tot_f / tot_t8 / 1e12 / MFMA_I8_PEAK_TOPS, 4)}
+    del ws, wsp, ws8, d1, d4
     return out
 
 
@@ -266,7 +276,16 @@ def main():
         tf = 2.0 * 4096 * k * n / pl / 1e12
         secondary["prefill_m4096"] = {"TFLOP/s": round(tf, 1), "frac_mfma_f16": round(tf / MFMA_F16_PEAK_TFLOPS, 4),
                                       "ms_per_call": round(pl * 1e3, 3)}
-        del wp, xp, wsp, yp
+        # the same prefill through the int8 path (row-quantizing input transform
+        # + fused decode-to-int8 / int8 MFMA GEMM)
+        ws8 = torch.empty(X.exl3_linear_int8_workspace_size(wp, 4096), dtype=torch.uint8, device=dev)
+        pl8, _ = time_calls(lambda i: X.exl3_linear_int8(xp, wp, out=yp, workspace=ws8, stream=stream), 20, 3,
+                            stream)
+        to = 2.0 * 4096 * k * n / pl8 / 1e12
+        secondary["prefill_int8_m4096"] = {"TOP/s": round(to, 1), "frac_mfma_i8": round(to / MFMA_I8_PEAK_TOPS, 4),
+                                           "ms_per_call": round(pl8 * 1e3, 3),
+                                           "speedup_vs_fp16": round(pl / pl8, 3)}
+        del wp, xp, wsp, yp, ws8
         secondary["mixed_layer"] = mixed_layer_leg(X, torch, synth, dev, stream)
         # routed experts: 256 experts, top-8, hidden 2048, intermediate 512, K=3
         for t in (1, 4096):

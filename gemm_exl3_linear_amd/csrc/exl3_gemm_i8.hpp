@@ -16,7 +16,8 @@
 //     pack into one dword and go to LDS in one 4-byte store; the decoded
 //     stage is 128 columns x 64 k bytes, read as one 16-byte B fragment per
 //     MFMA, in the same swizzled chunk layout as the fp16 stage;
-//   - the A fragment is 16 int8 activations straight from global memory.
+//   - the A fragment is 16 int8 activations straight from global memory,
+//     from the fragment-major layout the input transform writes.
 #pragma once
 
 #include "exl3_device.hpp"
@@ -26,15 +27,26 @@ namespace exl3 {
 
 constexpr int kGemmI8BK = 64;  // k rows per step: the depth of one int8 MFMA
 
+// Fragment-major int8 activations: for every group of 16 rows and every 64
+// k, the MFMA A operand in lane order, lane (g, j) = 16 g + j holding the 16
+// bytes of row j at k 16 g .. 16 g + 15:
+//   x_q[16 G + j][64 B + 16 g + e] at byte ((G * (k / 64) + B) * 64 + 16 g + j) * 16 + e.
+// One fragment is one contiguous kilobyte, so the GEMM reads it with fully
+// used 128-byte lines (a row-major layout gives each load 16 rows x 64
+// bytes, half-used lines, and measured about twice the time for the loads).
+constexpr int kI8FragBytes = 1024;
+
+typedef int32_t i32x4_t __attribute__((ext_vector_type(4)));
+
 // 3.453125 / 127: the weight step of the int8 decode
 constexpr float kI8WeightStep = 3.453125f / 127.0f;
 
 struct GemmI8Task {
   bool valid;
   int nb;                   // 128-column tile
-  const int8_t* a;          // int8 rows of x_q for this tile, row 0
+  const int8_t* a;          // x_q of this tile, fragment-major (first 16-row group)
   const float* ascale;      // fp32 row scales (max |x'| / 127), row 0
-  int64_t lda;              // bytes between rows of a
+  int64_t lda;              // bytes per 16-row group of a (16 k)
   int rows;                 // valid rows in this tile (<= BM)
   const uint16_t* trellis;  // tensor base [k/16][n/16][16K]
   const uint16_t* svh;      // fp16 [n]
@@ -47,6 +59,62 @@ struct GemmI8Task {
 // (DPP quad permutation 1, 2, 3, 0).  All four lanes must be active.
 __device__ __forceinline__ uint32_t spill_from_next4(uint32_t my_first_le) {
   return (uint32_t)__builtin_amdgcn_mov_dpp((int)stream_dword(my_first_le), 0x39, 0xF, 0xF, false);
+}
+
+// Epilogue of a wave's rows r0 .. r0 + 16 MI - 1 and the tile's 128 columns:
+// int32 -> fp32, output Hadamard over the 128 columns, then both scales with
+// svh, bias and the cast.
+template <int MI, bool Y_F32>
+__device__ __forceinline__ void gemm_i8_epilogue(const GemmI8Task& T,
+                                                 const i32x4_t (&acc)[MI][8], int r0,
+                                                 int col0, int j, int g) {
+  float sv[8], bv[8];
+#pragma unroll
+  for (int q = 0; q < 8; ++q) {
+    sv[q] = kInvSqrt128 * kI8WeightStep * h2f(T.svh[col0 + 16 * q + j]);
+    bv[q] = T.bias ? h2f(T.bias[col0 + 16 * q + j]) : 0.f;
+  }
+#pragma unroll
+  for (int mi = 0; mi < MI; ++mi) {
+#pragma unroll
+    for (int rr = 0; rr < 4; ++rr) {
+      const int row = r0 + 16 * mi + 4 * g + rr;
+      float v[8];
+#pragma unroll
+      for (int q = 0; q < 8; ++q) v[q] = (float)acc[mi][q][rr];
+#pragma unroll
+      for (int sd = 1; sd < 8; sd <<= 1)
+#pragma unroll
+        for (int q = 0; q < 8; ++q)
+          if ((q & sd) == 0) {
+            const float u0 = v[q], u1 = v[q + sd];
+            v[q] = u0 + u1;
+            v[q + sd] = u0 - u1;
+          }
+#pragma unroll
+      for (int msk = 1; msk < 16; msk <<= 1) {
+        const bool upper = (j & msk) != 0;
+#pragma unroll
+        for (int q = 0; q < 8; ++q) {
+          const float pv = shfl_xor_f(v[q], msk);
+          v[q] = upper ? (pv - v[q]) : (v[q] + pv);
+        }
+      }
+      if (row < T.rows) {
+        const float rs = T.ascale[row];
+#pragma unroll
+        for (int q = 0; q < 8; ++q) {
+          const int col = col0 + 16 * q + j;
+          float o = v[q] * rs * sv[q];
+          if (T.bias) o += bv[q];
+          if constexpr (Y_F32)
+            static_cast<float*>(T.y)[(int64_t)row * T.ldy + col] = o;
+          else
+            static_cast<uint16_t*>(T.y)[(int64_t)row * T.ldy + col] = f2h(o);
+        }
+      }
+    }
+  }
 }
 
 template <int K, int BM, bool Y_F32, class R>
@@ -78,19 +146,20 @@ __global__ __launch_bounds__(kGemmThreads, 2) void gemm_i8_kernel(R r, int k, in
   int bw_dw[8];
 #pragma unroll
   for (int c = 0; c < 8; ++c) bw_dw[c] = gemm_b_chunk(16 * t + 8 * h + c, kt) * 4 + p2;
-  // A fragment: 16 int8 of row 16 mi + j at k 16 g .. 16 g + 15 of the step;
-  // rows at or past T.rows read as zero (outside the descriptor's range)
-  const __amdgpu_buffer_rsrc_t a_rs = make_rsrc(T.a, (uint32_t)((uint64_t)T.rows * T.lda));
+  // A fragment of rows 16 mi .. 16 mi + 15 at the step's 64 k: one
+  // contiguous kilobyte of the fragment-major x_q, 16 bytes per lane; row
+  // groups past the tile's rows read as zero (outside the descriptor)
+  const __amdgpu_buffer_rsrc_t a_rs = make_rsrc(T.a, (uint32_t)((uint64_t)((T.rows + 15) >> 4) * T.lda));
   uint32_t a_voff[MI];
 #pragma unroll
   for (int mi = 0; mi < MI; ++mi)
-    a_voff[mi] = (uint32_t)((int64_t)(wave * WM + 16 * mi + j) * T.lda + 16 * g);
+    a_voff[mi] = (uint32_t)((int64_t)(wave * MI + mi) * T.lda + 16 * lane);
   // B fragment: chunk g (k 16 g .. 16 g + 15) of column 16 q + j
   int br_ch[8];
 #pragma unroll
   for (int q = 0; q < 8; ++q) br_ch[q] = gemm_b_chunk(16 * q + j, g);
 
-  typedef int32_t i32x4 __attribute__((ext_vector_type(4)));
+  typedef i32x4_t i32x4;
   i32x4 acc[MI][8];
 #pragma unroll
   for (int mi = 0; mi < MI; ++mi)
@@ -105,7 +174,7 @@ __global__ __launch_bounds__(kGemmThreads, 2) void gemm_i8_kernel(R r, int k, in
 #pragma unroll
     for (int mi = 0; mi < MI; ++mi)
       ra[set][mi] = __builtin_bit_cast(
-          i32x4, __builtin_amdgcn_raw_buffer_load_b128(a_rs, (int)a_voff[mi], ks * kGemmI8BK, 0));
+          i32x4, __builtin_amdgcn_raw_buffer_load_b128(a_rs, (int)a_voff[mi], ks * kI8FragBytes, 0));
   };
   auto load_t = [&](int set, int ks) {
     ks = ks < nsteps ? ks : nsteps - 1;
@@ -196,55 +265,8 @@ __global__ __launch_bounds__(kGemmThreads, 2) void gemm_i8_kernel(R r, int k, in
   else
     run(IntC<1>{});
 
-  // epilogue: int32 -> fp32, output Hadamard over the 128 columns, then both
-  // scales with svh, bias, cast
-  float sv[8], bv[8];
-#pragma unroll
-  for (int q = 0; q < 8; ++q) {
-    sv[q] = kInvSqrt128 * kI8WeightStep * h2f(T.svh[col0 + 16 * q + j]);
-    bv[q] = T.bias ? h2f(T.bias[col0 + 16 * q + j]) : 0.f;
-  }
-#pragma unroll
-  for (int mi = 0; mi < MI; ++mi) {
-#pragma unroll
-    for (int rr = 0; rr < 4; ++rr) {
-      const int row = wave * WM + 16 * mi + 4 * g + rr;
-      float v[8];
-#pragma unroll
-      for (int q = 0; q < 8; ++q) v[q] = (float)acc[mi][q][rr];
-#pragma unroll
-      for (int sd = 1; sd < 8; sd <<= 1)
-#pragma unroll
-        for (int q = 0; q < 8; ++q)
-          if ((q & sd) == 0) {
-            const float u0 = v[q], u1 = v[q + sd];
-            v[q] = u0 + u1;
-            v[q + sd] = u0 - u1;
-          }
-#pragma unroll
-      for (int msk = 1; msk < 16; msk <<= 1) {
-        const bool upper = (j & msk) != 0;
-#pragma unroll
-        for (int q = 0; q < 8; ++q) {
-          const float pv = shfl_xor_f(v[q], msk);
-          v[q] = upper ? (pv - v[q]) : (v[q] + pv);
-        }
-      }
-      if (row < T.rows) {
-        const float rs = T.ascale[row];
-#pragma unroll
-        for (int q = 0; q < 8; ++q) {
-          const int col = col0 + 16 * q + j;
-          float o = v[q] * rs * sv[q];
-          if (T.bias) o += bv[q];
-          if constexpr (Y_F32)
-            static_cast<float*>(T.y)[(int64_t)row * T.ldy + col] = o;
-          else
-            static_cast<uint16_t*>(T.y)[(int64_t)row * T.ldy + col] = f2h(o);
-        }
-      }
-    }
-  }
+  gemm_i8_epilogue<MI, Y_F32>(T, acc, wave * WM, col0, j, g);
 }
+
 
 }  // namespace exl3

@@ -4,7 +4,7 @@
 // int8 with both scales applied and writes fp16).
 //
 //   quant_rows_kernel  x' = (x .* suh) H_k in fp32 per row, a = max |x'|,
-//                      x_q = RNE(127 x' / a) (int8 [m][k]) and a / 127.
+//                      x_q = RNE(127 x' / a) (int8, fragment-major) and a / 127.
 //   gemm_i8_kernel     decode to int8 + v_mfma_i32_16x16x64_i8, epilogue with
 //                      both scales, the output transform, svh, bias, cast.
 //   reconstruct_i8_kernel  the int8 weights W_q [k][n], for the bit-exact
@@ -47,13 +47,30 @@ __device__ __forceinline__ void quant_block4(const uint16_t* __restrict__ xr,
   for (int e = 0; e < 8; ++e) v[e] *= kInvSqrt128;
 }
 
+// Rows m .. m_pad - 1 (up to the next multiple of 16) are written as zeros
+// with scale 0, so every 16-row group of x_q is complete.
 __global__ __launch_bounds__(kQuantThreads) void quant_rows_kernel(
-    const uint16_t* __restrict__ x, int64_t ldx, const uint16_t* __restrict__ suh, int k,
+    const uint16_t* __restrict__ x, int64_t ldx, const uint16_t* __restrict__ suh, int k, int64_t m,
     int8_t* __restrict__ xq, float* __restrict__ scale) {
   __shared__ float wmax[kQuantThreads / 64];
   const int64_t row = blockIdx.x;
   const int wave = (int)(threadIdx.x >> 6), lane = (int)(threadIdx.x & 63);
   const int nb = k / 128;
+  // fragment-major destination of this lane's 8 bytes (elements
+  // 128 b + 8 jj .. + 7, jj = lane % 16): 64-k block 2 b + jj / 8, lane group
+  // (jj % 8) / 2 of the fragment, byte 8 (jj % 2) of its 16
+  const int jj = lane & 15;
+  int8_t* qbase = xq + ((row >> 4) * (k / kGemmI8BK) * 64 + 16 * ((jj & 7) >> 1) + (row & 15)) * 16 +
+                  8 * (jj & 1);
+  auto qdst = [&](int b) { return qbase + (int64_t)(2 * b + (jj >> 3)) * kI8FragBytes; };
+  if (row >= m) {  // padding row of the last 16-row group
+    for (int b0 = 4 * wave; b0 < nb; b0 += 16) {
+      const int b = b0 + (lane >> 4);
+      if (b < nb) *reinterpret_cast<uint2*>(qdst(b)) = make_uint2(0u, 0u);
+    }
+    if (threadIdx.x == 0) scale[row] = 0.f;
+    return;
+  }
   const uint16_t* xr = x + row * ldx;
   float amax = 0.f;
   for (int b0 = 4 * wave; b0 < nb; b0 += 16) {
@@ -68,7 +85,6 @@ __global__ __launch_bounds__(kQuantThreads) void quant_rows_kernel(
   __syncthreads();
   const float a = fmaxf(fmaxf(wmax[0], wmax[1]), fmaxf(wmax[2], wmax[3]));
   const float inv = a > 0.f ? 127.0f / a : 0.f;
-  int8_t* qr = xq + row * k;
   for (int b0 = 4 * wave; b0 < nb; b0 += 16) {
     const int b = b0 + (lane >> 4);
     float v[8];
@@ -79,7 +95,7 @@ __global__ __launch_bounds__(kQuantThreads) void quant_rows_kernel(
       const float qf = fminf(fmaxf(rintf(v[e] * inv), -127.f), 127.f);
       w[e >> 2] |= ((uint32_t)(int32_t)qf & 0xFFu) << (8 * (e & 3));
     }
-    if (b < nb) *reinterpret_cast<uint2*>(qr + b * 128 + 8 * (lane & 15)) = make_uint2(w[0], w[1]);
+    if (b < nb) *reinterpret_cast<uint2*>(qdst(b)) = make_uint2(w[0], w[1]);
   }
   if (threadIdx.x == 0) scale[row] = a / 127.0f;
 }
@@ -88,9 +104,9 @@ __global__ __launch_bounds__(kQuantThreads) void quant_rows_kernel(
 // int8 GEMM dispatch (dense tensor)
 // ---------------------------------------------------------------------------
 struct DenseGemmI8Res {
-  const int8_t* a;
+  const int8_t* a;      // fragment-major x_q
   const float* ascale;
-  int64_t lda;
+  int64_t lda;          // bytes per 16-row group
   int m;
   int bm;
   int mt;   // row tiles
@@ -104,7 +120,8 @@ struct DenseGemmI8Res {
   // Workgroup -> (row tile, column tile), the XCD-aware order of the fp16
   // prefill GEMM: with a tile count that is a multiple of eight, the
   // workgroups of one XCD take one contiguous range of the tile order, which
-  // walks pairs of row tiles across all column tiles.
+  // walks two row tiles across all column tiles, so their int8 row panels
+  // (2.6 MB for 256-row tiles at k = 5120) stay in that XCD's 4 MB L2.
   __device__ GemmI8Task task() const {
     const int total = mt * nbt;
     const int bid = (int)blockIdx.x;
@@ -118,7 +135,7 @@ struct DenseGemmI8Res {
     T.nb = within / gs;
     const int r0 = mtile * bm;
     T.valid = r0 < m;
-    T.a = a + (int64_t)r0 * lda;
+    T.a = a + (int64_t)(r0 >> 4) * lda;  // r0 is a multiple of 16
     T.ascale = ascale + r0;
     T.lda = lda;
     T.rows = (m - r0) < bm ? (m - r0) : bm;
@@ -132,17 +149,22 @@ struct DenseGemmI8Res {
   }
 };
 
+// Rows per tile.  At K = 7 and 8 the 256-row tile needs a few more than 256
+// VGPRs and the compiler spills 16-28 bytes; measured at 4096 rows it is
+// still faster than the 128-row tile.  (An eight-wave 512-row tile, which
+// halves the decode per MFMA, measured 1-18 % slower than this once the
+// activations were fragment-major.)
 static int choose_bm_i8(int64_t m) { return m > 128 ? 256 : (m > 64 ? 128 : 64); }
 
 template <int K>
 struct DenseGemmI8Run {
   static hipError_t run(const DenseGemmI8Res& r, int k, int n, hipStream_t s) {
     const dim3 grid(r.mt * r.nbt);
-#define EXL3_GEMM_I8_LAUNCH(BM)                                                                     \
-  do {                                                                                              \
-    if (r.y_f32)                                                                                    \
+#define EXL3_GEMM_I8_LAUNCH(BM)                                                                    \
+  do {                                                                                             \
+    if (r.y_f32)                                                                                   \
       hipLaunchKernelGGL((gemm_i8_kernel<K, BM, true, DenseGemmI8Res>), grid, dim3(kGemmThreads), 0, s, r, k, n); \
-    else                                                                                            \
+    else                                                                                           \
       hipLaunchKernelGGL((gemm_i8_kernel<K, BM, false, DenseGemmI8Res>), grid, dim3(kGemmThreads), 0, s, r, k, n); \
   } while (0)
     if (r.bm == 256) EXL3_GEMM_I8_LAUNCH(256);
@@ -153,12 +175,13 @@ struct DenseGemmI8Run {
   }
 };
 
-// Workspace: x_q (int8 [m][k]) then the row scales (fp32 [m]), each on a
-// 256-byte boundary.
-static size_t i8_scale_offset(int k, int64_t m) { return ((size_t)m * k + 255) & ~(size_t)255; }
+// Workspace: x_q (int8, fragment-major, m rounded up to 16 rows) then the row
+// scales (fp32, same rows), each on a 256-byte boundary.
+static int64_t i8_rows(int64_t m) { return (m + 15) & ~(int64_t)15; }
+static size_t i8_scale_offset(int k, int64_t m) { return ((size_t)i8_rows(m) * k + 255) & ~(size_t)255; }
 
 size_t linear_int8_workspace(int k, int64_t m) {
-  return i8_scale_offset(k, m) + (((size_t)m * sizeof(float) + 255) & ~(size_t)255);
+  return i8_scale_offset(k, m) + (((size_t)i8_rows(m) * sizeof(float) + 255) & ~(size_t)255);
 }
 
 hipError_t launch_linear_int8(const uint16_t* trellis, const uint16_t* suh, const uint16_t* svh,
@@ -168,13 +191,13 @@ hipError_t launch_linear_int8(const uint16_t* trellis, const uint16_t* suh, cons
   unsigned char* base = static_cast<unsigned char*>(ws);
   int8_t* xq = reinterpret_cast<int8_t*>(base);
   float* sc = reinterpret_cast<float*>(base + i8_scale_offset(k, m));
-  hipLaunchKernelGGL(quant_rows_kernel, dim3((unsigned)m), dim3(kQuantThreads), 0, s, x, ldx, suh, k,
-                     xq, sc);
+  hipLaunchKernelGGL(quant_rows_kernel, dim3((unsigned)i8_rows(m)), dim3(kQuantThreads), 0, s, x, ldx,
+                     suh, k, m, xq, sc);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
   const int bm = choose_bm_i8(m);
-  DenseGemmI8Res r{xq, sc, k, (int)m, bm, (int)((m + bm - 1) / bm), n / kGemmBN, trellis, svh, bias,
-                   y, ldy, y_f32};
+  DenseGemmI8Res r{xq, sc, (int64_t)16 * k, (int)m, bm, (int)((m + bm - 1) / bm), n / kGemmBN, trellis,
+                   svh, bias, y, ldy, y_f32};
   return dispatch_bits<DenseGemmI8Run>(bits, r, k, n, s);
 }
 

@@ -85,7 +85,7 @@ hipError_t launch_gemm(const uint16_t* trellis, const uint16_t* suh, const uint1
                        hipStream_t s);
 
 // --- int8 prefill ------------------------------------------------------------
-// workspace: x_q (int8 [m][k]) and the row scales (fp32 [m])
+// workspace: x_q (int8, fragment-major, rows padded to 16) and the row scales
 size_t linear_int8_workspace(int k, int64_t m);
 hipError_t launch_linear_int8(const uint16_t* trellis, const uint16_t* suh, const uint16_t* svh,
                               const uint16_t* bias, int k, int n, int bits, const uint16_t* x,

@@ -49,12 +49,14 @@ def test_reconstruct_int8_bit_exact(bits):
 
 
 @pytest.mark.parametrize("bits", [1, 2, 3, 4, 5, 6, 7, 8])
-@pytest.mark.parametrize("m", [1, 70, 300])
+@pytest.mark.parametrize("m", [1, 70, 300, 700, 1030])
 def test_linear_int8_parity(bits, m):
     # several 128-column blocks, k of several 64-row steps, ragged row tiles
-    d = G.linear_case(810 + bits, 300, 512, 384, bits)
+    # of every tile height (64, 128 and 256 rows) and a last 16-row group of
+    # the fragment-major activations that is only partly filled
+    d = G.linear_case(810 + bits, 1030, 512, 384, bits)
     y = _run8(d, m=m).double().cpu().numpy()
-    ref = O.linear_int8(d["x"][:m], d["trellis"], d["suh"], d["svh"], bits, wq=_wq(810 + bits, 300, 512, 384, bits))
+    ref = O.linear_int8(d["x"][:m], d["trellis"], d["suh"], d["svh"], bits, wq=_wq(810 + bits, 1030, 512, 384, bits))
     assert O.rel_frobenius(y, ref) < TOL8
     ref16 = O.linear(d["x"][:m], d["trellis"], d["suh"], d["svh"], bits)
     assert O.rel_frobenius(y, ref16) < TOL_VS_FP16
@@ -71,10 +73,11 @@ def test_linear_int8_fp32_output_and_bias():
 
 def test_linear_int8_rows_independent_bit_exact():
     # each row is quantized and contracted on its own: any prefix of the
-    # batch gives the same rows, and m = 1 equals the row of a full batch
-    d = G.linear_case(821, 300, 512, 256, 3)
+    # batch gives the same rows, and m = 1 equals the row of a full batch,
+    # whichever tile height serves it
+    d = G.linear_case(821, 700, 512, 256, 3)
     full = G.f16_bits(_run8(d))
-    for m in (1, 20, 129):
+    for m in (1, 20, 129, 300, 512):
         np.testing.assert_array_equal(G.f16_bits(_run8(d, m=m)), full[:m])
 
 
