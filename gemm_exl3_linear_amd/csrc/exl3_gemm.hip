@@ -1,5 +1,5 @@
 // Dense prefill linear (m > 16): x' = (x .* suh) H is written once to the
-// workspace by the Hadamard kernel, then one fused decode + MFMA GEMM launch
+// workspace, fragment-major, by the input kernel, then one fused decode + MFMA GEMM launch
 // computes y = (x' W~) H .* svh (+ bias).  See exl3_gemm.hpp for the kernel.
 #include "exl3_gemm.hpp"
 #include "exl3_internal.hpp"
@@ -7,8 +7,9 @@
 namespace exl3 {
 
 struct DenseGemmRes {
+  static constexpr bool kAFrag = true;  // x' is fragment-major
   const uint16_t* a;
-  int64_t lda;
+  int64_t lda;  // elements per 16-row group (16 k)
   int m;
   int bm;
   int mt;   // row tiles
@@ -38,7 +39,7 @@ struct DenseGemmRes {
     T.nb = within / gs;
     const int r0 = mtile * bm;
     T.valid = r0 < m;
-    T.a = a + (int64_t)r0 * lda;
+    T.a = a + (int64_t)(r0 >> 4) * lda;  // r0 is a multiple of 16
     T.lda = lda;
     T.rows = (m - r0) < bm ? (m - r0) : bm;
     T.trellis = trellis;
@@ -73,22 +74,24 @@ struct DenseGemmRun {
 };
 
 // The workspace starts with the same arrival-counter region as the decode
-// GEMV's (left untouched here, so it stays zero), followed by x' (fp16 [m][k]).
+// GEMV's (left untouched here, so it stays zero), followed by x' (fp16,
+// fragment-major, m rounded up to 16 rows).
 static size_t counter_region(int n) { return ((size_t)(n / 128) * 4 + 255) & ~(size_t)255; }
+static int64_t frag_rows(int64_t m) { return (m + 15) & ~(int64_t)15; }
 
 size_t gemm_workspace(int k, int n, int m) {
-  return counter_region(n) + (size_t)m * k * sizeof(uint16_t);
+  return counter_region(n) + (size_t)frag_rows(m) * k * sizeof(uint16_t);
 }
 
 hipError_t launch_gemm(const uint16_t* trellis, const uint16_t* suh, const uint16_t* svh,
                        const uint16_t* bias, int k, int n, int bits, const uint16_t* x, int m,
                        int64_t ldx, void* y, int64_t ldy, bool y_f32, void* ws, hipStream_t s) {
   uint16_t* xp = reinterpret_cast<uint16_t*>(static_cast<unsigned char*>(ws) + counter_region(n));
-  hipError_t e = launch_hadamard(x, false, xp, false, m, k, ldx, k, suh, nullptr, s);
+  hipError_t e = launch_input_frag(x, ldx, m, k, suh, xp, s);
   if (e != hipSuccess) return e;
   const int bm = choose_bm(m);
-  DenseGemmRes r{xp, k, m, bm, (m + bm - 1) / bm, (n + kGemmBN - 1) / kGemmBN, trellis, svh, bias,
-                 y, ldy, y_f32};
+  DenseGemmRes r{xp, (int64_t)16 * k, m, bm, (m + bm - 1) / bm, (n + kGemmBN - 1) / kGemmBN, trellis,
+                 svh, bias, y, ldy, y_f32};
   return dispatch_bits<DenseGemmRun>(bits, r, k, n, s);
 }
 

@@ -48,6 +48,14 @@ constexpr int kGemmBN = 128;        // columns per workgroup tile (one Hadamard 
 constexpr int kGemmBK = 32;         // k rows per step (two trellis tiles)
 constexpr int kGemmThreads = 256;   // four waves, each BM/4 rows x 128 columns
 
+// Fragment-major fp16 activations (the dense prefill's x'): for every group of
+// 16 rows and every 32 k, the MFMA A operand in lane order, lane (g, j) =
+// 16 g + j holding the 8 elements of row j at k 8 g .. 8 g + 7:
+//   x'[16 G + j][32 B + 8 g + e] at element ((G * (k / 32) + B) * 64 + 16 g + j) * 8 + e.
+// One fragment is one contiguous kilobyte, read with fully used 128-byte
+// lines (row-major, each load covers 16 rows x 64 bytes, half of each line).
+constexpr int kGemmFragBytes = 1024;
+
 // Decoded-weight stage: 128 columns x 32 k (fp16) as 512 chunks of 16 bytes
 // (four k-pairs of one column each).  Each group of four columns G = col / 4
 // owns 16 consecutive chunks (256 bytes, one pass over 64 LDS banks); inside
@@ -110,11 +118,23 @@ __global__ __launch_bounds__(kGemmThreads, 2) void gemm_kernel(R r, int k, int n
 #pragma unroll
   for (int c = 0; c < 8; ++c) bw_dw[c] = gemm_b_chunk(16 * t + 8 * h + c, kp >> 2) * 4 + (kp & 3);
   // A fragment rows; rows at or past T.rows read as zero (outside the range)
-  const __amdgpu_buffer_rsrc_t a_rs = make_rsrc(T.a, (uint32_t)((uint64_t)T.rows * T.lda * 2));
-  uint32_t a_voff[MI];
+  // R::kAFrag: x' is fragment-major (see kGemmFragBytes), T.lda elements per
+  // 16-row group, and a fragment is one contiguous kilobyte; otherwise x' is
+  // row-major, T.lda elements per row
+  uint32_t a_bytes, a_voff[MI];
+  if constexpr (R::kAFrag) {
+    a_bytes = (uint32_t)((uint64_t)((T.rows + 15) >> 4) * T.lda * 2);
 #pragma unroll
-  for (int mi = 0; mi < MI; ++mi)
-    a_voff[mi] = (uint32_t)(((int64_t)(wm * WM + 16 * mi + j) * T.lda + 8 * g) * 2);
+    for (int mi = 0; mi < MI; ++mi)
+      a_voff[mi] = (uint32_t)((int64_t)(wm * MI + mi) * T.lda * 2 + 16 * lane);
+  } else {
+    a_bytes = (uint32_t)((uint64_t)T.rows * T.lda * 2);
+#pragma unroll
+    for (int mi = 0; mi < MI; ++mi)
+      a_voff[mi] = (uint32_t)(((int64_t)(wm * WM + 16 * mi + j) * T.lda + 8 * g) * 2);
+  }
+  const __amdgpu_buffer_rsrc_t a_rs = make_rsrc(T.a, a_bytes);
+  constexpr int kAStep = R::kAFrag ? kGemmFragBytes : kGemmBK * 2;  // bytes per k step
   // B fragment chunks this lane reads (column 128 wn + 16 q + j, chunk g)
   int br_ch[8];
 #pragma unroll
@@ -136,7 +156,7 @@ __global__ __launch_bounds__(kGemmThreads, 2) void gemm_kernel(R r, int k, int n
 #pragma unroll
     for (int mi = 0; mi < MI; ++mi)
       ra[set][mi] = __builtin_bit_cast(
-          half8_t, __builtin_amdgcn_raw_buffer_load_b128(a_rs, (int)a_voff[mi], ks * kGemmBK * 2, 0));
+          half8_t, __builtin_amdgcn_raw_buffer_load_b128(a_rs, (int)a_voff[mi], ks * kAStep, 0));
   };
   auto load_t = [&](int set, int ks) {
     ks = ks < nsteps ? ks : nsteps - 1;

@@ -445,6 +445,7 @@ __global__ __launch_bounds__(256) void combine_rows(const float* __restrict__ d,
 }
 
 struct GroupedGemmRes {
+  static constexpr bool kAFrag = false;  // gathered rows stay row-major
   const TileEntry* tiles;
   const int32_t* ntiles;
   const uint16_t* a;       // fp16 [slots][P][k]

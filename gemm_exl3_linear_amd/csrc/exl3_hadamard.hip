@@ -45,6 +45,45 @@ __global__ __launch_bounds__(256) void hadamard_kernel(const void* __restrict__ 
   }
 }
 
+// The dense prefill GEMM's input: x' = (x .* suh) H (fp16 in and out), written
+// fragment-major (kGemmFragBytes): element (r, c) at
+// ((r / 16 * (k / 32) + c / 32) * 64 + 16 ((c % 32) / 8) + r % 16) * 8 + c % 8.
+// Rows m .. m_pad - 1 (up to a multiple of 16) are written as zeros.  One wave
+// per 128-element block, lane l holding elements 2l, 2l + 1 (one 4-byte store).
+__global__ __launch_bounds__(256) void input_frag_kernel(const uint16_t* __restrict__ x, int64_t ldx,
+                                                         int64_t m, int64_t m_pad, int64_t bpr,
+                                                         const uint16_t* __restrict__ suh,
+                                                         uint16_t* __restrict__ out) {
+  const int64_t task = (int64_t)blockIdx.x * 4 + (threadIdx.x >> 6);
+  if (task >= m_pad * bpr) return;  // whole waves leave together
+  const int64_t row = task / bpr;
+  const int64_t col = (task % bpr) * 128 + 2 * (int64_t)lane_id();
+  float a = 0.f, b = 0.f;
+  if (row < m) {  // uniform per wave
+    const uint32_t v = *reinterpret_cast<const uint32_t*>(x + row * ldx + col);
+    const uint32_t sv = *reinterpret_cast<const uint32_t*>(suh + col);
+    a = h2f((uint16_t)(v & 0xFFFF)) * h2f((uint16_t)(sv & 0xFFFF));
+    b = h2f((uint16_t)(v >> 16)) * h2f((uint16_t)(sv >> 16));
+    fwht128_pair(a, b);
+    a *= kInvSqrt128;
+    b *= kInvSqrt128;
+  }
+  const int64_t kb = bpr * 4;  // 32-element k blocks per row
+  const int64_t e = ((row >> 4) * kb + (col >> 5)) * 512 + (((col & 31) >> 3) * 16 + (row & 15)) * 8 +
+                    (col & 7);
+  *reinterpret_cast<uint32_t*>(out + e) = (uint32_t)f2h(a) | ((uint32_t)f2h(b) << 16);
+}
+
+hipError_t launch_input_frag(const uint16_t* x, int64_t ldx, int64_t m, int64_t k,
+                             const uint16_t* suh, uint16_t* out, hipStream_t s) {
+  const int64_t bpr = k / 128;
+  const int64_t m_pad = (m + 15) & ~(int64_t)15;
+  const unsigned blocks = (unsigned)((m_pad * bpr + 3) / 4);
+  if (blocks == 0) return hipSuccess;
+  hipLaunchKernelGGL(input_frag_kernel, dim3(blocks), dim3(256), 0, s, x, ldx, m, m_pad, bpr, suh, out);
+  return hipGetLastError();
+}
+
 hipError_t launch_hadamard(const void* in, bool in_f32, void* out, bool out_f32, int64_t rows,
                            int64_t dim, int64_t ld_in, int64_t ld_out,
                            const uint16_t* sign_before, const uint16_t* sign_after,

@@ -32,6 +32,10 @@ hipError_t launch_reconstruct(const uint16_t* trellis, uint16_t* out, int k, int
 // --- Hadamard --------------------------------------------------------------
 // out = ((in .* sign_before) H) .* sign_after, blocks of 128, fp32 arithmetic.
 // in_f32 / out_f32 select the element types.  Rows are independent.
+// x' = (x .* suh) H for the dense prefill GEMM, fp16, fragment-major, rows
+// padded with zeros to a multiple of 16
+hipError_t launch_input_frag(const uint16_t* x, int64_t ldx, int64_t m, int64_t k,
+                             const uint16_t* suh, uint16_t* out, hipStream_t s);
 hipError_t launch_hadamard(const void* in, bool in_f32, void* out, bool out_f32, int64_t rows,
                            int64_t dim, int64_t ld_in, int64_t ld_out,
                            const uint16_t* sign_before, const uint16_t* sign_after,
