@@ -230,40 +230,81 @@ __device__ __forceinline__ float shfl_xor_f(float v, int mask) {
   return __int_as_float(__builtin_amdgcn_ds_bpermute(src << 2, __float_as_int(v)));
 }
 
-__device__ __forceinline__ void fwht128_pair(float& a, float& b) {
-  const float s = a + b, d = a - b;
-  a = s;
-  b = d;
-  const uint32_t l = lane_id();
-#pragma unroll
-  for (int m = 1; m < 64; m <<= 1) {
-    const float pa = shfl_xor_f(a, m);
-    const float pb = shfl_xor_f(b, m);
-    const bool upper = (l & (uint32_t)m) != 0;
-    a = upper ? (pa - a) : (a + pa);
-    b = upper ? (pb - b) : (b + pb);
+template <int V>
+struct PowC {
+  static constexpr int value = V;
+};
+// f(PowC<I>), f(PowC<2 I>), ... while below N
+template <int I, int N, class F>
+__device__ __forceinline__ void static_for_pow2(F&& f) {
+  if constexpr (I < N) {
+    f(PowC<I>{});
+    static_for_pow2<2 * I, N>(f);
   }
 }
 
-// Transform of up to four 128-element blocks at once by one wave: lane
-// l holds elements 8 (l % 16) .. 8 (l % 16) + 7 of block l / 16, so the three
-// lowest butterfly strides stay inside the lane and the other four pair
-// lanes l ^ 1, 2, 4, 8 of the same 16-lane group (ds_swizzle, no LDS
-// memory).  v[e] = x * suh on entry, the unnormalised transform on exit.
+// DPP moves that pair lane l with l ^ 1, l ^ 2 (quad permutations) and l ^ 8
+// (rotation by 8 inside each row of 16 lanes): full-rate VALU moves, no LDS.
+constexpr int kDppXor1 = 0xB1;    // quad_perm [1, 0, 3, 2]
+constexpr int kDppXor2 = 0x4E;    // quad_perm [2, 3, 0, 1]
+constexpr int kDppXor8 = 0x128;   // row_ror:8
+template <int CTRL>
+__device__ __forceinline__ float dpp_f(float v) {
+  return __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(v), CTRL, 0xF, 0xF, true));
+}
+
+// One butterfly across lanes: the lower lane of a pair keeps v + partner, the
+// upper one partner - v, written as one fma with a +-1 factor (exact: the
+// product is v itself or its negation).
+__device__ __forceinline__ float bfly(float v, float partner, bool upper) {
+  return __builtin_fmaf(v, upper ? -1.f : 1.f, partner);
+}
+
 template <int MASK>
 __device__ __forceinline__ float swizzle_xor_f(float v) {
   // bitmask mode: source lane = (lane & 0x1F) ^ MASK inside each 32 lanes
   return __int_as_float(__builtin_amdgcn_ds_swizzle(__float_as_int(v), (MASK << 10) | 0x1F));
 }
 
+// Value of lane l ^ MASK: DPP for 1, 2 and 8, ds_swizzle (no LDS memory, no
+// address operand) for 4 and 16, ds_bpermute for 32.
+template <int MASK>
+__device__ __forceinline__ float xor_partner(float v) {
+  if constexpr (MASK == 1) return dpp_f<kDppXor1>(v);
+  else if constexpr (MASK == 2) return dpp_f<kDppXor2>(v);
+  else if constexpr (MASK == 8) return dpp_f<kDppXor8>(v);
+  else if constexpr (MASK < 32) return swizzle_xor_f<MASK>(v);
+  else return shfl_xor_f(v, MASK);
+}
+
+__device__ __forceinline__ void fwht128_pair(float& a, float& b) {
+  const float s = a + b, d = a - b;
+  a = s;
+  b = d;
+  const uint32_t l = lane_id();
+  static_for_pow2<1, 64>([&](auto mc) {
+    constexpr int m = decltype(mc)::value;
+    const bool upper = (l & (uint32_t)m) != 0;
+    const float pa = xor_partner<m>(a);
+    const float pb = xor_partner<m>(b);
+    a = bfly(a, pa, upper);
+    b = bfly(b, pb, upper);
+  });
+}
+
+// Transform of up to four 128-element blocks at once by one wave: lane
+// l holds elements 8 (l % 16) .. 8 (l % 16) + 7 of block l / 16, so the three
+// lowest butterfly strides stay inside the lane and the other four pair
+// lanes l ^ 1, 2, 4, 8 of the same 16-lane group (xor_partner: no LDS
+// memory).  v[e] = x * suh on entry, the unnormalised transform on exit.
 template <int MASK>
 __device__ __forceinline__ void fwht_lane_stage(float (&v)[8]) {
   float pv[8];
 #pragma unroll
-  for (int e = 0; e < 8; ++e) pv[e] = swizzle_xor_f<MASK>(v[e]);
+  for (int e = 0; e < 8; ++e) pv[e] = xor_partner<MASK>(v[e]);
   const bool upper = (lane_id() & (uint32_t)MASK) != 0;
 #pragma unroll
-  for (int e = 0; e < 8; ++e) v[e] = upper ? (pv[e] - v[e]) : (v[e] + pv[e]);
+  for (int e = 0; e < 8; ++e) v[e] = bfly(v[e], pv[e], upper);
 }
 
 __device__ __forceinline__ void fwht128_x8(float (&v)[8]) {

@@ -2,8 +2,11 @@
 // shared by the dense linear and the grouped experts.
 //
 // One workgroup (four waves) computes a BM x 128 output tile over the full k
-// range: wave w owns rows w BM/4 .. (w+1) BM/4 - 1 and all 128 columns, one
-// whole Hadamard block.  Two workgroups share each CU (two waves per SIMD: a
+// range: wave w owns the 16-row groups w, w + 4, w + 8, ... (BM/64 of them)
+// and all 128 columns, one whole Hadamard block.  Interleaved groups keep the
+// waves' shares of a short tile even: a wave runs MFMAs only for its groups
+// that hold valid rows (for every group count when R::kFineSkip, else all or
+// none), while all four decode.  Two workgroups share each CU (two waves per SIMD: a
 // single wave cannot issue v_mfma_f32_16x16x32_f16 back to back), and being
 // independent they fill each other's barrier and memory stalls.
 //   per k step of 32 rows  - each wave loads its A fragments (activations
@@ -121,17 +124,18 @@ __global__ __launch_bounds__(kGemmThreads, 2) void gemm_kernel(R r, int k, int n
   // R::kAFrag: x' is fragment-major (see kGemmFragBytes), T.lda elements per
   // 16-row group, and a fragment is one contiguous kilobyte; otherwise x' is
   // row-major, T.lda elements per row
+  // (group 4 mi + wm of the tile is this wave's mi-th)
   uint32_t a_bytes, a_voff[MI];
   if constexpr (R::kAFrag) {
     a_bytes = (uint32_t)((uint64_t)((T.rows + 15) >> 4) * T.lda * 2);
 #pragma unroll
     for (int mi = 0; mi < MI; ++mi)
-      a_voff[mi] = (uint32_t)((int64_t)(wm * MI + mi) * T.lda * 2 + 16 * lane);
+      a_voff[mi] = (uint32_t)((int64_t)(4 * mi + wm) * T.lda * 2 + 16 * lane);
   } else {
     a_bytes = (uint32_t)((uint64_t)T.rows * T.lda * 2);
 #pragma unroll
     for (int mi = 0; mi < MI; ++mi)
-      a_voff[mi] = (uint32_t)(((int64_t)(wm * WM + 16 * mi + j) * T.lda + 8 * g) * 2);
+      a_voff[mi] = (uint32_t)(((int64_t)(16 * (4 * mi + wm) + j) * T.lda + 8 * g) * 2);
   }
   const __amdgpu_buffer_rsrc_t a_rs = make_rsrc(T.a, a_bytes);
   constexpr int kAStep = R::kAFrag ? kGemmFragBytes : kGemmBK * 2;  // bytes per k step
@@ -151,13 +155,6 @@ __global__ __launch_bounds__(kGemmThreads, 2) void gemm_kernel(R r, int k, int n
   // two register sets: A fragments of step s and trellis words of step s live in set s % 2
   half8_t ra[2][MI];
   uint32_t rt[2][K];
-  auto load_a = [&](int set, int ks) {
-    ks = ks < nsteps ? ks : nsteps - 1;  // past the end: re-read the last step (unused)
-#pragma unroll
-    for (int mi = 0; mi < MI; ++mi)
-      ra[set][mi] = __builtin_bit_cast(
-          half8_t, __builtin_amdgcn_raw_buffer_load_b128(a_rs, (int)a_voff[mi], ks * kAStep, 0));
-  };
   auto load_t = [&](int set, int ks) {
     ks = ks < nsteps ? ks : nsteps - 1;
     load_rowpair_buf<K>(t_rs, t_voff, (uint32_t)ks * t_step, rt[set]);
@@ -183,38 +180,56 @@ __global__ __launch_bounds__(kGemmThreads, 2) void gemm_kernel(R r, int k, int n
   // into stage `nxt`.  The schedule is fixed explicitly: the B fragment reads
   // first, then each MFMA followed by two decode instructions (the matrix
   // core runs while the wave decodes), then the decoded stores.
-  auto step = [&](const uint4* cur, uint4* nxt, int aset, int tset, auto hc) {
+  //
+  // NA (0..MI) is the number of this wave's row groups that run: A loads, B
+  // reads and MFMAs cover groups 0..NA-1 only.  A wave with NA = 0 (all its
+  // rows at or past T.rows) only decodes its share of B and joins the
+  // barriers.
+  auto step = [&](const uint4* cur, uint4* nxt, int aset, int tset, auto hc, auto ac) {
+    constexpr int NA = decltype(ac)::value;
     uint32_t B[K + 1];
     stream_of(tset, B);
     half8_t bv[8];
+    if constexpr (NA > 0) {
 #pragma unroll
-    for (int q = 0; q < 8; ++q) bv[q] = __builtin_bit_cast(half8_t, cur[br_ch[q]]);
+      for (int q = 0; q < 8; ++q) bv[q] = __builtin_bit_cast(half8_t, cur[br_ch[q]]);
+    }
     uint32_t wv[8];
     decode8(B, wv, hc);
 #pragma unroll
     for (int q = 0; q < 8; ++q)
 #pragma unroll
-      for (int mi = 0; mi < MI; ++mi)
+      for (int mi = 0; mi < NA; ++mi)
         acc[mi][q] = __builtin_amdgcn_mfma_f32_16x16x32_f16(ra[aset][mi], bv[q], acc[mi][q], 0, 0, 0);
     uint32_t* nd = reinterpret_cast<uint32_t*>(nxt);
 #pragma unroll
     for (int c = 0; c < 8; ++c) nd[bw_dw[c]] = wv[c];
-    __builtin_amdgcn_sched_group_barrier(kSchedDsRead, 9, 0);
-    static_for<0, 8 * MI>([&](auto) {
-      __builtin_amdgcn_sched_group_barrier(kSchedMfma, 1, 0);
-      __builtin_amdgcn_sched_group_barrier(kSchedValu, 64 / (8 * MI) + 1, 0);
-    });
-    __builtin_amdgcn_sched_group_barrier(kSchedDsWrite, 8, 0);
-    __builtin_amdgcn_sched_group_barrier(kSchedVmemRead, MI + (K + 3) / 4, 0);
+    if constexpr (NA > 0) {
+      __builtin_amdgcn_sched_group_barrier(kSchedDsRead, 9, 0);
+      static_for<0, 8 * NA>([&](auto) {
+        __builtin_amdgcn_sched_group_barrier(kSchedMfma, 1, 0);
+        __builtin_amdgcn_sched_group_barrier(kSchedValu, 64 / (8 * NA) + 1, 0);
+      });
+      __builtin_amdgcn_sched_group_barrier(kSchedDsWrite, 8, 0);
+      __builtin_amdgcn_sched_group_barrier(kSchedVmemRead, NA + (K + 3) / 4, 0);
+    }
   };
 
-  auto run = [&](auto hc) {
+  auto run = [&](auto hc, auto ac) {
+    constexpr int NA = decltype(ac)::value;
+    auto load_a_act = [&](int set, int ks) {
+      ks = ks < nsteps ? ks : nsteps - 1;  // past the end: re-read the last step (unused)
+#pragma unroll
+      for (int mi = 0; mi < NA; ++mi)
+        ra[set][mi] = __builtin_bit_cast(
+            half8_t, __builtin_amdgcn_raw_buffer_load_b128(a_rs, (int)a_voff[mi], ks * kAStep, 0));
+    };
     // prologue: step 0 decoded into stage 0; A of steps 0, 1 and trellis of
     // steps 1, 2 in flight
     load_t(0, 0);
-    load_a(0, 0);
+    load_a_act(0, 0);
     load_t(1, 1);
-    load_a(1, 1);
+    load_a_act(1, 1);
     {
       uint32_t B[K + 1], wv[8];
       stream_of(0, B);
@@ -234,22 +249,37 @@ __global__ __launch_bounds__(kGemmThreads, 2) void gemm_kernel(R r, int k, int n
     // register-only decode above the barrier, which forces a wait on the
     // loads issued one step earlier)
     for (int ks = 0; ks < nsteps; ks += 2) {
-      step(bst0, bst1, 0, 1, hc);
-      load_a(0, ks + 2);
+      step(bst0, bst1, 0, 1, hc, ac);
+      load_a_act(0, ks + 2);
       load_t(1, ks + 3);
       __syncthreads();
       __builtin_amdgcn_sched_barrier(0);
-      step(bst1, bst0, 1, 0, hc);
-      load_a(1, ks + 3);
+      step(bst1, bst0, 1, 0, hc, ac);
+      load_a_act(1, ks + 3);
       load_t(0, ks + 4);
       __syncthreads();
       __builtin_amdgcn_sched_barrier(0);
     }
   };
+  // row groups of this wave holding valid rows (uniform per wave)
+  const int g16 = (T.rows + 15) >> 4;
+  int na = (g16 - wm + 3) >> 2;
+  na = na < 0 ? 0 : (na > MI ? MI : na);
+  auto go = [&](auto hc) {
+    if constexpr (R::kFineSkip) {
+      static_for<0, MI + 1>([&](auto nc) {
+        if (na == decltype(nc)::value) run(hc, nc);
+      });
+    } else {
+      if (na > 0) run(hc, IntC<MI>{});
+      else run(hc, IntC<0>{});
+    }
+  };
   if (h == 0)
-    run(IntC<0>{});
+    go(IntC<0>{});
   else
-    run(IntC<1>{});
+    go(IntC<1>{});
+  if (na == 0) return;  // no barrier follows
 
   // epilogue: output Hadamard over each wave's 128 columns, svh, bias, cast
   const int cb = col0 + 128 * wn;
@@ -261,6 +291,7 @@ __global__ __launch_bounds__(kGemmThreads, 2) void gemm_kernel(R r, int k, int n
   }
 #pragma unroll
   for (int mi = 0; mi < MI; ++mi) {
+    if (mi >= na) break;
 #pragma unroll
     for (int rr = 0; rr < 4; ++rr) {
       float v[8];
@@ -284,7 +315,7 @@ __global__ __launch_bounds__(kGemmThreads, 2) void gemm_kernel(R r, int k, int n
           v[q] = upper ? (pv - v[q]) : (v[q] + pv);
         }
       }
-      const int row = wm * WM + 16 * mi + 4 * g + rr;
+      const int row = 16 * (4 * mi + wm) + 4 * g + rr;
       if (row < T.rows) {
 #pragma unroll
         for (int q = 0; q < 8; ++q) {

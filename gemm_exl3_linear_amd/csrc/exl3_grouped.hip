@@ -22,16 +22,14 @@
 //
 // Large P (prefill): device binning, then one grouped MFMA GEMM launch per
 // projection over a device-built tile list (expert, first row, rows), so each
-// expert's weights are decoded once per 128-row tile instead of once per row.
-//   1. zero counters, count pairs per expert (integer atomics: exact)
-//   2. one workgroup scans the counts into offsets and the tile list
-//   3. scatter pairs into expert order (the order inside an expert is not
-//      fixed, but every row is computed independently of its position, so
-//      the output does not depend on it)
+// expert's weights are decoded once per tile (128 or 256 rows) instead of once
+// per row.
+//   1-3. count the pairs per expert and chunk, scan the counts into offsets
+//      and the tile list (one workgroup), scatter the pairs into expert order
 //   4. x'_g, x'_u = (x_token .* suh_e,slot) H for each sorted row   -> fp16
-//   5. gemm_kernel over (128 cols, tile, slot)  -> g, u fp32 (transformed)
+//   5. gemm_kernel over (tile, slot, 128 cols)  -> g, u fp32 (transformed)
 //   6. a = silu(g) * u, x'_d = (a .* suh_down_e) H                  -> fp16
-//   7. gemm_kernel over (128 cols, tile)        -> d fp32 (transformed, svh)
+//   7. gemm_kernel over (tile, 128 cols)        -> d fp32 (transformed, svh)
 //   8. y[token] = sum over slots in order of w * d                  -> fp32
 #include "exl3_device.hpp"
 #include "exl3_gemm.hpp"
@@ -45,7 +43,23 @@ namespace exl3 {
 // (P = 512: 248 us against 261 us for the binned path) and slower from T = 128
 // (478 against 299 us).
 constexpr int kGroupedUnitMaxPairs = 512;
-constexpr int kGroupedBM = 128;           // rows per tile of the grouped GEMM
+// Rows per tile of the grouped GEMM: 256 when the experts average at least
+// 96 rows (one tile per expert instead of two, so each expert's weights are
+// decoded once per column block), else 128.  A wave runs MFMAs only for its
+// row groups that hold rows, so a half-filled 256-row tile costs about the
+// MFMA work of its rows.  Measured on MI355X at 256 experts x (2048 -> 2 x
+// 512 -> 2048), K=3, top-8: T=4096 (128 rows per expert on average) takes
+// 0.69 ms with 256-row tiles against 0.77 ms with 128; T=512 (16 rows)
+// 0.27 ms either way.
+constexpr int kGroupedMinRowsBig = 96;
+static inline int grouped_bm(int64_t P, int E) { return P >= (int64_t)kGroupedMinRowsBig * E ? 256 : 128; }
+// routing binning: pairs per chunk (one workgroup of the count and scatter
+// launches each)
+constexpr int kBinThreads = 256;
+constexpr int kBinPerThread = 8;
+constexpr int kBinIds = kBinThreads * kBinPerThread;
+
+static inline int64_t bin_chunks(int64_t P) { return (P + kBinIds - 1) / kBinIds; }
 
 __device__ __forceinline__ float silu_f(float z) { return z / (1.0f + __expf(-z)); }
 
@@ -242,17 +256,18 @@ struct TileEntry {
 };
 
 struct GemmLayout {
+  int bm;  // rows per tile
   int max_tiles;
-  size_t counts, cursor, offsets, ntiles, tiles, pos, sorted, xg, gu, xd, d, total;
+  size_t hist, offsets, ntiles, tiles, pos, sorted, xg, gu, xd, d, total;
 };
 
 static GemmLayout gemm_layout(const ArenaDesc& gu, const ArenaDesc& dn, int64_t P) {
   GemmLayout L;
   const int E = gu.experts;
-  L.max_tiles = (int)((P + kGroupedBM - 1) / kGroupedBM) + (int)(P < E ? P : E);
+  L.bm = grouped_bm(P, E);
+  L.max_tiles = (int)((P + L.bm - 1) / L.bm) + (int)(P < E ? P : E);
   size_t off = counter_region(gu, dn);
-  L.counts = off;  off += align256((size_t)E * 4);
-  L.cursor = off;  off += align256((size_t)E * 4);
+  L.hist = off;    off += align256((size_t)bin_chunks(P) * E * 4);
   L.offsets = off; off += align256((size_t)E * 4);
   L.ntiles = off;  off += 256;
   L.tiles = off;   off += align256((size_t)L.max_tiles * sizeof(TileEntry));
@@ -266,20 +281,51 @@ static GemmLayout gemm_layout(const ArenaDesc& gu, const ArenaDesc& dn, int64_t 
   return L;
 }
 
-__global__ void zero_i32(int32_t* __restrict__ p, int count) {
-  const int i = blockIdx.x * blockDim.x + threadIdx.x;
-  if (i < count) p[i] = 0;
-}
-
-__global__ void bin_count(const int32_t* __restrict__ ids, int64_t P, int32_t* __restrict__ counts) {
-  const int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
-  if (i < P) atomicAdd(&counts[ids[i]], 1);
-}
-
-// One workgroup: exclusive scans of the per-expert row counts and of their
-// tile counts (ceil(count / bm)), in chunks of kPlanThreads experts, then
-// every expert writes its offset and its row tiles.
+// Routing binning, three launches.  The pairs are cut into chunks of
+// kBinIds; chunk c is handled by workgroup c of bin_count and of bin_scatter.
+//   bin_count    per-chunk, per-expert counts hist[c][e] (LDS integer
+//                atomics: exact)
+//   bin_plan     one workgroup: the expert totals, their exclusive scan
+//                (offsets), the scan of the tile counts ceil(count / bm) (the
+//                tile list), and hist[c][e] replaced by the first row of
+//                chunk c's pairs of expert e
+//   bin_scatter  every chunk places its pairs from those first rows on,
+//                through per-expert cursors in LDS
+// Experts go through LDS kBinChunk at a time (one pass for up to kBinChunk
+// experts).  The order of the pairs inside a chunk's share of an expert is
+// not fixed (LDS atomics), but every row is computed independently of its
+// position, so the output does not depend on it.
+constexpr int kBinChunk = 8192;  // experts per pass (32 KB of LDS)
 constexpr int kPlanThreads = 1024;
+
+__device__ __forceinline__ void bin_load_ids(const int32_t* __restrict__ ids, int64_t P,
+                                             int (&ev)[kBinPerThread]) {
+  const int64_t i0 = (int64_t)blockIdx.x * kBinIds + threadIdx.x;
+#pragma unroll
+  for (int q = 0; q < kBinPerThread; ++q) {
+    const int64_t i = i0 + (int64_t)q * kBinThreads;
+    ev[q] = i < P ? ids[i] : -1;
+  }
+}
+
+__global__ __launch_bounds__(kBinThreads) void bin_count(const int32_t* __restrict__ ids, int64_t P,
+                                                         int E, int32_t* __restrict__ hist) {
+  __shared__ int cnt[kBinChunk];
+  int ev[kBinPerThread];
+  bin_load_ids(ids, P, ev);
+  int32_t* h = hist + (int64_t)blockIdx.x * E;
+  for (int c0 = 0; c0 < E; c0 += kBinChunk) {
+    const int ce = (E - c0) < kBinChunk ? (E - c0) : kBinChunk;
+    for (int e = threadIdx.x; e < ce; e += kBinThreads) cnt[e] = 0;
+    __syncthreads();
+#pragma unroll
+    for (int q = 0; q < kBinPerThread; ++q)
+      if ((unsigned)(ev[q] - c0) < (unsigned)ce) atomicAdd(&cnt[ev[q] - c0], 1);
+    __syncthreads();
+    for (int e = threadIdx.x; e < ce; e += kBinThreads) h[c0 + e] = cnt[e];
+    __syncthreads();
+  }
+}
 
 __device__ __forceinline__ int block_exclusive_scan(int v, int* sh, int& total) {
   const int tid = threadIdx.x;
@@ -297,21 +343,30 @@ __device__ __forceinline__ int block_exclusive_scan(int v, int* sh, int& total) 
   return incl - v;
 }
 
-__global__ __launch_bounds__(kPlanThreads) void bin_plan(const int32_t* __restrict__ counts, int E, int bm,
-                                                         int32_t* __restrict__ offsets,
+__global__ __launch_bounds__(kPlanThreads) void bin_plan(int32_t* __restrict__ hist, int chunks, int E,
+                                                         int bm, int32_t* __restrict__ offsets,
                                                          int32_t* __restrict__ ntiles,
                                                          TileEntry* __restrict__ tiles) {
   __shared__ int sh[kPlanThreads];
   int row_base = 0, tile_base = 0;
   for (int e0 = 0; e0 < E; e0 += kPlanThreads) {
     const int e = e0 + (int)threadIdx.x;
-    const int c = e < E ? counts[e] : 0;
+    int c = 0;
+    if (e < E)
+      for (int ch = 0; ch < chunks; ++ch) c += hist[(int64_t)ch * E + e];
     const int nt = (c + bm - 1) / bm;
     int rows_total, tiles_total;
     const int off = row_base + block_exclusive_scan(c, sh, rows_total);
     const int toff = tile_base + block_exclusive_scan(nt, sh, tiles_total);
     if (e < E) {
       offsets[e] = off;
+      int run = off;
+      for (int ch = 0; ch < chunks; ++ch) {
+        const int64_t hi = (int64_t)ch * E + e;
+        const int v = hist[hi];
+        hist[hi] = run;
+        run += v;
+      }
       for (int t = 0; t < nt; ++t) {
         TileEntry te;
         te.e = e;
@@ -327,28 +382,43 @@ __global__ __launch_bounds__(kPlanThreads) void bin_plan(const int32_t* __restri
   if (threadIdx.x == 0) *ntiles = tile_base;
 }
 
-__global__ void bin_scatter(const int32_t* __restrict__ ids, int64_t P,
-                            const int32_t* __restrict__ offsets, int32_t* __restrict__ cursor,
-                            int32_t* __restrict__ pos, int32_t* __restrict__ sorted) {
-  const int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
-  if (i >= P) return;
-  const int e = ids[i];
-  const int r = offsets[e] + atomicAdd(&cursor[e], 1);
-  sorted[r] = (int32_t)i;
-  pos[i] = r;
+__global__ __launch_bounds__(kBinThreads) void bin_scatter(const int32_t* __restrict__ ids, int64_t P,
+                                                           int E, const int32_t* __restrict__ first,
+                                                           int32_t* __restrict__ pos,
+                                                           int32_t* __restrict__ sorted) {
+  __shared__ int cur[kBinChunk];
+  int ev[kBinPerThread];
+  bin_load_ids(ids, P, ev);
+  const int32_t* f = first + (int64_t)blockIdx.x * E;
+  const int64_t i0 = (int64_t)blockIdx.x * kBinIds + threadIdx.x;
+  for (int c0 = 0; c0 < E; c0 += kBinChunk) {
+    const int ce = (E - c0) < kBinChunk ? (E - c0) : kBinChunk;
+    for (int e = threadIdx.x; e < ce; e += kBinThreads) cur[e] = f[c0 + e];
+    __syncthreads();
+#pragma unroll
+    for (int q = 0; q < kBinPerThread; ++q)
+      if ((unsigned)(ev[q] - c0) < (unsigned)ce) {
+        const int64_t i = i0 + (int64_t)q * kBinThreads;
+        const int r = atomicAdd(&cur[ev[q] - c0], 1);
+        sorted[r] = (int32_t)i;
+        pos[i] = r;
+      }
+    __syncthreads();
+  }
 }
 
-// x'_slot[r] = (x[token(r)] .* suh[e(r)][slot]) H, one wave per (sorted row,
-// slot), four 128-element blocks at a time (fwht128_x8 layout: lane l holds 8
-// elements of block 4 round + l / 16)
+// x'_slot[r] = (x[token(r)] .* suh[e(r)][slot]) H for both slots, one wave
+// per sorted row.  Lane l holds 8 elements of block 4 pass + l / 16 (the
+// fwht128_x8 layout); the x and sign loads of up to kGuPasses passes
+// (16 blocks, 2048 elements) are all issued before the first transform.
+constexpr int kGuPasses = 4;
+
 __global__ __launch_bounds__(256) void gu_input_transform(
     const uint16_t* __restrict__ x, int topk, int64_t P, int hidden,
     const int32_t* __restrict__ sorted, const int32_t* __restrict__ ids,
     const uint16_t* __restrict__ suh_gu, uint16_t* __restrict__ xg) {
-  const int64_t task = (int64_t)blockIdx.x * 4 + (threadIdx.x >> 6);
-  if (task >= P * 2) return;
-  const int64_t r = task >> 1;
-  const int slot = (int)(task & 1);
+  const int64_t r = (int64_t)blockIdx.x * 4 + (threadIdx.x >> 6);
+  if (r >= P) return;
   const int pair = sorted[r];
   const int e = ids[pair];
   const int64_t tok = pair / topk;
@@ -356,27 +426,49 @@ __global__ __launch_bounds__(256) void gu_input_transform(
   const int g = lane >> 4, j = lane & 15;
   const int nblk = hidden >> 7;
   const uint16_t* xr = x + tok * hidden;
-  const uint16_t* sr = suh_gu + (int64_t)(e * 2 + slot) * hidden;
-  uint16_t* dst = xg + ((int64_t)slot * P + r) * hidden;
-  for (int b0 = 0; b0 < nblk; b0 += 4) {
-    const int b = b0 + g;
-    const int kk = (b < nblk ? b : nblk - 1) * 128 + 8 * j;
-    const uint4 xv = *reinterpret_cast<const uint4*>(xr + kk);
-    const uint4 sv = *reinterpret_cast<const uint4*>(sr + kk);
-    const uint32_t xw[4] = {xv.x, xv.y, xv.z, xv.w};
-    const uint32_t sw[4] = {sv.x, sv.y, sv.z, sv.w};
-    float v[8];
+  const uint16_t* s0 = suh_gu + (int64_t)e * 2 * hidden;
+  const uint16_t* s1 = s0 + hidden;
+  uint16_t* d0 = xg + r * hidden;
+  uint16_t* d1 = xg + (P + r) * hidden;
+  for (int b0 = 0; b0 < nblk; b0 += 4 * kGuPasses) {
+    uint4 xv[kGuPasses], sv0[kGuPasses], sv1[kGuPasses];
 #pragma unroll
-    for (int q = 0; q < 4; ++q) {
-      v[2 * q] = h2f((uint16_t)(xw[q] & 0xFFFF)) * h2f((uint16_t)(sw[q] & 0xFFFF));
-      v[2 * q + 1] = h2f((uint16_t)(xw[q] >> 16)) * h2f((uint16_t)(sw[q] >> 16));
+    for (int q = 0; q < kGuPasses; ++q) {
+      const int b = b0 + 4 * q + g;
+      const int kk = (b < nblk ? b : nblk - 1) * 128 + 8 * j;
+      xv[q] = *reinterpret_cast<const uint4*>(xr + kk);
+      sv0[q] = *reinterpret_cast<const uint4*>(s0 + kk);
+      sv1[q] = *reinterpret_cast<const uint4*>(s1 + kk);
     }
-    fwht128_x8(v);
-    uint32_t o[4];
 #pragma unroll
-    for (int q = 0; q < 4; ++q)
-      o[q] = (uint32_t)f2h(v[2 * q] * kInvSqrt128) | ((uint32_t)f2h(v[2 * q + 1] * kInvSqrt128) << 16);
-    if (b < nblk) *reinterpret_cast<uint4*>(dst + kk) = make_uint4(o[0], o[1], o[2], o[3]);
+    for (int q = 0; q < kGuPasses; ++q) {
+      const int b = b0 + 4 * q + g;
+      const int kk = b * 128 + 8 * j;
+      const uint32_t xw[4] = {xv[q].x, xv[q].y, xv[q].z, xv[q].w};
+      const uint32_t w0[4] = {sv0[q].x, sv0[q].y, sv0[q].z, sv0[q].w};
+      const uint32_t w1[4] = {sv1[q].x, sv1[q].y, sv1[q].z, sv1[q].w};
+      float v0[8], v1[8];
+#pragma unroll
+      for (int c = 0; c < 4; ++c) {
+        const float xa = h2f((uint16_t)(xw[c] & 0xFFFF)), xb = h2f((uint16_t)(xw[c] >> 16));
+        v0[2 * c] = xa * h2f((uint16_t)(w0[c] & 0xFFFF));
+        v0[2 * c + 1] = xb * h2f((uint16_t)(w0[c] >> 16));
+        v1[2 * c] = xa * h2f((uint16_t)(w1[c] & 0xFFFF));
+        v1[2 * c + 1] = xb * h2f((uint16_t)(w1[c] >> 16));
+      }
+      fwht128_x8(v0);
+      fwht128_x8(v1);
+      uint32_t o0[4], o1[4];
+#pragma unroll
+      for (int c = 0; c < 4; ++c) {
+        o0[c] = (uint32_t)f2h(v0[2 * c] * kInvSqrt128) | ((uint32_t)f2h(v0[2 * c + 1] * kInvSqrt128) << 16);
+        o1[c] = (uint32_t)f2h(v1[2 * c] * kInvSqrt128) | ((uint32_t)f2h(v1[2 * c + 1] * kInvSqrt128) << 16);
+      }
+      if (b < nblk) {
+        *reinterpret_cast<uint4*>(d0 + kk) = make_uint4(o0[0], o0[1], o0[2], o0[3]);
+        *reinterpret_cast<uint4*>(d1 + kk) = make_uint4(o1[0], o1[1], o1[2], o1[3]);
+      }
+    }
   }
 }
 
@@ -444,8 +536,16 @@ __global__ __launch_bounds__(256) void combine_rows(const float* __restrict__ d,
   reinterpret_cast<float4*>(y + tok * hidden)[c4] = acc;
 }
 
+// Workgroup -> (tile, slot, 128-column block).  Dispatch hands workgroup b to
+// XCD b % 8, so the grid is laid out for that: group G = (tile, slot), with
+// the slot fastest, belongs to XCD G % 8, and that XCD's workgroups take its
+// groups in order, each across all column blocks.  The column blocks of one
+// group read the same gathered rows, which then come from that XCD's L2
+// instead of once per block; the groups past the tile count (the tile list's
+// length is known on the device only) spread evenly over the XCDs.
 struct GroupedGemmRes {
   static constexpr bool kAFrag = false;  // gathered rows stay row-major
+  static constexpr bool kFineSkip = true;  // tiles end wherever an expert's rows do
   const TileEntry* tiles;
   const int32_t* ntiles;
   const uint16_t* a;       // fp16 [slots][P][k]
@@ -457,9 +557,14 @@ struct GroupedGemmRes {
   int64_t tensor_words;
   float* y;                // fp32 [slots][P][n]
   __device__ GemmTask task() const {
-    const int tile = (int)blockIdx.y, slot = (int)blockIdx.z;
+    const int nbt = n / kGemmBN;
+    const int b = (int)blockIdx.x;
+    const int l = b >> 3;
+    const int gq = l / nbt;
+    const int G = 8 * gq + (b & 7);
+    const int tile = G / slots, slot = G - tile * slots;
     GemmTask T;
-    T.nb = (int)blockIdx.x;
+    T.nb = l - gq * nbt;
     T.valid = tile < *ntiles;
     if (!T.valid) return T;
     const TileEntry te = tiles[tile];
@@ -477,10 +582,13 @@ struct GroupedGemmRes {
 
 template <int K>
 struct GroupedGemmRun {
-  static hipError_t run(const GroupedGemmRes& r, int max_tiles, hipStream_t s) {
-    hipLaunchKernelGGL((gemm_kernel<K, kGroupedBM, true, GroupedGemmRes>),
-                       dim3((r.n + kGemmBN - 1) / kGemmBN, max_tiles, r.slots), dim3(kGemmThreads), 0, s, r,
-                       r.k, r.n);
+  static hipError_t run(const GroupedGemmRes& r, int bm, int max_tiles, hipStream_t s) {
+    const int64_t groups = ((int64_t)max_tiles * r.slots + 7) / 8 * 8;
+    const dim3 grid((unsigned)(groups * (r.n / kGemmBN)));
+    if (bm == 256)
+      hipLaunchKernelGGL((gemm_kernel<K, 256, true, GroupedGemmRes>), grid, dim3(kGemmThreads), 0, s, r, r.k, r.n);
+    else
+      hipLaunchKernelGGL((gemm_kernel<K, 128, true, GroupedGemmRes>), grid, dim3(kGemmThreads), 0, s, r, r.k, r.n);
     return hipGetLastError();
   }
 };
@@ -523,8 +631,7 @@ hipError_t launch_grouped(const ArenaDesc& gu, const ArenaDesc& dn, const uint16
 
   const GemmLayout L = gemm_layout(gu, dn, P);
   const int E = gu.experts;
-  int32_t* counts = reinterpret_cast<int32_t*>(base + L.counts);
-  int32_t* cursor = reinterpret_cast<int32_t*>(base + L.cursor);
+  int32_t* hist = reinterpret_cast<int32_t*>(base + L.hist);
   int32_t* offsets = reinterpret_cast<int32_t*>(base + L.offsets);
   int32_t* ntiles = reinterpret_cast<int32_t*>(base + L.ntiles);
   TileEntry* tiles = reinterpret_cast<TileEntry*>(base + L.tiles);
@@ -535,21 +642,20 @@ hipError_t launch_grouped(const ArenaDesc& gu, const ArenaDesc& dn, const uint16
   uint16_t* xd = reinterpret_cast<uint16_t*>(base + L.xd);
   float* dbuf = reinterpret_cast<float*>(base + L.d);
 
-  hipLaunchKernelGGL(zero_i32, dim3((E + 255) / 256), dim3(256), 0, s, counts, E);
-  hipLaunchKernelGGL(zero_i32, dim3((E + 255) / 256), dim3(256), 0, s, cursor, E);
-  hipLaunchKernelGGL(bin_count, dim3((unsigned)((P + 255) / 256)), dim3(256), 0, s, ids, P, counts);
-  hipLaunchKernelGGL(bin_plan, dim3(1), dim3(kPlanThreads), 0, s, counts, E, kGroupedBM, offsets,
-                     ntiles, tiles);
-  hipLaunchKernelGGL(bin_scatter, dim3((unsigned)((P + 255) / 256)), dim3(256), 0, s, ids, P,
-                     offsets, cursor, pos, sorted);
+  const int64_t chunks = bin_chunks(P);
+  hipLaunchKernelGGL(bin_count, dim3((unsigned)chunks), dim3(kBinThreads), 0, s, ids, P, E, hist);
+  hipLaunchKernelGGL(bin_plan, dim3(1), dim3(kPlanThreads), 0, s, hist, (int)chunks, E, L.bm,
+                     offsets, ntiles, tiles);
+  hipLaunchKernelGGL(bin_scatter, dim3((unsigned)chunks), dim3(kBinThreads), 0, s, ids, P, E, hist,
+                     pos, sorted);
   {
-    const int64_t tasks = P * 2;  // one wave each
+    const int64_t tasks = P;  // one wave each
     hipLaunchKernelGGL(gu_input_transform, dim3((unsigned)((tasks + 3) / 4)), dim3(256), 0, s, x,
                        topk, P, hidden, sorted, ids, gu.suh, xg);
   }
   if ((e = hipGetLastError()) != hipSuccess) return e;
   GroupedGemmRes rg{tiles, ntiles, xg, P, hidden, inter, gu.trellis, gu.svh, 2, words_gu, gbuf};
-  e = dispatch_bits<GroupedGemmRun>(gu.bits, rg, L.max_tiles, s);
+  e = dispatch_bits<GroupedGemmRun>(gu.bits, rg, L.bm, L.max_tiles, s);
   if (e != hipSuccess) return e;
   {
     const int64_t tasks = P;  // one wave each
@@ -558,7 +664,7 @@ hipError_t launch_grouped(const ArenaDesc& gu, const ArenaDesc& dn, const uint16
   }
   if ((e = hipGetLastError()) != hipSuccess) return e;
   GroupedGemmRes rd{tiles, ntiles, xd, P, inter, hidden, dn.trellis, dn.svh, 1, words_dn, dbuf};
-  e = dispatch_bits<GroupedGemmRun>(dn.bits, rd, L.max_tiles, s);
+  e = dispatch_bits<GroupedGemmRun>(dn.bits, rd, L.bm, L.max_tiles, s);
   if (e != hipSuccess) return e;
   {
     const int64_t n4 = t * (hidden / 4);

@@ -48,39 +48,58 @@ __global__ __launch_bounds__(256) void hadamard_kernel(const void* __restrict__ 
 // The dense prefill GEMM's input: x' = (x .* suh) H (fp16 in and out), written
 // fragment-major (kGemmFragBytes): element (r, c) at
 // ((r / 16 * (k / 32) + c / 32) * 64 + 16 ((c % 32) / 8) + r % 16) * 8 + c % 8.
-// Rows m .. m_pad - 1 (up to a multiple of 16) are written as zeros.  One wave
-// per 128-element block, lane l holding elements 2l, 2l + 1 (one 4-byte store).
+// Rows m .. m_pad - 1 (up to a multiple of 16) are written as zeros.
+// One workgroup per (16-row group, 128-element block): wave w transforms rows
+// 4 w .. 4 w + 3 of the group (fwht128_x8 layout, one row per 16 lanes, lane
+// j = l % 16 holding elements 8 j .. 8 j + 7), and the group's output for the
+// block, four whole fragments (4 KB, contiguous), comes from one workgroup:
+// every 128-byte line is written by one CU into one L2.  (A line holds eight
+// rows of the group; with one row per workgroup, lines were assembled from
+// workgroups on different XCDs and went to memory as partial writes.)
 __global__ __launch_bounds__(256) void input_frag_kernel(const uint16_t* __restrict__ x, int64_t ldx,
-                                                         int64_t m, int64_t m_pad, int64_t bpr,
+                                                         int64_t m, int64_t bpr,
                                                          const uint16_t* __restrict__ suh,
                                                          uint16_t* __restrict__ out) {
-  const int64_t task = (int64_t)blockIdx.x * 4 + (threadIdx.x >> 6);
-  if (task >= m_pad * bpr) return;  // whole waves leave together
-  const int64_t row = task / bpr;
-  const int64_t col = (task % bpr) * 128 + 2 * (int64_t)lane_id();
-  float a = 0.f, b = 0.f;
-  if (row < m) {  // uniform per wave
-    const uint32_t v = *reinterpret_cast<const uint32_t*>(x + row * ldx + col);
-    const uint32_t sv = *reinterpret_cast<const uint32_t*>(suh + col);
-    a = h2f((uint16_t)(v & 0xFFFF)) * h2f((uint16_t)(sv & 0xFFFF));
-    b = h2f((uint16_t)(v >> 16)) * h2f((uint16_t)(sv >> 16));
-    fwht128_pair(a, b);
-    a *= kInvSqrt128;
-    b *= kInvSqrt128;
+  const int64_t G = (int64_t)blockIdx.x / bpr;
+  const int64_t b = (int64_t)blockIdx.x - G * bpr;
+  const int wave = (int)(threadIdx.x >> 6), lane = (int)(threadIdx.x & 63);
+  const int r = 4 * wave + (lane >> 4);  // row inside the group
+  const int j = lane & 15;
+  const int64_t row = 16 * G + r;
+  const int64_t col = b * 128 + 8 * j;
+  float v[8];
+  if (row < m) {
+    const uint4 xv = *reinterpret_cast<const uint4*>(x + row * ldx + col);
+    const uint4 sv = *reinterpret_cast<const uint4*>(suh + col);
+    const uint32_t xw[4] = {xv.x, xv.y, xv.z, xv.w};
+    const uint32_t sw[4] = {sv.x, sv.y, sv.z, sv.w};
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      v[2 * e] = h2f((uint16_t)(xw[e] & 0xFFFF)) * h2f((uint16_t)(sw[e] & 0xFFFF));
+      v[2 * e + 1] = h2f((uint16_t)(xw[e] >> 16)) * h2f((uint16_t)(sw[e] >> 16));
+    }
+  } else {
+#pragma unroll
+    for (int e = 0; e < 8; ++e) v[e] = 0.f;
   }
+  fwht128_x8(v);  // every lane of the wave takes part (zero rows included)
+  uint32_t o[4];
+#pragma unroll
+  for (int e = 0; e < 4; ++e)
+    o[e] = (uint32_t)f2h(v[2 * e] * kInvSqrt128) | ((uint32_t)f2h(v[2 * e + 1] * kInvSqrt128) << 16);
+  // 16-byte piece (k block j / 4 of the four, lane group j % 4, row r)
   const int64_t kb = bpr * 4;  // 32-element k blocks per row
-  const int64_t e = ((row >> 4) * kb + (col >> 5)) * 512 + (((col & 31) >> 3) * 16 + (row & 15)) * 8 +
-                    (col & 7);
-  *reinterpret_cast<uint32_t*>(out + e) = (uint32_t)f2h(a) | ((uint32_t)f2h(b) << 16);
+  uint16_t* dst = out + ((G * kb + 4 * b) * 64 + (j >> 2) * 64 + (j & 3) * 16 + r) * 8;
+  *reinterpret_cast<uint4*>(dst) = make_uint4(o[0], o[1], o[2], o[3]);
 }
 
 hipError_t launch_input_frag(const uint16_t* x, int64_t ldx, int64_t m, int64_t k,
                              const uint16_t* suh, uint16_t* out, hipStream_t s) {
   const int64_t bpr = k / 128;
-  const int64_t m_pad = (m + 15) & ~(int64_t)15;
-  const unsigned blocks = (unsigned)((m_pad * bpr + 3) / 4);
+  const int64_t groups = (m + 15) / 16;
+  const unsigned blocks = (unsigned)(groups * bpr);
   if (blocks == 0) return hipSuccess;
-  hipLaunchKernelGGL(input_frag_kernel, dim3(blocks), dim3(256), 0, s, x, ldx, m, m_pad, bpr, suh, out);
+  hipLaunchKernelGGL(input_frag_kernel, dim3(blocks), dim3(256), 0, s, x, ldx, m, bpr, suh, out);
   return hipGetLastError();
 }
 

@@ -17,30 +17,31 @@ namespace exl3 {
 // ---------------------------------------------------------------------------
 // input transform with per-row int8 quantization
 // ---------------------------------------------------------------------------
-// One workgroup of four waves per row.  A wave transforms four 128-element
-// blocks at a time (lane l holds elements 8 (l % 16) .. + 7 of block l / 16,
-// the layout of fwht128_x8).  The row is transformed twice, once for its
-// maximum and once to quantize, instead of being held: k has no upper bound
-// here and the second pass reads the row from L2.
-constexpr int kQuantThreads = 256;
+// One workgroup of 16 waves per 16-row group, wave w on row w of the group,
+// so every 128-byte line of x_q (eight rows of one 16-k piece) is written by
+// one CU into one L2.  A wave transforms four 128-element blocks at a time
+// (lane l holds elements 8 (l % 16) .. + 7 of block l / 16, the layout of
+// fwht128_x8), with the loads of the next four blocks in flight.  The row is
+// transformed twice, once for its maximum and once to quantize, instead of
+// being held: k has no upper bound here and the second pass reads the row
+// from cache.
+constexpr int kQuantThreads = 1024;
 
-__device__ __forceinline__ void quant_block4(const uint16_t* __restrict__ xr,
-                                            const uint16_t* __restrict__ suh, int nb, int b,
-                                            float (&v)[8]) {
-  const int j = (int)(threadIdx.x & 15);
-  if (b < nb) {
-    const uint4 xv = *reinterpret_cast<const uint4*>(xr + b * 128 + 8 * j);
-    const uint4 sv = *reinterpret_cast<const uint4*>(suh + b * 128 + 8 * j);
-    const uint32_t xw[4] = {xv.x, xv.y, xv.z, xv.w};
-    const uint32_t sw[4] = {sv.x, sv.y, sv.z, sv.w};
+__device__ __forceinline__ void quant_load4(const uint16_t* __restrict__ xr,
+                                           const uint16_t* __restrict__ suh, int nb, int b, int j,
+                                           uint4& xv, uint4& sv) {
+  const int bb = b < nb ? b : nb - 1;  // past the end: re-read the last block (unused)
+  xv = *reinterpret_cast<const uint4*>(xr + bb * 128 + 8 * j);
+  sv = *reinterpret_cast<const uint4*>(suh + bb * 128 + 8 * j);
+}
+
+__device__ __forceinline__ void quant_transform4(const uint4& xv, const uint4& sv, float (&v)[8]) {
+  const uint32_t xw[4] = {xv.x, xv.y, xv.z, xv.w};
+  const uint32_t sw[4] = {sv.x, sv.y, sv.z, sv.w};
 #pragma unroll
-    for (int e = 0; e < 4; ++e) {
-      v[2 * e] = h2f((uint16_t)(xw[e] & 0xFFFF)) * h2f((uint16_t)(sw[e] & 0xFFFF));
-      v[2 * e + 1] = h2f((uint16_t)(xw[e] >> 16)) * h2f((uint16_t)(sw[e] >> 16));
-    }
-  } else {
-#pragma unroll
-    for (int e = 0; e < 8; ++e) v[e] = 0.f;
+  for (int e = 0; e < 4; ++e) {
+    v[2 * e] = h2f((uint16_t)(xw[e] & 0xFFFF)) * h2f((uint16_t)(sw[e] & 0xFFFF));
+    v[2 * e + 1] = h2f((uint16_t)(xw[e] >> 16)) * h2f((uint16_t)(sw[e] >> 16));
   }
   fwht128_x8(v);
 #pragma unroll
@@ -52,9 +53,8 @@ __device__ __forceinline__ void quant_block4(const uint16_t* __restrict__ xr,
 __global__ __launch_bounds__(kQuantThreads) void quant_rows_kernel(
     const uint16_t* __restrict__ x, int64_t ldx, const uint16_t* __restrict__ suh, int k, int64_t m,
     int8_t* __restrict__ xq, float* __restrict__ scale) {
-  __shared__ float wmax[kQuantThreads / 64];
-  const int64_t row = blockIdx.x;
   const int wave = (int)(threadIdx.x >> 6), lane = (int)(threadIdx.x & 63);
+  const int64_t row = (int64_t)blockIdx.x * 16 + wave;
   const int nb = k / 128;
   // fragment-major destination of this lane's 8 bytes (elements
   // 128 b + 8 jj .. + 7, jj = lane % 16): 64-k block 2 b + jj / 8, lane group
@@ -63,32 +63,41 @@ __global__ __launch_bounds__(kQuantThreads) void quant_rows_kernel(
   int8_t* qbase = xq + ((row >> 4) * (k / kGemmI8BK) * 64 + 16 * ((jj & 7) >> 1) + (row & 15)) * 16 +
                   8 * (jj & 1);
   auto qdst = [&](int b) { return qbase + (int64_t)(2 * b + (jj >> 3)) * kI8FragBytes; };
-  if (row >= m) {  // padding row of the last 16-row group
-    for (int b0 = 4 * wave; b0 < nb; b0 += 16) {
+  if (row >= m) {  // padding row of the last 16-row group (uniform per wave)
+    for (int b0 = 0; b0 < nb; b0 += 4) {
       const int b = b0 + (lane >> 4);
       if (b < nb) *reinterpret_cast<uint2*>(qdst(b)) = make_uint2(0u, 0u);
     }
-    if (threadIdx.x == 0) scale[row] = 0.f;
+    if (lane == 0) scale[row] = 0.f;
     return;
   }
   const uint16_t* xr = x + row * ldx;
   float amax = 0.f;
-  for (int b0 = 4 * wave; b0 < nb; b0 += 16) {
+  uint4 xv, sv;
+  quant_load4(xr, suh, nb, lane >> 4, jj, xv, sv);
+  for (int b0 = 0; b0 < nb; b0 += 4) {
+    uint4 xn, sn;
+    quant_load4(xr, suh, nb, b0 + 4 + (lane >> 4), jj, xn, sn);
     float v[8];
-    quant_block4(xr, suh, nb, b0 + (lane >> 4), v);
+    quant_transform4(xv, sv, v);
+    if (b0 + (lane >> 4) < nb) {
 #pragma unroll
-    for (int e = 0; e < 8; ++e) amax = fmaxf(amax, fabsf(v[e]));
+      for (int e = 0; e < 8; ++e) amax = fmaxf(amax, fabsf(v[e]));
+    }
+    xv = xn;
+    sv = sn;
   }
 #pragma unroll
   for (int msk = 32; msk >= 1; msk >>= 1) amax = fmaxf(amax, shfl_xor_f(amax, msk));
-  if (lane == 0) wmax[wave] = amax;
-  __syncthreads();
-  const float a = fmaxf(fmaxf(wmax[0], wmax[1]), fmaxf(wmax[2], wmax[3]));
+  const float a = amax;
   const float inv = a > 0.f ? 127.0f / a : 0.f;
-  for (int b0 = 4 * wave; b0 < nb; b0 += 16) {
+  quant_load4(xr, suh, nb, lane >> 4, jj, xv, sv);
+  for (int b0 = 0; b0 < nb; b0 += 4) {
+    uint4 xn, sn;
+    quant_load4(xr, suh, nb, b0 + 4 + (lane >> 4), jj, xn, sn);
     const int b = b0 + (lane >> 4);
     float v[8];
-    quant_block4(xr, suh, nb, b, v);
+    quant_transform4(xv, sv, v);
     uint32_t w[2] = {0u, 0u};
 #pragma unroll
     for (int e = 0; e < 8; ++e) {
@@ -96,8 +105,10 @@ __global__ __launch_bounds__(kQuantThreads) void quant_rows_kernel(
       w[e >> 2] |= ((uint32_t)(int32_t)qf & 0xFFu) << (8 * (e & 3));
     }
     if (b < nb) *reinterpret_cast<uint2*>(qdst(b)) = make_uint2(w[0], w[1]);
+    xv = xn;
+    sv = sn;
   }
-  if (threadIdx.x == 0) scale[row] = a / 127.0f;
+  if (lane == 0) scale[row] = a / 127.0f;
 }
 
 // ---------------------------------------------------------------------------
@@ -191,7 +202,7 @@ hipError_t launch_linear_int8(const uint16_t* trellis, const uint16_t* suh, cons
   unsigned char* base = static_cast<unsigned char*>(ws);
   int8_t* xq = reinterpret_cast<int8_t*>(base);
   float* sc = reinterpret_cast<float*>(base + i8_scale_offset(k, m));
-  hipLaunchKernelGGL(quant_rows_kernel, dim3((unsigned)i8_rows(m)), dim3(kQuantThreads), 0, s, x, ldx,
+  hipLaunchKernelGGL(quant_rows_kernel, dim3((unsigned)(i8_rows(m) / 16)), dim3(kQuantThreads), 0, s, x, ldx,
                      suh, k, m, xq, sc);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;

@@ -46,7 +46,17 @@ def test_random_routing(t):
     assert err < TOL, err
 
 
-@pytest.mark.parametrize("t", [3, 40, 200])
+# 256-row tiles serve calls whose experts average at least 96 rows: one tile
+# (t = 200 on 8 experts, ~100 rows each) or several with a short last one
+# (t = 700, ~350 rows), so waves run with 1..4 of their four row groups
+@pytest.mark.parametrize("t", [200, 700])
+def test_random_routing_large_tiles(t):
+    m = _small(t, experts=8, seed=47)
+    err = O.rel_frobenius(_run(m), _ref(m))
+    assert err < TOL, err
+
+
+@pytest.mark.parametrize("t", [3, 40, 200, 700])
 def test_all_tokens_same_experts(t):
     m = _small(t)
     ids = np.tile(np.array([5, 1, 9, 0], np.int32), (t, 1))
