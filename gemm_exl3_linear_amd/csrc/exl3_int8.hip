@@ -3,7 +3,8 @@
 // Hadamard, weights one static scale inside the decode, the product runs in
 // int8 with both scales applied and writes fp16).
 //
-//   quant_rows_kernel  x' = (x .* suh) H_k in fp32 per row, a = max |x'|,
+//   quant_groups_kernel / quant_rows_kernel
+//                      x' = (x .* suh) H_k in fp32 per row, a = max |x'|,
 //                      x_q = RNE(127 x' / a) (int8, fragment-major) and a / 127.
 //   gemm_i8_kernel     decode to int8 + v_mfma_i32_16x16x64_i8, epilogue with
 //                      both scales, the output transform, svh, bias, cast.
@@ -17,15 +18,23 @@ namespace exl3 {
 // ---------------------------------------------------------------------------
 // input transform with per-row int8 quantization
 // ---------------------------------------------------------------------------
-// One workgroup of 16 waves per 16-row group, wave w on row w of the group,
-// so every 128-byte line of x_q (eight rows of one 16-k piece) is written by
-// one CU into one L2.  A wave transforms four 128-element blocks at a time
-// (lane l holds elements 8 (l % 16) .. + 7 of block l / 16, the layout of
-// fwht128_x8), with the loads of the next four blocks in flight.  The row is
-// transformed twice, once for its maximum and once to quantize, instead of
-// being held: k has no upper bound here and the second pass reads the row
-// from cache.
-constexpr int kQuantThreads = 1024;
+// Two launch shapes of one computation (the same per-element arithmetic and
+// the same maximum, so their outputs are identical):
+//   quant_groups_kernel (m >= kQuantGroupMinRows): one workgroup of 16 waves
+//     per 16-row group, wave w on row w of the group, so every 128-byte line
+//     of x_q (eight rows of one 16-k piece) is written by one CU into one L2;
+//   quant_rows_kernel (smaller m): one workgroup of four waves per row, four
+//     times the waves for batches too small to fill the GPU with groups.
+// A wave transforms four 128-element blocks at a time (lane l holds elements
+// 8 (l % 16) .. + 7 of block l / 16, the layout of fwht128_x8), with the
+// loads of the next four blocks in flight.  The row is transformed twice,
+// once for its maximum and once to quantize, instead of being held: k has no
+// upper bound here and the second pass reads the row from cache.
+// Measured on MI355X (k = 5120, n = 17408, K = 4, whole int8 linear): m = 4096
+// 0.498 ms by groups against 0.512 by rows; m = 1000 0.191 against 0.181.
+constexpr int kQuantGroupMinRows = 2048;
+constexpr int kQuantGroupThreads = 1024;
+constexpr int kQuantRowThreads = 256;
 
 __device__ __forceinline__ void quant_load4(const uint16_t* __restrict__ xr,
                                            const uint16_t* __restrict__ suh, int nb, int b, int j,
@@ -48,67 +57,106 @@ __device__ __forceinline__ void quant_transform4(const uint4& xv, const uint4& s
   for (int e = 0; e < 8; ++e) v[e] *= kInvSqrt128;
 }
 
-// Rows m .. m_pad - 1 (up to the next multiple of 16) are written as zeros
-// with scale 0, so every 16-row group of x_q is complete.
-__global__ __launch_bounds__(kQuantThreads) void quant_rows_kernel(
-    const uint16_t* __restrict__ x, int64_t ldx, const uint16_t* __restrict__ suh, int k, int64_t m,
-    int8_t* __restrict__ xq, float* __restrict__ scale) {
-  const int wave = (int)(threadIdx.x >> 6), lane = (int)(threadIdx.x & 63);
-  const int64_t row = (int64_t)blockIdx.x * 16 + wave;
-  const int nb = k / 128;
-  // fragment-major destination of this lane's 8 bytes (elements
-  // 128 b + 8 jj .. + 7, jj = lane % 16): 64-k block 2 b + jj / 8, lane group
-  // (jj % 8) / 2 of the fragment, byte 8 (jj % 2) of its 16
-  const int jj = lane & 15;
-  int8_t* qbase = xq + ((row >> 4) * (k / kGemmI8BK) * 64 + 16 * ((jj & 7) >> 1) + (row & 15)) * 16 +
-                  8 * (jj & 1);
-  auto qdst = [&](int b) { return qbase + (int64_t)(2 * b + (jj >> 3)) * kI8FragBytes; };
-  if (row >= m) {  // padding row of the last 16-row group (uniform per wave)
-    for (int b0 = 0; b0 < nb; b0 += 4) {
-      const int b = b0 + (lane >> 4);
-      if (b < nb) *reinterpret_cast<uint2*>(qdst(b)) = make_uint2(0u, 0u);
-    }
-    if (lane == 0) scale[row] = 0.f;
-    return;
+// Fragment-major destination of lane `lane`'s 8 bytes of row `row` (elements
+// 128 b + 8 jj .. + 7, jj = lane % 16): 64-k block 2 b + jj / 8, lane group
+// (jj % 8) / 2 of the fragment, byte 8 (jj % 2) of its 16.
+struct QuantDst {
+  int8_t* base;
+  int jj;
+  __device__ QuantDst(int8_t* xq, int64_t row, int k, int lane) {
+    jj = lane & 15;
+    base = xq + ((row >> 4) * (k / kGemmI8BK) * 64 + 16 * ((jj & 7) >> 1) + (row & 15)) * 16 + 8 * (jj & 1);
   }
-  const uint16_t* xr = x + row * ldx;
+  __device__ int8_t* at(int b) const { return base + (int64_t)(2 * b + (jj >> 3)) * kI8FragBytes; }
+};
+
+// Blocks b0 + lane / 16 for b0 = first, first + stride, ...: the maximum of
+// |x'| (quantize = false) or the codes written with 127 / a (quantize = true).
+template <bool QUANT>
+__device__ __forceinline__ float quant_pass(const uint16_t* __restrict__ xr,
+                                            const uint16_t* __restrict__ suh, int nb, int first,
+                                            int stride, float inv, const QuantDst& dst) {
+  const int lane = (int)lane_id();
+  const int jj = lane & 15;
   float amax = 0.f;
   uint4 xv, sv;
-  quant_load4(xr, suh, nb, lane >> 4, jj, xv, sv);
-  for (int b0 = 0; b0 < nb; b0 += 4) {
+  quant_load4(xr, suh, nb, first + (lane >> 4), jj, xv, sv);
+  for (int b0 = first; b0 < nb; b0 += stride) {
     uint4 xn, sn;
-    quant_load4(xr, suh, nb, b0 + 4 + (lane >> 4), jj, xn, sn);
+    quant_load4(xr, suh, nb, b0 + stride + (lane >> 4), jj, xn, sn);
+    const int b = b0 + (lane >> 4);
     float v[8];
     quant_transform4(xv, sv, v);
-    if (b0 + (lane >> 4) < nb) {
+    if constexpr (QUANT) {
+      uint32_t w[2] = {0u, 0u};
+#pragma unroll
+      for (int e = 0; e < 8; ++e) {
+        const float qf = fminf(fmaxf(rintf(v[e] * inv), -127.f), 127.f);
+        w[e >> 2] |= ((uint32_t)(int32_t)qf & 0xFFu) << (8 * (e & 3));
+      }
+      if (b < nb) *reinterpret_cast<uint2*>(dst.at(b)) = make_uint2(w[0], w[1]);
+    } else if (b < nb) {
 #pragma unroll
       for (int e = 0; e < 8; ++e) amax = fmaxf(amax, fabsf(v[e]));
     }
     xv = xn;
     sv = sn;
   }
+  return amax;
+}
+
+__device__ __forceinline__ void quant_zero_row(int nb, int first, int stride, const QuantDst& dst) {
+  for (int b0 = first; b0 < nb; b0 += stride) {
+    const int b = b0 + (int)(lane_id() >> 4);
+    if (b < nb) *reinterpret_cast<uint2*>(dst.at(b)) = make_uint2(0u, 0u);
+  }
+}
+
+// Rows m .. m_pad - 1 (up to the next multiple of 16) are written as zeros
+// with scale 0, so every 16-row group of x_q is complete.
+__global__ __launch_bounds__(kQuantGroupThreads) void quant_groups_kernel(
+    const uint16_t* __restrict__ x, int64_t ldx, const uint16_t* __restrict__ suh, int k, int64_t m,
+    int8_t* __restrict__ xq, float* __restrict__ scale) {
+  const int wave = (int)(threadIdx.x >> 6), lane = (int)(threadIdx.x & 63);
+  const int64_t row = (int64_t)blockIdx.x * 16 + wave;
+  const int nb = k / 128;
+  const QuantDst dst(xq, row, k, lane);
+  if (row >= m) {  // padding row of the last 16-row group (uniform per wave)
+    quant_zero_row(nb, 0, 4, dst);
+    if (lane == 0) scale[row] = 0.f;
+    return;
+  }
+  const uint16_t* xr = x + row * ldx;
+  float amax = quant_pass<false>(xr, suh, nb, 0, 4, 0.f, dst);
 #pragma unroll
   for (int msk = 32; msk >= 1; msk >>= 1) amax = fmaxf(amax, shfl_xor_f(amax, msk));
   const float a = amax;
-  const float inv = a > 0.f ? 127.0f / a : 0.f;
-  quant_load4(xr, suh, nb, lane >> 4, jj, xv, sv);
-  for (int b0 = 0; b0 < nb; b0 += 4) {
-    uint4 xn, sn;
-    quant_load4(xr, suh, nb, b0 + 4 + (lane >> 4), jj, xn, sn);
-    const int b = b0 + (lane >> 4);
-    float v[8];
-    quant_transform4(xv, sv, v);
-    uint32_t w[2] = {0u, 0u};
-#pragma unroll
-    for (int e = 0; e < 8; ++e) {
-      const float qf = fminf(fmaxf(rintf(v[e] * inv), -127.f), 127.f);
-      w[e >> 2] |= ((uint32_t)(int32_t)qf & 0xFFu) << (8 * (e & 3));
-    }
-    if (b < nb) *reinterpret_cast<uint2*>(qdst(b)) = make_uint2(w[0], w[1]);
-    xv = xn;
-    sv = sn;
-  }
+  quant_pass<true>(xr, suh, nb, 0, 4, a > 0.f ? 127.0f / a : 0.f, dst);
   if (lane == 0) scale[row] = a / 127.0f;
+}
+
+__global__ __launch_bounds__(kQuantRowThreads) void quant_rows_kernel(
+    const uint16_t* __restrict__ x, int64_t ldx, const uint16_t* __restrict__ suh, int k, int64_t m,
+    int8_t* __restrict__ xq, float* __restrict__ scale) {
+  __shared__ float wmax[kQuantRowThreads / 64];
+  const int64_t row = blockIdx.x;
+  const int wave = (int)(threadIdx.x >> 6), lane = (int)(threadIdx.x & 63);
+  const int nb = k / 128;
+  const QuantDst dst(xq, row, k, lane);
+  if (row >= m) {  // padding row (uniform per workgroup)
+    quant_zero_row(nb, 4 * wave, 16, dst);
+    if (threadIdx.x == 0) scale[row] = 0.f;
+    return;
+  }
+  const uint16_t* xr = x + row * ldx;
+  float amax = quant_pass<false>(xr, suh, nb, 4 * wave, 16, 0.f, dst);
+#pragma unroll
+  for (int msk = 32; msk >= 1; msk >>= 1) amax = fmaxf(amax, shfl_xor_f(amax, msk));
+  if (lane == 0) wmax[wave] = amax;
+  __syncthreads();
+  const float a = fmaxf(fmaxf(wmax[0], wmax[1]), fmaxf(wmax[2], wmax[3]));
+  quant_pass<true>(xr, suh, nb, 4 * wave, 16, a > 0.f ? 127.0f / a : 0.f, dst);
+  if (threadIdx.x == 0) scale[row] = a / 127.0f;
 }
 
 // ---------------------------------------------------------------------------
@@ -202,8 +250,12 @@ hipError_t launch_linear_int8(const uint16_t* trellis, const uint16_t* suh, cons
   unsigned char* base = static_cast<unsigned char*>(ws);
   int8_t* xq = reinterpret_cast<int8_t*>(base);
   float* sc = reinterpret_cast<float*>(base + i8_scale_offset(k, m));
-  hipLaunchKernelGGL(quant_rows_kernel, dim3((unsigned)(i8_rows(m) / 16)), dim3(kQuantThreads), 0, s, x, ldx,
-                     suh, k, m, xq, sc);
+  if (m >= kQuantGroupMinRows)
+    hipLaunchKernelGGL(quant_groups_kernel, dim3((unsigned)(i8_rows(m) / 16)), dim3(kQuantGroupThreads), 0, s,
+                       x, ldx, suh, k, m, xq, sc);
+  else
+    hipLaunchKernelGGL(quant_rows_kernel, dim3((unsigned)i8_rows(m)), dim3(kQuantRowThreads), 0, s, x, ldx,
+                       suh, k, m, xq, sc);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
   const int bm = choose_bm_i8(m);

@@ -81,6 +81,20 @@ def test_linear_int8_rows_independent_bit_exact():
         np.testing.assert_array_equal(G.f16_bits(_run8(d, m=m)), full[:m])
 
 
+def test_linear_int8_quant_shapes_agree():
+    # from 2048 rows on the activations are quantized one 16-row group per
+    # workgroup, below one row per workgroup; both do the same arithmetic, so
+    # the rows of a short batch equal those of a long one bit for bit, and the
+    # long batch (2050 rows: its last group is two rows) matches the oracle
+    d = G.linear_case(826, 2050, 512, 256, 3)
+    full = _run8(d)
+    np.testing.assert_array_equal(G.f16_bits(_run8(d, m=1000)), G.f16_bits(full)[:1000])
+    rows = np.r_[0:8, 1020:1030, 2040:2050]
+    y = full.double().cpu().numpy()[rows]
+    ref = O.linear_int8(d["x"][rows], d["trellis"], d["suh"], d["svh"], 3)
+    assert O.rel_frobenius(y, ref) < TOL8
+
+
 def test_linear_int8_sign_and_zero_rows():
     import torch
     d = G.linear_case(822, 96, 256, 384, 5)
