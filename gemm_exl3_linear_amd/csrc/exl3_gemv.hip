@@ -102,9 +102,9 @@ static void sk_split_extent(const SkSplit& s, int64_t KT, int64_t NB, int64_t W,
 // 256-CU MI355X; more when runs would exceed kSkMaxRun row steps, fewer for
 // small tensors), their runs, the number of partial slots a block can
 // receive, and the workspace (fp32 partials, then the transformed activations
-// when m > 1).  For 2 <= m <= 16 the plan depends on (k, n) only, so all of
-// them see the same summation order; m == 1 (v_dot2, whose rounding order
-// differs anyway) takes the two-tier runs.  No device query.
+// on the MFMA path).  Within each path (v_dot2 for m <= kSkDotMaxRows, MFMA
+// above) the plan depends on (k, n) only, so all m of a path see the same
+// summation order; the dot path takes the two-tier runs.  No device query.
 GemvPlan plan_gemv(int k, int n, int m) {
   GemvPlan p;
   const int64_t KT = k / 16, NB = n / 128, R = KT * NB;
@@ -112,13 +112,14 @@ GemvPlan plan_gemv(int k, int n, int m) {
   if (W < (R + kSkMaxRun - 1) / kSkMaxRun) W = (R + kSkMaxRun - 1) / kSkMaxRun;
   W = (W + 3) / 4 * 4;
   if (W > R) W = (R + 3) / 4 * 4;  // runs of at least one row step (extra waves idle)
-  p.split = make_sk_split(R, W, m == 1 ? sk_first_round(0, W, W) : W);
+  const bool dot = m <= kSkDotMaxRows;
+  p.split = make_sk_split(R, W, dot ? sk_first_round(0, W, W) : W);
   p.splits = (int)W;
   sk_split_extent(p.split, KT, NB, W, p.slots, p.kc);
   p.lds = 0;
   p.ctr_bytes = 0;
   p.xprep_off = (((size_t)NB * p.slots * m * 128 * sizeof(float) + 255) & ~(size_t)255);
-  p.ws = p.xprep_off + (m > 1 ? (size_t)m * k * sizeof(uint16_t) : 0);
+  p.ws = p.xprep_off + (dot ? 0 : (size_t)m * k * sizeof(uint16_t));
   return p;
 }
 
@@ -127,9 +128,15 @@ struct SkRun {
   static hipError_t run(const SkArgs& a, const GemvPlan& plan, hipStream_t s) {
     const dim3 grid((unsigned)(a.W / 4));
     if (a.m == 1)
-      hipLaunchKernelGGL((gemv_sk_kernel<K, true, 4>), grid, dim3(256), 0, s, a);
+      hipLaunchKernelGGL((gemv_sk_kernel<K, 1, 4>), grid, dim3(256), 0, s, a);
+    else if (a.m == 2)
+      hipLaunchKernelGGL((gemv_sk_kernel<K, 2, 4>), grid, dim3(256), 0, s, a);
+    else if (a.m == 3)
+      hipLaunchKernelGGL((gemv_sk_kernel<K, 3, 4>), grid, dim3(256), 0, s, a);
+    else if (a.m == 4)
+      hipLaunchKernelGGL((gemv_sk_kernel<K, 4, 4>), grid, dim3(256), 0, s, a);
     else
-      hipLaunchKernelGGL((gemv_sk_kernel<K, false, 8>), grid, dim3(256), 0, s, a);
+      hipLaunchKernelGGL((gemv_sk_kernel<K, 0, 8>), grid, dim3(256), 0, s, a);
     const hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
     const int tasks = (a.n / 128) * a.m;  // one 64-thread workgroup each
@@ -144,9 +151,9 @@ hipError_t launch_gemv(const uint16_t* trellis, const uint16_t* suh, const uint1
                        const GemvPlan& plan, hipStream_t s) {
   unsigned char* base = static_cast<unsigned char*>(ws);
   uint16_t* xprep = nullptr;
-  if (m > 1) {
-    // several rows: one input-transform launch for all of them, instead of
-    // every workgroup transforming the blocks it needs
+  if (m > kSkDotMaxRows) {
+    // the MFMA path: one input-transform launch for all rows, instead of
+    // every wave transforming the blocks it needs
     xprep = reinterpret_cast<uint16_t*>(base + plan.xprep_off);
     const hipError_t e = launch_hadamard(x, false, xprep, false, m, k, ldx, k, suh, nullptr, s);
     if (e != hipSuccess) return e;

@@ -7,32 +7,34 @@
 // other: each keeps PF row-pair loads in flight from the start to the end of
 // its run, across block boundaries.
 //
-// At m == 1 run lengths come in two tiers (SkSplit).  With two waves per
+// Up to kSkDotMaxRows rows contract on the vector units (v_dot2), more on the
+// matrix cores.  On the dot path run lengths come in two tiers (SkSplit).
+// With two waves per
 // SIMD, the wave dispatched in the first round (one per SIMD, the lower wave
 // ids) is the older one and wins the instruction arbiter whenever both are
 // ready; measured on MI355X at 5120 x 17408, it completes about 1.9 times the
 // row steps of its younger partner in the same time, so equal runs leave the
 // younger waves finishing alone.  The first-round waves therefore take runs
 // kSkTierWeight1 / kSkTierWeight2 times longer than the rest (1 to 9 % less
-// time per call at 5120 x 17408 across K = 1..8, most at K = 3..6).  The MFMA kernel (m >= 2) gained nothing from
-// it and keeps equal runs.  The split is part of the plan (a function of k, n,
-// m == 1 and the grid only), never of timing.
+// time per call at 5120 x 17408 across K = 1..8, most at K = 3..6).  The MFMA
+// kernel gained nothing from it and keeps equal runs.  The split is part of
+// the plan (a function of k, n, the path and the grid only), never of timing.
 //
 // gemv_sk_kernel, per wave:
-//   1. m == 1: x' = (x .* suh) H for the (at most eight) k blocks its run
-//      touches, four blocks at a time, after the first trellis loads went out;
-//      m > 1: x' comes from one input-transform launch and each row step's
-//      A fragment travels with the trellis loads.
+//   1. dot path: x' = (x .* suh) H of every row for the (at most eight) k
+//      blocks its run touches, four blocks at a time, after the first trellis
+//      loads went out; MFMA path: x' comes from one input-transform launch and
+//      each row step's A fragment travels with the trellis loads.
 //   2. Row step: lane (t, p) loads row pair p of n tile t (one coalesced
 //      4K-byte load per lane) and the first dword of the next row pair (its
 //      spill word), decodes 32 weights into k-pairs of biased codes
 //      b = 1024 + sigma (decode_rowpair<K, true>) and contracts:
-//        m == 1 : v_dot2_f32_f16 with the x' pair of its two rows, 16 column
-//                 accumulators per lane;
-//        m >= 2 : k-pairs through a per-wave LDS transpose into MFMA
-//                 16x16x16 f16 (rows padded to 16).
-//      alongside, the sum of the segment's x' (a dot with ones at m == 1, a
-//      ninth MFMA against an all-ones B at m >= 2).
+//        dot  : v_dot2_f32_f16 with each row's x' pair of its two k rows, 16
+//               column accumulators per lane and row;
+//        MFMA : k-pairs through a per-wave LDS transpose into MFMA 16x16x16
+//               f16 (rows padded to 16).
+//      alongside, the sum of the segment's x' (a dot with ones per row, or a
+//      ninth MFMA against an all-ones B).
 //   3. Segment end (block changes or run ends): sum b x' - 1534 sum x' for
 //      each column goes to the segment's partial slot in the fp32 workspace
 //      (the codebook scale 1775 / 2^18 is applied once, in the finish).
@@ -43,8 +45,8 @@
 // (the L2 of one XCD does not see another XCD's writes before a device-scope
 // release, which at kernel granularity costs nothing extra).
 // The sums never depend on timing, so results are bit-reproducible; the plan
-// depends on (k, n) only, so a row's arithmetic does not depend on m within
-// the MFMA range (2..16).
+// depends on (k, n) and the path only and a row's sums on its own x only, so
+// a row's result does not depend on m within either range (1..4, 5..16).
 #pragma once
 
 #include "exl3_device.hpp"
@@ -58,14 +60,15 @@ constexpr int kSkTierWeight1 = 13;    // relative run length, first-round waves
 constexpr int kSkTierWeight2 = 7;     // relative run length, the others
 constexpr int kSkMaxRun = 48;         // longest run (the x' region of a wave)
 constexpr int kSkSlotBatch = 8;     // partial slots per lane loaded per batch in the finish
-constexpr int kSkMaxXBlocks = 8;    // k blocks a run may touch (m == 1)
+constexpr int kSkMaxXBlocks = 8;    // k blocks a run may touch (dot path)
+constexpr int kSkDotMaxRows = 4;    // rows served by the v_dot2 path (one kernel per row count)
 
 struct SkArgs {
   const uint16_t* trellis;  // [k/16][n/16][16K]
   const uint16_t* suh;      // fp16 [k]
   const uint16_t* x;        // fp16 [m][ldx]
   int64_t ldx;
-  const uint16_t* xprep;    // fp16 [m][k] already transformed (m > 1), else nullptr
+  const uint16_t* xprep;    // fp16 [m][k] already transformed (MFMA path), else nullptr
   int m;
   int k, n;
   int KT;                   // k / 16
@@ -114,8 +117,8 @@ __device__ __forceinline__ void reduce_rowpairs(float (&acc)[16], float& c0, flo
   }
 }
 
-// LDS per wave: m == 1: x' blocks [kSkMaxXBlocks][128] fp16 (2 KB);
-// m >= 2: transpose region [8 n tiles][8 row pairs][20] dwords (5 KB)
+// LDS per wave: dot path: x' blocks [kSkMaxXBlocks][128] fp16 (2 KB) per row;
+// MFMA path: transpose region [8 n tiles][8 row pairs][20] dwords (5 KB)
 constexpr int kSkWaveLdsDot = kSkMaxXBlocks * 128 * 2;
 constexpr int kSkWaveLdsMfma = 64 * 20 * 4;
 // a run of kSkMaxRun steps starting anywhere in a k block fits the x' region
@@ -123,8 +126,12 @@ static_assert(32 * (kSkMaxRun + 8) + 32 <= kSkWaveLdsDot, "x' region too small")
 static_assert((7 + kSkMaxRun + 7) / 8 <= kSkMaxXBlocks, "run touches too many k blocks");
 
 // The work of wave `wid` of a tensor's grid; wl is the wave's LDS region.
-template <int K, bool DOT, int PF>
+// MR > 0: the v_dot2 contraction for up to MR activation rows (x' of row i in
+// the wave's i-th kSkWaveLdsDot region); MR = 0: the matrix-core contraction.
+template <int K, int MR, int PF>
 __device__ __forceinline__ void sk_run(const SkArgs& a, int wid, unsigned char* wl) {
+  constexpr bool DOT = MR > 0;
+  constexpr int NR = DOT ? MR : 1;  // dot-path row slots
   const int len = sk_run_len(a.sp, wid);
   if (len <= 0) return;
   const int r0 = sk_run_start(a.sp, wid);
@@ -154,7 +161,7 @@ __device__ __forceinline__ void sk_run(const SkArgs& a, int wid, unsigned char* 
   int pf_nb = nb0, pf_kt = kt0, pf_left = len;
   uint32_t pf_soff = (uint32_t)kt0 * kt_bytes;
   __amdgpu_buffer_rsrc_t pf_rs = make_rsrc(tr0 + (int64_t)pf_nb * kBlkBytes, col_bytes);
-  // m >= 2: the A fragment of a row step, x'[j][16 kt + 4 g .. + 3]
+  // MFMA path: the A fragment of a row step, x'[j][16 kt + 4 g .. + 3]
   __amdgpu_buffer_rsrc_t x_rs = make_rsrc(a.xprep, DOT ? 0u : (uint32_t)m * a.k * 2);
   const uint32_t x_voff = (uint32_t)(((j < m ? j : 0) * a.k + 4 * g) * 2);
   auto pf_load = [&](uint32_t (&D)[K + 1], uint2& A) {
@@ -180,11 +187,11 @@ __device__ __forceinline__ void sk_run(const SkArgs& a, int wid, unsigned char* 
     }
   };
 
-  // ---- m == 1: x and suh of the k blocks the run touches go out first: k
+  // ---- dot path: x and suh of the k blocks the run touches go out first: k
   // block b of the run is (kt0 / 8 + b) mod k/128; lane l loads 8 elements of
-  // run block l / 16 (first round) and 4 + l / 16 (second round).
+  // run block l / 16 (first round) and 4 + l / 16 (second round), of every row.
   const int nblk = ((kt0 & 7) + len + 7) >> 3;
-  uint4 xv[DOT ? 2 : 1], sv[DOT ? 2 : 1];
+  uint4 xv[NR][DOT ? 2 : 1], sv[DOT ? 2 : 1];
   if constexpr (DOT) {
     const int kb0 = kt0 >> 3, KBn = KT >> 3;
 #pragma unroll
@@ -192,8 +199,10 @@ __device__ __forceinline__ void sk_run(const SkArgs& a, int wid, unsigned char* 
       const int b = 4 * rd + g;
       const int bb = b < nblk ? b : nblk - 1;
       const int kk = ((kb0 + bb) % KBn) * 128 + 8 * j;
-      xv[rd] = *reinterpret_cast<const uint4*>(a.x + kk);
       sv[rd] = *reinterpret_cast<const uint4*>(a.suh + kk);
+#pragma unroll
+      for (int i = 0; i < NR; ++i)  // rows past m read row 0 (their sums are not stored)
+        xv[i][rd] = *reinterpret_cast<const uint4*>(a.x + (i < m ? i : 0) * a.ldx + kk);
     }
   }
 
@@ -206,25 +215,28 @@ __device__ __forceinline__ void sk_run(const SkArgs& a, int wid, unsigned char* 
   }
 
   if constexpr (DOT) {
-    uint16_t* xs = reinterpret_cast<uint16_t*>(wl);
 #pragma unroll
-    for (int rd = 0; rd < 2; ++rd) {
-      if (4 * rd < nblk) {
-        const uint32_t xw[4] = {xv[rd].x, xv[rd].y, xv[rd].z, xv[rd].w};
-        const uint32_t sw[4] = {sv[rd].x, sv[rd].y, sv[rd].z, sv[rd].w};
-        float v[8];
+    for (int i = 0; i < NR; ++i) {
+      uint16_t* xs = reinterpret_cast<uint16_t*>(wl + i * kSkWaveLdsDot);
 #pragma unroll
-        for (int e = 0; e < 4; ++e) {
-          v[2 * e] = h2f((uint16_t)(xw[e] & 0xFFFF)) * h2f((uint16_t)(sw[e] & 0xFFFF));
-          v[2 * e + 1] = h2f((uint16_t)(xw[e] >> 16)) * h2f((uint16_t)(sw[e] >> 16));
+      for (int rd = 0; rd < 2; ++rd) {
+        if (4 * rd < nblk) {
+          const uint32_t xw[4] = {xv[i][rd].x, xv[i][rd].y, xv[i][rd].z, xv[i][rd].w};
+          const uint32_t sw[4] = {sv[rd].x, sv[rd].y, sv[rd].z, sv[rd].w};
+          float v[8];
+#pragma unroll
+          for (int e = 0; e < 4; ++e) {
+            v[2 * e] = h2f((uint16_t)(xw[e] & 0xFFFF)) * h2f((uint16_t)(sw[e] & 0xFFFF));
+            v[2 * e + 1] = h2f((uint16_t)(xw[e] >> 16)) * h2f((uint16_t)(sw[e] >> 16));
+          }
+          fwht128_x8(v);
+          uint32_t o[4];
+#pragma unroll
+          for (int e = 0; e < 4; ++e)
+            o[e] = (uint32_t)f2h(v[2 * e] * kInvSqrt128) | ((uint32_t)f2h(v[2 * e + 1] * kInvSqrt128) << 16);
+          if (4 * rd + g < nblk)
+            *reinterpret_cast<uint4*>(xs + (4 * rd + g) * 128 + 8 * j) = make_uint4(o[0], o[1], o[2], o[3]);
         }
-        fwht128_x8(v);
-        uint32_t o[4];
-#pragma unroll
-        for (int e = 0; e < 4; ++e)
-          o[e] = (uint32_t)f2h(v[2 * e] * kInvSqrt128) | ((uint32_t)f2h(v[2 * e + 1] * kInvSqrt128) << 16);
-        if (4 * rd + g < nblk)
-          *reinterpret_cast<uint4*>(xs + (4 * rd + g) * 128 + 8 * j) = make_uint4(o[0], o[1], o[2], o[3]);
       }
     }
     __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront", "local");
@@ -233,15 +245,18 @@ __device__ __forceinline__ void sk_run(const SkArgs& a, int wid, unsigned char* 
   }
 
   // ---- main loop
-  float dacc[16];
-  float dxs;        // m == 1: sum of the lane's x' pairs over the segment
+  float dacc[NR][16];
+  float dxs[NR];    // dot path: sum of the lane's x' pairs over the segment, per row
   float4_t macc[8];
-  float4_t mxs;     // m >= 2: sum of x' over the segment, per row (any column)
+  float4_t mxs;     // MFMA path: sum of x' over the segment, per row (any column)
   auto clear_acc = [&]() {
     if constexpr (DOT) {
 #pragma unroll
-      for (int c = 0; c < 16; ++c) dacc[c] = 0.f;
-      dxs = 0.f;
+      for (int i = 0; i < NR; ++i) {
+#pragma unroll
+        for (int c = 0; c < 16; ++c) dacc[i][c] = 0.f;
+        dxs[i] = 0.f;
+      }
     } else {
 #pragma unroll
       for (int q = 0; q < 8; ++q) macc[q] = float4_t{0.f, 0.f, 0.f, 0.f};
@@ -257,10 +272,15 @@ __device__ __forceinline__ void sk_run(const SkArgs& a, int wid, unsigned char* 
     float* dst = a.part + ((int64_t)nb * a.slots + slot) * m * 128;
     if constexpr (DOT) {
 #pragma unroll
-      for (int c = 0; c < 16; ++c) dacc[c] = __builtin_fmaf(-kSigmaBiasPlus1024, dxs, dacc[c]);
-      float c0, c1;
-      reduce_rowpairs(dacc, c0, c1);
-      *reinterpret_cast<float2*>(dst + 16 * t + 2 * p) = make_float2(c0, c1);
+      for (int i = 0; i < NR; ++i) {
+        if (i < m) {  // uniform
+#pragma unroll
+          for (int c = 0; c < 16; ++c) dacc[i][c] = __builtin_fmaf(-kSigmaBiasPlus1024, dxs[i], dacc[i][c]);
+          float c0, c1;
+          reduce_rowpairs(dacc[i], c0, c1);
+          *reinterpret_cast<float2*>(dst + i * 128 + 16 * t + 2 * p) = make_float2(c0, c1);
+        }
+      }
     } else {
 #pragma unroll
       for (int q = 0; q < 8; ++q)
@@ -279,8 +299,12 @@ __device__ __forceinline__ void sk_run(const SkArgs& a, int wid, unsigned char* 
   // ahead; the read after the last step stays inside the region
   // (runs are at most kSkMaxRun steps).
   const unsigned char* xlane = wl + 32 * (kt0 & 7) + 4 * p;
-  half2_t xp = {0, 0};
-  if constexpr (DOT) xp = *reinterpret_cast<const half2_t*>(xlane);
+  half2_t xp[NR];
+#pragma unroll
+  for (int i = 0; i < NR; ++i) {
+    xp[i] = half2_t{0, 0};
+    if constexpr (DOT) xp[i] = *reinterpret_cast<const half2_t*>(xlane + i * kSkWaveLdsDot);
+  }
   int c_nb = nb0, c_slot = slot0;
   int to_end = KT - kt0;  // row steps left in the current block
   for (int base = 0; base < len; base += PF) {
@@ -293,13 +317,16 @@ __device__ __forceinline__ void sk_run(const SkArgs& a, int wid, unsigned char* 
         decode_rowpair<K, true>(*reinterpret_cast<const uint32_t(*)[K]>(ring[s]),
                                 stream_dword(ring[s][K]), wp);
         if constexpr (DOT) {
-          const half2_t xc = xp;
-          xp = *reinterpret_cast<const half2_t*>(xg + 32 * (s + 1));
           const half2_t ones = {(_Float16)1.0f, (_Float16)1.0f};
-          dxs = __builtin_amdgcn_fdot2(xc, ones, dxs, false);
 #pragma unroll
-          for (int c = 0; c < 16; ++c)
-            dacc[c] = __builtin_amdgcn_fdot2(__builtin_bit_cast(half2_t, wp[c]), xc, dacc[c], false);
+          for (int i = 0; i < NR; ++i) {
+            const half2_t xc = xp[i];
+            xp[i] = *reinterpret_cast<const half2_t*>(xg + i * kSkWaveLdsDot + 32 * (s + 1));
+            dxs[i] = __builtin_amdgcn_fdot2(xc, ones, dxs[i], false);
+#pragma unroll
+            for (int c = 0; c < 16; ++c)
+              dacc[i][c] = __builtin_amdgcn_fdot2(__builtin_bit_cast(half2_t, wp[c]), xc, dacc[i][c], false);
+          }
         } else {
           uint4* my4 = reinterpret_cast<uint4*>(my);
           my4[0] = make_uint4(wp[0], wp[1], wp[2], wp[3]);
@@ -411,12 +438,12 @@ __device__ __forceinline__ void sk_finish(const SkArgs& a, int i, int nb) {
 }
 
 
-template <int K, bool DOT, int PF>
+template <int K, int MR, int PF>
 __global__ __launch_bounds__(256) void gemv_sk_kernel(SkArgs a) {
-  constexpr int WAVE_LDS = DOT ? kSkWaveLdsDot : kSkWaveLdsMfma;
+  constexpr int WAVE_LDS = MR > 0 ? MR * kSkWaveLdsDot : kSkWaveLdsMfma;
   __shared__ __align__(16) unsigned char smem[4 * WAVE_LDS];
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
-  sk_run<K, DOT, PF>(a, (int)blockIdx.x * 4 + wave, smem + wave * WAVE_LDS);
+  sk_run<K, MR, PF>(a, (int)blockIdx.x * 4 + wave, smem + wave * WAVE_LDS);
 }
 
 // One wave (a 64-thread workgroup, so the tasks spread over the CUs) per
@@ -451,7 +478,7 @@ template <int PF, int K = 1>
 __device__ __forceinline__ void sk_run_bits(int bits, const SkArgs& a, int wid, unsigned char* wl) {
   if constexpr (K <= 8) {
     if (bits == K)
-      sk_run<K, true, PF>(a, wid, wl);
+      sk_run<K, 1, PF>(a, wid, wl);
     else
       sk_run_bits<PF, K + 1>(bits, a, wid, wl);
   }

@@ -62,10 +62,11 @@ def _other_linear():
     return go
 
 
-@pytest.mark.parametrize("m", [1, 4, 300])
+@pytest.mark.parametrize("m", [1, 4, 8, 300])
 def test_graph_linear(m):
-    # m = 1: the two-tier decode GEMV plan (4096 x 4096 gives 8192 row steps);
-    # m = 4: the matrix-core GEMV; m = 300: the prefill GEMM
+    # m = 1, 4: the v_dot2 decode GEMV with its two-tier plan (4096 x 4096
+    # gives 8192 row steps); m = 8: the matrix-core GEMV; m = 300: the prefill
+    # GEMM
     import torch
     import gemm_exl3_linear_amd as X
     d = G.linear_case(901, 300, 4096, 4096, 4)

@@ -34,7 +34,7 @@ def test_single_tensor_2048x512_k4_m1():
 
 
 @pytest.mark.parametrize("bits", range(1, 9))
-@pytest.mark.parametrize("m", [1, 3, 16])
+@pytest.mark.parametrize("m", [1, 2, 3, 4, 5, 16])
 def test_gemv_all_widths(bits, m):
     d = synth.linear_inputs(200 + bits, m, 1024, 384, bits)
     y = _run(d)
@@ -71,7 +71,7 @@ def test_empty_batch_is_noop():
     torch.cuda.synchronize()
 
 
-@pytest.mark.parametrize("m", [1, 16, 40])
+@pytest.mark.parametrize("m", [1, 4, 16, 40])
 def test_sign_invariances_bit_exact(m):
     import torch
     d = synth.linear_inputs(500 + m, m, 512, 384, 4)
@@ -107,20 +107,23 @@ def test_constant_trellis_exact_zeros(m):
 
 
 def test_row_invariance_gemv():
-    # Within the matrix-core range (2 <= m <= 16) every row equals the same
-    # row of any other call, bit for bit: the summation order depends on
-    # (k, n) only.  m == 1 contracts with v_dot2 instead, whose fp32 rounding
-    # order differs, so there the rows agree to one fp16 ulp.
+    # Within each contraction path, v_dot2 (1 <= m <= 4) and the matrix cores
+    # (5 <= m <= 16), every row equals the same row of any other call, bit for
+    # bit: the plan depends on (k, n) and the path only, and a row's sums on
+    # its own activations only.  Across the two paths the fp32 rounding order
+    # differs, so there the rows agree to one fp16 ulp.
     d = synth.linear_inputs(700, 16, 1024, 512, 4)
     y16t = _run(d)
     y16 = G.f16_bits(y16t)
-    for m in (2, 4, 9):
-        ym = G.f16_bits(_run(d, m=m))
-        np.testing.assert_array_equal(ym, y16[:m])
-    y1 = _run(d, m=1).float()
-    ref = y16t[:1].float()
+    for m in (5, 9):
+        np.testing.assert_array_equal(G.f16_bits(_run(d, m=m)), y16[:m])
+    y4t = _run(d, m=4)
+    y4 = G.f16_bits(y4t)
+    for m in (1, 2, 3):
+        np.testing.assert_array_equal(G.f16_bits(_run(d, m=m)), y4[:m])
+    ref = y16t[:4].float()
     ulp = ref.abs().clamp(min=2.0 ** -14) * 2.0 ** -10
-    assert ((y1 - ref).abs() <= ulp).all()
+    assert ((y4t.float() - ref).abs() <= ulp).all()
 
 
 def test_row_invariance_gemm():
@@ -149,15 +152,15 @@ def test_dense_decode_5120x17408_k4(m):
 
 @pytest.mark.parametrize("k,n,bits", [(4096, 8192, 3), (3072, 12288, 5)])
 def test_single_row_two_tier_runs(k, n, bits):
-    # At m == 1 a grid of more than one wave per SIMD gives the first-round
-    # waves longer runs than the rest; these shapes put the tier boundary and
-    # the run ends at other places in the 128-column blocks than the
-    # 5120 x 17408 workload does.  Row 0 of the same call at m == 4 (equal
+    # On the v_dot2 path a grid of more than one wave per SIMD gives the
+    # first-round waves longer runs than the rest; these shapes put the tier
+    # boundary and the run ends at other places in the 128-column blocks than
+    # the 5120 x 17408 workload does.  Row 0 of the same call at m == 8 (equal
     # runs, matrix cores) sums the same fp32 products in another order: the
     # two agree to one fp16 ulp of the value plus 2^-11 of the row's rms,
     # while a partial slot lost or counted twice would move a whole 128-column
     # block by several percent of the rms.
-    d = synth.linear_inputs(710 + bits, 4, k, n, bits)
+    d = synth.linear_inputs(710 + bits, 8, k, n, bits)
     y1 = _run(d, m=1)
     err = O.rel_frobenius(y1.double().cpu().numpy(), _ref(d, m=1))
     assert err < TOL, err
