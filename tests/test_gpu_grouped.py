@@ -91,6 +91,21 @@ def test_unused_expert_has_no_effect(t):
         np.testing.assert_array_equal(_run(m2), y)
 
 
+def test_many_experts_binning_passes():
+    # the binning keeps at most 8192 expert counters in LDS and takes the
+    # experts in several passes beyond that: 8200 experts, with some pairs
+    # routed past expert 8191
+    m = _small(200, experts=8200, hidden=128, inter=128, bits=2, seed=48)
+    ids = m["ids"].copy()
+    for i in range(0, 200, 5):  # every fifth token: slot 0 to one of 8192..8199
+        e = 8192 + (i // 5) % 8
+        if e not in ids[i]:
+            ids[i, 0] = e
+    assert (ids >= 8192).sum() >= 30
+    err = O.rel_frobenius(_run(m, ids=ids), _ref(m, ids=ids))
+    assert err < TOL, err
+
+
 @pytest.mark.parametrize("t", [1, 50])
 def test_max_topk(t):
     m = _small(t, experts=32, topk=16)
