@@ -38,6 +38,10 @@ COMPILE_FLAGS = [
     "-Wno-unused-function",
     # keep hipcc from forming packed fp32 instructions on its own
     "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
+    # MFMA accumulators in ordinary VGPRs: left to its heuristics the backend
+    # put the decode GEMV's matrix-core accumulators in AGPRs and copied them
+    # back and forth every row step (1116 v_accvgpr moves in that kernel)
+    "-mllvm", "-amdgpu-mfma-vgpr-form",
     f"-I{INCLUDE}",
 ]
 
