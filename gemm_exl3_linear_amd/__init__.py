@@ -227,18 +227,28 @@ def exl3_linear_workspace_size(w: Exl3Weight, m: int) -> int:
     return int(lib().exl3_linear_workspace_size(ctypes.byref(cw), int(m)))
 
 
+def _ydt(dtype) -> int:
+    import torch
+    if dtype == torch.float16:
+        return EXL3_F16
+    if dtype == torch.float32:
+        return EXL3_F32
+    raise ValueError(f"output dtype {dtype} is not fp16 or fp32")
+
+
 def exl3_linear(x, w: Exl3Weight, out_dtype=None, out=None, workspace=None, stream=None):
     import torch
     assert x.dim() == 2 and x.dtype == torch.float16 and x.stride(1) == 1
     m = x.shape[0]
     if out is None:
         out = torch.empty((m, w.n), dtype=out_dtype or torch.float16, device=x.device)
-    ydt = {torch.float16: EXL3_F16, torch.float32: EXL3_F32}[out.dtype]
-    need = exl3_linear_workspace_size(w, m)
-    if workspace is None and need:
-        workspace = torch.zeros(need, dtype=torch.uint8, device=x.device)
-    wsb = 0 if workspace is None else workspace.numel() * workspace.element_size()
+    ydt = _ydt(out.dtype)
     cw = w._c()
+    if workspace is None:  # a caller's workspace is checked against the size by the library
+        need = int(lib().exl3_linear_workspace_size(ctypes.byref(cw), int(m)))
+        if need:
+            workspace = torch.zeros(need, dtype=torch.uint8, device=x.device)
+    wsb = 0 if workspace is None else workspace.numel() * workspace.element_size()
     _check(lib().exl3_linear(ctypes.byref(cw), _ptr(x), m, x.stride(0), _ptr(out), out.stride(0), ydt,
                              _ptr(workspace), wsb, _stream(stream)), "exl3_linear")
     return out
@@ -267,12 +277,13 @@ def exl3_linear_int8(x, w: Exl3Weight, out_dtype=None, out=None, workspace=None,
     m = x.shape[0]
     if out is None:
         out = torch.empty((m, w.n), dtype=out_dtype or torch.float16, device=x.device)
-    ydt = {torch.float16: EXL3_F16, torch.float32: EXL3_F32}[out.dtype]
-    need = exl3_linear_int8_workspace_size(w, m)
-    if workspace is None and need:
-        workspace = torch.empty(need, dtype=torch.uint8, device=x.device)
-    wsb = 0 if workspace is None else workspace.numel() * workspace.element_size()
+    ydt = _ydt(out.dtype)
     cw = w._c()
+    if workspace is None:
+        need = int(lib().exl3_linear_int8_workspace_size(ctypes.byref(cw), int(m)))
+        if need:
+            workspace = torch.empty(need, dtype=torch.uint8, device=x.device)
+    wsb = 0 if workspace is None else workspace.numel() * workspace.element_size()
     _check(lib().exl3_linear_int8(ctypes.byref(cw), _ptr(x), m, x.stride(0), _ptr(out), out.stride(0),
                                   ydt, _ptr(workspace), wsb, _stream(stream)), "exl3_linear_int8")
     return out
@@ -297,12 +308,13 @@ def exl3_linear_multi(x, ws, out_dtype=None, outs=None, workspace=None, stream=N
     m = x.shape[0]
     if outs is None:
         outs = [torch.empty((m, w.n), dtype=out_dtype or torch.float16, device=x.device) for w in ws]
-    ydt = {torch.float16: EXL3_F16, torch.float32: EXL3_F32}[outs[0].dtype]
-    need = exl3_linear_multi_workspace_size(ws, m)
-    if workspace is None and need:
-        workspace = torch.zeros(need, dtype=torch.uint8, device=x.device)
-    wsb = 0 if workspace is None else workspace.numel() * workspace.element_size()
+    ydt = _ydt(outs[0].dtype)
     arr, _recs = _weight_array(ws)
+    if workspace is None:
+        need = int(lib().exl3_linear_multi_workspace_size(arr, len(ws), int(m)))
+        if need:
+            workspace = torch.zeros(need, dtype=torch.uint8, device=x.device)
+    wsb = 0 if workspace is None else workspace.numel() * workspace.element_size()
     yp = (ctypes.c_void_p * len(outs))(*[_ptr(o) for o in outs])
     ld = (ctypes.c_int64 * len(outs))(*[o.stride(0) for o in outs])
     _check(lib().exl3_linear_multi(arr, len(ws), _ptr(x), m, x.stride(0), yp, ld, ydt, _ptr(workspace), wsb,
@@ -324,11 +336,12 @@ def exl3_grouped_experts(x, topk_ids, topk_weights, gate_up: Exl3Arena, down: Ex
     t, topk = topk_ids.shape
     if out is None:
         out = torch.empty((t, down.n), dtype=torch.float32, device=x.device)
-    need = exl3_grouped_experts_workspace_size(gate_up, down, t, topk)
-    if workspace is None and need:
-        workspace = torch.zeros(need, dtype=torch.uint8, device=x.device)
-    wsb = 0 if workspace is None else workspace.numel() * workspace.element_size()
     a, b = gate_up._c(), down._c()
+    if workspace is None:
+        need = int(lib().exl3_grouped_experts_workspace_size(ctypes.byref(a), ctypes.byref(b), int(t), int(topk)))
+        if need:
+            workspace = torch.zeros(need, dtype=torch.uint8, device=x.device)
+    wsb = 0 if workspace is None else workspace.numel() * workspace.element_size()
     _check(lib().exl3_grouped_experts(ctypes.byref(a), ctypes.byref(b), _ptr(x), _ptr(topk_ids),
                                       _ptr(topk_weights), t, topk, _ptr(out), _ptr(workspace), wsb,
                                       _stream(stream)), "exl3_grouped_experts")
