@@ -151,7 +151,6 @@ __global__ __launch_bounds__(kGemmThreads, 2) void gemm_kernel(R r, int k, int n
     for (int q = 0; q < 8; ++q) acc[mi][q] = float4_t{0.f, 0.f, 0.f, 0.f};
 
   const int nsteps = k / kGemmBK;  // k is a multiple of 128: nsteps is a multiple of 4
-  typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
   // two register sets: A fragments of step s and trellis words of step s live in set s % 2
   half8_t ra[2][MI];
   uint32_t rt[2][K];
