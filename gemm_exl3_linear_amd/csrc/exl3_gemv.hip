@@ -33,7 +33,13 @@ int gemv_prefetch(int kc) {
 
 // Split of k into ranges of kc rows (kc a multiple of 128).  Preference: at
 // least target_wgs workgroups in all, then the deepest prefetch (8 loads in
-// flight per lane), then the fewest splits.
+// flight per lane), then the fewest splits.  While the grid has fewer than
+// 4 target_wgs output groups, a range is at most kGemvMaxKc rows: there each
+// workgroup's serial chain (input transform, loads, decode, partial store,
+// arrival) is what the call waits for.  Measured on MI355X for the routed
+// experts (256 x (2048 -> 2 x 512 -> 2048), K=3, top-8): T=1 21.8 us and
+// T=2 24.8 us against 28.7 and 33.8 with 1024 target workgroups and no cap;
+// T=4 34.0 against 36.2; T=16..64 unchanged.
 int gemv_choose_splits(int k, int groups, int m, int target_wgs) {
   const int kb = k / 128;
   int best = -1, best_score = -1;
@@ -41,6 +47,7 @@ int gemv_choose_splits(int k, int groups, int m, int target_wgs) {
     if (kb % s) continue;
     const int kc = k / s;
     if (gemv_lds_bytes(kc, m) > kGemvMaxLds) continue;
+    if (kc > kGemvMaxKc && (int64_t)groups < 4 * target_wgs) continue;
     const bool enough = (int64_t)groups * s >= target_wgs;
     const int score = (enough ? 100 : 0) + gemv_prefetch(kc);
     if (score > best_score) { best = s; best_score = score; }

@@ -20,7 +20,8 @@ struct GemvTask {
 };
 
 constexpr size_t kGemvMaxLds = 64 * 1024;
-constexpr int kGemvTargetWorkgroups = 1024;
+constexpr int kGemvTargetWorkgroups = 256;
+constexpr int kGemvMaxKc = 1024;  // longest k range of one workgroup in small grids
 
 size_t gemv_lds_bytes(int kc, int m);
 int gemv_choose_splits(int k, int groups, int m, int target_wgs);
