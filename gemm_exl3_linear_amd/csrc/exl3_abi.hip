@@ -100,7 +100,8 @@ exl3_status check_grouped(const exl3_expert_weights* gu, const exl3_expert_weigh
   if ((st = check_arena(dn, 1)) != EXL3_OK) return st;
   if (dn->experts != gu->experts || dn->k != gu->n || dn->n != gu->k) return EXL3_E_INVALID;
   if (t < 0 || topk < 1 || topk > EXL3_MAX_TOPK) return EXL3_E_INVALID;
-  // the grouped GEMM grid holds one workgroup row per 128-row tile (< 65536)
+  // bounds the pair indices, the tile list and the grouped GEMM's grid
+  // (tiles x slots x column blocks) well inside 32-bit ranges
   if (t * topk > (int64_t)1 << 21) return EXL3_E_INVALID;
   return EXL3_OK;
 }
