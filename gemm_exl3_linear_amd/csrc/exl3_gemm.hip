@@ -9,6 +9,7 @@ namespace exl3 {
 struct DenseGemmRes {
   static constexpr bool kAFrag = true;  // x' is fragment-major
   static constexpr bool kFineSkip = false;  // only the last row tile is short
+  static constexpr bool kGateUp = false;
   const uint16_t* a;
   int64_t lda;  // elements per 16-row group (16 k)
   int m;

@@ -36,7 +36,7 @@ typedef _Float16 half8_t __attribute__((ext_vector_type(8)));
 
 struct GemmTask {
   bool valid;
-  int nb;                   // 256-column tile
+  int nb;                   // 128-column tile
   const uint16_t* a;        // fp16 rows of x' for this tile, row 0
   int64_t lda;
   int rows;                 // valid rows in this tile (<= BM)
@@ -45,7 +45,15 @@ struct GemmTask {
   const uint16_t* bias;     // fp16 [n] or nullptr
   void* y;                  // output row 0 of this tile
   int64_t ldy;
+  // R::kGateUp only: the second (up) projection of the same rows and shape,
+  // and the sign vector of the next layer's input transform
+  const uint16_t* a2;
+  const uint16_t* trellis2;
+  const uint16_t* svh2;
+  const uint16_t* snext;    // fp16 [n]
 };
+
+__device__ __forceinline__ float silu_f(float z) { return z / (1.0f + __expf(-z)); }
 
 constexpr int kGemmBN = 128;        // columns per workgroup tile (one Hadamard block)
 constexpr int kGemmBK = 32;         // k rows per step (two trellis tiles)
@@ -72,6 +80,28 @@ __device__ __forceinline__ int gemm_b_chunk(int col, int gc) {
   return 16 * G + 4 * (cl ^ ((G >> 2) & 3)) + (gc ^ (G & 3));
 }
 
+// The 128-point transform across a wave's 128 columns: v[q] holds column
+// 16 q + j (j = lane % 16) of one row; three stages over q in registers, four
+// across the lanes of each 16-lane group (unnormalised).
+__device__ __forceinline__ void gemm_col_fwht(float (&v)[8]) {
+  const uint32_t j = lane_id() & 15u;
+#pragma unroll
+  for (int sd = 1; sd < 8; sd <<= 1)
+#pragma unroll
+    for (int q = 0; q < 8; ++q)
+      if ((q & sd) == 0) {
+        const float u0 = v[q], u1 = v[q + sd];
+        v[q] = u0 + u1;
+        v[q + sd] = u0 - u1;
+      }
+  static_for_pow2<1, 16>([&](auto mc) {
+    constexpr int msk = decltype(mc)::value;
+    const bool upper = (j & (uint32_t)msk) != 0;
+#pragma unroll
+    for (int q = 0; q < 8; ++q) v[q] = bfly(v[q], xor_partner<msk>(v[q]), upper);
+  });
+}
+
 // __builtin_amdgcn_sched_group_barrier instruction classes
 constexpr int kSchedValu = 0x002, kSchedMfma = 0x008, kSchedVmemRead = 0x020,
               kSchedDsRead = 0x100, kSchedDsWrite = 0x200;
@@ -95,6 +125,9 @@ __global__ __launch_bounds__(kGemmThreads, 2) void gemm_kernel(R r, int k, int n
   constexpr int MI = WM / 16;          // 16-row MFMA tiles per wave
   static_assert(MI >= 1, "BM must be a multiple of 64");
   __shared__ uint4 bst0[kGemmBN * 4], bst1[kGemmBN * 4];
+  // R::kGateUp: the gate result of every lane's rows and columns (fp16,
+  // four rows per 8-byte entry) between the two passes
+  __shared__ uint2 gst[R::kGateUp ? 4 * MI * 8 * 64 : 1];
 
   const GemmTask T = r.task();
   if (!T.valid) return;
@@ -110,8 +143,8 @@ __global__ __launch_bounds__(kGemmThreads, 2) void gemm_kernel(R r, int k, int n
   // each n tile, waves 2-3 columns 8-15)
   const int p = tid & 7, kt = (tid >> 3) & 1, t = (tid >> 4) & 7, h = tid >> 7;
   constexpr uint32_t kTileBytes = 32 * K;
-  const __amdgpu_buffer_rsrc_t t_rs =
-      make_rsrc(T.trellis, (uint32_t)((uint64_t)(k >> 4) * nt16 * kTileBytes));
+  const uint32_t t_bytes = (uint32_t)((uint64_t)(k >> 4) * nt16 * kTileBytes);
+  __amdgpu_buffer_rsrc_t t_rs = make_rsrc(T.trellis, t_bytes);
   const uint32_t t_voff = (uint32_t)(kt * nt16 + T.nb * 8 + t) * kTileBytes + 4 * K * p;
   const uint32_t t_step = 2u * (uint32_t)nt16 * kTileBytes;
   // LDS dword of each decoded k-pair this thread writes (k-pair 8 kt + p of
@@ -137,7 +170,7 @@ __global__ __launch_bounds__(kGemmThreads, 2) void gemm_kernel(R r, int k, int n
     for (int mi = 0; mi < MI; ++mi)
       a_voff[mi] = (uint32_t)(((int64_t)(16 * (4 * mi + wm) + j) * T.lda + 8 * g) * 2);
   }
-  const __amdgpu_buffer_rsrc_t a_rs = make_rsrc(T.a, a_bytes);
+  __amdgpu_buffer_rsrc_t a_rs = make_rsrc(T.a, a_bytes);
   constexpr int kAStep = R::kAFrag ? kGemmFragBytes : kGemmBK * 2;  // bytes per k step
   // B fragment chunks this lane reads (column 128 wn + 16 q + j, chunk g)
   int br_ch[8];
@@ -274,14 +307,91 @@ __global__ __launch_bounds__(kGemmThreads, 2) void gemm_kernel(R r, int k, int n
       else run(hc, IntC<0>{});
     }
   };
-  if (h == 0)
-    go(IntC<0>{});
-  else
-    go(IntC<1>{});
+  const int cb = col0 + 128 * wn;
+  // R::kGateUp: two passes over the same rows and columns, gate then up; the
+  // gate result goes to LDS as fp16, four rows of one column per entry (each
+  // lane reads back only what it wrote).  One call site of the k loop, so it
+  // stays inlined.
+  constexpr int kPasses = R::kGateUp ? 2 : 1;
+  for (int pass = 0; pass < kPasses; ++pass) {
+    if (pass == 1) {
+#pragma unroll
+      for (int mi = 0; mi < MI; ++mi)
+#pragma unroll
+        for (int q = 0; q < 8; ++q) acc[mi][q] = float4_t{0.f, 0.f, 0.f, 0.f};
+      t_rs = make_rsrc(T.trellis2, t_bytes);
+      a_rs = make_rsrc(T.a2, a_bytes);
+    }
+    if (h == 0)
+      go(IntC<0>{});
+    else
+      go(IntC<1>{});
+    if constexpr (R::kGateUp) {
+      if (pass == 0 && na > 0) {
+        float sg[8];
+#pragma unroll
+        for (int q = 0; q < 8; ++q) sg[q] = kInvSqrt128 * h2f(T.svh[cb + 16 * q + j]);
+#pragma unroll
+        for (int mi = 0; mi < MI; ++mi) {
+          if (mi >= na) break;
+          float v[4][8];
+#pragma unroll
+          for (int rr = 0; rr < 4; ++rr) {
+#pragma unroll
+            for (int q = 0; q < 8; ++q) v[rr][q] = acc[mi][q][rr];
+            gemm_col_fwht(v[rr]);
+          }
+#pragma unroll
+          for (int q = 0; q < 8; ++q)
+            gst[((wm * MI + mi) * 8 + q) * 64 + lane] =
+                make_uint2((uint32_t)f2h(v[0][q] * sg[q]) | ((uint32_t)f2h(v[1][q] * sg[q]) << 16),
+                           (uint32_t)f2h(v[2][q] * sg[q]) | ((uint32_t)f2h(v[3][q] * sg[q]) << 16));
+        }
+      }
+    }
+  }
   if (na == 0) return;  // no barrier follows
 
+  if constexpr (R::kGateUp) {
+    // a = silu(g) u, then the next projection's input transform on this
+    // 128-column block: (a .* snext) H / sqrt(128), fp16
+    float su[8], sn[8];
+#pragma unroll
+    for (int q = 0; q < 8; ++q) {
+      su[q] = kInvSqrt128 * h2f(T.svh2[cb + 16 * q + j]);
+      sn[q] = kInvSqrt128 * h2f(T.snext[cb + 16 * q + j]);
+    }
+#pragma unroll
+    for (int mi = 0; mi < MI; ++mi) {
+      if (mi >= na) break;
+      uint2 gw[8];
+#pragma unroll
+      for (int q = 0; q < 8; ++q) gw[q] = gst[((wm * MI + mi) * 8 + q) * 64 + lane];
+#pragma unroll
+      for (int rr = 0; rr < 4; ++rr) {
+        float v[8];
+#pragma unroll
+        for (int q = 0; q < 8; ++q) v[q] = acc[mi][q][rr];
+        gemm_col_fwht(v);
+#pragma unroll
+        for (int q = 0; q < 8; ++q) {
+          const uint32_t w2 = (rr < 2) ? gw[q].x : gw[q].y;
+          const float gv = h2f((uint16_t)((rr & 1) ? (w2 >> 16) : (w2 & 0xFFFF)));
+          v[q] = silu_f(gv) * (v[q] * su[q]) * sn[q];
+        }
+        gemm_col_fwht(v);
+        const int row = 16 * (4 * mi + wm) + 4 * g + rr;
+        if (row < T.rows) {
+#pragma unroll
+          for (int q = 0; q < 8; ++q)
+            static_cast<uint16_t*>(T.y)[(int64_t)row * T.ldy + cb + 16 * q + j] = f2h(v[q]);
+        }
+      }
+    }
+    return;
+  }
+
   // epilogue: output Hadamard over each wave's 128 columns, svh, bias, cast
-  const int cb = col0 + 128 * wn;
   float sv[8], bv[8];
 #pragma unroll
   for (int q = 0; q < 8; ++q) {
@@ -296,24 +406,7 @@ __global__ __launch_bounds__(kGemmThreads, 2) void gemm_kernel(R r, int k, int n
       float v[8];
 #pragma unroll
       for (int q = 0; q < 8; ++q) v[q] = acc[mi][q][rr];
-#pragma unroll
-      for (int sd = 1; sd < 8; sd <<= 1)
-#pragma unroll
-        for (int q = 0; q < 8; ++q)
-          if ((q & sd) == 0) {
-            const float u0 = v[q], u1 = v[q + sd];
-            v[q] = u0 + u1;
-            v[q + sd] = u0 - u1;
-          }
-#pragma unroll
-      for (int msk = 1; msk < 16; msk <<= 1) {
-        const bool upper = (j & msk) != 0;
-#pragma unroll
-        for (int q = 0; q < 8; ++q) {
-          const float pv = shfl_xor_f(v[q], msk);
-          v[q] = upper ? (pv - v[q]) : (v[q] + pv);
-        }
-      }
+      gemm_col_fwht(v);
       const int row = 16 * (4 * mi + wm) + 4 * g + rr;
       if (row < T.rows) {
 #pragma unroll

@@ -27,10 +27,10 @@
 //   1-3. count the pairs per expert and chunk, scan the counts into offsets
 //      and the tile list (one workgroup), scatter the pairs into expert order
 //   4. x'_g, x'_u = (x_token .* suh_e,slot) H for each sorted row   -> fp16
-//   5. gemm_kernel over (tile, slot, 128 cols)  -> g, u fp32 (transformed)
-//   6. a = silu(g) * u, x'_d = (a .* suh_down_e) H                  -> fp16
-//   7. gemm_kernel over (tile, 128 cols)        -> d fp32 (transformed, svh)
-//   8. y[token] = sum over slots in order of w * d                  -> fp32
+//   5. gemm_kernel over (tile, 128 cols): g, then u (transformed, svh), then
+//      a = silu(g) * u and x'_d = (a .* suh_down_e) H on the block    -> fp16
+//   6. gemm_kernel over (tile, 128 cols)        -> d fp32 (transformed, svh)
+//   7. y[token] = sum over slots in order of w * d                  -> fp32
 #include "exl3_device.hpp"
 #include "exl3_gemm.hpp"
 #include "exl3_gemv.hpp"
@@ -61,7 +61,6 @@ constexpr int kBinIds = kBinThreads * kBinPerThread;
 
 static inline int64_t bin_chunks(int64_t P) { return (P + kBinIds - 1) / kBinIds; }
 
-__device__ __forceinline__ float silu_f(float z) { return z / (1.0f + __expf(-z)); }
 
 static inline size_t align256(size_t v) { return (v + 255) & ~(size_t)255; }
 
@@ -258,7 +257,7 @@ struct TileEntry {
 struct GemmLayout {
   int bm;  // rows per tile
   int max_tiles;
-  size_t hist, offsets, ntiles, tiles, pos, sorted, xg, gu, xd, d, total;
+  size_t hist, offsets, ntiles, tiles, pos, sorted, xg, xd, d, total;
 };
 
 static GemmLayout gemm_layout(const ArenaDesc& gu, const ArenaDesc& dn, int64_t P) {
@@ -274,7 +273,6 @@ static GemmLayout gemm_layout(const ArenaDesc& gu, const ArenaDesc& dn, int64_t 
   L.pos = off;     off += align256((size_t)P * 4);
   L.sorted = off;  off += align256((size_t)P * 4);
   L.xg = off;      off += align256((size_t)2 * P * gu.k * sizeof(uint16_t));
-  L.gu = off;      off += align256((size_t)2 * P * gu.n * sizeof(float));
   L.xd = off;      off += align256((size_t)P * dn.k * sizeof(uint16_t));
   L.d = off;       off += align256((size_t)P * dn.n * sizeof(float));
   L.total = off;
@@ -472,47 +470,6 @@ __global__ __launch_bounds__(256) void gu_input_transform(
   }
 }
 
-// a = silu(g) * u, x'_d = (a .* suh_down_e) H, one wave per sorted row, four
-// 128-element blocks at a time
-__global__ __launch_bounds__(256) void silu_down_transform(
-    const float* __restrict__ gu, int64_t P, int inter, const int32_t* __restrict__ sorted,
-    const int32_t* __restrict__ ids, const uint16_t* __restrict__ suh_dn,
-    uint16_t* __restrict__ xd) {
-  const int64_t r = (int64_t)blockIdx.x * 4 + (threadIdx.x >> 6);
-  if (r >= P) return;
-  const int e = ids[sorted[r]];
-  const int lane = (int)lane_id();
-  const int g = lane >> 4, j = lane & 15;
-  const int nblk = inter >> 7;
-  const float* gr = gu + r * inter;
-  const float* ur = gu + (P + r) * inter;
-  const uint16_t* sr = suh_dn + (int64_t)e * inter;
-  for (int b0 = 0; b0 < nblk; b0 += 4) {
-    const int b = b0 + g;
-    const int kk = (b < nblk ? b : nblk - 1) * 128 + 8 * j;
-    const float4 g0 = *reinterpret_cast<const float4*>(gr + kk);
-    const float4 g1 = *reinterpret_cast<const float4*>(gr + kk + 4);
-    const float4 u0 = *reinterpret_cast<const float4*>(ur + kk);
-    const float4 u1 = *reinterpret_cast<const float4*>(ur + kk + 4);
-    const uint4 sv = *reinterpret_cast<const uint4*>(sr + kk);
-    const float gv[8] = {g0.x, g0.y, g0.z, g0.w, g1.x, g1.y, g1.z, g1.w};
-    const float uv[8] = {u0.x, u0.y, u0.z, u0.w, u1.x, u1.y, u1.z, u1.w};
-    const uint32_t sw[4] = {sv.x, sv.y, sv.z, sv.w};
-    float v[8];
-#pragma unroll
-    for (int q = 0; q < 4; ++q) {
-      v[2 * q] = silu_f(gv[2 * q]) * uv[2 * q] * h2f((uint16_t)(sw[q] & 0xFFFF));
-      v[2 * q + 1] = silu_f(gv[2 * q + 1]) * uv[2 * q + 1] * h2f((uint16_t)(sw[q] >> 16));
-    }
-    fwht128_x8(v);
-    uint32_t o[4];
-#pragma unroll
-    for (int q = 0; q < 4; ++q)
-      o[q] = (uint32_t)f2h(v[2 * q] * kInvSqrt128) | ((uint32_t)f2h(v[2 * q + 1] * kInvSqrt128) << 16);
-    if (b < nblk) *reinterpret_cast<uint4*>(xd + r * inter + kk) = make_uint4(o[0], o[1], o[2], o[3]);
-  }
-}
-
 // y[token] = sum over slots in order of w[token, slot] * d[pos(token, slot)]
 __global__ __launch_bounds__(256) void combine_rows(const float* __restrict__ d,
                                                    const int32_t* __restrict__ pos,
@@ -546,6 +503,7 @@ __global__ __launch_bounds__(256) void combine_rows(const float* __restrict__ d,
 struct GroupedGemmRes {
   static constexpr bool kAFrag = false;  // gathered rows stay row-major
   static constexpr bool kFineSkip = true;  // tiles end wherever an expert's rows do
+  static constexpr bool kGateUp = false;
   const TileEntry* tiles;
   const int32_t* ntiles;
   const uint16_t* a;       // fp16 [slots][P][k]
@@ -589,6 +547,65 @@ struct GroupedGemmRun {
       hipLaunchKernelGGL((gemm_kernel<K, 256, true, GroupedGemmRes>), grid, dim3(kGemmThreads), 0, s, r, r.k, r.n);
     else
       hipLaunchKernelGGL((gemm_kernel<K, 128, true, GroupedGemmRes>), grid, dim3(kGemmThreads), 0, s, r, r.k, r.n);
+    return hipGetLastError();
+  }
+};
+
+// Gate and up of one (tile, 128-column block) in one workgroup, one after the
+// other over the same gathered rows, then a = silu(g) u and the down
+// projection's input transform on that block (the down input's 128-element
+// Hadamard blocks are the gate/up column blocks), written as fp16 x'_d rows.
+// Same XCD-aware order as GroupedGemmRes with one group per tile.
+struct GroupedGateUpRes {
+  static constexpr bool kAFrag = false;
+  static constexpr bool kFineSkip = true;
+  static constexpr bool kGateUp = true;
+  const TileEntry* tiles;
+  const int32_t* ntiles;
+  const uint16_t* a;       // fp16 [2][P][k]: x'_gate, x'_up
+  int64_t P;
+  int k, n;
+  const uint16_t* trellis; // arena [E][2][k/16][n/16][16K]
+  const uint16_t* svh;     // fp16 [E][2][n]
+  const uint16_t* suh_dn;  // fp16 [E][n], the down projection's input signs
+  int64_t tensor_words;
+  uint16_t* y;             // fp16 [P][n]: x'_d
+  __device__ GemmTask task() const {
+    const int nbt = n / kGemmBN;
+    const int b = (int)blockIdx.x;
+    const int l = b >> 3;
+    const int gq = l / nbt;
+    const int tile = 8 * gq + (b & 7);
+    GemmTask T;
+    T.nb = l - gq * nbt;
+    T.valid = tile < *ntiles;
+    if (!T.valid) return T;
+    const TileEntry te = tiles[tile];
+    T.a = a + te.row0 * (int64_t)k;
+    T.a2 = a + (P + te.row0) * (int64_t)k;
+    T.lda = k;
+    T.rows = te.rows;
+    T.trellis = trellis + (int64_t)te.e * 2 * tensor_words;
+    T.trellis2 = T.trellis + tensor_words;
+    T.svh = svh + (int64_t)te.e * 2 * n;
+    T.svh2 = T.svh + n;
+    T.snext = suh_dn + (int64_t)te.e * n;
+    T.bias = nullptr;
+    T.y = y + te.row0 * (int64_t)n;
+    T.ldy = n;
+    return T;
+  }
+};
+
+template <int K>
+struct GroupedGateUpRun {
+  static hipError_t run(const GroupedGateUpRes& r, int bm, int max_tiles, hipStream_t s) {
+    const int64_t groups = ((int64_t)max_tiles + 7) / 8 * 8;
+    const dim3 grid((unsigned)(groups * (r.n / kGemmBN)));
+    if (bm == 256)
+      hipLaunchKernelGGL((gemm_kernel<K, 256, false, GroupedGateUpRes>), grid, dim3(kGemmThreads), 0, s, r, r.k, r.n);
+    else
+      hipLaunchKernelGGL((gemm_kernel<K, 128, false, GroupedGateUpRes>), grid, dim3(kGemmThreads), 0, s, r, r.k, r.n);
     return hipGetLastError();
   }
 };
@@ -638,7 +655,6 @@ hipError_t launch_grouped(const ArenaDesc& gu, const ArenaDesc& dn, const uint16
   int32_t* pos = reinterpret_cast<int32_t*>(base + L.pos);
   int32_t* sorted = reinterpret_cast<int32_t*>(base + L.sorted);
   uint16_t* xg = reinterpret_cast<uint16_t*>(base + L.xg);
-  float* gbuf = reinterpret_cast<float*>(base + L.gu);
   uint16_t* xd = reinterpret_cast<uint16_t*>(base + L.xd);
   float* dbuf = reinterpret_cast<float*>(base + L.d);
 
@@ -654,15 +670,9 @@ hipError_t launch_grouped(const ArenaDesc& gu, const ArenaDesc& dn, const uint16
                        topk, P, hidden, sorted, ids, gu.suh, xg);
   }
   if ((e = hipGetLastError()) != hipSuccess) return e;
-  GroupedGemmRes rg{tiles, ntiles, xg, P, hidden, inter, gu.trellis, gu.svh, 2, words_gu, gbuf};
-  e = dispatch_bits<GroupedGemmRun>(gu.bits, rg, L.bm, L.max_tiles, s);
+  GroupedGateUpRes rg{tiles, ntiles, xg, P, hidden, inter, gu.trellis, gu.svh, dn.suh, words_gu, xd};
+  e = dispatch_bits<GroupedGateUpRun>(gu.bits, rg, L.bm, L.max_tiles, s);
   if (e != hipSuccess) return e;
-  {
-    const int64_t tasks = P;  // one wave each
-    hipLaunchKernelGGL(silu_down_transform, dim3((unsigned)((tasks + 3) / 4)), dim3(256), 0, s,
-                       gbuf, P, inter, sorted, ids, dn.suh, xd);
-  }
-  if ((e = hipGetLastError()) != hipSuccess) return e;
   GroupedGemmRes rd{tiles, ntiles, xd, P, inter, hidden, dn.trellis, dn.svh, 1, words_dn, dbuf};
   e = dispatch_bits<GroupedGemmRun>(dn.bits, rd, L.bm, L.max_tiles, s);
   if (e != hipSuccess) return e;
