@@ -82,24 +82,7 @@ __device__ __forceinline__ void gemm_i8_epilogue(const GemmI8Task& T,
       float v[8];
 #pragma unroll
       for (int q = 0; q < 8; ++q) v[q] = (float)acc[mi][q][rr];
-#pragma unroll
-      for (int sd = 1; sd < 8; sd <<= 1)
-#pragma unroll
-        for (int q = 0; q < 8; ++q)
-          if ((q & sd) == 0) {
-            const float u0 = v[q], u1 = v[q + sd];
-            v[q] = u0 + u1;
-            v[q + sd] = u0 - u1;
-          }
-#pragma unroll
-      for (int msk = 1; msk < 16; msk <<= 1) {
-        const bool upper = (j & msk) != 0;
-#pragma unroll
-        for (int q = 0; q < 8; ++q) {
-          const float pv = shfl_xor_f(v[q], msk);
-          v[q] = upper ? (pv - v[q]) : (v[q] + pv);
-        }
-      }
+      gemm_col_fwht(v);
       if (row < T.rows) {
         const float rs = T.ascale[row];
 #pragma unroll
