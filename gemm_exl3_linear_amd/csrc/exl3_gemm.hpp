@@ -26,6 +26,10 @@
 //                            (3 stages in registers, 4 across lanes), then
 //                            svh, bias and the cast.
 // One barrier per step; the loads of the next steps are in flight meanwhile.
+// R::kGateUp (routed experts' gate and up): the k loop runs twice over the
+// same rows, for gate and then for up; the transformed gate block waits in
+// LDS as fp16, and the epilogue forms silu(g) u and the next projection's
+// input transform of the block instead of storing the product.
 #pragma once
 
 #include "exl3_device.hpp"
