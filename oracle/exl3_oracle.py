@@ -334,6 +334,11 @@ def grouped_experts(x, ids, weights, gate_up: dict, down: dict) -> np.ndarray:
     of e applied to a; Y[t] += weights[t, s] * d.  Experts are evaluated one
     (token, slot) pair at a time through ``linear``; decoded weights are cached
     per expert only to save time.
+
+    An arena's ``bits`` is one width for every expert, or a sequence with the
+    width of each expert (TensorFold issue #832, "Activity": the consolidated
+    module keeps a width per expert); ``trellis[e][slot]`` is then expert e's
+    tensor at its own width.
     """
     x = np.asarray(x)
     ids = np.asarray(ids)
@@ -343,23 +348,27 @@ def grouped_experts(x, ids, weights, gate_up: dict, down: dict) -> np.ndarray:
     y = np.zeros((t_count, hidden), dtype=np.float64)
     cache = {}
 
+    def width(arena, e):
+        b = arena["bits"]
+        return int(b[e]) if np.ndim(b) else int(b)
+
     def dec(arena, e, slot):
         key = (id(arena), e, slot)
         if key not in cache:
-            cache[key] = decode_tensor(arena["trellis"][e, slot], arena["bits"])
+            cache[key] = decode_tensor(arena["trellis"][e][slot], width(arena, e))
         return cache[key]
 
     for t in range(t_count):
         for s in range(topk):
             e = int(ids[t, s])
             xt = x[t:t + 1]
-            g = linear(xt, gate_up["trellis"][e, 0], gate_up["suh"][e, 0], gate_up["svh"][e, 0],
-                       gate_up["bits"], w_decoded=dec(gate_up, e, 0))
-            u = linear(xt, gate_up["trellis"][e, 1], gate_up["suh"][e, 1], gate_up["svh"][e, 1],
-                       gate_up["bits"], w_decoded=dec(gate_up, e, 1))
+            g = linear(xt, gate_up["trellis"][e][0], gate_up["suh"][e, 0], gate_up["svh"][e, 0],
+                       width(gate_up, e), w_decoded=dec(gate_up, e, 0))
+            u = linear(xt, gate_up["trellis"][e][1], gate_up["suh"][e, 1], gate_up["svh"][e, 1],
+                       width(gate_up, e), w_decoded=dec(gate_up, e, 1))
             a = silu(g) * u
-            d = linear(a, down["trellis"][e, 0], down["suh"][e, 0], down["svh"][e, 0],
-                       down["bits"], w_decoded=dec(down, e, 0))
+            d = linear(a, down["trellis"][e][0], down["suh"][e, 0], down["svh"][e, 0],
+                       width(down, e), w_decoded=dec(down, e, 0))
             y[t] += weights[t, s] * d[0]
     return y
 

@@ -98,6 +98,19 @@ def expert_arena(g: np.random.Generator, experts: int, slots: int, k: int, n: in
     return dict(trellis=t, suh=suh, svh=svh, experts=experts, slots=slots, k=k, n=n, bits=bits)
 
 
+def mixed_expert_arena(g: np.random.Generator, slots: int, k: int, n: int, widths):
+    """Arena with a width per expert: trellis is a list whose entry e is
+    [slots, k/16, n/16, 16*widths[e]]; suh [E, slots, k], svh [E, slots, n];
+    bits int32 [E]."""
+    widths = np.asarray(widths, dtype=np.int32)
+    t = [g.integers(0, 65536, size=(slots, k // 16, n // 16, 16 * int(b)), dtype=np.uint16)
+         for b in widths]
+    e = len(widths)
+    suh = (g.integers(0, 2, size=(e, slots, k), dtype=np.int8) * 2 - 1).astype(np.float16)
+    svh = (g.integers(0, 2, size=(e, slots, n), dtype=np.int8) * 2 - 1).astype(np.float16)
+    return dict(trellis=t, suh=suh, svh=svh, experts=e, slots=slots, k=k, n=n, bits=widths)
+
+
 def router_logits(g: np.random.Generator, t: int, experts: int) -> np.ndarray:
     return g.standard_normal((t, experts)).astype(np.float32)
 
@@ -125,6 +138,23 @@ def moe_inputs(seed: int, t: int, experts: int = 256, topk: int = 8, hidden: int
     g = rng(seed)
     gate_up = expert_arena(g, experts, 2, hidden, inter, bits)
     down = expert_arena(g, experts, 1, inter, hidden, bits)
+    x = activations(g, t, hidden)
+    logits = router_logits(g, t, experts)
+    ids, w = topk_routing(logits, topk)
+    return dict(gate_up=gate_up, down=down, x=x, ids=ids, weights=w, topk=topk)
+
+
+def moe_mixed_inputs(seed: int, t: int, experts: int = 256, topk: int = 8, hidden: int = 2048,
+                     inter: int = 512, widths=(2, 3, 4, 5, 6)):
+    """Routed-expert workload whose experts each have their own width, drawn
+    uniformly from ``widths`` (gate/up widths first, then down), then the
+    arenas, activations and routing in the order of ``moe_inputs``."""
+    g = rng(seed)
+    choices = np.asarray(widths, dtype=np.int32)
+    w_gu = choices[g.integers(0, len(choices), size=experts)]
+    w_dn = choices[g.integers(0, len(choices), size=experts)]
+    gate_up = mixed_expert_arena(g, 2, hidden, inter, w_gu)
+    down = mixed_expert_arena(g, 1, inter, hidden, w_dn)
     x = activations(g, t, hidden)
     logits = router_logits(g, t, experts)
     ids, w = topk_routing(logits, topk)

@@ -70,6 +70,57 @@ def test_tokens_independent():
         np.testing.assert_allclose(yt[0], y[t], atol=1e-12)
 
 
+def _mixed(seed=23, t=4, experts=6, topk=2, hidden=256, inter=128, widths=(2, 3, 5, 8)):
+    return synth.moe_mixed_inputs(seed, t, experts=experts, topk=topk, hidden=hidden, inter=inter,
+                                  widths=widths)
+
+
+def test_mixed_widths_top1_is_dense_swiglu_at_each_width():
+    # every token's output is its one expert's SwiGLU MLP, each projection
+    # decoded at that expert's own width (a wrong width changes the tensor's
+    # word count, so decoding it at another width cannot give this result)
+    d = _mixed(topk=1, t=6)
+    gu, dn = d["gate_up"], d["down"]
+    assert len(set(gu["bits"].tolist())) > 1 and len(set(dn["bits"].tolist())) > 1
+    w = np.ones_like(d["weights"])
+    y = O.grouped_experts(d["x"], d["ids"], w, gu, dn)
+    for t in range(d["ids"].shape[0]):
+        e = int(d["ids"][t, 0])
+        kg, kd = int(gu["bits"][e]), int(dn["bits"][e])
+        assert gu["trellis"][e].shape[-1] == 16 * kg and dn["trellis"][e].shape[-1] == 16 * kd
+        Wg = O.effective_weight(gu["trellis"][e][0], gu["suh"][e, 0], gu["svh"][e, 0], kg)
+        Wu = O.effective_weight(gu["trellis"][e][1], gu["suh"][e, 1], gu["svh"][e, 1], kg)
+        Wd = O.effective_weight(dn["trellis"][e][0], dn["suh"][e, 0], dn["svh"][e, 0], kd)
+        xt = d["x"][t].astype(np.float64)
+        g = xt @ Wg
+        u = xt @ Wu
+        ref = (g * scipy.special.expit(g) * u) @ Wd
+        assert O.rel_frobenius(y[t], ref) < 1e-12
+
+
+def test_mixed_widths_equal_widths_match_uniform_arena():
+    # a per-expert width list with one value is the uniform arena
+    d = _small(experts=5)
+    gu, dn = d["gate_up"], d["down"]
+    y = O.grouped_experts(d["x"], d["ids"], d["weights"], gu, dn)
+    gu_m = dict(gu, trellis=[gu["trellis"][e] for e in range(5)], bits=np.full(5, gu["bits"], np.int32))
+    dn_m = dict(dn, trellis=[dn["trellis"][e] for e in range(5)], bits=np.full(5, dn["bits"], np.int32))
+    np.testing.assert_array_equal(O.grouped_experts(d["x"], d["ids"], d["weights"], gu_m, dn_m), y)
+
+
+def test_mixed_widths_slots_sum_over_experts_of_other_widths():
+    # topk=2: each token's output is the weighted sum of two single-expert
+    # outputs, whatever the two experts' widths
+    d = _mixed(topk=2, t=3)
+    y = O.grouped_experts(d["x"], d["ids"], d["weights"], d["gate_up"], d["down"])
+    for s in range(2):
+        ids1 = d["ids"][:, s:s + 1].copy()
+        w1 = d["weights"][:, s:s + 1].astype(np.float64)
+        part = O.grouped_experts(d["x"], ids1, w1, d["gate_up"], d["down"])
+        y = y - part
+    assert np.abs(y).max() < 1e-12
+
+
 def test_routing_properties():
     g = np.random.default_rng(9)
     logits = synth.router_logits(g, 64, 256)
