@@ -304,6 +304,24 @@ def main():
             secondary[f"moe_t{t}"] = {"us_per_call": round(pl * 1e6, 2),
                                       "TFLOP/s": round(flops / pl / 1e12, 2)}
             del gu, dn, xm, ids, wt, wsm, ym
+        # the same shape with a width per expert drawn from {2, 3, 4}
+        for t in (1, 4096):
+            mo = synth.moe_mixed_inputs(synth.SEED_MOE_MIXED_WIDTHS, t, widths=(2, 3, 4))
+            gu = X.Exl3MixedArena.from_numpy(mo["gate_up"], dev)
+            dn = X.Exl3MixedArena.from_numpy(mo["down"], dev)
+            xm = torch.from_numpy(mo["x"]).to(dev)
+            ids = torch.from_numpy(mo["ids"]).to(dev)
+            wt = torch.from_numpy(mo["weights"]).to(dev)
+            wsm = torch.zeros(X.exl3_grouped_experts_mixed_workspace_size(gu, dn, t, 8), dtype=torch.uint8,
+                              device=dev)
+            ym = torch.empty((t, 2048), dtype=torch.float32, device=dev)
+            reps = 200 if t == 1 else 10
+            pl, _ = time_calls(lambda i: X.exl3_grouped_experts_mixed(xm, ids, wt, gu, dn, out=ym, workspace=wsm,
+                                                                      stream=stream), reps, 3, stream)
+            flops = 2.0 * t * 8 * 3 * 2048 * 512
+            secondary[f"moe_mixed_widths_t{t}"] = {"us_per_call": round(pl * 1e6, 2),
+                                                   "TFLOP/s": round(flops / pl / 1e12, 2)}
+            del gu, dn, xm, ids, wt, wsm, ym
 
     cpu = None
     if not args.no_cpu_baseline:

@@ -49,6 +49,10 @@ class _Arena(ctypes.Structure):
                 ("n", ctypes.c_int32), ("bits", ctypes.c_int32), ("codebook", ctypes.c_int32)]
 
 
+class _Widths(ctypes.Structure):
+    _fields_ = [("bits_host", ctypes.c_void_p), ("bits", ctypes.c_void_p), ("offsets", ctypes.c_void_p)]
+
+
 _lib = None
 
 
@@ -96,6 +100,13 @@ def lib() -> ctypes.CDLL:
     L.exl3_grouped_experts.restype = i32
     L.exl3_grouped_experts.argtypes = [ctypes.POINTER(_Arena), ctypes.POINTER(_Arena), vp, vp, vp, i64, i32,
                                        vp, vp, sz, vp]
+    Wp = ctypes.POINTER(_Widths)
+    L.exl3_grouped_experts_mixed_workspace_size.restype = sz
+    L.exl3_grouped_experts_mixed_workspace_size.argtypes = [ctypes.POINTER(_Arena), Wp, ctypes.POINTER(_Arena),
+                                                            Wp, i64, i32]
+    L.exl3_grouped_experts_mixed.restype = i32
+    L.exl3_grouped_experts_mixed.argtypes = [ctypes.POINTER(_Arena), Wp, ctypes.POINTER(_Arena), Wp, vp, vp, vp,
+                                             i64, i32, vp, vp, sz, vp]
     _lib = L
     return L
 
@@ -196,6 +207,62 @@ class Exl3Arena:
                          torch.from_numpy(arena["suh"].astype("float16")).to(device),
                          torch.from_numpy(arena["svh"].astype("float16")).to(device),
                          int(arena["bits"]))
+
+
+@dataclass
+class Exl3MixedArena:
+    """Expert arena with a width per expert on the GPU: trellis int16/uint16
+    [total words] with expert e's slots at word offsets[e] on, widths int32
+    [E] both on the host (``bits_host``, a ctypes array the record points to)
+    and on the GPU (``bits``), offsets int64 [E] on the GPU, suh fp16
+    [E, slots, k], svh fp16 [E, slots, n]."""
+    trellis: "object"
+    suh: "object"
+    svh: "object"
+    bits: "object"
+    offsets: "object"
+    bits_host: "object"
+    codebook: int = CODEBOOK_MUL1
+
+    @property
+    def experts(self) -> int:
+        return int(self.suh.shape[0])
+
+    @property
+    def slots(self) -> int:
+        return int(self.suh.shape[1])
+
+    @property
+    def k(self) -> int:
+        return int(self.suh.shape[2])
+
+    @property
+    def n(self) -> int:
+        return int(self.svh.shape[2])
+
+    def _c(self) -> _Arena:
+        return _Arena(_ptr(self.trellis), _ptr(self.suh), _ptr(self.svh), self.experts, self.slots,
+                      self.k, self.n, 0, int(self.codebook))
+
+    def _w(self) -> _Widths:
+        return _Widths(ctypes.addressof(self.bits_host), _ptr(self.bits), _ptr(self.offsets))
+
+    @staticmethod
+    def from_numpy(arena: dict, device="cuda"):
+        """Packs the per-expert trellis arrays (entry e [slots, k/16, n/16,
+        16*bits[e]]) one after the other into one allocation."""
+        import numpy as np
+        import torch
+        widths = [int(b) for b in arena["bits"]]
+        sizes = [int(t.size) for t in arena["trellis"]]
+        offsets = np.concatenate([[0], np.cumsum(sizes)[:-1]]).astype(np.int64)
+        flat = np.concatenate([np.ascontiguousarray(t).reshape(-1) for t in arena["trellis"]])
+        host = (ctypes.c_int32 * len(widths))(*widths)
+        return Exl3MixedArena(torch.from_numpy(flat.view("int16").copy()).to(device),
+                              torch.from_numpy(arena["suh"].astype("float16")).to(device),
+                              torch.from_numpy(arena["svh"].astype("float16")).to(device),
+                              torch.tensor(widths, dtype=torch.int32, device=device),
+                              torch.from_numpy(offsets).to(device), host)
 
 
 # ---------------------------------------------------------------------------
@@ -345,4 +412,37 @@ def exl3_grouped_experts(x, topk_ids, topk_weights, gate_up: Exl3Arena, down: Ex
     _check(lib().exl3_grouped_experts(ctypes.byref(a), ctypes.byref(b), _ptr(x), _ptr(topk_ids),
                                       _ptr(topk_weights), t, topk, _ptr(out), _ptr(workspace), wsb,
                                       _stream(stream)), "exl3_grouped_experts")
+    return out
+
+
+def exl3_grouped_experts_mixed_workspace_size(gate_up: Exl3MixedArena, down: Exl3MixedArena, t: int,
+                                              topk: int) -> int:
+    a, b = gate_up._c(), down._c()
+    wa, wb = gate_up._w(), down._w()
+    return int(lib().exl3_grouped_experts_mixed_workspace_size(ctypes.byref(a), ctypes.byref(wa), ctypes.byref(b),
+                                                               ctypes.byref(wb), int(t), int(topk)))
+
+
+def exl3_grouped_experts_mixed(x, topk_ids, topk_weights, gate_up: Exl3MixedArena, down: Exl3MixedArena,
+                               out=None, workspace=None, stream=None):
+    """exl3_grouped_experts over arenas whose experts each have their own width."""
+    import torch
+    assert x.dtype == torch.float16 and x.is_contiguous()
+    assert topk_ids.dtype == torch.int32 and topk_ids.is_contiguous()
+    assert topk_weights.dtype == torch.float32 and topk_weights.is_contiguous()
+    t, topk = topk_ids.shape
+    if out is None:
+        out = torch.empty((t, down.n), dtype=torch.float32, device=x.device)
+    a, b = gate_up._c(), down._c()
+    wa, wb = gate_up._w(), down._w()
+    if workspace is None:
+        need = int(lib().exl3_grouped_experts_mixed_workspace_size(ctypes.byref(a), ctypes.byref(wa),
+                                                                   ctypes.byref(b), ctypes.byref(wb), int(t),
+                                                                   int(topk)))
+        if need:
+            workspace = torch.zeros(need, dtype=torch.uint8, device=x.device)
+    wsb = 0 if workspace is None else workspace.numel() * workspace.element_size()
+    _check(lib().exl3_grouped_experts_mixed(ctypes.byref(a), ctypes.byref(wa), ctypes.byref(b), ctypes.byref(wb),
+                                            _ptr(x), _ptr(topk_ids), _ptr(topk_weights), t, topk, _ptr(out),
+                                            _ptr(workspace), wsb, _stream(stream)), "exl3_grouped_experts_mixed")
     return out

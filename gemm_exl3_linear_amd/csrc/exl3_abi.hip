@@ -89,8 +89,46 @@ size_t multi_ws(const exl3_weight* const* w, int32_t count, int64_t m) {
   return need;
 }
 
+// An arena whose experts each have their own width: the record's bits is 0
+// and the widths record supplies them, checked on the host from bits_host;
+// the rest is checked as for a uniform arena.
+exl3_status check_mixed_arena(const exl3_expert_weights* a, const exl3_expert_widths* w, int slots) {
+  if (!a || !w) return EXL3_E_INVALID;
+  if (a->bits != 0) return EXL3_E_INVALID;
+  exl3_expert_weights u = *a;
+  u.bits = 1;
+  const exl3_status st = check_arena(&u, slots);
+  if (st != EXL3_OK) return st;
+  if (!w->bits_host || !w->bits || !w->offsets) return EXL3_E_INVALID;
+  if (!aligned4(w->bits) || (reinterpret_cast<uintptr_t>(w->offsets) & 7u)) return EXL3_E_INVALID;
+  for (int e = 0; e < a->experts; ++e) {
+    const int32_t b = w->bits_host[e];
+    if (b < 1 || b > 8) return EXL3_E_INVALID;
+  }
+  return EXL3_OK;
+}
+
 exl3::ArenaDesc desc(const exl3_expert_weights* a) {
   return exl3::ArenaDesc{a->trellis, a->suh, a->svh, a->experts, a->slots, a->k, a->n, a->bits};
+}
+
+exl3::ArenaDesc desc_mixed(const exl3_expert_weights* a, const exl3_expert_widths* w) {
+  exl3::ArenaDesc d{a->trellis, a->suh, a->svh, a->experts, a->slots, a->k, a->n, 0};
+  d.ebits = w->bits;
+  d.eoff = w->offsets;
+  return d;
+}
+
+// Checks shared by both grouped entry points, after the arenas' own: the
+// arenas fit together and the routing sizes are in range.
+exl3_status check_grouped_pair(const exl3_expert_weights* gu, const exl3_expert_weights* dn,
+                               int64_t t, int32_t topk) {
+  if (dn->experts != gu->experts || dn->k != gu->n || dn->n != gu->k) return EXL3_E_INVALID;
+  if (t < 0 || topk < 1 || topk > EXL3_MAX_TOPK) return EXL3_E_INVALID;
+  // bounds the pair indices, the tile list and the grouped GEMM's grid
+  // (tiles x slots x column blocks) well inside 32-bit ranges
+  if (t * topk > (int64_t)1 << 21) return EXL3_E_INVALID;
+  return EXL3_OK;
 }
 
 exl3_status check_grouped(const exl3_expert_weights* gu, const exl3_expert_weights* dn, int64_t t,
@@ -98,12 +136,32 @@ exl3_status check_grouped(const exl3_expert_weights* gu, const exl3_expert_weigh
   exl3_status st = check_arena(gu, 2);
   if (st != EXL3_OK) return st;
   if ((st = check_arena(dn, 1)) != EXL3_OK) return st;
-  if (dn->experts != gu->experts || dn->k != gu->n || dn->n != gu->k) return EXL3_E_INVALID;
-  if (t < 0 || topk < 1 || topk > EXL3_MAX_TOPK) return EXL3_E_INVALID;
-  // bounds the pair indices, the tile list and the grouped GEMM's grid
-  // (tiles x slots x column blocks) well inside 32-bit ranges
-  if (t * topk > (int64_t)1 << 21) return EXL3_E_INVALID;
-  return EXL3_OK;
+  return check_grouped_pair(gu, dn, t, topk);
+}
+
+exl3_status check_grouped_mixed(const exl3_expert_weights* gu, const exl3_expert_widths* guw,
+                                const exl3_expert_weights* dn, const exl3_expert_widths* dnw,
+                                int64_t t, int32_t topk) {
+  exl3_status st = check_mixed_arena(gu, guw, 2);
+  if (st != EXL3_OK) return st;
+  if ((st = check_mixed_arena(dn, dnw, 1)) != EXL3_OK) return st;
+  return check_grouped_pair(gu, dn, t, topk);
+}
+
+// The common part of both grouped entry points, once the arenas are checked.
+exl3_status run_grouped(const exl3::ArenaDesc& gu, const exl3::ArenaDesc& dn, const void* x,
+                        const int32_t* topk_ids, const float* topk_weights, int64_t t,
+                        int32_t topk, float* y, void* ws, size_t ws_bytes, exl3_stream_t stream) {
+  if (t == 0) return EXL3_OK;
+  if (!x || !topk_ids || !topk_weights || !y) return EXL3_E_INVALID;
+  if (!aligned16(x) || !aligned16(y) || !aligned4(topk_ids) || !aligned4(topk_weights))
+    return EXL3_E_INVALID;
+  const size_t need = exl3::grouped_workspace(gu, dn, t, topk);
+  if (!ws || ws_bytes < need || !aligned16(ws)) return EXL3_E_WORKSPACE;
+  trace("grouped t topk experts bits", t, topk, gu.experts, gu.bits);
+  return from_hip(exl3::launch_grouped(gu, dn, static_cast<const uint16_t*>(x), topk_ids,
+                                       topk_weights, t, topk, y, ws, ws_bytes,
+                                       reinterpret_cast<hipStream_t>(stream)));
 }
 
 }  // namespace
@@ -272,19 +330,34 @@ exl3_status exl3_grouped_experts(const exl3_expert_weights* gate_up,
                                  const int32_t* topk_ids, const float* topk_weights, int64_t t,
                                  int32_t topk, float* y, void* ws, size_t ws_bytes,
                                  exl3_stream_t stream) {
-  exl3_status st = check_grouped(gate_up, down, t, topk);
+  const exl3_status st = check_grouped(gate_up, down, t, topk);
   if (st != EXL3_OK) return st;
-  if (t == 0) return EXL3_OK;
-  if (!x || !topk_ids || !topk_weights || !y) return EXL3_E_INVALID;
-  if (!aligned16(x) || !aligned16(y) || !aligned4(topk_ids) || !aligned4(topk_weights))
-    return EXL3_E_INVALID;
-  const size_t need = exl3::grouped_workspace(desc(gate_up), desc(down), t, topk);
-  if (!ws || ws_bytes < need || !aligned16(ws)) return EXL3_E_WORKSPACE;
-  trace("grouped t topk experts bits", t, topk, gate_up->experts, gate_up->bits);
-  return from_hip(exl3::launch_grouped(desc(gate_up), desc(down),
-                                       static_cast<const uint16_t*>(x), topk_ids, topk_weights, t,
-                                       topk, y, ws, ws_bytes,
-                                       reinterpret_cast<hipStream_t>(stream)));
+  return run_grouped(desc(gate_up), desc(down), x, topk_ids, topk_weights, t, topk, y, ws,
+                     ws_bytes, stream);
+}
+
+size_t exl3_grouped_experts_mixed_workspace_size(const exl3_expert_weights* gate_up,
+                                                 const exl3_expert_widths* gate_up_widths,
+                                                 const exl3_expert_weights* down,
+                                                 const exl3_expert_widths* down_widths, int64_t t,
+                                                 int32_t topk) {
+  if (check_grouped_mixed(gate_up, gate_up_widths, down, down_widths, t, topk) != EXL3_OK || t == 0)
+    return 0;
+  return exl3::grouped_workspace(desc_mixed(gate_up, gate_up_widths), desc_mixed(down, down_widths),
+                                 t, topk);
+}
+
+exl3_status exl3_grouped_experts_mixed(const exl3_expert_weights* gate_up,
+                                       const exl3_expert_widths* gate_up_widths,
+                                       const exl3_expert_weights* down,
+                                       const exl3_expert_widths* down_widths, const void* x,
+                                       const int32_t* topk_ids, const float* topk_weights,
+                                       int64_t t, int32_t topk, float* y, void* ws,
+                                       size_t ws_bytes, exl3_stream_t stream) {
+  const exl3_status st = check_grouped_mixed(gate_up, gate_up_widths, down, down_widths, t, topk);
+  if (st != EXL3_OK) return st;
+  return run_grouped(desc_mixed(gate_up, gate_up_widths), desc_mixed(down, down_widths), x,
+                     topk_ids, topk_weights, t, topk, y, ws, ws_bytes, stream);
 }
 
 }  // extern "C"

@@ -55,6 +55,7 @@ struct GemmTask {
   const uint16_t* trellis2;
   const uint16_t* svh2;
   const uint16_t* snext;    // fp16 [n]
+  int bits;                 // width of the tensors, read when the kernel's K is 0
 };
 
 __device__ __forceinline__ float silu_f(float z) { return z / (1.0f + __expf(-z)); }
@@ -123,18 +124,14 @@ __device__ __forceinline__ void static_for(F&& f) {
   }
 }
 
+// The workgroup's tile at width K; LDS comes from the kernel (two decoded
+// stages, and the gate results between the passes of R::kGateUp).
 template <int K, int BM, bool Y_F32, class R>
-__global__ __launch_bounds__(kGemmThreads, 2) void gemm_kernel(R r, int k, int n) {
+__device__ __forceinline__ void gemm_tile(const R& r, const GemmTask& T, int k, int n, uint4* bst0,
+                                          uint4* bst1, uint2* gst) {
   constexpr int WM = BM / 4;           // rows per wave tile
   constexpr int MI = WM / 16;          // 16-row MFMA tiles per wave
   static_assert(MI >= 1, "BM must be a multiple of 64");
-  __shared__ uint4 bst0[kGemmBN * 4], bst1[kGemmBN * 4];
-  // R::kGateUp: the gate result of every lane's rows and columns (fp16,
-  // four rows per 8-byte entry) between the two passes
-  __shared__ uint2 gst[R::kGateUp ? 4 * MI * 8 * 64 : 1];
-
-  const GemmTask T = r.task();
-  if (!T.valid) return;
   const int nt16 = n >> 4;
   const int tid = threadIdx.x;
   const int wave = tid >> 6, lane = tid & 63;
@@ -425,6 +422,36 @@ __global__ __launch_bounds__(kGemmThreads, 2) void gemm_kernel(R r, int k, int n
         }
       }
     }
+  }
+}
+
+// K = 1..8: every tile has that width.  K = 0: each tile has its own width
+// (T.bits, a width per expert), taken in the workgroup from one launch; the
+// eight bodies share the kernel's LDS.
+template <int K, int BM, bool Y_F32, class R>
+__global__ __launch_bounds__(kGemmThreads, 2) void gemm_kernel(R r, int k, int n) {
+  constexpr int MI = BM / 64;
+  __shared__ uint4 bst0[kGemmBN * 4], bst1[kGemmBN * 4];
+  // R::kGateUp: the gate result of every lane's rows and columns (fp16,
+  // four rows per 8-byte entry) between the two passes
+  __shared__ uint2 gst[R::kGateUp ? 4 * MI * 8 * 64 : 1];
+
+  const GemmTask T = r.task();
+  if (!T.valid) return;
+  if constexpr (K == 0) {
+    switch (T.bits) {
+      case 1: gemm_tile<1, BM, Y_F32>(r, T, k, n, bst0, bst1, gst); break;
+      case 2: gemm_tile<2, BM, Y_F32>(r, T, k, n, bst0, bst1, gst); break;
+      case 3: gemm_tile<3, BM, Y_F32>(r, T, k, n, bst0, bst1, gst); break;
+      case 4: gemm_tile<4, BM, Y_F32>(r, T, k, n, bst0, bst1, gst); break;
+      case 5: gemm_tile<5, BM, Y_F32>(r, T, k, n, bst0, bst1, gst); break;
+      case 6: gemm_tile<6, BM, Y_F32>(r, T, k, n, bst0, bst1, gst); break;
+      case 7: gemm_tile<7, BM, Y_F32>(r, T, k, n, bst0, bst1, gst); break;
+      case 8: gemm_tile<8, BM, Y_F32>(r, T, k, n, bst0, bst1, gst); break;
+      default: break;
+    }
+  } else {
+    gemm_tile<K, BM, Y_F32>(r, T, k, n, bst0, bst1, gst);
   }
 }
 

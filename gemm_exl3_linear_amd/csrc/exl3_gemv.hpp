@@ -17,6 +17,7 @@ struct GemvTask {
   int64_t ldx;
   int m;                    // activation rows, 1..16
   float* partial;           // fp32 [m][n] slice of this k range
+  int bits;                 // width of the tensor, read when the kernel's K is 0
 };
 
 constexpr size_t kGemvMaxLds = 64 * 1024;
@@ -126,13 +127,8 @@ __device__ __forceinline__ void gemv_tile(const uint32_t (&D)[K], int kt, int m,
 // multiple of PF (the planner guarantees it), so the loop has no tail and no
 // branch around its loads.
 template <int K, int PF, class R>
-__global__ __launch_bounds__(256) void gemv_kernel(R r, int k, int n, int kc) {
-  extern __shared__ __align__(16) unsigned char smem[];
-  __shared__ int last_flag;
-  int unit, split, nb;
-  if (!r.place((int)blockIdx.x, unit, split, nb)) return;  // uniform over the workgroup
-  const GemvTask T = r.task(unit, split);
-  if (!T.valid) return;
+__device__ __forceinline__ void gemv_unit(const R& r, const GemvTask& T, int unit, int split, int nb,
+                                          int n, int kc, unsigned char* smem, int& last_flag) {
   const int m = T.m;
   const int k0 = split * kc;
   const int nt = n >> 4;
@@ -217,6 +213,33 @@ __global__ __launch_bounds__(256) void gemv_kernel(R r, int k, int n, int kc) {
   r.finish(unit, nb, n);
   if (threadIdx.x == 0)  // ready for the next call
     __hip_atomic_store(r.counter(unit, nb), 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+
+// K = 1..8: every unit has that width.  K = 0: each unit has its own width
+// (T.bits, a width per expert), all of them in one launch.
+template <int K, int PF, class R>
+__global__ __launch_bounds__(256) void gemv_kernel(R r, int /*k*/, int n, int kc) {
+  extern __shared__ __align__(16) unsigned char smem[];
+  __shared__ int last_flag;
+  int unit, split, nb;
+  if (!r.place((int)blockIdx.x, unit, split, nb)) return;  // uniform over the workgroup
+  const GemvTask T = r.task(unit, split);
+  if (!T.valid) return;
+  if constexpr (K == 0) {
+    switch (T.bits) {
+      case 1: gemv_unit<1, PF>(r, T, unit, split, nb, n, kc, smem, last_flag); break;
+      case 2: gemv_unit<2, PF>(r, T, unit, split, nb, n, kc, smem, last_flag); break;
+      case 3: gemv_unit<3, PF>(r, T, unit, split, nb, n, kc, smem, last_flag); break;
+      case 4: gemv_unit<4, PF>(r, T, unit, split, nb, n, kc, smem, last_flag); break;
+      case 5: gemv_unit<5, PF>(r, T, unit, split, nb, n, kc, smem, last_flag); break;
+      case 6: gemv_unit<6, PF>(r, T, unit, split, nb, n, kc, smem, last_flag); break;
+      case 7: gemv_unit<7, PF>(r, T, unit, split, nb, n, kc, smem, last_flag); break;
+      case 8: gemv_unit<8, PF>(r, T, unit, split, nb, n, kc, smem, last_flag); break;
+      default: break;
+    }
+  } else {
+    gemv_unit<K, PF>(r, T, unit, split, nb, n, kc, smem, last_flag);
+  }
 }
 
 // Launch with the prefetch depth the k range allows.

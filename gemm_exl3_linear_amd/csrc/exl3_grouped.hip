@@ -5,7 +5,9 @@
 // launch per projection, routing kept on device.  Arc 140V MoE post, section 2:
 // gate+up as one launch over (expert, slot) units sharing the input row, SiLU
 // between the launches, device-side binning of tokens into contiguous
-// per-expert slices (2D), fp32 weighted gather (2D).
+// per-expert slices (2D), fp32 weighted gather (2D).  An arena has one width,
+// or one per expert (TensorFold issue #832, "Activity"); then each launch's
+// workgroups take their expert's width from the device (width-0 kernels).
 //
 // Two regimes, chosen on the host from the number of (token, slot) pairs
 // P = t * topk (no device data is read back):
@@ -64,6 +66,29 @@ static inline int64_t bin_chunks(int64_t P) { return (P + kBinIds - 1) / kBinIds
 
 static inline size_t align256(size_t v) { return (v + 255) & ~(size_t)255; }
 
+// Where an expert's tensors start and how wide they are.  A uniform arena
+// (bits == nullptr) packs expert e at e * slots tensors of the launch's one
+// width; an arena with a width per expert gives each expert's first word and
+// width, and one launch (kernel width 0) serves every width, each workgroup
+// taking its own.
+struct ExpertWidths {
+  const int32_t* bits = nullptr;  // device int32 [experts]
+  const int64_t* off = nullptr;   // device int64 [experts]
+  int64_t words_per_bit = 0;      // words of one (expert, slot) tensor per bit of width
+};
+struct ExpertTensors {
+  const uint16_t* base;  // slot 0
+  int64_t stride;        // words from one slot to the next
+  int bits;              // 0 in a uniform arena (the kernel's own width)
+};
+__device__ __forceinline__ ExpertTensors expert_tensors(const uint16_t* trellis,
+                                                        const ExpertWidths& w, int e, int slots,
+                                                        int64_t tensor_words) {
+  if (!w.bits) return ExpertTensors{trellis + (int64_t)e * slots * tensor_words, tensor_words, 0};
+  const int b = w.bits[e];
+  return ExpertTensors{trellis + w.off[e], w.words_per_bit * b, b};
+}
+
 // ---------------------------------------------------------------------------
 // small-P path
 // ---------------------------------------------------------------------------
@@ -83,6 +108,7 @@ struct GuUnitRes {
   const uint16_t* suh_dn;
   uint16_t* xd;          // fp16 [P][n]: input of the down projection, Hadamard domain
   int pairs;             // P
+  ExpertWidths ew;
   // output group (pair, 128 columns); members (gate|up, k range)
   __device__ bool place(int b, int& u, int& split, int& nb) const {
     int grp, mem;
@@ -98,8 +124,10 @@ struct GuUnitRes {
     const int pair = u >> 1, slot = u & 1;
     const int e = ids[pair];
     const int tok = pair / topk;
+    const ExpertTensors et = expert_tensors(trellis, ew, e, 2, tensor_words);
     T.valid = true;
-    T.trellis = trellis + (int64_t)(e * 2 + slot) * tensor_words;
+    T.trellis = et.base + slot * et.stride;
+    T.bits = et.bits;
     T.suh = suh + (int64_t)(e * 2 + slot) * k;
     T.x = x + (int64_t)tok * k;
     T.ldx = k;
@@ -155,6 +183,7 @@ struct DnUnitRes {
   unsigned int* ctr;   // [t][n/128]
   float* y;            // fp32 [t][n]
   int tokens;          // t
+  ExpertWidths ew;
   // output group (token, 128 columns); members (slot, k range)
   __device__ bool place(int b, int& u, int& split, int& nb) const {
     int grp, mem;
@@ -168,8 +197,10 @@ struct DnUnitRes {
   __device__ GemvTask task(int u, int split) const {
     GemvTask T;
     const int e = ids[u];
+    const ExpertTensors et = expert_tensors(trellis, ew, e, 1, tensor_words);
     T.valid = true;
-    T.trellis = trellis + (int64_t)e * tensor_words;
+    T.trellis = et.base;
+    T.bits = et.bits;
     T.suh = nullptr;
     T.x = xd + (int64_t)u * k;
     T.ldx = k;
@@ -514,6 +545,7 @@ struct GroupedGemmRes {
   int slots;
   int64_t tensor_words;
   float* y;                // fp32 [slots][P][n]
+  ExpertWidths ew;
   __device__ GemmTask task() const {
     const int nbt = n / kGemmBN;
     const int b = (int)blockIdx.x;
@@ -526,10 +558,12 @@ struct GroupedGemmRes {
     T.valid = tile < *ntiles;
     if (!T.valid) return T;
     const TileEntry te = tiles[tile];
+    const ExpertTensors et = expert_tensors(trellis, ew, te.e, slots, tensor_words);
     T.a = a + ((int64_t)slot * P + te.row0) * k;
     T.lda = k;
     T.rows = te.rows;
-    T.trellis = trellis + (int64_t)(te.e * slots + slot) * tensor_words;
+    T.trellis = et.base + slot * et.stride;
+    T.bits = et.bits;
     T.svh = svh + (int64_t)(te.e * slots + slot) * n;
     T.bias = nullptr;
     T.y = y + ((int64_t)slot * P + te.row0) * n;
@@ -570,6 +604,7 @@ struct GroupedGateUpRes {
   const uint16_t* suh_dn;  // fp16 [E][n], the down projection's input signs
   int64_t tensor_words;
   uint16_t* y;             // fp16 [P][n]: x'_d
+  ExpertWidths ew;
   __device__ GemmTask task() const {
     const int nbt = n / kGemmBN;
     const int b = (int)blockIdx.x;
@@ -581,12 +616,14 @@ struct GroupedGateUpRes {
     T.valid = tile < *ntiles;
     if (!T.valid) return T;
     const TileEntry te = tiles[tile];
+    const ExpertTensors et = expert_tensors(trellis, ew, te.e, 2, tensor_words);
     T.a = a + te.row0 * (int64_t)k;
     T.a2 = a + (P + te.row0) * (int64_t)k;
     T.lda = k;
     T.rows = te.rows;
-    T.trellis = trellis + (int64_t)te.e * 2 * tensor_words;
-    T.trellis2 = T.trellis + tensor_words;
+    T.trellis = et.base;
+    T.trellis2 = et.base + et.stride;
+    T.bits = et.bits;
     T.svh = svh + (int64_t)te.e * 2 * n;
     T.svh2 = T.svh + n;
     T.snext = suh_dn + (int64_t)te.e * n;
@@ -611,6 +648,25 @@ struct GroupedGateUpRun {
 };
 
 // ---------------------------------------------------------------------------
+// Words of one (expert, slot) tensor per bit of width.
+static int64_t words_per_bit(const ArenaDesc& a) { return (int64_t)(a.k / 16) * (a.n / 16) * 16; }
+static ExpertWidths arena_widths(const ArenaDesc& a) {
+  ExpertWidths w;
+  if (a.bits == 0) {
+    w.bits = a.ebits;
+    w.off = a.eoff;
+    w.words_per_bit = words_per_bit(a);
+  }
+  return w;
+}
+// One launch of F at the arena's width, or at width 0 (each workgroup takes
+// its expert's width) when the arena has a width per expert.
+template <template <int> class F, class... Args>
+static hipError_t run_widths(const ArenaDesc& a, Args&&... args) {
+  if (a.bits == 0) return F<0>::run(args...);
+  return dispatch_bits<F>(a.bits, args...);
+}
+
 size_t grouped_workspace(const ArenaDesc& gu, const ArenaDesc& dn, int64_t t, int topk) {
   const int64_t P = t * topk;
   if (P <= kGroupedUnitMaxPairs) return unit_layout(gu, dn, P).total;
@@ -622,8 +678,6 @@ hipError_t launch_grouped(const ArenaDesc& gu, const ArenaDesc& dn, const uint16
                           void* ws, size_t /*ws_bytes*/, hipStream_t s) {
   const int64_t P = t * topk;
   const int hidden = gu.k, inter = gu.n;
-  const int64_t words_gu = (int64_t)(gu.k / 16) * (gu.n / 16) * 16 * gu.bits;
-  const int64_t words_dn = (int64_t)(dn.k / 16) * (dn.n / 16) * 16 * dn.bits;
   unsigned char* base = static_cast<unsigned char*>(ws);
   hipError_t e;
   if (P <= kGroupedUnitMaxPairs) {
@@ -633,17 +687,17 @@ hipError_t launch_grouped(const ArenaDesc& gu, const ArenaDesc& dn, const uint16
     float* part_gu = reinterpret_cast<float*>(base + L.part_gu);
     uint16_t* xd = reinterpret_cast<uint16_t*>(base + L.xd);
     float* part_dn = reinterpret_cast<float*>(base + L.part_dn);
-    GuUnitRes rg{gu.trellis, gu.suh, gu.svh, words_gu, hidden, inter, x, topk, ids,
-                 part_gu, L.s_gu, ctr_gu, dn.suh, xd, (int)P};
+    GuUnitRes rg{gu.trellis, gu.suh, gu.svh, words_per_bit(gu) * gu.bits, hidden, inter, x, topk,
+                 ids, part_gu, L.s_gu, ctr_gu, dn.suh, xd, (int)P};
+    rg.ew = arena_widths(gu);
     const int kc_g = hidden / L.s_gu;
-    e = dispatch_bits<GuUnitRun>(gu.bits, rg, hidden, inter, (int)(P * 2), kc_g,
-                                 gemv_lds_bytes(kc_g, 1), s);
+    e = run_widths<GuUnitRun>(gu, rg, hidden, inter, (int)(P * 2), kc_g, gemv_lds_bytes(kc_g, 1), s);
     if (e != hipSuccess) return e;
-    DnUnitRes rd{dn.trellis, dn.svh, words_dn, inter, hidden, xd, ids, w, topk,
+    DnUnitRes rd{dn.trellis, dn.svh, words_per_bit(dn) * dn.bits, inter, hidden, xd, ids, w, topk,
                  part_dn, L.s_dn, ctr_dn, y, (int)t};
+    rd.ew = arena_widths(dn);
     const int kc_d = inter / L.s_dn;
-    return dispatch_bits<DnUnitRun>(dn.bits, rd, inter, hidden, (int)P, kc_d,
-                                    gemv_lds_bytes(kc_d, 1), s);
+    return run_widths<DnUnitRun>(dn, rd, inter, hidden, (int)P, kc_d, gemv_lds_bytes(kc_d, 1), s);
   }
 
   const GemmLayout L = gemm_layout(gu, dn, P);
@@ -670,11 +724,15 @@ hipError_t launch_grouped(const ArenaDesc& gu, const ArenaDesc& dn, const uint16
                        topk, P, hidden, sorted, ids, gu.suh, xg);
   }
   if ((e = hipGetLastError()) != hipSuccess) return e;
-  GroupedGateUpRes rg{tiles, ntiles, xg, P, hidden, inter, gu.trellis, gu.svh, dn.suh, words_gu, xd};
-  e = dispatch_bits<GroupedGateUpRun>(gu.bits, rg, L.bm, L.max_tiles, s);
+  GroupedGateUpRes rg{tiles, ntiles, xg, P, hidden, inter, gu.trellis, gu.svh, dn.suh,
+                      words_per_bit(gu) * gu.bits, xd};
+  rg.ew = arena_widths(gu);
+  e = run_widths<GroupedGateUpRun>(gu, rg, L.bm, L.max_tiles, s);
   if (e != hipSuccess) return e;
-  GroupedGemmRes rd{tiles, ntiles, xd, P, inter, hidden, dn.trellis, dn.svh, 1, words_dn, dbuf};
-  e = dispatch_bits<GroupedGemmRun>(dn.bits, rd, L.bm, L.max_tiles, s);
+  GroupedGemmRes rd{tiles, ntiles, xd, P, inter, hidden, dn.trellis, dn.svh, 1,
+                    words_per_bit(dn) * dn.bits, dbuf};
+  rd.ew = arena_widths(dn);
+  e = run_widths<GroupedGemmRun>(dn, rd, L.bm, L.max_tiles, s);
   if (e != hipSuccess) return e;
   {
     const int64_t n4 = t * (hidden / 4);

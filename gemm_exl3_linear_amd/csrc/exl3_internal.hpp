@@ -103,7 +103,9 @@ struct ArenaDesc {
   const uint16_t* trellis;
   const uint16_t* suh;
   const uint16_t* svh;
-  int experts, slots, k, n, bits;
+  int experts, slots, k, n, bits;  // bits == 0: a width per expert (below)
+  const int32_t* ebits = nullptr;  // device int32 [experts]: width of expert e
+  const int64_t* eoff = nullptr;   // device int64 [experts]: first word of expert e
 };
 size_t grouped_workspace(const ArenaDesc& gu, const ArenaDesc& dn, int64_t t, int topk);
 hipError_t launch_grouped(const ArenaDesc& gu, const ArenaDesc& dn, const uint16_t* x,

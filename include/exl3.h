@@ -99,7 +99,8 @@ typedef struct exl3_weight {
  *   trellis  uint16 [experts][slots][k/16][n/16][16*bits]
  *   suh      fp16 [experts][slots][k]
  *   svh      fp16 [experts][slots][n]
- * Width and codebook are uniform over the arena.                          */
+ * Width and codebook are uniform over the arena (exl3_grouped_experts), or
+ * the width is per expert (exl3_expert_widths, exl3_grouped_experts_mixed). */
 typedef struct exl3_expert_weights {
     const uint16_t* trellis;
     const uint16_t* suh;
@@ -252,6 +253,53 @@ exl3_status exl3_grouped_experts(const exl3_expert_weights* gate_up,
                                  const int32_t* topk_ids, const float* topk_weights, int64_t t,
                                  int32_t topk, float* y, void* ws, size_t ws_bytes,
                                  exl3_stream_t stream);
+
+/* The widths of an arena whose experts each have their own width
+ * (TensorFold issue #832, "Activity": the consolidated module keeps a width
+ * per expert in the representation).  The arena record then has bits == 0,
+ * and expert e's tensors are bits_host[e] bits wide:
+ *   bits_host  int32 [experts] host pointer, each in 1..8; checked on the
+ *              host during the call (nothing is enqueued if one is not)
+ *   bits       int32 [experts] device pointer, 4-byte aligned, the same
+ *              values (read by the kernels)
+ *   offsets    int64 [experts] device pointer, 8-byte aligned: the word
+ *              index in the arena's trellis where expert e's slot 0 starts,
+ *              a multiple of 8; slot s follows at
+ *              offsets[e] + s * (k/16) * (n/16) * 16 * bits[e].
+ *              Experts may be packed in any order.
+ * suh and svh keep the uniform layout [experts][slots][k or n].  Device
+ * values that differ from bits_host, or offsets past the trellis allocation,
+ * are a contract violation and are not checked on device.               */
+typedef struct exl3_expert_widths {
+    const int32_t* bits_host;
+    const int32_t* bits;
+    const int64_t* offsets;
+} exl3_expert_widths;
+
+/* Bytes of device workspace exl3_grouped_experts_mixed needs (0 if
+ * invalid); the same figure as for uniform arenas of the same shapes.     */
+size_t exl3_grouped_experts_mixed_workspace_size(const exl3_expert_weights* gate_up,
+                                                 const exl3_expert_widths* gate_up_widths,
+                                                 const exl3_expert_weights* down,
+                                                 const exl3_expert_widths* down_widths,
+                                                 int64_t t, int32_t topk);
+
+/* exl3_grouped_experts_mixed - exl3_grouped_experts over arenas with a width
+ * per expert (gate_up_widths for the gate/up arena, down_widths for the down
+ * arena; an expert's gate and up share its width).  Arguments, workspace
+ * rules, errors and the result are those of exl3_grouped_experts; each
+ * (token, slot) pair is computed by the same kernels and in the same order
+ * as a uniform arena of its expert's width would compute it, so when every
+ * expert has one width the result is bit-identical to exl3_grouped_experts.
+ * Each projection is still one launch: every workgroup reads its expert's
+ * width and runs the decode of that width.                                 */
+exl3_status exl3_grouped_experts_mixed(const exl3_expert_weights* gate_up,
+                                       const exl3_expert_widths* gate_up_widths,
+                                       const exl3_expert_weights* down,
+                                       const exl3_expert_widths* down_widths, const void* x,
+                                       const int32_t* topk_ids, const float* topk_weights,
+                                       int64_t t, int32_t topk, float* y, void* ws,
+                                       size_t ws_bytes, exl3_stream_t stream);
 
 #ifdef __cplusplus
 }

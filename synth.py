@@ -27,6 +27,7 @@ SEED_DENSE_5120x17408 = 1
 SEED_PREFILL_4096x5120x17408 = 2
 SEED_MIXED_LAYER = 3
 SEED_MOE_256x2048x512 = 4
+SEED_MOE_MIXED_WIDTHS = 5  # the same MoE shape, a width per expert from {2, 3, 4}
 
 
 def rng(seed: int) -> np.random.Generator:

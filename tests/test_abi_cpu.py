@@ -107,6 +107,51 @@ def test_grouped_rejects():
     assert args(gu_cb, dn, 1, 2) == X.EXL3_E_UNSUPPORTED
 
 
+def test_grouped_mixed_widths_validation_host_only():
+    # widths are read from the host array; the device pointers only need to
+    # be present and aligned for the checks (no call here reaches a kernel)
+    L = X.lib()
+    E = 8
+    host = (ctypes.c_int32 * E)(2, 3, 4, 3, 2, 6, 8, 1)
+    wgu = X._Widths(ctypes.addressof(host), 16, 16)
+    wdn = X._Widths(ctypes.addressof(host), 16, 16)
+    gu = X._Arena(16, 16, 16, E, 2, 256, 128, 0, X.CODEBOOK_MUL1)
+    dn = X._Arena(16, 16, 16, E, 1, 128, 256, 0, X.CODEBOOK_MUL1)
+    size = lambda g, wg, d, wd, t, k: L.exl3_grouped_experts_mixed_workspace_size(
+        ctypes.byref(g), ctypes.byref(wg), ctypes.byref(d), ctypes.byref(wd), t, k)
+    call = lambda g, wg, d, wd, t, k, ws=0, n=0: L.exl3_grouped_experts_mixed(
+        ctypes.byref(g), ctypes.byref(wg), ctypes.byref(d), ctypes.byref(wd), 16, 16, 16, t, k, 16, ws, n, 0)
+    # the workspace does not depend on the widths: same as a uniform arena of these shapes
+    gu_u = X._Arena(16, 16, 16, E, 2, 256, 128, 3, X.CODEBOOK_MUL1)
+    dn_u = X._Arena(16, 16, 16, E, 1, 128, 256, 3, X.CODEBOOK_MUL1)
+    for t in (1, 3, 48, 200):
+        want = L.exl3_grouped_experts_workspace_size(ctypes.byref(gu_u), ctypes.byref(dn_u), t, 2)
+        assert want > 0 and size(gu, wgu, dn, wdn, t, 2) == want
+    assert call(gu, wgu, dn, wdn, 1, 2) == X.EXL3_E_WORKSPACE
+    assert call(gu, wgu, dn, wdn, 0, 2) == X.EXL3_OK
+    assert call(gu, wgu, dn, wdn, 1, 0) == X.EXL3_E_INVALID
+    # a uniform record (bits != 0) is not a mixed arena
+    assert call(gu_u, wgu, dn, wdn, 1, 2) == X.EXL3_E_INVALID
+    assert size(gu_u, wgu, dn, wdn, 1, 2) == 0
+    # a width outside 1..8 anywhere in the host array
+    for bad in (0, 9, -1):
+        host[5] = bad
+        assert call(gu, wgu, dn, wdn, 1, 2) == X.EXL3_E_INVALID
+        assert size(gu, wgu, dn, wdn, 1, 2) == 0
+    host[5] = 6
+    # missing or misaligned width arrays
+    for w in (X._Widths(0, 16, 16), X._Widths(ctypes.addressof(host), 0, 16),
+              X._Widths(ctypes.addressof(host), 16, 0), X._Widths(ctypes.addressof(host), 18, 16),
+              X._Widths(ctypes.addressof(host), 16, 20)):
+        assert call(gu, w, dn, wdn, 1, 2) == X.EXL3_E_INVALID
+        assert call(gu, wgu, dn, w, 1, 2) == X.EXL3_E_INVALID
+    # shapes and codebook as for uniform arenas
+    dn_bad = X._Arena(16, 16, 16, E - 1, 1, 128, 256, 0, X.CODEBOOK_MUL1)
+    assert call(gu, wgu, dn_bad, wdn, 1, 2) == X.EXL3_E_INVALID
+    gu_cb = X._Arena(16, 16, 16, E, 2, 256, 128, 0, 1)
+    assert call(gu_cb, wgu, dn, wdn, 1, 2) == X.EXL3_E_UNSUPPORTED
+
+
 def _multi(ws):
     recs = list(ws)
     arr = (ctypes.POINTER(X._Weight) * len(recs))(*[ctypes.pointer(r) for r in recs])

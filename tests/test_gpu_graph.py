@@ -122,3 +122,25 @@ def test_graph_grouped_experts(tt):
         X.exl3_grouped_experts(x, ids, wt, gu, dn, workspace=ws)
         torch.cuda.synchronize()
     _check_graph(lambda: X.exl3_grouped_experts(x, ids, wt, gu, dn, out=y, workspace=ws), [y], between)
+
+
+@pytest.mark.parametrize("tt", [1, 200])
+def test_graph_grouped_experts_mixed_widths(tt):
+    # a width per expert: one launch per width and projection, the token
+    # slots of the unit path arriving over several of them
+    import torch
+    import gemm_exl3_linear_amd as X
+    m = synth.moe_mixed_inputs(909 + tt, tt, experts=16, topk=4, hidden=256, inter=128, widths=(2, 3, 5))
+    gu = X.Exl3MixedArena.from_numpy(m["gate_up"], G.dev())
+    dn = X.Exl3MixedArena.from_numpy(m["down"], G.dev())
+    x = G.to_dev(m["x"])
+    ids = G.to_dev(m["ids"].astype(np.int32))
+    wt = G.to_dev(m["weights"].astype(np.float32))
+    y = torch.empty((tt, 256), dtype=torch.float32, device=G.dev())
+    ws = torch.zeros(X.exl3_grouped_experts_mixed_workspace_size(gu, dn, tt, 4), dtype=torch.uint8,
+                     device=G.dev())
+
+    def between(i):
+        X.exl3_grouped_experts_mixed(x, ids, wt, gu, dn, workspace=ws)
+        torch.cuda.synchronize()
+    _check_graph(lambda: X.exl3_grouped_experts_mixed(x, ids, wt, gu, dn, out=y, workspace=ws), [y], between)
