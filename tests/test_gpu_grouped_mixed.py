@@ -131,3 +131,59 @@ def test_moe_256x2048x512_mixed_widths_t4096_sampled_tokens():
     tokens = np.sort(np.random.default_rng(2).choice(4096, 8, replace=False))
     err = O.rel_frobenius(y[tokens], _ref(m, tokens=tokens))
     assert err < TOL, err
+
+
+def _pack(arena, order, device):
+    """Exl3MixedArena with the experts' tensors laid out in `order` (offsets
+    follow), to check that only the offsets place an expert."""
+    import ctypes
+    import torch
+    import gemm_exl3_linear_amd as X
+    widths = [int(b) for b in arena["bits"]]
+    offsets = np.zeros(len(widths), np.int64)
+    pos, parts = 0, []
+    for e in order:
+        offsets[e] = pos
+        flat = np.ascontiguousarray(arena["trellis"][e]).reshape(-1)
+        parts.append(flat)
+        pos += flat.size
+    flat = np.concatenate(parts)
+    return X.Exl3MixedArena(torch.from_numpy(flat.view(np.int16).copy()).to(device),
+                            torch.from_numpy(arena["suh"].astype(np.float16)).to(device),
+                            torch.from_numpy(arena["svh"].astype(np.float16)).to(device),
+                            torch.tensor(widths, dtype=torch.int32, device=device),
+                            torch.from_numpy(offsets).to(device), (ctypes.c_int32 * len(widths))(*widths))
+
+
+# experts packed in reverse (and shuffled) order: identical results
+@pytest.mark.parametrize("t", [3, 200])
+def test_packing_order_only_moves_offsets(t):
+    import torch
+    import gemm_exl3_linear_amd as X
+    m = _small(t, experts=12, seed=63)
+    ys = []
+    for order in (list(range(12)), list(range(11, -1, -1)), list(np.random.default_rng(7).permutation(12))):
+        gu = _pack(m["gate_up"], order, G.dev())
+        dn = _pack(m["down"], order, G.dev())
+        y = X.exl3_grouped_experts_mixed(G.to_dev(m["x"]), G.to_dev(m["ids"].astype(np.int32)),
+                                         G.to_dev(m["weights"].astype(np.float32)), gu, dn)
+        torch.cuda.synchronize()
+        ys.append(y.cpu().numpy())
+    np.testing.assert_array_equal(ys[1], ys[0])
+    np.testing.assert_array_equal(ys[2], ys[0])
+    err = O.rel_frobenius(ys[0], _ref(m))
+    assert err < TOL, err
+
+
+@pytest.mark.parametrize("t", [1, 50])
+def test_mixed_widths_max_topk(t):
+    m = _small(t, experts=32, topk=16, seed=64)
+    err = O.rel_frobenius(_run_mixed(m), _ref(m))
+    assert err < TOL, err
+
+
+@pytest.mark.parametrize("t", [2, 200])
+def test_mixed_widths_zero_weights_exact_zero(t):
+    m = _small(t, seed=65)
+    y = _run_mixed(m, w=np.zeros_like(m["weights"]))
+    assert (y == 0).all()
