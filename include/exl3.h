@@ -269,7 +269,9 @@ exl3_status exl3_grouped_experts(const exl3_expert_weights* gate_up,
  *              Experts may be packed in any order.
  * suh and svh keep the uniform layout [experts][slots][k or n].  Device
  * values that differ from bits_host, or offsets past the trellis allocation,
- * are a contract violation and are not checked on device.               */
+ * are a contract violation and are not checked on device (a device width
+ * outside 1..8 leaves that expert's pairs uncomputed, the output undefined
+ * and the workspace to be zero-filled again before its next use).        */
 typedef struct exl3_expert_widths {
     const int32_t* bits_host;
     const int32_t* bits;
