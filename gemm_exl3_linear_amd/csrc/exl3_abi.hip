@@ -30,6 +30,13 @@ void trace(const char* what, long long a, long long b, long long c, long long d)
 
 exl3_status from_hip(hipError_t e) { return e == hipSuccess ? EXL3_OK : EXL3_E_HIP; }
 
+// EXL3_CHECK_IDS set and not "0": the grouped calls check their routing ids
+// on the device first (read at every call, so it can be switched at run time).
+bool check_ids_on() {
+  const char* v = getenv("EXL3_CHECK_IDS");
+  return v && v[0] && v[0] != '0';
+}
+
 // Common checks of a tensor record; `mult` is the required multiple of k, n.
 exl3_status check_weight(const exl3_weight* w, int mult, bool need_signs) {
   if (!w) return EXL3_E_INVALID;
@@ -159,6 +166,14 @@ exl3_status run_grouped(const exl3::ArenaDesc& gu, const exl3::ArenaDesc& dn, co
   const size_t need = exl3::grouped_workspace(gu, dn, t, topk);
   if (!ws || ws_bytes < need || !aligned16(ws)) return EXL3_E_WORKSPACE;
   trace("grouped t topk experts bits", t, topk, gu.experts, gu.bits);
+  if (check_ids_on()) {
+    unsigned int bad = 0;
+    const hipError_t e = exl3::count_bad_ids(gu, dn, topk_ids, t, topk, ws,
+                                             reinterpret_cast<hipStream_t>(stream), bad);
+    if (e != hipSuccess) return EXL3_E_HIP;
+    trace("grouped routing ids out of range", (long long)bad, t, topk, gu.experts);
+    if (bad) return EXL3_E_INVALID;
+  }
   return from_hip(exl3::launch_grouped(gu, dn, static_cast<const uint16_t*>(x), topk_ids,
                                        topk_weights, t, topk, y, ws, ws_bytes,
                                        reinterpret_cast<hipStream_t>(stream)));

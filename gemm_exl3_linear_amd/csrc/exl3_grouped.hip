@@ -667,10 +667,45 @@ static hipError_t run_widths(const ArenaDesc& a, Args&&... args) {
   return dispatch_bits<F>(a.bits, args...);
 }
 
+// The layout's own bytes; the routing check's count follows them.
+static size_t layout_bytes(const ArenaDesc& gu, const ArenaDesc& dn, int64_t P) {
+  return P <= kGroupedUnitMaxPairs ? unit_layout(gu, dn, P).total : gemm_layout(gu, dn, P).total;
+}
+
 size_t grouped_workspace(const ArenaDesc& gu, const ArenaDesc& dn, int64_t t, int topk) {
+  return layout_bytes(gu, dn, t * topk) + 256;
+}
+
+// Routing check (debug option): one workgroup counts the ids outside
+// [0, E) and stores the count (no atomics on global memory, no clearing
+// launch).  Reads ids[0 .. P) only.
+constexpr int kCheckThreads = 1024;
+__global__ __launch_bounds__(kCheckThreads) void check_ids_kernel(const int32_t* __restrict__ ids,
+                                                                  int64_t P, int E,
+                                                                  unsigned int* __restrict__ bad) {
+  __shared__ unsigned int cnt;
+  if (threadIdx.x == 0) cnt = 0;
+  __syncthreads();
+  unsigned int mine = 0;
+  for (int64_t i = threadIdx.x; i < P; i += kCheckThreads) {
+    const int e = ids[i];
+    mine += (e < 0 || e >= E) ? 1u : 0u;
+  }
+  if (mine) atomicAdd(&cnt, mine);
+  __syncthreads();
+  if (threadIdx.x == 0) *bad = cnt;
+}
+
+hipError_t count_bad_ids(const ArenaDesc& gu, const ArenaDesc& dn, const int32_t* ids, int64_t t,
+                         int topk, void* ws, hipStream_t s, unsigned int& bad) {
   const int64_t P = t * topk;
-  if (P <= kGroupedUnitMaxPairs) return unit_layout(gu, dn, P).total;
-  return gemm_layout(gu, dn, P).total;
+  unsigned int* dev = reinterpret_cast<unsigned int*>(static_cast<unsigned char*>(ws) +
+                                                      layout_bytes(gu, dn, P));
+  hipLaunchKernelGGL(check_ids_kernel, dim3(1), dim3(kCheckThreads), 0, s, ids, P, gu.experts, dev);
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  if ((e = hipMemcpyAsync(&bad, dev, sizeof(bad), hipMemcpyDeviceToHost, s)) != hipSuccess) return e;
+  return hipStreamSynchronize(s);
 }
 
 hipError_t launch_grouped(const ArenaDesc& gu, const ArenaDesc& dn, const uint16_t* x,

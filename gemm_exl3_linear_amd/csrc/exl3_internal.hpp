@@ -108,6 +108,10 @@ struct ArenaDesc {
   const int64_t* eoff = nullptr;   // device int64 [experts]: first word of expert e
 };
 size_t grouped_workspace(const ArenaDesc& gu, const ArenaDesc& dn, int64_t t, int topk);
+// Counts the routing ids outside [0, experts) on the device and waits for
+// the count (a host synchronisation on s).
+hipError_t count_bad_ids(const ArenaDesc& gu, const ArenaDesc& dn, const int32_t* ids, int64_t t,
+                         int topk, void* ws, hipStream_t s, unsigned int& bad);
 hipError_t launch_grouped(const ArenaDesc& gu, const ArenaDesc& dn, const uint16_t* x,
                           const int32_t* ids, const float* w, int64_t t, int topk, float* y,
                           void* ws, size_t ws_bytes, hipStream_t s);

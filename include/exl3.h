@@ -247,7 +247,12 @@ size_t exl3_grouped_experts_workspace_size(const exl3_expert_weights* gate_up,
  *   ws            device workspace of at least the queried size, zero-filled
  *                 before its first use (same counter rule as exl3_linear)
  * 1 <= topk <= EXL3_MAX_TOPK.  t == 0 returns EXL3_OK without work.
- * Out-of-range ids are a contract violation and are not checked on device. */
+ * Out-of-range ids are a contract violation and are not checked by default.
+ * With the environment variable EXL3_CHECK_IDS set (not "0"; read at every
+ * call), the call first counts the ids outside [0, experts) on the device,
+ * waits for that count on the host (so such calls block and cannot be
+ * graph-captured), and returns EXL3_E_INVALID, with nothing else enqueued,
+ * if there is any.  The same holds for exl3_grouped_experts_mixed.        */
 exl3_status exl3_grouped_experts(const exl3_expert_weights* gate_up,
                                  const exl3_expert_weights* down, const void* x,
                                  const int32_t* topk_ids, const float* topk_weights, int64_t t,

@@ -126,3 +126,36 @@ def test_moe_256x2048x512_k3_t4096_sampled_tokens():
     tokens = np.sort(np.random.default_rng(1).choice(4096, 12, replace=False))
     err = O.rel_frobenius(y[tokens], _ref(m, tokens=tokens))
     assert err < TOL, err
+
+
+# EXL3_CHECK_IDS: ids outside [0, experts) are counted on the device before
+# any expert kernel runs, and the call fails with EXL3_E_INVALID; valid ids
+# give the same result as without the check (both regimes, both entry points)
+@pytest.mark.parametrize("t", [5, 200])
+def test_check_ids_debug_option(t, monkeypatch):
+    import torch
+    import gemm_exl3_linear_amd as X
+    m = _small(t, seed=49)
+    y_off = _run(m)
+    monkeypatch.setenv("EXL3_CHECK_IDS", "1")
+    np.testing.assert_array_equal(_run(m), y_off)
+    gu = X.Exl3Arena.from_numpy(m["gate_up"], G.dev())
+    dn = X.Exl3Arena.from_numpy(m["down"], G.dev())
+    mg = X.Exl3MixedArena.from_numpy(dict(m["gate_up"], trellis=list(m["gate_up"]["trellis"]),
+                                          bits=np.full(16, 3, np.int32)), G.dev())
+    md = X.Exl3MixedArena.from_numpy(dict(m["down"], trellis=list(m["down"]["trellis"]),
+                                          bits=np.full(16, 3, np.int32)), G.dev())
+    x = G.to_dev(m["x"])
+    w = G.to_dev(m["weights"].astype(np.float32))
+    for bad in (16, -1, 1 << 20):
+        ids = m["ids"].copy()
+        ids[t // 2, 1] = bad
+        for call in (lambda i: X.exl3_grouped_experts(x, i, w, gu, dn),
+                     lambda i: X.exl3_grouped_experts_mixed(x, i, w, mg, md)):
+            with pytest.raises(X.Exl3Error) as ei:
+                call(G.to_dev(ids.astype(np.int32)))
+            assert ei.value.status == X.EXL3_E_INVALID
+    torch.cuda.synchronize()
+    y_mixed = X.exl3_grouped_experts_mixed(x, G.to_dev(m["ids"].astype(np.int32)), w, mg, md)
+    torch.cuda.synchronize()
+    np.testing.assert_array_equal(y_mixed.double().cpu().numpy(), y_off)
