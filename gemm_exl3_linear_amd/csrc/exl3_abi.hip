@@ -12,6 +12,14 @@
 namespace {
 
 constexpr int kGemvMaxRows = 16;  // rows up to this use the decode GEMV
+constexpr int64_t kMaxRows = (int64_t)1 << 24;  // activation rows of one call
+// Workgroups of one launch: a grid of 256-thread workgroups must stay below
+// 2^32 threads.
+constexpr int64_t kMaxWorkgroups = ((int64_t)1 << 24) - 1;
+// Bytes of one tensor's trellis: the kernels address it with 32-bit offsets.
+constexpr int64_t kMaxTrellisBytes = (int64_t)1 << 32;
+
+int64_t trellis_bytes(int64_t k, int64_t n, int64_t bits) { return k * n / 8 * bits; }
 
 bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
 bool aligned4(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 3u) == 0; }
@@ -59,6 +67,10 @@ exl3_status check_arena(const exl3_expert_weights* a, int slots) {
   if (a->codebook != EXL3_CODEBOOK_MUL1) return EXL3_E_UNSUPPORTED;
   if (a->slots != slots || a->experts <= 0) return EXL3_E_INVALID;
   if (a->k <= 0 || a->n <= 0 || a->k % 128 || a->n % 128) return EXL3_E_INVALID;
+  // one (expert, slot) tensor: tile counts index 32-bit work plans, and the
+  // grouped GEMM addresses its trellis through a 32-bit buffer descriptor
+  if ((int64_t)(a->k / 16) * (a->n / 16) >= ((int64_t)1 << 31)) return EXL3_E_INVALID;
+  if (trellis_bytes(a->k, a->n, a->bits) >= kMaxTrellisBytes) return EXL3_E_INVALID;
   if (!a->trellis || !a->suh || !a->svh) return EXL3_E_INVALID;
   if (!aligned16(a->trellis) || !aligned16(a->suh) || !aligned16(a->svh)) return EXL3_E_INVALID;
   return EXL3_OK;
@@ -77,7 +89,7 @@ exl3_status check_multi(const exl3_weight* const* w, int32_t count) {
     const exl3_status st = check_weight(w[i], 128, true);
     if (st != EXL3_OK) return st;
     if (w[i]->k != w[0]->k) return EXL3_E_INVALID;
-    if ((int64_t)w[i]->k * w[i]->n / 8 * w[i]->bits >= ((int64_t)1 << 32)) return EXL3_E_INVALID;
+    if (trellis_bytes(w[i]->k, w[i]->n, w[i]->bits) >= kMaxTrellisBytes) return EXL3_E_INVALID;
   }
   return EXL3_OK;
 }
@@ -103,7 +115,7 @@ exl3_status check_mixed_arena(const exl3_expert_weights* a, const exl3_expert_wi
   if (!a || !w) return EXL3_E_INVALID;
   if (a->bits != 0) return EXL3_E_INVALID;
   exl3_expert_weights u = *a;
-  u.bits = 1;
+  u.bits = 8;  // the size limits for the widest width an expert may have
   const exl3_status st = check_arena(&u, slots);
   if (st != EXL3_OK) return st;
   if (!w->bits_host || !w->bits || !w->offsets) return EXL3_E_INVALID;
@@ -167,6 +179,15 @@ exl3_status run_grouped(const exl3::ArenaDesc& gu, const exl3::ArenaDesc& dn, co
   if (!ws || ws_bytes < need || !aligned16(ws)) return EXL3_E_WORKSPACE;
   trace("grouped t topk experts bits", t, topk, gu.experts, gu.bits);
   if (check_ids_on()) {
+    // The check waits on the host for a device count, which a stream being
+    // captured into a graph cannot do: refuse before anything is enqueued,
+    // so the caller's capture stays valid.
+    hipStreamCaptureStatus cs = hipStreamCaptureStatusNone;
+    if (hipStreamIsCapturing(reinterpret_cast<hipStream_t>(stream), &cs) != hipSuccess) {
+      (void)hipGetLastError();
+      return EXL3_E_HIP;
+    }
+    if (cs != hipStreamCaptureStatusNone) return EXL3_E_INVALID;
     unsigned int bad = 0;
     const hipError_t e = exl3::count_bad_ids(gu, dn, topk_ids, t, topk, ws,
                                              reinterpret_cast<hipStream_t>(stream), bad);
@@ -196,9 +217,15 @@ const char* exl3_status_str(exl3_status status) {
   }
 }
 
+// Eight threads per tile, in 256-thread workgroups.
+bool reconstruct_fits(const exl3_weight* w) {
+  return ((int64_t)(w->k / 16) * (w->n / 16) * 8 + 255) / 256 <= kMaxWorkgroups;
+}
+
 exl3_status exl3_reconstruct(const exl3_weight* w, uint16_t* w_out, exl3_stream_t stream) {
   exl3_status st = check_weight(w, 16, false);
   if (st != EXL3_OK) return st;
+  if (!reconstruct_fits(w)) return EXL3_E_INVALID;
   if (!w_out || !aligned16(w_out)) return EXL3_E_INVALID;
   trace("reconstruct k n bits", w->k, w->n, w->bits, 0);
   return from_hip(exl3::launch_reconstruct(w->trellis, w_out, w->k, w->n, w->bits,
@@ -210,6 +237,8 @@ exl3_status exl3_hadamard(const void* in, void* out, int32_t dtype, int64_t rows
                           const uint16_t* sign_after, exl3_stream_t stream) {
   if (dtype != EXL3_F16 && dtype != EXL3_F32) return EXL3_E_INVALID;
   if (rows < 0 || dim <= 0 || dim % 128) return EXL3_E_INVALID;
+  // four 128-element blocks per 256-thread workgroup
+  if (rows > kMaxWorkgroups * 4 || (rows * (dim / 128) + 3) / 4 > kMaxWorkgroups) return EXL3_E_INVALID;
   if (ld_in < dim || ld_out < dim || ld_in % 8 || ld_out % 8) return EXL3_E_INVALID;
   if (rows == 0) return EXL3_OK;
   if (!in || !out || !aligned16(in) || !aligned16(out)) return EXL3_E_INVALID;
@@ -223,7 +252,7 @@ exl3_status exl3_hadamard(const void* in, void* out, int32_t dtype, int64_t rows
 }
 
 size_t exl3_linear_workspace_size(const exl3_weight* w, int64_t m) {
-  if (check_weight(w, 128, false) != EXL3_OK || m < 0) return 0;
+  if (check_weight(w, 128, false) != EXL3_OK || m < 0 || m > kMaxRows) return 0;
   if (m == 0) return 0;
   return linear_ws(w, m);
 }
@@ -233,11 +262,12 @@ exl3_status exl3_linear(const exl3_weight* w, const void* x, int64_t m, int64_t 
                         exl3_stream_t stream) {
   exl3_status st = check_weight(w, 128, true);
   if (st != EXL3_OK) return st;
-  if (m < 0 || m > ((int64_t)1 << 24)) return EXL3_E_INVALID;
+  if (m < 0 || m > kMaxRows) return EXL3_E_INVALID;
   if (y_dtype != EXL3_F16 && y_dtype != EXL3_F32) return EXL3_E_INVALID;
   if (ldx < w->k || ldy < w->n || ldx % 8 || ldy % 8) return EXL3_E_INVALID;
   // the kernels address a tensor's trellis with 32-bit byte offsets
-  if ((int64_t)w->k * w->n / 8 * w->bits >= ((int64_t)1 << 32)) return EXL3_E_INVALID;
+  if (trellis_bytes(w->k, w->n, w->bits) >= kMaxTrellisBytes) return EXL3_E_INVALID;
+  if (m > kGemvMaxRows && exl3::gemm_max_workgroups(w->k, w->n, m) > kMaxWorkgroups) return EXL3_E_INVALID;
   if (m == 0) return EXL3_OK;
   if (!x || !y || !aligned16(x) || !aligned16(y)) return EXL3_E_INVALID;
   const size_t need = linear_ws(w, m);
@@ -258,7 +288,7 @@ exl3_status exl3_linear(const exl3_weight* w, const void* x, int64_t m, int64_t 
 }
 
 size_t exl3_linear_int8_workspace_size(const exl3_weight* w, int64_t m) {
-  if (check_weight(w, 128, false) != EXL3_OK || m <= 0 || m > ((int64_t)1 << 24)) return 0;
+  if (check_weight(w, 128, false) != EXL3_OK || m <= 0 || m > kMaxRows) return 0;
   return exl3::linear_int8_workspace(w->k, m);
 }
 
@@ -267,12 +297,13 @@ exl3_status exl3_linear_int8(const exl3_weight* w, const void* x, int64_t m, int
                              exl3_stream_t stream) {
   exl3_status st = check_weight(w, 128, true);
   if (st != EXL3_OK) return st;
-  if (m < 0 || m > ((int64_t)1 << 24)) return EXL3_E_INVALID;
+  if (m < 0 || m > kMaxRows) return EXL3_E_INVALID;
   if (y_dtype != EXL3_F16 && y_dtype != EXL3_F32) return EXL3_E_INVALID;
   if (ldx < w->k || ldy < w->n || ldx % 8 || ldy % 8) return EXL3_E_INVALID;
-  if ((int64_t)w->k * w->n / 8 * w->bits >= ((int64_t)1 << 32)) return EXL3_E_INVALID;
+  if (trellis_bytes(w->k, w->n, w->bits) >= kMaxTrellisBytes) return EXL3_E_INVALID;
   // the GEMM addresses a 256-row tile of int8 activations with 32-bit offsets
   if ((int64_t)w->k * 256 >= ((int64_t)1 << 31)) return EXL3_E_INVALID;
+  if (exl3::linear_int8_max_workgroups(w->k, w->n, m) > kMaxWorkgroups) return EXL3_E_INVALID;
   if (m == 0) return EXL3_OK;
   if (!x || !y || !aligned16(x) || !aligned16(y)) return EXL3_E_INVALID;
   const size_t need = exl3::linear_int8_workspace(w->k, m);
@@ -287,6 +318,7 @@ exl3_status exl3_linear_int8(const exl3_weight* w, const void* x, int64_t m, int
 exl3_status exl3_reconstruct_int8(const exl3_weight* w, int8_t* w_out, exl3_stream_t stream) {
   exl3_status st = check_weight(w, 16, false);
   if (st != EXL3_OK) return st;
+  if (!reconstruct_fits(w)) return EXL3_E_INVALID;
   if (!w_out || !aligned16(w_out)) return EXL3_E_INVALID;
   trace("reconstruct_int8 k n bits", w->k, w->n, w->bits, 0);
   return from_hip(exl3::launch_reconstruct_int8(w->trellis, w_out, w->k, w->n, w->bits,
@@ -294,7 +326,7 @@ exl3_status exl3_reconstruct_int8(const exl3_weight* w, int8_t* w_out, exl3_stre
 }
 
 size_t exl3_linear_multi_workspace_size(const exl3_weight* const* w, int32_t count, int64_t m) {
-  if (check_multi(w, count) != EXL3_OK || m <= 0) return 0;
+  if (check_multi(w, count) != EXL3_OK || m <= 0 || m > kMaxRows) return 0;
   return multi_ws(w, count, m);
 }
 
@@ -303,9 +335,12 @@ exl3_status exl3_linear_multi(const exl3_weight* const* w, int32_t count, const 
                               void* ws, size_t ws_bytes, exl3_stream_t stream) {
   exl3_status st = check_multi(w, count);
   if (st != EXL3_OK) return st;
-  if (m < 0 || m > ((int64_t)1 << 24)) return EXL3_E_INVALID;
+  if (m < 0 || m > kMaxRows) return EXL3_E_INVALID;
   if (y_dtype != EXL3_F16 && y_dtype != EXL3_F32) return EXL3_E_INVALID;
   if (!y || !ldy || ldx < w[0]->k || ldx % 8) return EXL3_E_INVALID;
+  if (m > kGemvMaxRows)
+    for (int i = 0; i < count; ++i)
+      if (exl3::gemm_max_workgroups(w[i]->k, w[i]->n, m) > kMaxWorkgroups) return EXL3_E_INVALID;
   for (int i = 0; i < count; ++i)
     if (ldy[i] < w[i]->n || ldy[i] % 8) return EXL3_E_INVALID;
   if (m == 0) return EXL3_OK;

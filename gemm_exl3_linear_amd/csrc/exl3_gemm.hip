@@ -85,6 +85,13 @@ size_t gemm_workspace(int k, int n, int m) {
   return counter_region(n) + (size_t)frag_rows(m) * k * sizeof(uint16_t);
 }
 
+int64_t gemm_max_workgroups(int k, int n, int64_t m) {
+  const int64_t frag = (m + 15) / 16 * (k / 128);  // launch_input_frag
+  const int64_t bm = choose_bm(m > (1 << 30) ? (1 << 30) : (int)m);
+  const int64_t gemm = (m + bm - 1) / bm * ((n + kGemmBN - 1) / kGemmBN);
+  return frag > gemm ? frag : gemm;
+}
+
 hipError_t launch_gemm(const uint16_t* trellis, const uint16_t* suh, const uint16_t* svh,
                        const uint16_t* bias, int k, int n, int bits, const uint16_t* x, int m,
                        int64_t ldx, void* y, int64_t ldy, bool y_f32, void* ws, hipStream_t s) {

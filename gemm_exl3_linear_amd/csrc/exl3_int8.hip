@@ -243,6 +243,14 @@ size_t linear_int8_workspace(int k, int64_t m) {
   return i8_scale_offset(k, m) + (((size_t)i8_rows(m) * sizeof(float) + 255) & ~(size_t)255);
 }
 
+int64_t linear_int8_max_workgroups(int k, int n, int64_t m) {
+  (void)k;
+  const int64_t quant = m >= kQuantGroupMinRows ? i8_rows(m) / 16 : i8_rows(m);
+  const int64_t bm = choose_bm_i8(m);
+  const int64_t gemm = (m + bm - 1) / bm * (n / kGemmBN);
+  return quant > gemm ? quant : gemm;
+}
+
 hipError_t launch_linear_int8(const uint16_t* trellis, const uint16_t* suh, const uint16_t* svh,
                               const uint16_t* bias, int k, int n, int bits, const uint16_t* x,
                               int64_t m, int64_t ldx, void* y, int64_t ldy, bool y_f32, void* ws,

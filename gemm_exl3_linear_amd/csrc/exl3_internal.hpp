@@ -83,6 +83,9 @@ hipError_t launch_gemv_multi(const MultiTensor* t, int count, int k, const uint1
                              hipStream_t s);
 
 size_t gemm_workspace(int k, int n, int m);
+// Largest workgroup count of the launches of a prefill call (input transform
+// and GEMM), for the host's check that every grid fits a launch.
+int64_t gemm_max_workgroups(int k, int n, int64_t m);
 hipError_t launch_gemm(const uint16_t* trellis, const uint16_t* suh, const uint16_t* svh,
                        const uint16_t* bias, int k, int n, int bits, const uint16_t* x,
                        int m, int64_t ldx, void* y, int64_t ldy, bool y_f32, void* ws,
@@ -91,6 +94,7 @@ hipError_t launch_gemm(const uint16_t* trellis, const uint16_t* suh, const uint1
 // --- int8 prefill ------------------------------------------------------------
 // workspace: x_q (int8, fragment-major, rows padded to 16) and the row scales
 size_t linear_int8_workspace(int k, int64_t m);
+int64_t linear_int8_max_workgroups(int k, int n, int64_t m);
 hipError_t launch_linear_int8(const uint16_t* trellis, const uint16_t* suh, const uint16_t* svh,
                               const uint16_t* bias, int k, int n, int bits, const uint16_t* x,
                               int64_t m, int64_t ldx, void* y, int64_t ldy, bool y_f32, void* ws,

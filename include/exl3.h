@@ -35,7 +35,16 @@
  *     error nothing is enqueued and a status other than EXL3_OK is returned.
  *     There is no fallback to another code path.
  *   - Device pointers must be 16-byte aligned unless stated otherwise.
- *   - A tensor holds fewer than 2^31 tiles: (k/16) * (n/16) < 2^31.
+ *   - A tensor holds fewer than 2^31 tiles: (k/16) * (n/16) < 2^31, and its
+ *     trellis is smaller than 4 GiB (k * n * bits / 8 < 2^32 bytes); for an
+ *     arena this holds for each (expert, slot) tensor, at width 8 when the
+ *     width is per expert.
+ *   - Sizes whose launches would not fit the hardware's grid limit (2^24 - 1
+ *     workgroups of 256 threads) return EXL3_E_INVALID: calls with m > 2^24
+ *     rows; prefill calls with ceil(m/16) * (k/128) or ceil(m/64) * (n/128)
+ *     at or above that limit; exl3_reconstruct* with (k/16) * (n/16) >= 2^29;
+ *     exl3_hadamard with rows * (dim/128) >= 2^26.  Workspace-size queries
+ *     return 0 for m > 2^24.
  *   - Calls on different streams may run concurrently; a call must not
  *     overlap another call that writes the same output or workspace.
  */
@@ -252,7 +261,9 @@ size_t exl3_grouped_experts_workspace_size(const exl3_expert_weights* gate_up,
  * call), the call first counts the ids outside [0, experts) on the device,
  * waits for that count on the host (so such calls block and cannot be
  * graph-captured), and returns EXL3_E_INVALID, with nothing else enqueued,
- * if there is any.  The same holds for exl3_grouped_experts_mixed.        */
+ * if there is any.  With EXL3_CHECK_IDS set, a call on a stream that is
+ * being captured returns EXL3_E_INVALID without enqueueing anything (the
+ * capture stays valid).  The same holds for exl3_grouped_experts_mixed.    */
 exl3_status exl3_grouped_experts(const exl3_expert_weights* gate_up,
                                  const exl3_expert_weights* down, const void* x,
                                  const int32_t* topk_ids, const float* topk_weights, int64_t t,

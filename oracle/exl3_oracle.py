@@ -374,8 +374,41 @@ def grouped_experts(x, ids, weights, gate_up: dict, down: dict) -> np.ndarray:
 
 
 def rel_frobenius(a, ref) -> float:
-    """||a - ref||_F / ||ref||_F in float64 (the layer-output tolerance metric)."""
+    """||a - ref||_F / ||ref||_F in float64 (the layer-output tolerance metric).
+
+    The Frobenius norm is the square root of the sum of squares over every
+    element, whatever the array's rank.  A zero reference gives the absolute
+    norm ||a||_F instead.
+    """
+    a = np.asarray(a, dtype=np.float64).ravel()
+    ref = np.asarray(ref, dtype=np.float64).ravel()
+    den = math.sqrt(float(np.dot(ref, ref)))
+    diff = a - ref
+    num = math.sqrt(float(np.dot(diff, diff)))
+    return num / den if den > 0 else num
+
+
+def fp16_ulp(v) -> np.ndarray:
+    """Spacing of the fp16 values at |v|: 2^(e - 10) for 2^e <= |v| < 2^(e+1)
+    in the normal range, 2^-24 below it (float64)."""
+    a = np.abs(np.asarray(v, dtype=np.float64))
+    _, e = np.frexp(np.maximum(a, 2.0 ** -14))  # a = f 2^e with f in [0.5, 1)
+    return np.ldexp(1.0, e - 11)
+
+
+def elementwise_excess(a, ref, rel_rms: float, ulps: float = 1.0) -> float:
+    """Largest |a - ref| / (rel_rms * rms(ref) + ulps * fp16_ulp(ref)) over the
+    elements (float64); the per-element bound holds when this is <= 1.
+
+    rms(ref) is the root mean square over the whole array.  The bound sits
+    beside the Frobenius one: a few wrong elements can hide in a norm over
+    millions of them, but not here.
+    """
     a = np.asarray(a, dtype=np.float64)
     ref = np.asarray(ref, dtype=np.float64)
-    den = np.linalg.norm(ref)
-    return float(np.linalg.norm(a - ref) / den) if den > 0 else float(np.linalg.norm(a - ref))
+    assert a.shape == ref.shape
+    if ref.size == 0:
+        return 0.0
+    rms = math.sqrt(float(np.mean(ref * ref)))
+    bound = rel_rms * rms + ulps * fp16_ulp(ref)
+    return float(np.max(np.abs(a - ref) / bound))

@@ -211,3 +211,72 @@ def test_linear_int8_validation_host_only():
     assert L.exl3_reconstruct_int8(ctypes.byref(_w(cb=1)), 16, 0) == X.EXL3_E_UNSUPPORTED
     assert L.exl3_reconstruct_int8(ctypes.byref(_w()), 0, 0) == X.EXL3_E_INVALID
     assert L.exl3_reconstruct_int8(ctypes.byref(_w()), 17, 0) == X.EXL3_E_INVALID
+
+
+def test_row_count_limits_in_workspace_queries():
+    # m above 2^24 rows is refused everywhere, queries included (they return 0
+    # instead of planning with a truncated row count)
+    L = X.lib()
+    w = _w(5120, 17408, 4)
+    assert L.exl3_linear_workspace_size(ctypes.byref(w), 1 << 24) > 0
+    for m in ((1 << 24) + 1, 1 << 31, 1 << 40):
+        assert L.exl3_linear_workspace_size(ctypes.byref(w), m) == 0
+        assert L.exl3_linear_int8_workspace_size(ctypes.byref(w), m) == 0
+        arr = (ctypes.POINTER(X._Weight) * 1)(ctypes.pointer(w))
+        assert L.exl3_linear_multi_workspace_size(arr, 1, m) == 0
+    big = 1 << 25
+    assert L.exl3_linear(ctypes.byref(w), 16, big, 5120, 16, 17408, X.EXL3_F16, 16, 1 << 40, 0) == X.EXL3_E_INVALID
+
+
+def test_prefill_grids_must_fit_one_launch():
+    # 2^24 rows: the GEMM over 32768 columns would need 65536 row tiles x 256
+    # column blocks = 2^24 workgroups, and the input transform of k = 5120
+    # 2^20 x 40 of them; both past the launch limit, refused before any work
+    L = X.lib()
+    m = 1 << 24
+    wide = _w(128, 32768, 1)
+    deep = _w(5120, 128, 1)
+    for w in (wide, deep):
+        st = L.exl3_linear(ctypes.byref(w), 16, m, w.k, 16, w.n, X.EXL3_F16, 16, 1 << 50, 0)
+        assert st == X.EXL3_E_INVALID
+    st = L.exl3_linear_int8(ctypes.byref(wide), 16, m, wide.k, 16, wide.n, X.EXL3_F16, 16, 1 << 50, 0)
+    assert st == X.EXL3_E_INVALID
+    # one row group less keeps the GEMM grid below the limit: the call goes on
+    # to its workspace check
+    ok = L.exl3_linear(ctypes.byref(wide), 16, m - 256, wide.k, 16, wide.n, X.EXL3_F16, 0, 0, 0)
+    assert ok == X.EXL3_E_WORKSPACE
+
+
+def test_reconstruct_and_hadamard_grid_limits():
+    L = X.lib()
+    # (k/16)(n/16) = 2^29 tiles is below the 2^31 tile limit but 8 threads
+    # per tile would need 2^24 workgroups
+    w = _w(1 << 19, 1 << 18, 1)
+    assert L.exl3_reconstruct(ctypes.byref(w), 16, 0) == X.EXL3_E_INVALID
+    assert L.exl3_reconstruct_int8(ctypes.byref(w), 16, 0) == X.EXL3_E_INVALID
+    assert L.exl3_hadamard(16, 16, 0, 1 << 26, 128, 128, 128, 0, 0, 0) == X.EXL3_E_INVALID
+    assert L.exl3_hadamard(16, 16, 0, 1 << 25, 256, 256, 256, 0, 0, 0) == X.EXL3_E_INVALID
+
+
+def test_arena_tensor_size_limits():
+    # one (expert, slot) tensor of 4 GiB (65536 x 65536 at 8 bits) is refused,
+    # also for an arena with a width per expert (checked at width 8 whatever
+    # the host widths say)
+    L = X.lib()
+    big_gu = X._Arena(16, 16, 16, 2, 2, 65536, 65536, 8, X.CODEBOOK_MUL1)
+    big_dn = X._Arena(16, 16, 16, 2, 1, 65536, 65536, 8, X.CODEBOOK_MUL1)
+    ok_gu = X._Arena(16, 16, 16, 2, 2, 65536, 32768, 8, X.CODEBOOK_MUL1)
+    ok_dn = X._Arena(16, 16, 16, 2, 1, 32768, 65536, 8, X.CODEBOOK_MUL1)
+    size = lambda g, d: L.exl3_grouped_experts_workspace_size(ctypes.byref(g), ctypes.byref(d), 1, 2)
+    assert size(ok_gu, ok_dn) > 0
+    assert size(big_gu, big_dn) == 0
+    call = lambda g, d: L.exl3_grouped_experts(ctypes.byref(g), ctypes.byref(d), 16, 16, 16, 1, 2, 16, 0, 0, 0)
+    assert call(big_gu, big_dn) == X.EXL3_E_INVALID
+    assert call(ok_gu, ok_dn) == X.EXL3_E_WORKSPACE
+    host = (ctypes.c_int32 * 2)(2, 2)
+    wd = X._Widths(ctypes.addressof(host), 16, 16)
+    mgu = X._Arena(16, 16, 16, 2, 2, 65536, 65536, 0, X.CODEBOOK_MUL1)
+    mdn = X._Arena(16, 16, 16, 2, 1, 65536, 65536, 0, X.CODEBOOK_MUL1)
+    st = L.exl3_grouped_experts_mixed(ctypes.byref(mgu), ctypes.byref(wd), ctypes.byref(mdn), ctypes.byref(wd),
+                                      16, 16, 16, 1, 2, 16, 0, 0, 0)
+    assert st == X.EXL3_E_INVALID
