@@ -62,8 +62,9 @@ def measured_traffic():
     return t.get("hbm_bytes_per_launch")
 
 
-def time_calls(fn, steps, warmup, stream):
-    """Returns (mean per-launch time from per-call event pairs, whole-loop time).
+def time_calls(fn, steps, warmup, stream, median=False):
+    """Returns (mean per-launch time from per-call event pairs, whole-loop time),
+    and with median=True also the median of the per-call event pairs.
 
     Two timed passes over the same `steps` calls: the whole-loop time comes
     from one event pair around back-to-back calls (nothing recorded between
@@ -87,8 +88,104 @@ def time_calls(fn, steps, warmup, stream):
         fn(warmup + i)
         ends[i].record(stream)
     torch.cuda.synchronize()
-    per = sum(s.elapsed_time(e) for s, e in zip(starts, ends)) / steps
+    times = sorted(s.elapsed_time(e) for s, e in zip(starts, ends))
+    per = sum(times) / steps
+    if median:
+        return per * 1e-3, total, times[steps // 2] * 1e-3
     return per * 1e-3, total
+
+
+def time_graph(calls, replays, stream):
+    """Per-call time of `calls` (a list of functions taking a stream) captured
+    into one graph and replayed: the GPU time of the calls without the host's
+    per-call cost."""
+    import torch
+    side = torch.cuda.Stream()
+    side.wait_stream(stream)
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.stream(side):
+        g.capture_begin()
+        for c in calls:
+            c(side)
+        g.capture_end()
+    stream.wait_stream(side)
+    torch.cuda.synchronize()
+    with torch.cuda.stream(stream):
+        for _ in range(3):
+            g.replay()
+    torch.cuda.synchronize()
+    t0 = torch.cuda.Event(enable_timing=True)
+    t1 = torch.cuda.Event(enable_timing=True)
+    with torch.cuda.stream(stream):
+        t0.record(stream)
+        for _ in range(replays):
+            g.replay()
+        t1.record(stream)
+    torch.cuda.synchronize()
+    return t0.elapsed_time(t1) * 1e-3 / (replays * len(calls))
+
+
+def bench_lib():
+    """The benchmark's measurement kernels (libexl3_bench.so)."""
+    import ctypes
+    path = os.path.join(ROOT, "gemm_exl3_linear_amd", "libexl3_bench.so")
+    if not os.path.exists(path):
+        raise RuntimeError(f"{path} is missing: build first (python -m gemm_exl3_linear_amd.build)")
+    L = ctypes.CDLL(path)
+    L.exl3_bench_stream_read.restype = ctypes.c_int
+    L.exl3_bench_stream_read.argtypes = [ctypes.c_void_p, ctypes.c_size_t, ctypes.c_void_p, ctypes.c_int,
+                                         ctypes.c_int, ctypes.c_void_p]
+    return L
+
+
+def read_ceiling(buffers, nbytes, stream, reps=200):
+    """Practical HBM read ceiling: a plain streaming-read kernel over the same
+    rotated buffers the GEMV reads, back to back; the best of a few launch
+    shapes."""
+    import torch
+    B = bench_lib()
+    sink = torch.empty(1 << 13, dtype=torch.int32, device=buffers[0].device)
+    best = None
+    for wg in (1024, 2048, 4096):
+        for un in (4, 8):
+            def call(i, wg=wg, un=un):
+                rc = B.exl3_bench_stream_read(buffers[i % len(buffers)].data_ptr(), nbytes, sink.data_ptr(), wg, un,
+                                              stream.cuda_stream)
+                if rc != 0:
+                    raise RuntimeError(f"stream read launch failed ({rc})")
+            per, total, med = time_calls(call, reps, 20, stream, median=True)
+            gbs = nbytes * reps / total / 1e9
+            if best is None or gbs > best["GB/s"]:
+                best = {"GB/s": round(gbs, 1), "frac_hbm": round(gbs / HBM_PEAK_GBS, 4),
+                        "us_per_read": round(total / reps * 1e6, 3), "us_per_read_event_median": round(med * 1e6, 3),
+                        "workgroups": wg, "loads_in_flight_per_thread": un, "bytes": nbytes,
+                        "kernel": f"stream_read_kernel<{un}>"}
+    return best
+
+
+def moe_id_sets(ids, experts, torch, dev):
+    """Routing for the one-token legs: the drawn token's top-k slots mapped
+    onto `experts / topk` disjoint expert sets that together cover every
+    expert (a seeded permutation), so that rotating through them makes each
+    call read its experts' weights from HBM, not from the last-level cache."""
+    import numpy as np
+    topk = ids.shape[1]
+    perm = np.random.default_rng(11).permutation(experts).astype(np.int32)
+    return [torch.from_numpy(perm[i * topk:(i + 1) * topk].reshape(1, topk).copy()).to(dev)
+            for i in range(experts // topk)]
+
+
+def moe_t1_bytes(mo):
+    """Algorithmic bytes of one routed-expert call at one token: the trellis
+    and signs of the gate, up and down tensors of the topk experts it
+    reaches, x, the fp32 output and the routing, each once."""
+    t, topk = mo["ids"].shape
+    gu, dn = mo["gate_up"], mo["down"]
+    per_expert = 0
+    for arena, slots in ((gu, 2), (dn, 1)):
+        k, n, b = arena["k"], arena["n"], arena["bits"]
+        per_expert += slots * (k * n * b // 8 + 2 * k + 2 * n)
+    return topk * t * per_expert + 2 * t * gu["k"] + 4 * t * gu["k"] + 8 * t * topk
 
 
 def mixed_layer_leg(X, torch, synth, dev, stream, reps=50):
@@ -254,10 +351,15 @@ def main():
                           "gemv_source_hash": gemv_source_hash()}))
         return
 
-    per_launch, total = time_calls(gemv(1), args.steps, args.warmup, stream)
+    per_launch, total, per_median = time_calls(gemv(1), args.steps, args.warmup, stream, median=True)
     nbytes = linear_bytes(k, n, bits, 1)
     value = nbytes * args.steps / total / 1e9
     achieved = nbytes / per_launch / 1e9
+    # the same calls replayed from one graph (one call per weight copy), and
+    # the plain streaming read of the same copies
+    graph_t = time_graph([lambda st, w=w: X.exl3_linear(xs[:1], w, out=y[:1], workspace=ws, stream=st)
+                          for w in weights], 40, stream)
+    ceiling = read_ceiling(trellis, trellis_bytes, stream)
 
     secondary = {}
     if not args.no_secondary:
@@ -293,35 +395,49 @@ def main():
             gu = X.Exl3Arena.from_numpy(mo["gate_up"], dev)
             dn = X.Exl3Arena.from_numpy(mo["down"], dev)
             xm = torch.from_numpy(mo["x"]).to(dev)
-            ids = torch.from_numpy(mo["ids"]).to(dev)
+            ids_list = moe_id_sets(mo["ids"], 256, torch, dev) if t == 1 else [torch.from_numpy(mo["ids"]).to(dev)]
             wt = torch.from_numpy(mo["weights"]).to(dev)
             wsm = torch.zeros(X.exl3_grouped_experts_workspace_size(gu, dn, t, 8), dtype=torch.uint8, device=dev)
             ym = torch.empty((t, 2048), dtype=torch.float32, device=dev)
             reps = 200 if t == 1 else 10
-            pl, _ = time_calls(lambda i: X.exl3_grouped_experts(xm, ids, wt, gu, dn, out=ym, workspace=wsm,
-                                                                stream=stream), reps, 3, stream)
+            pl, _ = time_calls(lambda i: X.exl3_grouped_experts(xm, ids_list[i % len(ids_list)], wt, gu, dn, out=ym,
+                                                                workspace=wsm, stream=stream), reps, 3, stream)
             flops = 2.0 * t * 8 * 3 * 2048 * 512
-            secondary[f"moe_t{t}"] = {"us_per_call": round(pl * 1e6, 2),
-                                      "TFLOP/s": round(flops / pl / 1e12, 2)}
-            del gu, dn, xm, ids, wt, wsm, ym
+            leg = {"us_per_call": round(pl * 1e6, 2), "TFLOP/s": round(flops / pl / 1e12, 2)}
+            if t == 1:
+                b = moe_t1_bytes(mo)
+                leg.update({"GB/s": round(b / pl / 1e9, 1), "frac_hbm": round(b / pl / 1e9 / HBM_PEAK_GBS, 4),
+                            "algorithmic_bytes": b, "routing": f"{len(ids_list)} id sets rotated over all 256 experts"})
+                leg["us_per_call_graph"] = round(time_graph(
+                    [lambda st, ids=ids: X.exl3_grouped_experts(xm, ids, wt, gu, dn, out=ym, workspace=wsm, stream=st)
+                     for ids in ids_list], 20, stream) * 1e6, 2)
+            else:
+                leg["frac_mfma_f16"] = round(flops / pl / 1e12 / MFMA_F16_PEAK_TFLOPS, 4)
+            secondary[f"moe_t{t}"] = leg
+            del gu, dn, xm, ids_list, wt, wsm, ym
         # the same shape with a width per expert drawn from {2, 3, 4}
         for t in (1, 4096):
             mo = synth.moe_mixed_inputs(synth.SEED_MOE_MIXED_WIDTHS, t, widths=(2, 3, 4))
             gu = X.Exl3MixedArena.from_numpy(mo["gate_up"], dev)
             dn = X.Exl3MixedArena.from_numpy(mo["down"], dev)
             xm = torch.from_numpy(mo["x"]).to(dev)
-            ids = torch.from_numpy(mo["ids"]).to(dev)
+            ids_list = moe_id_sets(mo["ids"], 256, torch, dev) if t == 1 else [torch.from_numpy(mo["ids"]).to(dev)]
             wt = torch.from_numpy(mo["weights"]).to(dev)
             wsm = torch.zeros(X.exl3_grouped_experts_mixed_workspace_size(gu, dn, t, 8), dtype=torch.uint8,
                               device=dev)
             ym = torch.empty((t, 2048), dtype=torch.float32, device=dev)
             reps = 200 if t == 1 else 10
-            pl, _ = time_calls(lambda i: X.exl3_grouped_experts_mixed(xm, ids, wt, gu, dn, out=ym, workspace=wsm,
-                                                                      stream=stream), reps, 3, stream)
+            pl, _ = time_calls(lambda i: X.exl3_grouped_experts_mixed(xm, ids_list[i % len(ids_list)], wt, gu, dn,
+                                                                      out=ym, workspace=wsm, stream=stream),
+                               reps, 3, stream)
             flops = 2.0 * t * 8 * 3 * 2048 * 512
-            secondary[f"moe_mixed_widths_t{t}"] = {"us_per_call": round(pl * 1e6, 2),
-                                                   "TFLOP/s": round(flops / pl / 1e12, 2)}
-            del gu, dn, xm, ids, wt, wsm, ym
+            leg = {"us_per_call": round(pl * 1e6, 2), "TFLOP/s": round(flops / pl / 1e12, 2)}
+            if t == 1:
+                leg["routing"] = f"{len(ids_list)} id sets rotated over all 256 experts"
+            else:
+                leg["frac_mfma_f16"] = round(flops / pl / 1e12 / MFMA_F16_PEAK_TFLOPS, 4)
+            secondary[f"moe_mixed_widths_t{t}"] = leg
+            del gu, dn, xm, ids_list, wt, wsm, ym
 
     cpu = None
     if not args.no_cpu_baseline:
@@ -361,7 +477,12 @@ def main():
                    "algorithmic_bytes_per_call": nbytes},
         "roofline": {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
                      "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": traffic,
-                     "kernel": GEMV_KERNELS, "us_per_launch": round(per_launch * 1e6, 3)},
+                     "kernel": GEMV_KERNELS, "us_per_launch": round(per_launch * 1e6, 3),
+                     "us_per_launch_median": round(per_median * 1e6, 3),
+                     "us_per_call_back_to_back": round(total / args.steps * 1e6, 3),
+                     "us_per_call_graph_replay": round(graph_t * 1e6, 3),
+                     "read_ceiling": ceiling,
+                     "frac_of_read_ceiling": round(achieved / ceiling["GB/s"], 4)},
         "cpu_baseline": cpu,
         "secondary": secondary,
     }

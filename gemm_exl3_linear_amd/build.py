@@ -52,8 +52,20 @@ def _compile(src: str, obj: str) -> tuple[str, int, str]:
     return src, p.returncode, p.stdout + p.stderr
 
 
+CSRC_BENCH = os.path.join(HERE, "csrc_bench")
+LIB_BENCH = os.path.join(HERE, "libexl3_bench.so")
+
+
 def build(verbose: bool = False, jobs: int | None = None) -> str:
-    sources = sorted(os.path.join(CSRC, f) for f in os.listdir(CSRC) if f.endswith(".hip"))
+    """Build libexl3.so (the library) and libexl3_bench.so (the benchmark's
+    measurement kernels)."""
+    _build_lib(CSRC, LIB, verbose, jobs)
+    _build_lib(CSRC_BENCH, LIB_BENCH, verbose, jobs)
+    return LIB
+
+
+def _build_lib(src_dir: str, lib_path: str, verbose: bool, jobs: int | None) -> str:
+    sources = sorted(os.path.join(src_dir, f) for f in os.listdir(src_dir) if f.endswith(".hip"))
     jobs = jobs or min(len(sources), max(1, min(os.cpu_count() or 1, 16)))
     with tempfile.TemporaryDirectory(prefix="exl3build_") as tmp:
         objs = [os.path.join(tmp, os.path.basename(s)[:-4] + ".o") for s in sources]
@@ -66,13 +78,13 @@ def build(verbose: bool = False, jobs: int | None = None) -> str:
         if failed:
             msg = "\n".join(f"--- {os.path.basename(s)}\n{out}" for s, out in failed)
             raise RuntimeError(f"hipcc failed:\n{msg}")
-        tmp_lib = LIB + ".tmp"
+        tmp_lib = lib_path + ".tmp"
         cmd = [hipcc(), f"--offload-arch={ARCH}", "-shared", "-fPIC", "-o", tmp_lib, *objs]
         p = subprocess.run(cmd, capture_output=True, text=True)
         if p.returncode != 0:
             raise RuntimeError(f"link failed:\n{p.stdout}{p.stderr}")
-        os.replace(tmp_lib, LIB)
-    return LIB
+        os.replace(tmp_lib, lib_path)
+    return lib_path
 
 
 if __name__ == "__main__":

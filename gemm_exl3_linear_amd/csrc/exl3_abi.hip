@@ -45,6 +45,14 @@ bool check_ids_on() {
   return v && v[0] && v[0] != '0';
 }
 
+// EXL3_FORCE_DEVICE_SCOPE set and not "0" (debug): every workgroup of the
+// grouped token-parallel path takes the device-scope hand-off that a
+// workgroup dispatched to another XCD than planned takes (read at every call).
+bool force_device_scope_on() {
+  const char* v = getenv("EXL3_FORCE_DEVICE_SCOPE");
+  return v && v[0] && v[0] != '0';
+}
+
 // Common checks of a tensor record; `mult` is the required multiple of k, n.
 exl3_status check_weight(const exl3_weight* w, int mult, bool need_signs) {
   if (!w) return EXL3_E_INVALID;
@@ -196,7 +204,7 @@ exl3_status run_grouped(const exl3::ArenaDesc& gu, const exl3::ArenaDesc& dn, co
     if (bad) return EXL3_E_INVALID;
   }
   return from_hip(exl3::launch_grouped(gu, dn, static_cast<const uint16_t*>(x), topk_ids,
-                                       topk_weights, t, topk, y, ws, ws_bytes,
+                                       topk_weights, t, topk, y, ws, ws_bytes, force_device_scope_on(),
                                        reinterpret_cast<hipStream_t>(stream)));
 }
 

@@ -59,9 +59,8 @@ __device__ __forceinline__ void gemv_prologue(const GemvTask& T, int k0, int kc,
 
 // Sum of the fp32 partial slices s = 0..splits-1 (fixed order) for the two
 // columns col, col+1 of one row; slices are `stride` floats apart.  The
-// slices were written by other workgroups of the same kernel on the same XCD
-// (see gemv_kernel), so the loads are device scope: past this CU's L1, from
-// the XCD's L2.
+// slices were written by other workgroups of the same kernel with
+// device-scope stores (see gemv_unit), so the loads are device scope too.
 __device__ __forceinline__ void sum_partials(const float* p, int splits, int64_t stride, float& a,
                                              float& b) {
   a = 0.f;
@@ -80,7 +79,25 @@ __device__ __forceinline__ void sum_partials(const float* p, int splits, int64_t
 // the group's partial sums pass through one XCD's L2 and the hand-off needs no
 // L2 write-back or invalidate.  Index b: XCD x = b % 8, position i = b / 8;
 // group 8 (i / members) + x, member i % members.
+//
+// Nothing in the programming model promises that dispatch order, so every
+// workgroup checks it (gemv_off_xcd): the partial sums are stored with
+// device-scope stores and read with device-scope loads whatever the
+// placement, and a workgroup found on another XCD than planned (or every
+// workgroup, when the caller forces it) also takes the device-scope release
+// before it arrives, and marks the group so that its finisher takes the
+// device-scope acquire.  Another dispatch policy then costs time, not
+// correctness.
 constexpr int kGemvXcds = 8;
+constexpr unsigned int kGemvOffXcdFlag = 1u << 16;  // arrival of a workgroup off its planned XCD
+
+// XCC_ID hardware register (bits 3:0: the XCD this wave runs on)
+__device__ __forceinline__ int xcc_id() {
+  return __builtin_amdgcn_s_getreg((3 << 11) | 20) & 15;  // hwreg(HW_REG_XCC_ID, 0, 4)
+}
+__device__ __forceinline__ bool gemv_off_xcd(int b, int force) {
+  return force != 0 || xcc_id() != b % kGemvXcds;
+}
 __device__ __forceinline__ bool gemv_place(int b, int groups, int members, int& group, int& member) {
   const int x = b % kGemvXcds, i = b / kGemvXcds;
   group = (i / members) * kGemvXcds + x;
@@ -193,23 +210,34 @@ __device__ __forceinline__ void gemv_unit(const R& r, const GemvTask& T, int uni
     s += red[(m + i) * 128 + c];
     s += red[(2 * m + i) * 128 + c];
     s += red[(3 * m + i) * 128 + c];
-    T.partial[(int64_t)i * n + nb * 128 + c] = s;
+    __hip_atomic_store(T.partial + (int64_t)i * n + nb * 128 + c, s, __ATOMIC_RELAXED,
+                       __HIP_MEMORY_SCOPE_AGENT);
   }
 
   // arrival: the last workgroup of the output group finishes it.  Every
-  // thread's partial stores are complete in the XCD's L2 (vmcnt(0)) before
-  // the workgroup barrier, and the counter moves after it.
-  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup");
+  // thread's partial stores are complete (vmcnt(0)) before the workgroup
+  // barrier, and the counter moves after it.  Off the planned XCD, the
+  // device-scope release comes first and the arrival carries the flag.
+  const bool off = gemv_off_xcd((int)blockIdx.x, r.off_xcd_all);
+  if (off)
+    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "agent");
+  else
+    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup");
   __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0)
   __syncthreads();
   if (threadIdx.x == 0) {
     unsigned int* ctr = r.counter(unit, nb);
-    const unsigned int old = __hip_atomic_fetch_add(ctr, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-    last_flag = (old + 1u == r.arrivals(unit)) ? 1 : 0;
+    const unsigned int inc = off ? 1u + kGemvOffXcdFlag : 1u;
+    const unsigned int now = __hip_atomic_fetch_add(ctr, inc, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) + inc;
+    const bool last = (now & (kGemvOffXcdFlag - 1u)) == r.arrivals(unit);
+    last_flag = !last ? 0 : ((now >= kGemvOffXcdFlag || off) ? 2 : 1);
   }
   __syncthreads();
   if (!last_flag) return;
-  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup");
+  if (last_flag == 2)
+    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "agent");
+  else
+    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup");
   r.finish(unit, nb, n);
   if (threadIdx.x == 0)  // ready for the next call
     __hip_atomic_store(r.counter(unit, nb), 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);

@@ -109,6 +109,7 @@ struct GuUnitRes {
   uint16_t* xd;          // fp16 [P][n]: input of the down projection, Hadamard domain
   int pairs;             // P
   ExpertWidths ew;
+  int off_xcd_all = 0;   // 1: every workgroup takes the device-scope hand-off
   // output group (pair, 128 columns); members (gate|up, k range)
   __device__ bool place(int b, int& u, int& split, int& nb) const {
     int grp, mem;
@@ -184,6 +185,7 @@ struct DnUnitRes {
   float* y;            // fp32 [t][n]
   int tokens;          // t
   ExpertWidths ew;
+  int off_xcd_all = 0; // 1: every workgroup takes the device-scope hand-off
   // output group (token, 128 columns); members (slot, k range)
   __device__ bool place(int b, int& u, int& split, int& nb) const {
     int grp, mem;
@@ -710,7 +712,7 @@ hipError_t count_bad_ids(const ArenaDesc& gu, const ArenaDesc& dn, const int32_t
 
 hipError_t launch_grouped(const ArenaDesc& gu, const ArenaDesc& dn, const uint16_t* x,
                           const int32_t* ids, const float* w, int64_t t, int topk, float* y,
-                          void* ws, size_t /*ws_bytes*/, hipStream_t s) {
+                          void* ws, size_t /*ws_bytes*/, bool off_xcd_all, hipStream_t s) {
   const int64_t P = t * topk;
   const int hidden = gu.k, inter = gu.n;
   unsigned char* base = static_cast<unsigned char*>(ws);
@@ -725,12 +727,14 @@ hipError_t launch_grouped(const ArenaDesc& gu, const ArenaDesc& dn, const uint16
     GuUnitRes rg{gu.trellis, gu.suh, gu.svh, words_per_bit(gu) * gu.bits, hidden, inter, x, topk,
                  ids, part_gu, L.s_gu, ctr_gu, dn.suh, xd, (int)P};
     rg.ew = arena_widths(gu);
+    rg.off_xcd_all = off_xcd_all ? 1 : 0;
     const int kc_g = hidden / L.s_gu;
     e = run_widths<GuUnitRun>(gu, rg, hidden, inter, (int)(P * 2), kc_g, gemv_lds_bytes(kc_g, 1), s);
     if (e != hipSuccess) return e;
     DnUnitRes rd{dn.trellis, dn.svh, words_per_bit(dn) * dn.bits, inter, hidden, xd, ids, w, topk,
                  part_dn, L.s_dn, ctr_dn, y, (int)t};
     rd.ew = arena_widths(dn);
+    rd.off_xcd_all = off_xcd_all ? 1 : 0;
     const int kc_d = inter / L.s_dn;
     return run_widths<DnUnitRun>(dn, rd, inter, hidden, (int)P, kc_d, gemv_lds_bytes(kc_d, 1), s);
   }

@@ -116,8 +116,10 @@ size_t grouped_workspace(const ArenaDesc& gu, const ArenaDesc& dn, int64_t t, in
 // the count (a host synchronisation on s).
 hipError_t count_bad_ids(const ArenaDesc& gu, const ArenaDesc& dn, const int32_t* ids, int64_t t,
                          int topk, void* ws, hipStream_t s, unsigned int& bad);
+// off_xcd_all: every workgroup of the token-parallel path takes the
+// device-scope hand-off (as one dispatched off its planned XCD does).
 hipError_t launch_grouped(const ArenaDesc& gu, const ArenaDesc& dn, const uint16_t* x,
                           const int32_t* ids, const float* w, int64_t t, int topk, float* y,
-                          void* ws, size_t ws_bytes, hipStream_t s);
+                          void* ws, size_t ws_bytes, bool off_xcd_all, hipStream_t s);
 
 }  // namespace exl3

@@ -263,7 +263,13 @@ size_t exl3_grouped_experts_workspace_size(const exl3_expert_weights* gate_up,
  * graph-captured), and returns EXL3_E_INVALID, with nothing else enqueued,
  * if there is any.  With EXL3_CHECK_IDS set, a call on a stream that is
  * being captured returns EXL3_E_INVALID without enqueueing anything (the
- * capture stays valid).  The same holds for exl3_grouped_experts_mixed.    */
+ * capture stays valid).  The same holds for exl3_grouped_experts_mixed.
+ * Small calls (t * topk <= 384) hand partial sums between workgroups planned
+ * on one XCD; a workgroup that finds itself on another XCD takes a
+ * device-scope release/acquire hand-off instead, so results never depend on
+ * the dispatch order.  The environment variable EXL3_FORCE_DEVICE_SCOPE (not
+ * "0"; read at every call) makes every workgroup take that hand-off: the
+ * results are the same bits, only slower (a debug check of the guard).    */
 exl3_status exl3_grouped_experts(const exl3_expert_weights* gate_up,
                                  const exl3_expert_weights* down, const void* x,
                                  const int32_t* topk_ids, const float* topk_weights, int64_t t,

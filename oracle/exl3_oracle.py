@@ -326,7 +326,7 @@ def silu(z: np.ndarray) -> np.ndarray:
     return z / (1.0 + np.exp(-z))
 
 
-def grouped_experts(x, ids, weights, gate_up: dict, down: dict) -> np.ndarray:
+def grouped_experts(x, ids, weights, gate_up: dict, down: dict, decoded=None) -> np.ndarray:
     """Routed contribution Y [t, hidden] (float64).
 
     For each token t and slot s: e = ids[t, s]; g and u are the gate (slot 0)
@@ -339,6 +339,10 @@ def grouped_experts(x, ids, weights, gate_up: dict, down: dict) -> np.ndarray:
     width of each expert (TensorFold issue #832, "Activity": the consolidated
     module keeps a width per expert); ``trellis[e][slot]`` is then expert e's
     tensor at its own width.
+
+    ``decoded`` lets a caller that already holds decode_tensor of some expert
+    tensors skip decoding them: a dict from ("gate_up" or "down", e, slot) to
+    the decoded fp16 [k, n] weight.
     """
     x = np.asarray(x)
     ids = np.asarray(ids)
@@ -355,7 +359,11 @@ def grouped_experts(x, ids, weights, gate_up: dict, down: dict) -> np.ndarray:
     def dec(arena, e, slot):
         key = (id(arena), e, slot)
         if key not in cache:
-            cache[key] = decode_tensor(arena["trellis"][e][slot], width(arena, e))
+            kind = "gate_up" if arena is gate_up else "down"
+            if decoded is not None and (kind, e, slot) in decoded:
+                cache[key] = decoded[(kind, e, slot)]
+            else:
+                cache[key] = decode_tensor(arena["trellis"][e][slot], width(arena, e))
         return cache[key]
 
     for t in range(t_count):

@@ -128,9 +128,8 @@ def test_moe_256x2048x512_mixed_widths_small_t(t):
 def test_moe_256x2048x512_mixed_widths_t4096_sampled_tokens():
     m = synth.moe_mixed_inputs(84, 4096, widths=(2, 3, 4))
     y = _run_mixed(m)
-    tokens = np.sort(np.random.default_rng(2).choice(4096, 8, replace=False))
-    err = O.rel_frobenius(y[tokens], _ref(m, tokens=tokens))
-    assert err < TOL, err
+    tokens = np.sort(np.random.default_rng(2).choice(4096, 256, replace=False))
+    G.assert_parity(y[tokens], G.grouped_ref(m, tokens=tokens), what="mixed widths T=4096")
 
 
 def _pack(arena, order, device):

@@ -142,15 +142,10 @@ def test_linear_int8_workspace_reused_across_sizes():
 
 
 # --- the full-size prefill workload, in the launch configuration the benchmark times ---
-def test_int8_prefill_4096x5120x17408_k4_sampled_rows():
-    # all 4096 rows on the GPU; the oracle on a seeded sample of 24 rows (rows
-    # are independent: quantization and contraction are per row)
+def test_int8_prefill_4096x5120x17408_k4_all_rows():
     d = G.linear_case(synth.SEED_PREFILL_4096x5120x17408, 4096, 5120, 17408, 4)
     y = _run8(d).double().cpu().numpy()
-    rows = np.sort(np.random.default_rng(825).choice(4096, 24, replace=False))
     wq = _wq(synth.SEED_PREFILL_4096x5120x17408, 4096, 5120, 17408, 4)
-    ref = O.linear_int8(d["x"][rows], d["trellis"], d["suh"], d["svh"], 4, wq=wq)
-    assert O.rel_frobenius(y[rows], ref) < TOL8
+    G.assert_parity(y, G.linear_int8_ref(d, Wq=wq), tol=TOL8, what="int8 vs int8 oracle")
     W = G.decoded(synth.SEED_PREFILL_4096x5120x17408, 4096, 5120, 17408, 4)
-    ref16 = O.linear(d["x"][rows], d["trellis"], d["suh"], d["svh"], 4, w_decoded=W)
-    assert O.rel_frobenius(y[rows], ref16) < TOL_VS_FP16
+    assert O.rel_frobenius(y, G.linear_ref(d, W=W)) < TOL_VS_FP16
