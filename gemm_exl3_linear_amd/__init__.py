@@ -29,6 +29,7 @@ EXL3_F32 = 1
 CODEBOOK_MUL1 = 2
 MAX_TOPK = 16
 MAX_MULTI = 8
+SCRATCH_BYTES = 32 << 20  # EXL3_SCRATCH_BYTES
 
 
 class Exl3Error(RuntimeError):
@@ -84,6 +85,8 @@ def lib() -> ctypes.CDLL:
     L.exl3_linear_workspace_size.argtypes = [ctypes.POINTER(_Weight), i64]
     L.exl3_linear.restype = i32
     L.exl3_linear.argtypes = [ctypes.POINTER(_Weight), vp, i64, i64, vp, i64, i32, vp, sz, vp]
+    L.exl3_linear_no_workspace.restype = i32
+    L.exl3_linear_no_workspace.argtypes = [ctypes.POINTER(_Weight), vp, i64, i64, vp, i64, i32, vp]
     L.exl3_reconstruct_int8.restype = i32
     L.exl3_reconstruct_int8.argtypes = [ctypes.POINTER(_Weight), vp, vp]
     L.exl3_linear_int8_workspace_size.restype = sz
@@ -318,6 +321,20 @@ def exl3_linear(x, w: Exl3Weight, out_dtype=None, out=None, workspace=None, stre
     wsb = 0 if workspace is None else workspace.numel() * workspace.element_size()
     _check(lib().exl3_linear(ctypes.byref(cw), _ptr(x), m, x.stride(0), _ptr(out), out.stride(0), ydt,
                              _ptr(workspace), wsb, _stream(stream)), "exl3_linear")
+    return out
+
+
+def exl3_linear_no_workspace(x, w: Exl3Weight, out, stream=None):
+    """exl3_linear_no_workspace: exl3_linear with the library's own device
+    array as workspace; the caller passes the output (nothing is allocated
+    here or in the library)."""
+    import torch
+    assert x.dim() == 2 and x.dtype == torch.float16 and x.stride(1) == 1
+    assert out.dim() == 2 and out.shape[0] == x.shape[0]
+    cw = w._c()
+    _check(lib().exl3_linear_no_workspace(ctypes.byref(cw), _ptr(x), x.shape[0], x.stride(0), _ptr(out),
+                                          out.stride(0), _ydt(out.dtype), _stream(stream)),
+           "exl3_linear_no_workspace")
     return out
 
 

@@ -5,6 +5,9 @@
 #include <stdio.h>
 #include <stdlib.h>
 
+#include <atomic>
+#include <mutex>
+
 #include "exl3.h"
 #include "exl3_gemv.hpp"
 #include "exl3_internal.hpp"
@@ -208,6 +211,71 @@ exl3_status run_grouped(const exl3::ArenaDesc& gu, const exl3::ArenaDesc& dn, co
                                        reinterpret_cast<hipStream_t>(stream)));
 }
 
+// Arguments of exl3_linear other than the workspace (EXL3_OK for m == 0 too).
+exl3_status check_linear_args(const exl3_weight* w, const void* x, int64_t m, int64_t ldx, const void* y,
+                              int64_t ldy, int32_t y_dtype) {
+  exl3_status st = check_weight(w, 128, true);
+  if (st != EXL3_OK) return st;
+  if (m < 0 || m > kMaxRows) return EXL3_E_INVALID;
+  if (y_dtype != EXL3_F16 && y_dtype != EXL3_F32) return EXL3_E_INVALID;
+  if (ldx < w->k || ldy < w->n || ldx % 8 || ldy % 8) return EXL3_E_INVALID;
+  // the kernels address a tensor's trellis with 32-bit byte offsets
+  if (trellis_bytes(w->k, w->n, w->bits) >= kMaxTrellisBytes) return EXL3_E_INVALID;
+  if (m > kGemvMaxRows && exl3::gemm_max_workgroups(w->k, w->n, m) > kMaxWorkgroups) return EXL3_E_INVALID;
+  if (m == 0) return EXL3_OK;
+  if (!x || !y || !aligned16(x) || !aligned16(y)) return EXL3_E_INVALID;
+  return EXL3_OK;
+}
+
+// Eight threads per tile, in 256-thread workgroups.
+bool reconstruct_fits(const exl3_weight* w) {
+  return ((int64_t)(w->k / 16) * (w->n / 16) * 8 + 255) / 256 <= kMaxWorkgroups;
+}
+
+}  // namespace
+
+// ---------------------------------------------------------------------------
+// Scratch for exl3_linear_no_workspace: the workspace of one call, in a
+// file-scope device array (every GPU the library runs on holds its own copy
+// until the process ends).  Host code never uses the array's name as an
+// address: the device address comes from hipGetSymbolAddress, taken once per
+// device with that device current, and is kept per device.
+// ---------------------------------------------------------------------------
+static __device__ __align__(256) unsigned char scratch[EXL3_SCRATCH_BYTES];
+
+namespace {
+
+constexpr int kMaxDevices = 64;
+std::mutex g_scratch_mu;
+std::atomic<void*> g_scratch_ptr[kMaxDevices];
+
+// Device address of `scratch` on the current device (looked up on the first
+// call on that device).
+exl3_status scratch_on_current_device(void** out) {
+  int dev = -1;
+  if (hipGetDevice(&dev) != hipSuccess) {
+    (void)hipGetLastError();
+    return EXL3_E_HIP;
+  }
+  if (dev < 0 || dev >= kMaxDevices) return EXL3_E_HIP;
+  void* p = g_scratch_ptr[dev].load(std::memory_order_acquire);
+  if (!p) {
+    std::lock_guard<std::mutex> lock(g_scratch_mu);
+    p = g_scratch_ptr[dev].load(std::memory_order_relaxed);
+    if (!p) {
+      void* q = nullptr;
+      if (hipGetSymbolAddress(&q, HIP_SYMBOL(scratch)) != hipSuccess || !q) {
+        (void)hipGetLastError();
+        return EXL3_E_HIP;
+      }
+      g_scratch_ptr[dev].store(q, std::memory_order_release);
+      p = q;
+    }
+  }
+  *out = p;
+  return EXL3_OK;
+}
+
 }  // namespace
 
 extern "C" {
@@ -223,11 +291,6 @@ const char* exl3_status_str(exl3_status status) {
     case EXL3_E_HIP: return "HIP launch error";
     default: return "unknown status";
   }
-}
-
-// Eight threads per tile, in 256-thread workgroups.
-bool reconstruct_fits(const exl3_weight* w) {
-  return ((int64_t)(w->k / 16) * (w->n / 16) * 8 + 255) / 256 <= kMaxWorkgroups;
 }
 
 exl3_status exl3_reconstruct(const exl3_weight* w, uint16_t* w_out, exl3_stream_t stream) {
@@ -265,19 +328,23 @@ size_t exl3_linear_workspace_size(const exl3_weight* w, int64_t m) {
   return linear_ws(w, m);
 }
 
+exl3_status exl3_linear_no_workspace(const exl3_weight* w, const void* x, int64_t m, int64_t ldx,
+                                     void* y, int64_t ldy, int32_t y_dtype, exl3_stream_t stream) {
+  exl3_status st = check_linear_args(w, x, m, ldx, y, ldy, y_dtype);
+  if (st != EXL3_OK || m == 0) return st;
+  const size_t need = linear_ws(w, m);
+  if (need > EXL3_SCRATCH_BYTES) return EXL3_E_WORKSPACE;
+  void* ws = nullptr;
+  if (need > 0 && (st = scratch_on_current_device(&ws)) != EXL3_OK) return st;
+  trace("linear_no_workspace k n m bytes", w->k, w->n, m, (long long)need);
+  return exl3_linear(w, x, m, ldx, y, ldy, y_dtype, ws, need, stream);
+}
+
 exl3_status exl3_linear(const exl3_weight* w, const void* x, int64_t m, int64_t ldx, void* y,
                         int64_t ldy, int32_t y_dtype, void* ws, size_t ws_bytes,
                         exl3_stream_t stream) {
-  exl3_status st = check_weight(w, 128, true);
-  if (st != EXL3_OK) return st;
-  if (m < 0 || m > kMaxRows) return EXL3_E_INVALID;
-  if (y_dtype != EXL3_F16 && y_dtype != EXL3_F32) return EXL3_E_INVALID;
-  if (ldx < w->k || ldy < w->n || ldx % 8 || ldy % 8) return EXL3_E_INVALID;
-  // the kernels address a tensor's trellis with 32-bit byte offsets
-  if (trellis_bytes(w->k, w->n, w->bits) >= kMaxTrellisBytes) return EXL3_E_INVALID;
-  if (m > kGemvMaxRows && exl3::gemm_max_workgroups(w->k, w->n, m) > kMaxWorkgroups) return EXL3_E_INVALID;
-  if (m == 0) return EXL3_OK;
-  if (!x || !y || !aligned16(x) || !aligned16(y)) return EXL3_E_INVALID;
+  exl3_status st = check_linear_args(w, x, m, ldx, y, ldy, y_dtype);
+  if (st != EXL3_OK || m == 0) return st;
   const size_t need = linear_ws(w, m);
   if (need > 0 && (!ws || ws_bytes < need || !aligned16(ws))) return EXL3_E_WORKSPACE;
   const hipStream_t s = reinterpret_cast<hipStream_t>(stream);

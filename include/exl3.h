@@ -175,6 +175,31 @@ exl3_status exl3_linear(const exl3_weight* w, const void* x, int64_t m, int64_t 
                         int64_t ldy, int32_t y_dtype, void* ws, size_t ws_bytes,
                         exl3_stream_t stream);
 
+/* Bytes of the device array behind exl3_linear_no_workspace (32 MiB). */
+#define EXL3_SCRATCH_BYTES ((size_t)32 << 20)
+
+/* exl3_linear_no_workspace - exl3_linear without a workspace argument, for
+ * callers that cannot allocate device memory at all: code recorded into a
+ * graph, tight serving loops, harnesses that forbid allocation.  The same
+ * operation, arguments (minus ws and ws_bytes), validation, kernels and
+ * results, bit for bit, as exl3_linear with a workspace.  The workspace is a
+ * device array of EXL3_SCRATCH_BYTES that the library holds on every GPU it
+ * runs on until the process ends; the call itself allocates nothing.
+ *   - A call that needs more than EXL3_SCRATCH_BYTES of workspace
+ *     (exl3_linear_workspace_size(w, m) > EXL3_SCRATCH_BYTES) returns
+ *     EXL3_E_WORKSPACE with nothing enqueued.  Every decode call (m <= 16)
+ *     of tensors up to 5120 x 17408 fits, and prefill calls while
+ *     m * k * 2 bytes (plus a small head) fit.
+ *   - All calls on one GPU share that GPU's array: two calls whose work
+ *     overlaps in time on one GPU (other streams, other host threads) race
+ *     and give undefined results.  Calls in order on one stream are safe.
+ *     Nothing in the array needs to start at zero (these kernels keep no
+ *     state in it between calls).
+ *   - The first call on each GPU looks up the array's device address (a
+ *     host-side query, nothing enqueued); make it outside graph capture.   */
+exl3_status exl3_linear_no_workspace(const exl3_weight* w, const void* x, int64_t m, int64_t ldx,
+                                     void* y, int64_t ldy, int32_t y_dtype, exl3_stream_t stream);
+
 /* Bytes of device workspace exl3_linear_multi needs for m rows of these
  * tensors (0 if the arguments are invalid). */
 size_t exl3_linear_multi_workspace_size(const exl3_weight* const* w, int32_t count, int64_t m);

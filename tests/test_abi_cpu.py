@@ -280,3 +280,21 @@ def test_arena_tensor_size_limits():
     st = L.exl3_grouped_experts_mixed(ctypes.byref(mgu), ctypes.byref(wd), ctypes.byref(mdn), ctypes.byref(wd),
                                       16, 16, 16, 1, 2, 16, 0, 0, 0)
     assert st == X.EXL3_E_INVALID
+
+
+def test_no_workspace_entry_point_host_checks():
+    # exl3_linear_no_workspace validates like exl3_linear and refuses, before
+    # any HIP call, a call whose workspace would exceed the library's array
+    L = X.lib()
+    w = _w(5120, 17408, 4)
+    need = L.exl3_linear_workspace_size(ctypes.byref(w), 4096)
+    assert need > X.SCRATCH_BYTES
+    assert L.exl3_linear_no_workspace(ctypes.byref(w), 16, 4096, 5120, 16, 17408, X.EXL3_F16, 0) == X.EXL3_E_WORKSPACE
+    assert L.exl3_linear_no_workspace(ctypes.byref(_w(bits=9)), 16, 1, 256, 16, 256, X.EXL3_F16, 0) == X.EXL3_E_INVALID
+    assert L.exl3_linear_no_workspace(ctypes.byref(_w(cb=1)), 16, 1, 256, 16, 256, X.EXL3_F16, 0) == X.EXL3_E_UNSUPPORTED
+    assert L.exl3_linear_no_workspace(ctypes.byref(w), 16, 1, 5119, 16, 17408, X.EXL3_F16, 0) == X.EXL3_E_INVALID
+    assert L.exl3_linear_no_workspace(ctypes.byref(w), 16, 0, 5120, 16, 17408, X.EXL3_F16, 0) == X.EXL3_OK
+    # every decode call of the largest workload tensors fits
+    for k, n in ((5120, 17408), (17408, 5120)):
+        for m in range(1, 17):
+            assert L.exl3_linear_workspace_size(ctypes.byref(_w(k, n, 8)), m) <= X.SCRATCH_BYTES
