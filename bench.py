@@ -30,9 +30,9 @@ HBM_PEAK_GBS = 8000.0          # MI355X HBM3E, published
 MFMA_F16_PEAK_TFLOPS = 2500.0  # MI355X dense fp16 matrix, published
 MFMA_I8_PEAK_TOPS = 5000.0     # MI355X dense int8 matrix, published
 METRIC = "EXL3 GEMV HBM GB/s (% of 8 TB/s) at M=1; prefill GEMM TFLOPS (% MFMA)"
-GEMV_SOURCES = ["gemm_exl3_linear_amd/csrc/exl3_device.hpp", "gemm_exl3_linear_amd/csrc/exl3_gemv_sk.hpp",
-                "gemm_exl3_linear_amd/csrc/exl3_gemv.hip"]
-GEMV_KERNELS = "gemv_sk_kernel<4, 1, 4> + gemv_sk_finish"
+GEMV_SOURCES = ["gemm_exl3_linear_amd/csrc/exl3_device.hpp", "gemm_exl3_linear_amd/csrc/exl3_gemv_mf.hpp",
+                "gemm_exl3_linear_amd/csrc/exl3_sk_split.hpp", "gemm_exl3_linear_amd/csrc/exl3_gemv.hip"]
+GEMV_KERNELS = "gemv_mf_kernel<4, 1> + gemv_mf_finish<true>"
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "gemv_dense_5120x17408_k4_m1_traffic.json")
 
 

@@ -5,12 +5,14 @@
 // int8 linears ...": the product runs in the Hadamard domain; "Layout": the
 // Hadamard-in and Hadamard-out kernels around the vector GEMV).
 //
-// Dense tensors run the persistent stream-k kernel of exl3_gemv_sk.hpp
-// followed by its finishing launch.  The workgroup-per-(block, k range)
+// Dense tensors run the matrix-core kernel of exl3_gemv_mf.hpp followed by
+// its finishing launch; the several-tensor call (m == 1) runs the persistent
+// stream-k kernel of exl3_gemv_sk.hpp followed by its finishing launch.  The workgroup-per-(block, k range)
 // gemv_kernel of exl3_gemv.hpp serves the grouped experts' small-batch path;
 // its planning helpers live here.
 #include "exl3_device.hpp"
 #include "exl3_gemv.hpp"
+#include "exl3_gemv_mf.hpp"
 #include "exl3_gemv_sk.hpp"
 #include "exl3_internal.hpp"
 
@@ -55,17 +57,16 @@ int gemv_choose_splits(int k, int groups, int m, int target_wgs) {
   return best > 0 ? best : kb;
 }
 
-// Runs of R row steps over W waves, the first H of which (the first-round
-// waves) take runs kSkTierWeight1 / kSkTierWeight2 times longer than the
-// others.  Falls back to equal runs (H = W) when the weighted split would
-// leave a wave without a step or exceed kSkMaxRun.
-SkSplit make_sk_split(int64_t R, int64_t W, int64_t H) {
+// Runs of R row steps over W waves (or workgroups), the first H of which (the
+// first-round ones) take runs w1 / w2 times longer than the others.  Falls back to equal runs (H = W) when the weighted split would
+// leave a wave without a step or exceed max_run.
+SkSplit make_sk_split(int64_t R, int64_t W, int64_t H, int64_t max_run, int64_t w1, int64_t w2) {
   SkSplit s;
   int64_t B1 = R;
   if (H > 0 && H < W) {
-    const int64_t den = H * kSkTierWeight1 + (W - H) * kSkTierWeight2;
-    B1 = (R * H * kSkTierWeight1 + den / 2) / den;
-    if (B1 < H || R - B1 < W - H || (B1 + H - 1) / H > kSkMaxRun) {
+    const int64_t den = H * w1 + (W - H) * w2;
+    B1 = (R * H * w1 + den / 2) / den;
+    if (B1 < H || R - B1 < W - H || (B1 + H - 1) / H > max_run) {
       H = W;
       B1 = R;
     }
@@ -105,49 +106,52 @@ static void sk_split_extent(const SkSplit& s, int64_t KT, int64_t NB, int64_t W,
   if (W > s.H && s.q2 + (s.rem2 > 0 ? 1 : 0) > longest) longest = s.q2 + (s.rem2 > 0 ? 1 : 0);
 }
 
-// Plan of the dense decode GEMV: W waves (kGemvSkWaves = eight per CU of the
-// 256-CU MI355X; more when runs would exceed kSkMaxRun row steps, fewer for
-// small tensors), their runs, the number of partial slots a block can
-// receive, and the workspace (fp32 partials, then the transformed activations
-// on the MFMA path).  Within each path (v_dot2 for m <= kSkDotMaxRows, MFMA
-// above) the plan depends on (k, n) only, so all m of a path see the same
-// summation order; the dot path takes the two-tier runs.  No device query.
+// Plan of the dense decode GEMV (exl3_gemv_mf.hpp): W workgroups
+// (kMfWorkgroups = two per CU of the 256-CU MI355X, all resident at once;
+// more when runs would exceed kMfMaxRunWG units, fewer for small tensors),
+// their runs over the units (k tile x 256-column pair) in two tiers (the
+// kMfRoundWorkgroups dispatched first take runs kMfTierWeight1 /
+// kMfTierWeight2 longer), the number of partial slots a pair can receive,
+// and the workspace (fp32 partials: four wave slots per workgroup slot for
+// m <= kMfLdsRows, one otherwise; then the transformed activations when
+// m > kMfLdsRows).  The plan depends on (k, n) only, so every m from 1 to 16
+// sums in the same order.  No device query.
 GemvPlan plan_gemv(int k, int n, int m) {
   GemvPlan p;
-  const int64_t KT = k / 16, NB = n / 128, R = KT * NB;
-  int64_t W = kGemvSkWaves;
-  if (W < (R + kSkMaxRun - 1) / kSkMaxRun) W = (R + kSkMaxRun - 1) / kSkMaxRun;
-  W = (W + 3) / 4 * 4;
-  if (W > R) W = (R + 3) / 4 * 4;  // runs of at least one row step (extra waves idle)
-  const bool dot = m <= kSkDotMaxRows;
-  p.split = make_sk_split(R, W, dot ? sk_first_round(0, W, W) : W);
+  const int64_t KT = k / 16, NB = n / 128, NP = (NB + 1) / 2, R = KT * NP;
+  int64_t W = kMfWorkgroups;
+  if (W < (R + kMfMaxRunWG - 1) / kMfMaxRunWG) W = (R + kMfMaxRunWG - 1) / kMfMaxRunWG;
+  if (W > R) W = R;  // runs of at least one unit
+  p.split = make_sk_split(R, W, W > kMfRoundWorkgroups ? kMfRoundWorkgroups : W, kMfMaxRunWG, kMfTierWeight1,
+                          kMfTierWeight2);
   p.splits = (int)W;
-  sk_split_extent(p.split, KT, NB, W, p.slots, p.kc);
+  sk_split_extent(p.split, KT, NP, W, p.slots, p.kc);
   p.lds = 0;
   p.ctr_bytes = 0;
-  p.xprep_off = (((size_t)NB * p.slots * m * 128 * sizeof(float) + 255) & ~(size_t)255);
-  p.ws = p.xprep_off + (dot ? 0 : (size_t)m * k * sizeof(uint16_t));
+  const size_t per_slot = (m <= kMfLdsRows ? 4 : 1) * (size_t)m * 256 * sizeof(float);  // wave or workgroup slots
+  p.xprep_off = ((size_t)NP * p.slots * per_slot + 255) & ~(size_t)255;
+  p.ws = p.xprep_off + (m > kMfLdsRows ? (size_t)m * k * sizeof(uint16_t) : 0);
   return p;
 }
 
 template <int K>
-struct SkRun {
-  static hipError_t run(const SkArgs& a, const GemvPlan& plan, hipStream_t s) {
-    const dim3 grid((unsigned)(a.W / 4));
+struct MfRun {
+  static hipError_t run(const MfArgs& a, const GemvPlan& plan, hipStream_t s) {
+    (void)plan;
+    const dim3 grid((unsigned)a.W);
     if (a.m == 1)
-      hipLaunchKernelGGL((gemv_sk_kernel<K, 1, 4>), grid, dim3(256), 0, s, a);
-    else if (a.m == 2)
-      hipLaunchKernelGGL((gemv_sk_kernel<K, 2, 4>), grid, dim3(256), 0, s, a);
-    else if (a.m == 3)
-      hipLaunchKernelGGL((gemv_sk_kernel<K, 3, 4>), grid, dim3(256), 0, s, a);
-    else if (a.m == 4)
-      hipLaunchKernelGGL((gemv_sk_kernel<K, 4, 4>), grid, dim3(256), 0, s, a);
+      hipLaunchKernelGGL((gemv_mf_kernel<K, 1>), grid, dim3(256), 0, s, a);
+    else if (a.m <= kMfLdsRows)
+      hipLaunchKernelGGL((gemv_mf_kernel<K, kMfLdsRows>), grid, dim3(256), 0, s, a);
     else
-      hipLaunchKernelGGL((gemv_sk_kernel<K, 0, 8>), grid, dim3(256), 0, s, a);
+      hipLaunchKernelGGL((gemv_mf_kernel<K, 0>), grid, dim3(256), 0, s, a);
     const hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
     const int tasks = (a.n / 128) * a.m;  // one 64-thread workgroup each
-    hipLaunchKernelGGL(gemv_sk_finish, dim3((unsigned)tasks), dim3(64), 0, s, a);
+    if (a.m <= kMfLdsRows)
+      hipLaunchKernelGGL(gemv_mf_finish<true>, dim3((unsigned)tasks), dim3(64), 0, s, a);
+    else
+      hipLaunchKernelGGL(gemv_mf_finish<false>, dim3((unsigned)tasks), dim3(64), 0, s, a);
     return hipGetLastError();
   }
 };
@@ -158,14 +162,17 @@ hipError_t launch_gemv(const uint16_t* trellis, const uint16_t* suh, const uint1
                        const GemvPlan& plan, hipStream_t s) {
   unsigned char* base = static_cast<unsigned char*>(ws);
   uint16_t* xprep = nullptr;
-  if (m > kSkDotMaxRows) {
-    // the MFMA path: one input-transform launch for all rows, instead of
-    // every wave transforming the blocks it needs
+  if (m > kMfLdsRows) {
+    // one input-transform launch for all rows (the arithmetic of the waves'
+    // own transform at fewer rows, so a row's x' does not depend on m)
     xprep = reinterpret_cast<uint16_t*>(base + plan.xprep_off);
-    const hipError_t e = launch_hadamard(x, false, xprep, false, m, k, ldx, k, suh, nullptr, s);
+    const int tasks = m * ((k / 128 + 3) / 4);
+    hipLaunchKernelGGL(gemv_xprep_kernel, dim3((unsigned)((tasks + 3) / 4)), dim3(256), 0, s, x, ldx, suh, m, k,
+                       xprep);
+    const hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
   }
-  SkArgs a;
+  MfArgs a;
   a.trellis = trellis;
   a.suh = suh;
   a.x = x;
@@ -175,7 +182,8 @@ hipError_t launch_gemv(const uint16_t* trellis, const uint16_t* suh, const uint1
   a.k = k;
   a.n = n;
   a.KT = k / 16;
-  a.R = a.KT * (n / 128);
+  a.NP = (n / 128 + 1) / 2;
+  a.R = a.KT * a.NP;
   a.W = plan.splits;
   a.sp = plan.split;
   a.slots = plan.slots;
@@ -185,7 +193,7 @@ hipError_t launch_gemv(const uint16_t* trellis, const uint16_t* suh, const uint1
   a.y = y;
   a.ldy = ldy;
   a.y_f32 = y_f32 ? 1 : 0;
-  return dispatch_bits<SkRun>(bits, a, plan, s);
+  return dispatch_bits<MfRun>(bits, a, plan, s);
 }
 
 // ---------------------------------------------------------------------------
@@ -223,7 +231,8 @@ MultiPlan plan_gemv_multi(const MultiTensor* t, int count, int k) {
   size_t off = 0;
   for (int i = 0; i < count; ++i) {
     const int64_t NB = t[i].n / 128, R = KT * NB, W = mp.waves[i];
-    mp.split[i] = make_sk_split(R, W, sk_first_round(mp.wbase[i], W, wsum));
+    mp.split[i] = make_sk_split(R, W, sk_first_round(mp.wbase[i], W, wsum), kSkMaxRun, kSkTierWeight1,
+                                kSkTierWeight2);
     int longest;
     sk_split_extent(mp.split[i], KT, NB, W, mp.slots[i], longest);
     mp.part_off[i] = off;
@@ -249,7 +258,6 @@ hipError_t launch_gemv_multi(const MultiTensor* t, int count, int k, const uint1
     a.suh = t[i].suh;
     a.x = x;
     a.ldx = k;
-    a.xprep = nullptr;
     a.m = 1;
     a.k = k;
     a.n = t[i].n;

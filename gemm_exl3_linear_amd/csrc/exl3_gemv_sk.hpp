@@ -1,52 +1,40 @@
-// Persistent decode GEMV for 1..16 activation rows (dense EXL3 linear).
+// Decode GEMV of several tensors that share one activation row (m == 1) in
+// one launch pair: the projections that read the same input (q, k and v;
+// gate and up) through exl3_linear_multi.
 //
 // Work decomposition ("stream-k" at wave granularity).  A row step is one k
-// tile (16 rows of k) of one 128-column block (8 n tiles of 16 columns): the
-// R = (n/128) * (k/16) row steps are ordered block-major and every wave of the
-// persistent grid takes one contiguous run of them.  Waves never wait for each
-// other: each keeps PF row-pair loads in flight from the start to the end of
-// its run, across block boundaries.
+// tile (16 rows of k) of one 128-column block (8 n tiles of 16 columns): a
+// tensor's R = (n/128) * (k/16) row steps are ordered block-major and every
+// wave of its share of the persistent grid takes one contiguous run of them.
+// Waves never wait for each other: each keeps PF row-pair loads in flight from
+// the start to the end of its run, across block boundaries.  The row
+// contracts on the vector units (v_dot2).  Run lengths come in two tiers
+// (SkSplit).  With two waves per SIMD, the wave dispatched in the first round
+// (one per SIMD, the lower wave ids) is the older one and wins the
+// instruction arbiter whenever both are ready; measured on MI355X at
+// 5120 x 17408, it completes about 1.9 times the row steps of its younger
+// partner in the same time, so equal runs leave the younger waves finishing
+// alone.  The first-round waves therefore take runs kSkTierWeight1 /
+// kSkTierWeight2 times longer than the rest.  The split is part of the plan
+// (a function of k, n and the grid only), never of timing.
 //
-// Up to kSkDotMaxRows rows contract on the vector units (v_dot2), more on the
-// matrix cores.  On the dot path run lengths come in two tiers (SkSplit).
-// With two waves per
-// SIMD, the wave dispatched in the first round (one per SIMD, the lower wave
-// ids) is the older one and wins the instruction arbiter whenever both are
-// ready; measured on MI355X at 5120 x 17408, it completes about 1.9 times the
-// row steps of its younger partner in the same time, so equal runs leave the
-// younger waves finishing alone.  The first-round waves therefore take runs
-// kSkTierWeight1 / kSkTierWeight2 times longer than the rest (1 to 9 % less
-// time per call at 5120 x 17408 across K = 1..8, most at K = 3..6).  The MFMA
-// kernel gained nothing from it and keeps equal runs.  The split is part of
-// the plan (a function of k, n, the path and the grid only), never of timing.
-//
-// gemv_sk_kernel, per wave:
-//   1. dot path: x' = (x .* suh) H of every row for the (at most eight) k
-//      blocks its run touches, four blocks at a time, after the first trellis
-//      loads went out; MFMA path: x' comes from one input-transform launch and
-//      each row step's A fragment travels with the trellis loads.
+// sk_run, per wave:
+//   1. x' = (x .* suh) H for the (at most eight) k blocks its run touches,
+//      four blocks at a time, after the first trellis loads went out.
 //   2. Row step: lane (t, p) loads row pair p of n tile t (one coalesced
 //      4K-byte load per lane) and the first dword of the next row pair (its
 //      spill word), decodes 32 weights into k-pairs of biased codes
-//      b = 1024 + sigma (decode_rowpair<K, true>) and contracts:
-//        dot  : v_dot2_f32_f16 with each row's x' pair of its two k rows, 16
-//               column accumulators per lane and row;
-//        MFMA : k-pairs through a per-wave LDS transpose into MFMA 16x16x16
-//               f16 (rows padded to 16).
-//      alongside, the sum of the segment's x' (a dot with ones per row, or a
-//      ninth MFMA against an all-ones B).
+//      b = 1024 + sigma (decode_rowpair<K, true>) and contracts them with
+//      v_dot2_f32_f16 against the row's x' pair of its two k rows, 16 column
+//      accumulators per lane; alongside, the sum of the segment's x' (a dot
+//      with ones).
 //   3. Segment end (block changes or run ends): sum b x' - 1534 sum x' for
 //      each column goes to the segment's partial slot in the fp32 workspace
 //      (the codebook scale 1775 / 2^18 is applied once, in the finish).
-// gemv_sk_finish, one wave per (activation row, 128-column block): adds the
-// block's slots in slot order, applies the output transform, svh and bias,
-// casts and stores y.  The hand-off between the two is the kernel boundary:
-// no wave waits on another and no cache maintenance runs inside a kernel
-// (the L2 of one XCD does not see another XCD's writes before a device-scope
-// release, which at kernel granularity costs nothing extra).
-// The sums never depend on timing, so results are bit-reproducible; the plan
-// depends on (k, n) and the path only and a row's sums on its own x only, so
-// a row's result does not depend on m within either range (1..4, 5..16).
+// gemv_sk_multi_finish, one wave per 128-column block: adds the block's slots
+// in slot order, applies the output transform, svh and bias, casts and stores
+// y.  The hand-off between the two is the kernel boundary.  The sums never
+// depend on timing, so results are bit-reproducible.
 #pragma once
 
 #include "exl3_device.hpp"
@@ -60,15 +48,13 @@ constexpr int kSkTierWeight1 = 13;    // relative run length, first-round waves
 constexpr int kSkTierWeight2 = 7;     // relative run length, the others
 constexpr int kSkMaxRun = 48;         // longest run (the x' region of a wave)
 constexpr int kSkSlotBatch = 8;     // partial slots per lane loaded per batch in the finish
-constexpr int kSkMaxXBlocks = 8;    // k blocks a run may touch (dot path)
-constexpr int kSkDotMaxRows = 4;    // rows served by the v_dot2 path (one kernel per row count)
+constexpr int kSkMaxXBlocks = 8;    // k blocks a run may touch
 
 struct SkArgs {
   const uint16_t* trellis;  // [k/16][n/16][16K]
   const uint16_t* suh;      // fp16 [k]
   const uint16_t* x;        // fp16 [m][ldx]
   int64_t ldx;
-  const uint16_t* xprep;    // fp16 [m][k] already transformed (MFMA path), else nullptr
   int m;
   int k, n;
   int KT;                   // k / 16
@@ -117,21 +103,17 @@ __device__ __forceinline__ void reduce_rowpairs(float (&acc)[16], float& c0, flo
   }
 }
 
-// LDS per wave: dot path: x' blocks [kSkMaxXBlocks][128] fp16 (2 KB) per row;
-// MFMA path: transpose region [8 n tiles][8 row pairs][20] dwords (5 KB)
+// LDS per wave: x' blocks [kSkMaxXBlocks][128] fp16 (2 KB) per row
 constexpr int kSkWaveLdsDot = kSkMaxXBlocks * 128 * 2;
-constexpr int kSkWaveLdsMfma = 64 * 20 * 4;
 // a run of kSkMaxRun steps starting anywhere in a k block fits the x' region
 static_assert(32 * (kSkMaxRun + 8) + 32 <= kSkWaveLdsDot, "x' region too small");
 static_assert((7 + kSkMaxRun + 7) / 8 <= kSkMaxXBlocks, "run touches too many k blocks");
 
-// The work of wave `wid` of a tensor's grid; wl is the wave's LDS region.
-// MR > 0: the v_dot2 contraction for up to MR activation rows (x' of row i in
-// the wave's i-th kSkWaveLdsDot region); MR = 0: the matrix-core contraction.
-template <int K, int MR, int PF>
+// The work of wave `wid` of a tensor's grid; wl is the wave's LDS region:
+// the v_dot2 contraction for up to NR activation rows (x' of row i in the
+// wave's i-th kSkWaveLdsDot region).
+template <int K, int NR, int PF>
 __device__ __forceinline__ void sk_run(const SkArgs& a, int wid, unsigned char* wl) {
-  constexpr bool DOT = MR > 0;
-  constexpr int NR = DOT ? MR : 1;  // dot-path row slots
   const int len = sk_run_len(a.sp, wid);
   if (len <= 0) return;
   const int r0 = sk_run_start(a.sp, wid);
@@ -139,7 +121,7 @@ __device__ __forceinline__ void sk_run(const SkArgs& a, int wid, unsigned char* 
   const int KT = a.KT;
   const int lane = threadIdx.x & 63;
   const int t = lane >> 3, p = lane & 7;   // decode role
-  const int g = lane >> 4, j = lane & 15;  // MFMA role
+  const int g = lane >> 4, j = lane & 15;  // input-transform role
 
   // The run starts at k tile kt0 of block nb0; the wave is partial slot
   // slot0 of that block and slot 0 of every later one.
@@ -161,17 +143,9 @@ __device__ __forceinline__ void sk_run(const SkArgs& a, int wid, unsigned char* 
   int pf_nb = nb0, pf_kt = kt0, pf_left = len;
   uint32_t pf_soff = (uint32_t)kt0 * kt_bytes;
   __amdgpu_buffer_rsrc_t pf_rs = make_rsrc(tr0 + (int64_t)pf_nb * kBlkBytes, col_bytes);
-  // MFMA path: the A fragment of a row step, x'[j][16 kt + 4 g .. + 3]
-  __amdgpu_buffer_rsrc_t x_rs = make_rsrc(a.xprep, DOT ? 0u : (uint32_t)m * a.k * 2);
-  const uint32_t x_voff = (uint32_t)(((j < m ? j : 0) * a.k + 4 * g) * 2);
-  auto pf_load = [&](uint32_t (&D)[K + 1], uint2& A) {
+  auto pf_load = [&](uint32_t (&D)[K + 1]) {
     load_rowpair_buf<K>(pf_rs, lane_off, pf_soff, D);
     D[K] = __builtin_amdgcn_raw_buffer_load_b32(pf_rs, (int)spill_off, (int)pf_soff, 0);
-    if constexpr (!DOT) {
-      typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
-      const u32x2 v = __builtin_amdgcn_raw_buffer_load_b64(x_rs, (int)x_voff, pf_kt * 32, 0);
-      A = make_uint2(v.x, v.y);
-    }
   };
   auto pf_advance = [&]() {  // stays on the last row step once the run is exhausted
     if (pf_left > 1) {
@@ -187,12 +161,12 @@ __device__ __forceinline__ void sk_run(const SkArgs& a, int wid, unsigned char* 
     }
   };
 
-  // ---- dot path: x and suh of the k blocks the run touches go out first: k
-  // block b of the run is (kt0 / 8 + b) mod k/128; lane l loads 8 elements of
-  // run block l / 16 (first round) and 4 + l / 16 (second round), of every row.
+  // ---- x and suh of the k blocks the run touches go out first: k block b of
+  // the run is (kt0 / 8 + b) mod k/128; lane l loads 8 elements of run block
+  // l / 16 (first round) and 4 + l / 16 (second round), of every row.
   const int nblk = ((kt0 & 7) + len + 7) >> 3;
-  uint4 xv[NR][DOT ? 2 : 1], sv[DOT ? 2 : 1];
-  if constexpr (DOT) {
+  uint4 xv[NR][2], sv[2];
+  {
     const int kb0 = kt0 >> 3, KBn = KT >> 3;
 #pragma unroll
     for (int rd = 0; rd < 2; ++rd) {
@@ -207,14 +181,13 @@ __device__ __forceinline__ void sk_run(const SkArgs& a, int wid, unsigned char* 
   }
 
   uint32_t ring[PF][K + 1];
-  uint2 aring[PF];
 #pragma unroll
   for (int s = 0; s < PF; ++s) {
-    pf_load(ring[s], aring[s]);
+    pf_load(ring[s]);
     pf_advance();
   }
 
-  if constexpr (DOT) {
+  {
 #pragma unroll
     for (int i = 0; i < NR; ++i) {
       uint16_t* xs = reinterpret_cast<uint16_t*>(wl + i * kSkWaveLdsDot);
@@ -246,49 +219,29 @@ __device__ __forceinline__ void sk_run(const SkArgs& a, int wid, unsigned char* 
 
   // ---- main loop
   float dacc[NR][16];
-  float dxs[NR];    // dot path: sum of the lane's x' pairs over the segment, per row
-  float4_t macc[8];
-  float4_t mxs;     // MFMA path: sum of x' over the segment, per row (any column)
+  float dxs[NR];    // sum of the lane's x' pairs over the segment, per row
   auto clear_acc = [&]() {
-    if constexpr (DOT) {
 #pragma unroll
-      for (int i = 0; i < NR; ++i) {
+    for (int i = 0; i < NR; ++i) {
 #pragma unroll
-        for (int c = 0; c < 16; ++c) dacc[i][c] = 0.f;
-        dxs[i] = 0.f;
-      }
-    } else {
-#pragma unroll
-      for (int q = 0; q < 8; ++q) macc[q] = float4_t{0.f, 0.f, 0.f, 0.f};
-      mxs = float4_t{0.f, 0.f, 0.f, 0.f};
+      for (int c = 0; c < 16; ++c) dacc[i][c] = 0.f;
+      dxs[i] = 0.f;
     }
   };
   clear_acc();
-  uint32_t* tr = reinterpret_cast<uint32_t*>(wl);
-  uint32_t* my = tr + (t * 8 + p) * 20;
 
   // segment end: the wave's column sums to the segment's slot (no wait)
   auto flush = [&](int nb, int slot) {
     float* dst = a.part + ((int64_t)nb * a.slots + slot) * m * 128;
-    if constexpr (DOT) {
 #pragma unroll
-      for (int i = 0; i < NR; ++i) {
-        if (i < m) {  // uniform
+    for (int i = 0; i < NR; ++i) {
+      if (i < m) {  // uniform
 #pragma unroll
-          for (int c = 0; c < 16; ++c) dacc[i][c] = __builtin_fmaf(-kSigmaBiasPlus1024, dxs[i], dacc[i][c]);
-          float c0, c1;
-          reduce_rowpairs(dacc[i], c0, c1);
-          *reinterpret_cast<float2*>(dst + i * 128 + 16 * t + 2 * p) = make_float2(c0, c1);
-        }
+        for (int c = 0; c < 16; ++c) dacc[i][c] = __builtin_fmaf(-kSigmaBiasPlus1024, dxs[i], dacc[i][c]);
+        float c0, c1;
+        reduce_rowpairs(dacc[i], c0, c1);
+        *reinterpret_cast<float2*>(dst + i * 128 + 16 * t + 2 * p) = make_float2(c0, c1);
       }
-    } else {
-#pragma unroll
-      for (int q = 0; q < 8; ++q)
-#pragma unroll
-        for (int rr = 0; rr < 4; ++rr) {
-          const int i = 4 * g + rr;
-          if (i < m) dst[i * 128 + 16 * q + j] = __builtin_fmaf(-kSigmaBiasPlus1024, mxs[rr], macc[q][rr]);
-        }
     }
     clear_acc();
   };
@@ -302,8 +255,7 @@ __device__ __forceinline__ void sk_run(const SkArgs& a, int wid, unsigned char* 
   half2_t xp[NR];
 #pragma unroll
   for (int i = 0; i < NR; ++i) {
-    xp[i] = half2_t{0, 0};
-    if constexpr (DOT) xp[i] = *reinterpret_cast<const half2_t*>(xlane + i * kSkWaveLdsDot);
+    xp[i] = *reinterpret_cast<const half2_t*>(xlane + i * kSkWaveLdsDot);
   }
   int c_nb = nb0, c_slot = slot0;
   int to_end = KT - kt0;  // row steps left in the current block
@@ -316,40 +268,15 @@ __device__ __forceinline__ void sk_run(const SkArgs& a, int wid, unsigned char* 
         uint32_t wp[16];
         decode_rowpair<K, true>(*reinterpret_cast<const uint32_t(*)[K]>(ring[s]),
                                 stream_dword(ring[s][K]), wp);
-        if constexpr (DOT) {
-          const half2_t ones = {(_Float16)1.0f, (_Float16)1.0f};
+        const half2_t ones = {(_Float16)1.0f, (_Float16)1.0f};
 #pragma unroll
-          for (int i = 0; i < NR; ++i) {
-            const half2_t xc = xp[i];
-            xp[i] = *reinterpret_cast<const half2_t*>(xg + i * kSkWaveLdsDot + 32 * (s + 1));
-            dxs[i] = __builtin_amdgcn_fdot2(xc, ones, dxs[i], false);
+        for (int i = 0; i < NR; ++i) {
+          const half2_t xc = xp[i];
+          xp[i] = *reinterpret_cast<const half2_t*>(xg + i * kSkWaveLdsDot + 32 * (s + 1));
+          dxs[i] = __builtin_amdgcn_fdot2(xc, ones, dxs[i], false);
 #pragma unroll
-            for (int c = 0; c < 16; ++c)
-              dacc[i][c] = __builtin_amdgcn_fdot2(__builtin_bit_cast(half2_t, wp[c]), xc, dacc[i][c], false);
-          }
-        } else {
-          uint4* my4 = reinterpret_cast<uint4*>(my);
-          my4[0] = make_uint4(wp[0], wp[1], wp[2], wp[3]);
-          my4[1] = make_uint4(wp[4], wp[5], wp[6], wp[7]);
-          my4[2] = make_uint4(wp[8], wp[9], wp[10], wp[11]);
-          my4[3] = make_uint4(wp[12], wp[13], wp[14], wp[15]);
-          __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront", "local");
-          __builtin_amdgcn_wave_barrier();
-          __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront", "local");
-          half4_t av = {0, 0, 0, 0};
-          if (j < m) av = __builtin_bit_cast(half4_t, aring[s]);
-#pragma unroll
-          for (int q = 0; q < 8; ++q) {
-            const uint32_t b0 = tr[(q * 8 + 2 * g) * 20 + j];
-            const uint32_t b1 = tr[(q * 8 + 2 * g + 1) * 20 + j];
-            const half4_t bv = __builtin_bit_cast(half4_t, make_uint2(b0, b1));
-            macc[q] = __builtin_amdgcn_mfma_f32_16x16x16f16(av, bv, macc[q], 0, 0, 0);
-          }
-          const half4_t ones4 = {(_Float16)1.0f, (_Float16)1.0f, (_Float16)1.0f, (_Float16)1.0f};
-          mxs = __builtin_amdgcn_mfma_f32_16x16x16f16(av, ones4, mxs, 0, 0, 0);
-          __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront", "local");
-          __builtin_amdgcn_wave_barrier();
-          __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront", "local");
+          for (int c = 0; c < 16; ++c)
+            dacc[i][c] = __builtin_amdgcn_fdot2(__builtin_bit_cast(half2_t, wp[c]), xc, dacc[i][c], false);
         }
         // segment end at a block end or the run's end
         --to_end;
@@ -364,7 +291,7 @@ __device__ __forceinline__ void sk_run(const SkArgs& a, int wid, unsigned char* 
       }
       // refill the slot (unconditionally: every step issues the same loads, so
       // the wait counts stay static); past the end, re-read the last step
-      pf_load(ring[s], aring[s]);
+      pf_load(ring[s]);
       pf_advance();
     }
   }
@@ -437,23 +364,6 @@ __device__ __forceinline__ void sk_finish(const SkArgs& a, int i, int nb) {
   }
 }
 
-
-template <int K, int MR, int PF>
-__global__ __launch_bounds__(256) void gemv_sk_kernel(SkArgs a) {
-  constexpr int WAVE_LDS = MR > 0 ? MR * kSkWaveLdsDot : kSkWaveLdsMfma;
-  __shared__ __align__(16) unsigned char smem[4 * WAVE_LDS];
-  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
-  sk_run<K, MR, PF>(a, (int)blockIdx.x * 4 + wave, smem + wave * WAVE_LDS);
-}
-
-// One wave (a 64-thread workgroup, so the tasks spread over the CUs) per
-// (activation row i, 128-column block nb).
-__global__ __launch_bounds__(64) void gemv_sk_finish(SkArgs a) {
-  const int NB = a.n >> 7;
-  const int task = (int)blockIdx.x;
-  const int i = task / NB;
-  sk_finish(a, i, task - i * NB);
-}
 
 // ---------------------------------------------------------------------------
 // Several tensors that share one activation row (m == 1) in one launch pair:

@@ -43,13 +43,13 @@ hipError_t launch_hadamard(const void* in, bool in_f32, void* out, bool out_f32,
 
 // --- dense linear ----------------------------------------------------------
 struct GemvPlan {
-  SkSplit split;     // runs of the waves
-  int splits;        // waves of the persistent grid
-  int kc;            // longest run of row steps per wave
-  int slots;         // partial-sum slots per 128-column block
+  SkSplit split;     // runs of the workgroups
+  int splits;        // workgroups of the grid
+  int kc;            // longest run of units
+  int slots;         // partial-sum slots per 256-column pair
   size_t lds;        // dynamic LDS bytes of the kernel
   size_t ctr_bytes;  // bytes before the fp32 partials (0: no arrival counters)
-  size_t xprep_off;  // offset of the transformed rows x' (m > 1)
+  size_t xprep_off;  // offset of the transformed rows x' (m > 4)
   size_t ws;         // workspace bytes (partials + x')
 };
 GemvPlan plan_gemv(int k, int n, int m);

@@ -36,9 +36,53 @@ __global__ __launch_bounds__(256) void stream_read_kernel(const uint4* __restric
   }
 }
 
+typedef _Float16 half4_t __attribute__((ext_vector_type(4)));
+typedef float float4_t __attribute__((ext_vector_type(4)));
+
+// A chain of kMfmaChain v_mfma_f32_16x16x16_f16 per wave, each on its own A
+// and B fragments (lane l holds A[l % 16][4 (l / 16) .. + 3] and
+// B[4 (l / 16) .. + 3][l % 16]), accumulating into the previous result as a
+// decode GEMV accumulates over k: once with every A and once with every A
+// negated (sign bits flipped), nothing else around them.  out holds the
+// result for problem w at [w][0][lane][4], the negated one at [w][1][lane][4].
+constexpr int kMfmaChain = 4;
+__global__ __launch_bounds__(64) void mfma_negation_kernel(const uint16_t* __restrict__ a,
+                                                           const uint16_t* __restrict__ b,
+                                                           float* __restrict__ out) {
+  const int w = blockIdx.x, l = threadIdx.x;
+  float4_t dp = {0.f, 0.f, 0.f, 0.f}, dn = {0.f, 0.f, 0.f, 0.f};
+  for (int c = 0; c < kMfmaChain; ++c) {
+    half4_t av, an, bv;
+    for (int i = 0; i < 4; ++i) {
+      const int64_t e = (((int64_t)w * kMfmaChain + c) * 64 + l) * 4 + i;
+      const uint16_t x = a[e];
+      av[i] = __builtin_bit_cast(_Float16, x);
+      an[i] = __builtin_bit_cast(_Float16, (uint16_t)(x ^ 0x8000u));
+      bv[i] = __builtin_bit_cast(_Float16, b[e]);
+    }
+    dp = __builtin_amdgcn_mfma_f32_16x16x16f16(av, bv, dp, 0, 0, 0);
+    dn = __builtin_amdgcn_mfma_f32_16x16x16f16(an, bv, dn, 0, 0, 0);
+  }
+  for (int i = 0; i < 4; ++i) {
+    out[((w * 2 + 0) * 64 + l) * 4 + i] = dp[i];
+    out[((w * 2 + 1) * 64 + l) * 4 + i] = dn[i];
+  }
+}
+
 }  // namespace
 
 extern "C" {
+
+// `problems` independent chains of four 16x16x16 fp16 products on the
+// matrix cores, each with A and with -A: a, b fp16 [problems][4][64][4]
+// (lane fragments), out fp32 [problems][2][64][4].  Returns 0, -1 for invalid arguments, or the HIP
+// error code of the launch.
+int exl3_bench_mfma_negation(const uint16_t* a, const uint16_t* b, float* out, int problems,
+                             hipStream_t stream) {
+  if (!a || !b || !out || problems < 1 || problems > (1 << 20)) return -1;
+  hipLaunchKernelGGL(mfma_negation_kernel, dim3(problems), dim3(64), 0, stream, a, b, out);
+  return (int)hipGetLastError();
+}
 
 // Reads `bytes` bytes (a multiple of 16) at the 16-byte aligned device
 // pointer p on `stream` with `workgroups` workgroups of 256 threads and

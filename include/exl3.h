@@ -166,9 +166,9 @@ size_t exl3_linear_workspace_size(const exl3_weight* w, int64_t m);
  *          (of any size, on the same stream) without clearing it.
  * m == 0 returns EXL3_OK without enqueueing anything.  The kernel (decode
  * GEMV for m <= 16, MFMA GEMM above) is chosen internally from m.  Within
- * each of the ranges 1 <= m <= 4, 5 <= m <= 16 and m > 16 a row's result
- * does not depend on m or on the other rows (bit for bit); across them the
- * summation order differs, so results agree to rounding.
+ * each of the ranges 1 <= m <= 16 and m > 16 a row's result does not depend
+ * on m or on the other rows (bit for bit); across them the summation order
+ * differs, so results agree to rounding.
  * The trellis of the tensor must be smaller than 4 GiB (k * n * bits / 8 <
  * 2^32 bytes), else EXL3_E_INVALID.                                        */
 exl3_status exl3_linear(const exl3_weight* w, const void* x, int64_t m, int64_t ldx, void* y,

@@ -37,6 +37,20 @@ def decoded(seed, m, k, n, bits):
     return O.decode_tensor(d["trellis"], bits)
 
 
+def bench_lib():
+    """The benchmark's measurement kernels (libexl3_bench.so), for tests that
+    look at one instruction with nothing around it."""
+    import ctypes
+    import os
+    path = os.path.join(os.path.dirname(os.path.dirname(os.path.abspath(__file__))), "gemm_exl3_linear_amd",
+                        "libexl3_bench.so")
+    L = ctypes.CDLL(path)
+    L.exl3_bench_mfma_negation.restype = ctypes.c_int
+    L.exl3_bench_mfma_negation.argtypes = [ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p, ctypes.c_int,
+                                           ctypes.c_void_p]
+    return L
+
+
 def f16_bits(t):
     return t.detach().cpu().numpy().view(np.uint16)
 
