@@ -12,7 +12,11 @@ the same stream), timed per call with HIP events on the launch stream.  The
 float64 oracle is timed on the host on the same workload as the CPU baseline.
 
 python bench.py [--gpus 1] [--steps K] [--warmup W] [--no-cpu-baseline]
-                [--no-secondary] [--profile-pass]
+                [--no-secondary] [--profile-pass [gemv|prefill|prefill_int8|moe4096]]
+
+--profile-pass runs a short fixed sequence for counter collection instead of
+the benchmark: a plain 256 MiB device copy (the scale of the HBM byte
+counters), then a few calls of one leg.
 """
 from __future__ import annotations
 
@@ -301,8 +305,11 @@ def main():
     ap.add_argument("--warmup", type=int, default=100)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-secondary", action="store_true")
-    ap.add_argument("--profile-pass", action="store_true",
-                    help="short run for counter collection: a plain copy of known size, then 50 GEMV calls")
+    ap.add_argument("--profile-pass", nargs="?", const="gemv", default=None,
+                    choices=["gemv", "prefill", "prefill_int8", "moe4096"],
+                    help="short run for counter collection: a plain copy of known size, then a few calls of "
+                         "one leg (gemv: 50 M=1 calls; prefill / prefill_int8: 10 M=4096 calls; moe4096: 5 "
+                         "routed-expert calls at T=4096)")
     args = ap.parse_args()
     world = int(os.environ.get("WORLD_SIZE", "1"))
     if args.gpus != 1 or world != 1:
@@ -344,10 +351,41 @@ def main():
         b = torch.empty_like(a)
         for _ in range(5):
             b.copy_(a)
-        for i in range(50):
-            gemv(1)(i)
         torch.cuda.synchronize()
-        print(json.dumps({"profile_pass": True, "copy_bytes": a.numel(), "gemv_calls": 50,
+        del a, b
+        kind = args.profile_pass
+        if kind == "gemv":
+            for i in range(50):
+                gemv(1)(i)
+            calls = 50
+        elif kind in ("prefill", "prefill_int8"):
+            dp = synth.linear_inputs(synth.SEED_PREFILL_4096x5120x17408, 4096, k, n, bits)
+            wp = X.Exl3Weight.from_numpy(dp["trellis"], dp["suh"], dp["svh"], bits, device=dev)
+            xp = torch.from_numpy(dp["x"]).to(dev)
+            yp = torch.empty((4096, n), dtype=torch.float16, device=dev)
+            if kind == "prefill":
+                wsp = torch.zeros(X.exl3_linear_workspace_size(wp, 4096), dtype=torch.uint8, device=dev)
+                fn = lambda: X.exl3_linear(xp, wp, out=yp, workspace=wsp, stream=stream)
+            else:
+                wsp = torch.empty(X.exl3_linear_int8_workspace_size(wp, 4096), dtype=torch.uint8, device=dev)
+                fn = lambda: X.exl3_linear_int8(xp, wp, out=yp, workspace=wsp, stream=stream)
+            calls = 10
+            for _ in range(calls):
+                fn()
+        else:
+            mo = synth.moe_inputs(synth.SEED_MOE_256x2048x512, 4096)
+            gu = X.Exl3Arena.from_numpy(mo["gate_up"], dev)
+            dn = X.Exl3Arena.from_numpy(mo["down"], dev)
+            xm = torch.from_numpy(mo["x"]).to(dev)
+            ids = torch.from_numpy(mo["ids"]).to(dev)
+            wt = torch.from_numpy(mo["weights"]).to(dev)
+            wsm = torch.zeros(X.exl3_grouped_experts_workspace_size(gu, dn, 4096, 8), dtype=torch.uint8, device=dev)
+            ym = torch.empty((4096, 2048), dtype=torch.float32, device=dev)
+            calls = 5
+            for _ in range(calls):
+                X.exl3_grouped_experts(xm, ids, wt, gu, dn, out=ym, workspace=wsm, stream=stream)
+        torch.cuda.synchronize()
+        print(json.dumps({"profile_pass": kind, "copy_bytes": 256 << 20, "calls": calls,
                           "gemv_source_hash": gemv_source_hash()}))
         return
 

@@ -258,11 +258,15 @@ __device__ __forceinline__ void gemm_tile(const R& r, const GemmTask& T, int k, 
             half8_t, __builtin_amdgcn_raw_buffer_load_b128(a_rs, (int)a_voff[mi], ks * kAStep, 0));
     };
     // prologue: step 0 decoded into stage 0; A of steps 0, 1 and trellis of
-    // steps 1, 2 in flight
+    // steps 1, 2 in flight.  The loads go out in a fixed order (scheduling
+    // barriers) that leaves, at the loop's entry, at least as many loads
+    // issued after each register set as the loop body leaves at its back
+    // edge: the wait counts the compiler derives for the loop are the minimum
+    // over both edges, so a prologue that ended on the trellis set the first
+    // step needs would make every step wait for nearly all loads in flight.
     load_t(0, 0);
-    load_a_act(0, 0);
     load_t(1, 1);
-    load_a_act(1, 1);
+    __builtin_amdgcn_sched_barrier(0);
     {
       uint32_t B[K + 1], wv[8];
       stream_of(0, B);
@@ -271,6 +275,11 @@ __device__ __forceinline__ void gemm_tile(const R& r, const GemmTask& T, int k, 
 #pragma unroll
       for (int c = 0; c < 8; ++c) nd[bw_dw[c]] = wv[c];
     }
+    __builtin_amdgcn_sched_barrier(0);
+    load_a_act(0, 0);
+    __builtin_amdgcn_sched_barrier(0);
+    load_a_act(1, 1);
+    __builtin_amdgcn_sched_barrier(0);
     load_t(0, 2);
     __syncthreads();
     __builtin_amdgcn_sched_barrier(0);

@@ -214,11 +214,12 @@ __global__ __launch_bounds__(kGemmThreads, 2) void gemm_i8_kernel(R r, int k, in
 
   auto run = [&](auto hc) {
     // prologue: step 0 decoded into stage 0; A of steps 0, 1 and trellis of
-    // steps 1, 2 in flight
+    // steps 1, 2 in flight, issued in the order that leaves the loop's entry
+    // with as many later loads behind each register set as its back edge (the
+    // loop's wait counts are the minimum over both edges; see gemm_tile)
     load_t(0, 0);
-    load_a(0, 0);
     load_t(1, 1);
-    load_a(1, 1);
+    __builtin_amdgcn_sched_barrier(0);
     {
       uint32_t B[K2 + 1], wv[8];
       stream_of(0, B);
@@ -227,6 +228,11 @@ __global__ __launch_bounds__(kGemmThreads, 2) void gemm_i8_kernel(R r, int k, in
 #pragma unroll
       for (int c = 0; c < 8; ++c) nd[bw_dw[c]] = wv[c];
     }
+    __builtin_amdgcn_sched_barrier(0);
+    load_a(0, 0);
+    __builtin_amdgcn_sched_barrier(0);
+    load_a(1, 1);
+    __builtin_amdgcn_sched_barrier(0);
     load_t(0, 2);
     __syncthreads();
     __builtin_amdgcn_sched_barrier(0);
