@@ -142,6 +142,30 @@ def bench_lib():
     return L
 
 
+def host_call_times(X, weights, x, y, ws, stream, calls=200):
+    """Seconds of host time per exl3_linear call: (Python binding, direct C
+    ABI call through ctypes with prepared arguments)."""
+    import ctypes
+    import torch
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for i in range(calls):
+        X.exl3_linear(x, weights[i % len(weights)], out=y, workspace=ws, stream=stream)
+    py = (time.perf_counter() - t0) / calls
+    torch.cuda.synchronize()
+    L = X.lib()
+    recs = [w._c() for w in weights]
+    refs = [ctypes.byref(r) for r in recs]
+    xp, yp, wp = x.data_ptr(), y.data_ptr(), ws.data_ptr()
+    ldx, ldy, nws, sp = x.stride(0), y.stride(0), ws.numel(), stream.cuda_stream
+    t0 = time.perf_counter()
+    for i in range(calls):
+        L.exl3_linear(refs[i % len(refs)], xp, 1, ldx, yp, ldy, 0, wp, nws, sp)
+    c = (time.perf_counter() - t0) / calls
+    torch.cuda.synchronize()
+    return py, c
+
+
 def read_ceiling(buffers, nbytes, stream, reps=200):
     """Practical HBM read ceiling: a plain streaming-read kernel over the same
     rotated buffers the GEMV reads, back to back; the best of a few launch
@@ -236,6 +260,13 @@ def mixed_layer_leg(X, torch, synth, dev, stream, reps=50):
                          "frac_hbm": round(b / t / 1e9 / HBM_PEAK_GBS, 4)}
     out["m1"]["layer"] = {"us": round(tot_t * 1e6, 2), "GB/s": round(tot_b / tot_t / 1e9, 1),
                           "frac_hbm": round(tot_b / tot_t / 1e9 / HBM_PEAK_GBS, 4)}
+    # the seven calls captured into one graph and replayed: the layer's GPU
+    # time without the host's per-call cost
+    layer_calls = [lambda st, nm=nm: X.exl3_linear(xs[nm], ws[nm], out=ys[nm], workspace=wsp, stream=st)
+                   for nm in names]
+    tg = time_graph(layer_calls, 20, stream) * len(names)
+    out["m1"]["layer_graph_replay"] = {"us": round(tg * 1e6, 2), "GB/s": round(tot_b / tg / 1e9, 1),
+                                       "frac_hbm": round(tot_b / tg / 1e9 / HBM_PEAK_GBS, 4)}
     # the same layer with the projections that share an input fused into one
     # exl3_linear_multi call each: (q, k, v), o, (gate, up), down
     groups = [("q", "k", "v"), ("o",), ("gate", "up"), ("down",)]
@@ -267,6 +298,10 @@ def mixed_layer_leg(X, torch, synth, dev, stream, reps=50):
                                         "frac_hbm": round(b / t / 1e9 / HBM_PEAK_GBS, 4)}
     out["m1_fused"]["layer"] = {"us": round(tot_t * 1e6, 2), "GB/s": round(tot_b / tot_t / 1e9, 1),
                                 "frac_hbm": round(tot_b / tot_t / 1e9 / HBM_PEAK_GBS, 4)}
+    tg = time_graph([lambda st, g=g: X.exl3_linear_multi(xs[g[0]], gws[g], outs=gouts[g], workspace=wsm, stream=st)
+                     for g in groups], 20, stream) * len(groups)
+    out["m1_fused"]["layer_graph_replay"] = {"us": round(tg * 1e6, 2), "GB/s": round(tot_b / tg / 1e9, 1),
+                                             "frac_hbm": round(tot_b / tg / 1e9 / HBM_PEAK_GBS, 4)}
     del wsm
     del xs, ys
     d4 = synth.mixed_layer_inputs(synth.SEED_MIXED_LAYER, 4096)
@@ -397,15 +432,31 @@ def main():
     # the plain streaming read of the same copies
     graph_t = time_graph([lambda st, w=w: X.exl3_linear(xs[:1], w, out=y[:1], workspace=ws, stream=st)
                           for w in weights], 40, stream)
+    # host time to enqueue one call (wall clock over a burst of 200 launches
+    # while the GPU works through them): through the Python binding, and
+    # through ctypes straight into the C ABI with the arguments prepared
+    host_py, host_c = host_call_times(X, weights, xs[:1], y[:1], ws, stream)
     ceiling = read_ceiling(trellis, trellis_bytes, stream)
 
     secondary = {}
     if not args.no_secondary:
         for m in (4, 16):
-            pl, _ = time_calls(gemv(m), 200, 20, stream)
+            pl, tot = time_calls(gemv(m), 200, 20, stream)
             gb = linear_bytes(k, n, bits, m) / pl / 1e9
             secondary[f"gemv_m{m}"] = {"GB/s": round(gb, 1), "frac_hbm": round(gb / HBM_PEAK_GBS, 4),
-                                       "us_per_call": round(pl * 1e6, 2)}
+                                       "us_per_call": round(pl * 1e6, 2),
+                                       "us_per_call_back_to_back": round(tot / 200 * 1e6, 2)}
+        # The stream-k v_dot2 kernel at M=1 (the several-tensor call with one
+        # tensor): the cost of giving every row count 1..16 one contraction is
+        # the difference between this and the headline call on the same box.
+        wsd = torch.zeros(X.exl3_linear_multi_workspace_size([weights[0]], 1), dtype=torch.uint8, device=dev)
+        pl, tot = time_calls(lambda i: X.exl3_linear_multi(xs[:1], [weights[i % copies]], outs=[y[:1]], workspace=wsd,
+                                                           stream=stream), 200, 20, stream)
+        gb = nbytes * 200 / tot / 1e9
+        secondary["gemv_m1_v_dot2_one_tensor"] = {"GB/s": round(gb, 1), "frac_hbm": round(gb / HBM_PEAK_GBS, 4),
+                                                  "us_per_call": round(pl * 1e6, 2),
+                                                  "us_per_call_back_to_back": round(tot / 200 * 1e6, 2)}
+        del wsd
         # prefill: M=4096 (input transform kernel + fused decode/MFMA GEMM kernel)
         dp = synth.linear_inputs(synth.SEED_PREFILL_4096x5120x17408, 4096, k, n, bits)
         wp = X.Exl3Weight.from_numpy(dp["trellis"], dp["suh"], dp["svh"], bits, device=dev)
@@ -519,6 +570,8 @@ def main():
                      "us_per_launch_median": round(per_median * 1e6, 3),
                      "us_per_call_back_to_back": round(total / args.steps * 1e6, 3),
                      "us_per_call_graph_replay": round(graph_t * 1e6, 3),
+                     "host_us_per_call_python": round(host_py * 1e6, 2),
+                     "host_us_per_call_c_abi": round(host_c * 1e6, 2),
                      "read_ceiling": ceiling,
                      "frac_of_read_ceiling": round(achieved / ceiling["GB/s"], 4)},
         "cpu_baseline": cpu,

@@ -64,9 +64,9 @@ def _other_linear():
 
 @pytest.mark.parametrize("m", [1, 4, 8, 300])
 def test_graph_linear(m):
-    # m = 1, 4: the v_dot2 decode GEMV with its two-tier plan (4096 x 4096
-    # gives 8192 row steps); m = 8: the matrix-core GEMV; m = 300: the prefill
-    # GEMM
+    # m = 1, 4: the decode GEMV with every wave staging its own x' and the
+    # finish forming the workgroup terms; m = 8: the input-transform launch
+    # and the workgroup combine in LDS; m = 300: the prefill GEMM
     import torch
     import gemm_exl3_linear_amd as X
     d = G.linear_case(901, 300, 4096, 4096, 4)
