@@ -57,46 +57,52 @@ __device__ __forceinline__ void gemv_prologue(const GemvTask& T, int k0, int kc,
   }
 }
 
-// Sum of the fp32 partial slices s = 0..splits-1 (fixed order) for the two
-// columns col, col+1 of one row; slices are `stride` floats apart.  The
-// slices were written by other workgroups of the same kernel with
-// device-scope stores (see gemv_unit), so the loads are device scope too.
-__device__ __forceinline__ void sum_partials(const float* p, int splits, int64_t stride, float& a,
-                                             float& b) {
-  a = 0.f;
-  b = 0.f;
-  for (int s = 0; s < splits; ++s) {
-    const float* q = p + (int64_t)s * stride;
-    a += __hip_atomic_load(q, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-    b += __hip_atomic_load(q + 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-  }
-}
-
-// Workgroups are dispatched to the eight XCDs of MI355X round robin
-// (workgroup b runs on XCD b % 8; verified by reading the XCC_ID hardware
-// register of every workgroup).  An output group's workgroups (all k ranges
-// of all units that one finish reads) are given indices congruent mod 8, so
-// the group's partial sums pass through one XCD's L2 and the hand-off needs no
-// L2 write-back or invalidate.  Index b: XCD x = b % 8, position i = b / 8;
+// Workgroups are dispatched to the eight XCDs of MI355X round robin: within
+// one launch, the workgroups b with the same b % 8 all run on one XCD
+// (verified by reading the XCC_ID hardware register of every workgroup).
+// Which XCD that is can change for the life of a process: once a second
+// stream has run work, launches on the first one have been seen rotated by
+// one XCD, every workgroup b on XCD (b + 7) % 8.  An output group's
+// workgroups (all k ranges of all units that one finish reads) are given
+// indices congruent mod 8, so they share one XCD and its L2 whatever the
+// rotation, and the group's partial sums can be handed over without an L2
+// write-back or invalidate.  Index b: residue x = b % 8, position i = b / 8;
 // group 8 (i / members) + x, member i % members.
 //
-// Nothing in the programming model promises that dispatch order, so every
-// workgroup checks it (gemv_off_xcd): the partial sums are stored with
+// The XCD a group is expected on is learned: its finisher records its own XCD
+// in the group's arrival counter for the next call (see GemvCtr), and a group
+// with no record yet expects XCD b % 8.  Every workgroup compares its XCC_ID
+// with that expectation (gemv_off_xcd).  The partial sums are stored with
 // device-scope stores and read with device-scope loads whatever the
-// placement, and a workgroup found on another XCD than planned (or every
-// workgroup, when the caller forces it) also takes the device-scope release
-// before it arrives, and marks the group so that its finisher takes the
-// device-scope acquire.  Another dispatch policy then costs time, not
-// correctness.
+// placement; a workgroup found on another XCD (or every workgroup, when the
+// caller forces it) also takes the device-scope release before it arrives and
+// marks its arrival, and the finisher of a marked group, or one that is
+// itself off the expected XCD, takes the device-scope acquire.  A placement
+// that differs from the expectation then costs time, not correctness, for
+// one call.
 constexpr int kGemvXcds = 8;
-constexpr unsigned int kGemvOffXcdFlag = 1u << 16;  // arrival of a workgroup off its planned XCD
+
+// Arrival counter word of an output group: bits 0..13 count the arrivals,
+// bits 14..27 count the arrivals that took the device-scope release, bits
+// 28..31 hold 1 + the XCD the group was finished on in the previous call (0:
+// none).  The finisher stores the record, count fields zero, for the next
+// call.  Groups have at most kMaxArrivals members (checked on the host).
+struct GemvCtr {
+  static constexpr unsigned int kCountMask = (1u << 14) - 1u;
+  static constexpr unsigned int kOffOne = 1u << 14;
+  static constexpr unsigned int kOffMask = ((1u << 14) - 1u) << 14;
+  static constexpr int kXcdShift = 28;
+  static constexpr int kMaxArrivals = (1 << 14) - 1;
+};
 
 // XCC_ID hardware register (bits 3:0: the XCD this wave runs on)
 __device__ __forceinline__ int xcc_id() {
   return __builtin_amdgcn_s_getreg((3 << 11) | 20) & 15;  // hwreg(HW_REG_XCC_ID, 0, 4)
 }
-__device__ __forceinline__ bool gemv_off_xcd(int b, int force) {
-  return force != 0 || xcc_id() != b % kGemvXcds;
+// rec: the record field of the group's counter word (0: none)
+__device__ __forceinline__ bool gemv_off_xcd(int b, unsigned int rec, int force) {
+  const int expect = rec ? (int)rec - 1 : b % kGemvXcds;
+  return force != 0 || xcc_id() != expect;
 }
 __device__ __forceinline__ bool gemv_place(int b, int groups, int members, int& group, int& member) {
   const int x = b % kGemvXcds, i = b / kGemvXcds;
@@ -140,9 +146,12 @@ __device__ __forceinline__ void gemv_tile(const uint32_t (&D)[K], int kt, int m,
   __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
 }
 
-// PF = loads kept in flight per lane; the per-wave trip count kc/64 must be a
-// multiple of PF (the planner guarantees it), so the loop has no tail and no
-// branch around its loads.
+// One unit's k range, its partial store and its arrival; last_flag (shared,
+// valid after the final barrier) is 0, or 1 / 2 for the group's last arrival
+// (2: the finish takes the device-scope acquire).  PF = loads kept in flight
+// per lane; the per-wave trip count kc/64 must be a multiple of PF (the
+// planner guarantees it), so the loop has no tail and no branch around its
+// loads.
 template <int K, int PF, class R>
 __device__ __forceinline__ void gemv_unit(const R& r, const GemvTask& T, int unit, int split, int nb,
                                           int n, int kc, unsigned char* smem, int& last_flag) {
@@ -166,6 +175,13 @@ __device__ __forceinline__ void gemv_unit(const R& r, const GemvTask& T, int uni
                           ((int64_t)((k0 >> 4) + wave) * nt + nb * 8 + t) * (8 * K) + K * p;
   const int64_t it_stride = (int64_t)4 * nt * (8 * K);
   const int cnt = kc >> 6;
+
+  // the group's XCD record (constant during the call: arrivals change only
+  // the count fields, and the finisher rewrites it after every arrival),
+  // read first so that its latency hides behind the whole unit
+  unsigned int* const ctr = r.counter(unit, nb);
+  const unsigned int rec =
+      __hip_atomic_load(ctr, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) >> GemvCtr::kXcdShift;
 
   // the first PF trellis loads go out before the prologue so that their
   // latency overlaps the input transform
@@ -216,9 +232,9 @@ __device__ __forceinline__ void gemv_unit(const R& r, const GemvTask& T, int uni
 
   // arrival: the last workgroup of the output group finishes it.  Every
   // thread's partial stores are complete (vmcnt(0)) before the workgroup
-  // barrier, and the counter moves after it.  Off the planned XCD, the
-  // device-scope release comes first and the arrival carries the flag.
-  const bool off = gemv_off_xcd((int)blockIdx.x, r.off_xcd_all);
+  // barrier, and the counter moves after it.  Off the expected XCD, the
+  // device-scope release comes first and the arrival is marked.
+  const bool off = gemv_off_xcd((int)blockIdx.x, rec, r.off_xcd_all);
   if (off)
     __builtin_amdgcn_fence(__ATOMIC_RELEASE, "agent");
   else
@@ -226,21 +242,26 @@ __device__ __forceinline__ void gemv_unit(const R& r, const GemvTask& T, int uni
   __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0)
   __syncthreads();
   if (threadIdx.x == 0) {
-    unsigned int* ctr = r.counter(unit, nb);
-    const unsigned int inc = off ? 1u + kGemvOffXcdFlag : 1u;
+    const unsigned int inc = off ? 1u + GemvCtr::kOffOne : 1u;
     const unsigned int now = __hip_atomic_fetch_add(ctr, inc, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) + inc;
-    const bool last = (now & (kGemvOffXcdFlag - 1u)) == r.arrivals(unit);
-    last_flag = !last ? 0 : ((now >= kGemvOffXcdFlag || off) ? 2 : 1);
+    const bool last = (now & GemvCtr::kCountMask) == r.arrivals(unit);
+    last_flag = !last ? 0 : (((now & GemvCtr::kOffMask) != 0 || off) ? 2 : 1);
   }
   __syncthreads();
-  if (!last_flag) return;
+}
+
+// The finish of an output group, run by its last-arriving workgroup (one copy
+// for every width of a width-0 kernel).
+template <class R>
+__device__ __forceinline__ void gemv_group_finish(const R& r, int unit, int nb, int n, int last_flag) {
   if (last_flag == 2)
     __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "agent");
   else
     __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup");
   r.finish(unit, nb, n);
-  if (threadIdx.x == 0)  // ready for the next call
-    __hip_atomic_store(r.counter(unit, nb), 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  if (threadIdx.x == 0)  // counts zero and this XCD recorded, for the next call
+    __hip_atomic_store(r.counter(unit, nb), (unsigned int)(xcc_id() + 1) << GemvCtr::kXcdShift,
+                       __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
 
 // K = 1..8: every unit has that width.  K = 0: each unit has its own width
@@ -263,11 +284,12 @@ __global__ __launch_bounds__(256) void gemv_kernel(R r, int /*k*/, int n, int kc
       case 6: gemv_unit<6, PF>(r, T, unit, split, nb, n, kc, smem, last_flag); break;
       case 7: gemv_unit<7, PF>(r, T, unit, split, nb, n, kc, smem, last_flag); break;
       case 8: gemv_unit<8, PF>(r, T, unit, split, nb, n, kc, smem, last_flag); break;
-      default: break;
+      default: return;  // a width outside 1..8: the unit is left out
     }
   } else {
     gemv_unit<K, PF>(r, T, unit, split, nb, n, kc, smem, last_flag);
   }
+  if (last_flag) gemv_group_finish(r, unit, nb, n, last_flag);
 }
 
 // Launch with the prefetch depth the k range allows.

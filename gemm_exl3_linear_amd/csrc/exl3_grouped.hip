@@ -92,6 +92,48 @@ __device__ __forceinline__ ExpertTensors expert_tensors(const uint16_t* trellis,
 // ---------------------------------------------------------------------------
 // small-P path
 // ---------------------------------------------------------------------------
+// Per-row sums over k ranges of the fp32 partials of two adjacent columns:
+// row r (r < rows <= R) has its slices j = 0..splits-1 at p + r * row_stride +
+// j * stride.  Each row is summed in slice order from 0.f (the order of a
+// plain loop over the slices); the loads of B slices of every row are issued
+// before any of them is added, so the finish waits one round trip per B
+// slices, not one per slice and row.  The slices were written by other
+// workgroups of the same launch with device-scope stores, so the loads are
+// device scope too.
+template <int R, int B>
+__device__ __forceinline__ void sum_slices(const float* p, int64_t row_stride, int splits,
+                                           int64_t stride, float (&sum)[R][2], int rows = R) {
+#pragma unroll
+  for (int r = 0; r < R; ++r) sum[r][0] = sum[r][1] = 0.f;
+  for (int j0 = 0; j0 < splits; j0 += B) {
+    float v[R][B][2];
+#pragma unroll
+    for (int r = 0; r < R; ++r) {
+#pragma unroll
+      for (int q = 0; q < B; ++q) {
+        if (r < rows && j0 + q < splits) {
+          const float* a = p + r * row_stride + (int64_t)(j0 + q) * stride;
+          v[r][q][0] = __hip_atomic_load(a, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+          v[r][q][1] = __hip_atomic_load(a + 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        }
+      }
+    }
+#pragma unroll
+    for (int r = 0; r < R; ++r) {
+#pragma unroll
+      for (int q = 0; q < B; ++q) {
+        if (r < rows && j0 + q < splits) {
+          sum[r][0] += v[r][q][0];
+          sum[r][1] += v[r][q][1];
+        }
+      }
+    }
+  }
+}
+
+// Slots of one token that a down finish takes at a time.
+constexpr int kDnFinishSlots = 8;
+
 struct GuUnitRes {
   const uint16_t* trellis;
   const uint16_t* suh;
@@ -139,26 +181,31 @@ struct GuUnitRes {
   __device__ unsigned int* counter(int u, int nb) const { return ctr + (u >> 1) * (n >> 7) + nb; }
   __device__ unsigned int arrivals(int) const { return 2u * (unsigned int)splits; }
   // gate and up of one pair: sum, output transform, svh; a = silu(g) * u;
-  // then the down projection's input transform (a .* suh_down) H
+  // then the down projection's input transform (a .* suh_down) H.  Every
+  // load is issued before the arithmetic that needs it (one round trip per
+  // kUnitSliceBatch k ranges instead of one per slice).
   __device__ void finish(int u, int nb, int) const {
     if ((threadIdx.x >> 6) != 0) return;
     const int pair = u >> 1;
     const int e = ids[pair];
     const int col = nb * 128 + 2 * (int)lane_id();
+    const uint32_t sv0 = *reinterpret_cast<const uint32_t*>(svh + (int64_t)(e * 2) * n + col);
+    const uint32_t sv1 = *reinterpret_cast<const uint32_t*>(svh + (int64_t)(e * 2 + 1) * n + col);
+    const uint32_t su = *reinterpret_cast<const uint32_t*>(suh_dn + (int64_t)e * n + col);
+    // slices (pair, gate, 0..splits-1) then (pair, up, 0..splits-1)
+    float sum[2][2];
+    sum_slices<2, 4>(part + (int64_t)pair * 2 * splits * n + col, (int64_t)splits * n, splits, n, sum);
     float gv[2], uv[2];
     for (int slot = 0; slot < 2; ++slot) {
-      float a, b;
-      sum_partials(part + ((int64_t)(pair * 2 + slot) * splits) * n + col, splits, n, a, b);
+      float a = sum[slot][0], b = sum[slot][1];
       fwht128_pair(a, b);
-      const uint32_t sv =
-          *reinterpret_cast<const uint32_t*>(svh + (int64_t)(e * 2 + slot) * n + col);
+      const uint32_t sv = slot == 0 ? sv0 : sv1;
       a *= kInvSqrt128 * h2f((uint16_t)(sv & 0xFFFF));
       b *= kInvSqrt128 * h2f((uint16_t)(sv >> 16));
       if (slot == 0) { gv[0] = a; gv[1] = b; } else { uv[0] = a; uv[1] = b; }
     }
     float a = silu_f(gv[0]) * uv[0];
     float b = silu_f(gv[1]) * uv[1];
-    const uint32_t su = *reinterpret_cast<const uint32_t*>(suh_dn + (int64_t)e * n + col);
     a *= h2f((uint16_t)(su & 0xFFFF));
     b *= h2f((uint16_t)(su >> 16));
     fwht128_pair(a, b);
@@ -212,22 +259,39 @@ struct DnUnitRes {
   }
   __device__ unsigned int* counter(int u, int nb) const { return ctr + (u / topk) * (n >> 7) + nb; }
   __device__ unsigned int arrivals(int) const { return (unsigned int)(topk * splits); }
-  // y[token, block] = sum over slots in order of w * ((sum_s partial) H .* svh)
+  // y[token, block] = sum over slots in order of w * ((sum_s partial) H .* svh).
+  // The routing, svh and partial loads of kDnFinishSlots slots go out before
+  // their arithmetic.
   __device__ void finish(int u, int nb, int) const {
     if ((threadIdx.x >> 6) != 0) return;
     const int tok = u / topk;
     const int col = nb * 128 + 2 * (int)lane_id();
     float ya = 0.f, yb = 0.f;
-    for (int s = 0; s < topk; ++s) {
-      const int pair = tok * topk + s;
-      const int e = ids[pair];
-      float a, b;
-      sum_partials(part + ((int64_t)pair * splits) * n + col, splits, n, a, b);
-      fwht128_pair(a, b);
-      const uint32_t sv = *reinterpret_cast<const uint32_t*>(svh + (int64_t)e * n + col);
-      const float wt = w[pair];
-      ya += wt * (a * kInvSqrt128 * h2f((uint16_t)(sv & 0xFFFF)));
-      yb += wt * (b * kInvSqrt128 * h2f((uint16_t)(sv >> 16)));
+    for (int p0 = tok * topk, pend = p0 + topk; p0 < pend; p0 += kDnFinishSlots) {
+      const int rows = pend - p0 < kDnFinishSlots ? pend - p0 : kDnFinishSlots;
+      uint32_t sv[kDnFinishSlots];
+      float wt[kDnFinishSlots];
+#pragma unroll
+      for (int s = 0; s < kDnFinishSlots; ++s) {
+        if (s < rows) {
+          const int e = ids[p0 + s];
+          sv[s] = *reinterpret_cast<const uint32_t*>(svh + (int64_t)e * n + col);
+          wt[s] = w[p0 + s];
+        }
+      }
+      // slices (pair p0 + s, 0..splits-1)
+      float sum[kDnFinishSlots][2];
+      sum_slices<kDnFinishSlots, 2>(part + (int64_t)p0 * splits * n + col, (int64_t)splits * n, splits, n,
+                                    sum, rows);
+#pragma unroll
+      for (int s = 0; s < kDnFinishSlots; ++s) {
+        if (s < rows) {
+          float a = sum[s][0], b = sum[s][1];
+          fwht128_pair(a, b);
+          ya += wt[s] * (a * kInvSqrt128 * h2f((uint16_t)(sv[s] & 0xFFFF)));
+          yb += wt[s] * (b * kInvSqrt128 * h2f((uint16_t)(sv[s] >> 16)));
+        }
+      }
     }
     *reinterpret_cast<float2*>(y + (int64_t)tok * n + col) = make_float2(ya, yb);
   }
@@ -253,8 +317,9 @@ struct DnUnitRun {
 
 // Arrival counters of the unit path live at the start of the workspace, in a
 // region whose size depends only on the arena shapes (enough for the largest
-// unit-path call).  Both regimes leave this region zero when a call ends, so
-// one workspace can serve calls of any size.
+// unit-path call).  A unit-path call leaves every counter it used with zero
+// counts (and the XCD record of GemvCtr), the binned path does not touch the
+// region, so one workspace can serve calls of any size.
 static size_t counter_region(const ArenaDesc& gu, const ArenaDesc& dn) {
   const size_t c = (size_t)kGroupedUnitMaxPairs * (gu.n / 128) +
                    (size_t)kGroupedUnitMaxPairs * (dn.n / 128);
@@ -670,12 +735,21 @@ static hipError_t run_widths(const ArenaDesc& a, Args&&... args) {
 }
 
 // The layout's own bytes; the routing check's count follows them.
-static size_t layout_bytes(const ArenaDesc& gu, const ArenaDesc& dn, int64_t P) {
-  return P <= kGroupedUnitMaxPairs ? unit_layout(gu, dn, P).total : gemm_layout(gu, dn, P).total;
+// The small-P path, unless a group would have more members than its arrival
+// counter can count (k ranges of at most kGemvMaxKc rows keep that far off
+// for any realistic width).
+static bool unit_path(const ArenaDesc& gu, const ArenaDesc& dn, int64_t P, int topk) {
+  if (P > kGroupedUnitMaxPairs) return false;
+  const UnitLayout L = unit_layout(gu, dn, P);
+  return 2 * L.s_gu <= GemvCtr::kMaxArrivals && topk * L.s_dn <= GemvCtr::kMaxArrivals;
+}
+
+static size_t layout_bytes(const ArenaDesc& gu, const ArenaDesc& dn, int64_t P, int topk) {
+  return unit_path(gu, dn, P, topk) ? unit_layout(gu, dn, P).total : gemm_layout(gu, dn, P).total;
 }
 
 size_t grouped_workspace(const ArenaDesc& gu, const ArenaDesc& dn, int64_t t, int topk) {
-  return layout_bytes(gu, dn, t * topk) + 256;
+  return layout_bytes(gu, dn, t * topk, topk) + 256;
 }
 
 // Routing check (debug option): one workgroup counts the ids outside
@@ -702,7 +776,7 @@ hipError_t count_bad_ids(const ArenaDesc& gu, const ArenaDesc& dn, const int32_t
                          int topk, void* ws, hipStream_t s, unsigned int& bad) {
   const int64_t P = t * topk;
   unsigned int* dev = reinterpret_cast<unsigned int*>(static_cast<unsigned char*>(ws) +
-                                                      layout_bytes(gu, dn, P));
+                                                      layout_bytes(gu, dn, P, topk));
   hipLaunchKernelGGL(check_ids_kernel, dim3(1), dim3(kCheckThreads), 0, s, ids, P, gu.experts, dev);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
@@ -717,7 +791,7 @@ hipError_t launch_grouped(const ArenaDesc& gu, const ArenaDesc& dn, const uint16
   const int hidden = gu.k, inter = gu.n;
   unsigned char* base = static_cast<unsigned char*>(ws);
   hipError_t e;
-  if (P <= kGroupedUnitMaxPairs) {
+  if (unit_path(gu, dn, P, topk)) {
     const UnitLayout L = unit_layout(gu, dn, P);
     unsigned int* ctr_gu = reinterpret_cast<unsigned int*>(base + L.ctr_gu);
     unsigned int* ctr_dn = reinterpret_cast<unsigned int*>(base + L.ctr_dn);

@@ -55,6 +55,10 @@ def f16_bits(t):
     return t.detach().cpu().numpy().view(np.uint16)
 
 
+def f32_bits(t):
+    return t.detach().cpu().numpy().view(np.uint32)
+
+
 # ---------------------------------------------------------------------------
 # full-size oracle results in reasonable time: the oracle's own functions,
 # applied to independent pieces (tiles of the trellis, rows of x, expert

@@ -148,6 +148,56 @@ def test_forced_device_scope_hand_off_same_bits(t, monkeypatch):
     np.testing.assert_array_equal(_run(m), y0)
 
 
+# The XCD a group's workgroups are expected on is learned from the previous
+# call: its finisher stores 1 + its XCD in bits 28..31 of the group's arrival
+# counter (count fields zero).  The counter region starts the workspace: 384
+# pairs x (intermediate / 128) gate/up groups, then 384 x (hidden / 128) down
+# groups, one uint32 each.  Records that name the wrong XCD (planted here from
+# the host), or work run on a second stream (which has been seen to rotate the
+# dispatch of later launches by one XCD), change which hand-off the groups
+# take, never the bits; after every call the count fields are zero again.
+def _counter_words(ws, m):
+    n = 384 * (m["gate_up"]["n"] // 128 + m["down"]["n"] // 128)
+    return ws[:4 * n].view(dtype=__import__("torch").int32)
+
+
+@pytest.mark.parametrize("t", [1, 4, 48])
+def test_xcd_records_only_change_the_hand_off(t):
+    import torch
+    import gemm_exl3_linear_amd as X
+    m = synth.moe_inputs(synth.SEED_MOE_256x2048x512, t)
+    gu = X.Exl3Arena.from_numpy(m["gate_up"], G.dev())
+    dn = X.Exl3Arena.from_numpy(m["down"], G.dev())
+    x, ids, w = G.to_dev(m["x"]), G.to_dev(m["ids"].astype(np.int32)), G.to_dev(m["weights"].astype(np.float32))
+    ws = torch.zeros(X.exl3_grouped_experts_workspace_size(gu, dn, t, 8), dtype=torch.uint8, device=G.dev())
+
+    def call():
+        y = X.exl3_grouped_experts(x, ids, w, gu, dn, workspace=ws)
+        torch.cuda.synchronize()
+        c = _counter_words(ws, m).cpu().numpy().view(np.uint32)
+        assert not np.any(c & np.uint32((1 << 28) - 1)), "count fields left nonzero"
+        assert np.all((c >> 28) <= 8)
+        return G.f32_bits(y), c >> 28
+
+    y0, rec = call()
+    gu_used = t * 8 * (512 // 128)
+    assert np.all((rec[:gu_used] >= 1) & (rec[:gu_used] <= 8)), "a finished group left no record"
+    # records naming other XCDs than the ones found: every group off its expected XCD
+    planted = torch.from_numpy(((((rec.astype(np.int64) + 2) % 8) + 1) << 28).astype(np.uint32).view(np.int32))
+    _counter_words(ws, m).copy_(planted.to(G.dev()))
+    y1, rec1 = call()
+    np.testing.assert_array_equal(y1, y0)
+    # work on a second stream, then the same call again
+    side = torch.cuda.Stream()
+    with torch.cuda.stream(side):
+        z = torch.zeros(1000, device=G.dev())
+        z.add_(1)
+    torch.cuda.synchronize()
+    for _ in range(2):
+        y2, _ = call()
+        np.testing.assert_array_equal(y2, y0)
+
+
 def test_check_ids_refuses_a_capturing_stream(monkeypatch):
     # EXL3_CHECK_IDS waits for a device count on the host, which a stream in
     # graph capture cannot do: the call returns EXL3_E_INVALID with nothing

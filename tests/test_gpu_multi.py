@@ -115,3 +115,16 @@ def test_multi_mixed_layer_groups_m1(group):
         ref = O.linear(x, d["trellis"], d["suh"], d["svh"], d["bits"])
         err = O.rel_frobenius(y.double().cpu().numpy(), ref)
         assert err < TOL, (nm, d["bits"], err)
+
+
+def test_multi_negation_bit_exact():
+    # The several-tensor call contracts one row on the vector units (v_dot2,
+    # fp32 round to nearest even), and every step (input transform, products,
+    # the -1534 * sum(x') correction, the fixed-order slot sums, the output
+    # transform, svh, the fp16 cast) is symmetric under negation: y(-x) is
+    # -y(x) bit for bit.
+    ts, x = _tensors(740, 1024, [(640, 3), (384, 5)], 1)
+    y = _run_multi(ts, x)
+    yn = _run_multi(ts, -x)
+    for a, b in zip(y, yn):
+        np.testing.assert_array_equal(G.f16_bits(b), G.f16_bits(-a))
