@@ -1,8 +1,12 @@
-// Decode-GEMV kernel template shared by the dense linear and the grouped
-// experts (design notes in exl3_gemv.hip).  A resolver R supplies, per
+// Decode-GEMV kernel template of the grouped experts' small-batch path (one
+// workgroup per (unit, 128 columns, k range); planning helpers in
+// exl3_gemv.hip).  A resolver R supplies, per
 // workgroup, the tensor, the activations and the partial-sum slice, and
 // implements the finishing step that the last-arriving workgroup of an
-// output group runs (split-k sum in a fixed order, output transform, ...).
+// output group runs (split-k sum in a fixed order, output transform, ...):
+// R::FinishPre holds what the finish reads that does not depend on the
+// partial sums, loaded by every workgroup during its k range
+// (finish_prefetch), and R::finish runs on all four waves of the finisher.
 #pragma once
 
 #include "exl3_device.hpp"
@@ -154,7 +158,8 @@ __device__ __forceinline__ void gemv_tile(const uint32_t (&D)[K], int kt, int m,
 // loads.
 template <int K, int PF, class R>
 __device__ __forceinline__ void gemv_unit(const R& r, const GemvTask& T, int unit, int split, int nb,
-                                          int n, int kc, unsigned char* smem, int& last_flag) {
+                                          int n, int kc, unsigned char* smem, int& last_flag,
+                                          typename R::FinishPre& pre) {
   const int m = T.m;
   const int k0 = split * kc;
   const int nt = n >> 4;
@@ -191,6 +196,10 @@ __device__ __forceinline__ void gemv_unit(const R& r, const GemvTask& T, int uni
 
   gemv_prologue(T, k0, kc, xs);
   __syncthreads();
+  // what the finish needs besides the partial sums, in case this workgroup
+  // arrives last: issued after the input transform (which waits for its own
+  // loads) so that its latency hides behind the k range instead
+  pre = r.finish_prefetch(unit, nb);
 
   float4_t acc[8];
 #pragma unroll
@@ -253,12 +262,13 @@ __device__ __forceinline__ void gemv_unit(const R& r, const GemvTask& T, int uni
 // The finish of an output group, run by its last-arriving workgroup (one copy
 // for every width of a width-0 kernel).
 template <class R>
-__device__ __forceinline__ void gemv_group_finish(const R& r, int unit, int nb, int n, int last_flag) {
+__device__ __forceinline__ void gemv_group_finish(const R& r, int unit, int nb, int n, int last_flag,
+                                                  const typename R::FinishPre& pre, unsigned char* smem) {
   if (last_flag == 2)
     __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "agent");
   else
     __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup");
-  r.finish(unit, nb, n);
+  r.finish(unit, nb, n, pre, smem);
   if (threadIdx.x == 0)  // counts zero and this XCD recorded, for the next call
     __hip_atomic_store(r.counter(unit, nb), (unsigned int)(xcc_id() + 1) << GemvCtr::kXcdShift,
                        __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
@@ -270,26 +280,27 @@ template <int K, int PF, class R>
 __global__ __launch_bounds__(256) void gemv_kernel(R r, int /*k*/, int n, int kc) {
   extern __shared__ __align__(16) unsigned char smem[];
   __shared__ int last_flag;
+  typename R::FinishPre pre;
   int unit, split, nb;
   if (!r.place((int)blockIdx.x, unit, split, nb)) return;  // uniform over the workgroup
   const GemvTask T = r.task(unit, split);
   if (!T.valid) return;
   if constexpr (K == 0) {
     switch (T.bits) {
-      case 1: gemv_unit<1, PF>(r, T, unit, split, nb, n, kc, smem, last_flag); break;
-      case 2: gemv_unit<2, PF>(r, T, unit, split, nb, n, kc, smem, last_flag); break;
-      case 3: gemv_unit<3, PF>(r, T, unit, split, nb, n, kc, smem, last_flag); break;
-      case 4: gemv_unit<4, PF>(r, T, unit, split, nb, n, kc, smem, last_flag); break;
-      case 5: gemv_unit<5, PF>(r, T, unit, split, nb, n, kc, smem, last_flag); break;
-      case 6: gemv_unit<6, PF>(r, T, unit, split, nb, n, kc, smem, last_flag); break;
-      case 7: gemv_unit<7, PF>(r, T, unit, split, nb, n, kc, smem, last_flag); break;
-      case 8: gemv_unit<8, PF>(r, T, unit, split, nb, n, kc, smem, last_flag); break;
+      case 1: gemv_unit<1, PF>(r, T, unit, split, nb, n, kc, smem, last_flag, pre); break;
+      case 2: gemv_unit<2, PF>(r, T, unit, split, nb, n, kc, smem, last_flag, pre); break;
+      case 3: gemv_unit<3, PF>(r, T, unit, split, nb, n, kc, smem, last_flag, pre); break;
+      case 4: gemv_unit<4, PF>(r, T, unit, split, nb, n, kc, smem, last_flag, pre); break;
+      case 5: gemv_unit<5, PF>(r, T, unit, split, nb, n, kc, smem, last_flag, pre); break;
+      case 6: gemv_unit<6, PF>(r, T, unit, split, nb, n, kc, smem, last_flag, pre); break;
+      case 7: gemv_unit<7, PF>(r, T, unit, split, nb, n, kc, smem, last_flag, pre); break;
+      case 8: gemv_unit<8, PF>(r, T, unit, split, nb, n, kc, smem, last_flag, pre); break;
       default: return;  // a width outside 1..8: the unit is left out
     }
   } else {
-    gemv_unit<K, PF>(r, T, unit, split, nb, n, kc, smem, last_flag);
+    gemv_unit<K, PF>(r, T, unit, split, nb, n, kc, smem, last_flag, pre);
   }
-  if (last_flag) gemv_group_finish(r, unit, nb, n, last_flag);
+  if (last_flag) gemv_group_finish(r, unit, nb, n, last_flag, pre, smem);
 }
 
 // Launch with the prefetch depth the k range allows.

@@ -131,8 +131,8 @@ __device__ __forceinline__ void sum_slices(const float* p, int64_t row_stride, i
   }
 }
 
-// Slots of one token that a down finish takes at a time.
-constexpr int kDnFinishSlots = 8;
+// Slots of one token per wave in a down finish (four waves, top-k <= 16).
+constexpr int kDnSlotsPerWave = 4;
 
 struct GuUnitRes {
   const uint16_t* trellis;
@@ -181,33 +181,47 @@ struct GuUnitRes {
   __device__ unsigned int* counter(int u, int nb) const { return ctr + (u >> 1) * (n >> 7) + nb; }
   __device__ unsigned int arrivals(int) const { return 2u * (unsigned int)splits; }
   // gate and up of one pair: sum, output transform, svh; a = silu(g) * u;
-  // then the down projection's input transform (a .* suh_down) H.  Every
-  // load is issued before the arithmetic that needs it (one round trip per
-  // kUnitSliceBatch k ranges instead of one per slice).
-  __device__ void finish(int u, int nb, int) const {
-    if ((threadIdx.x >> 6) != 0) return;
-    const int pair = u >> 1;
-    const int e = ids[pair];
-    const int col = nb * 128 + 2 * (int)lane_id();
-    const uint32_t sv0 = *reinterpret_cast<const uint32_t*>(svh + (int64_t)(e * 2) * n + col);
-    const uint32_t sv1 = *reinterpret_cast<const uint32_t*>(svh + (int64_t)(e * 2 + 1) * n + col);
-    const uint32_t su = *reinterpret_cast<const uint32_t*>(suh_dn + (int64_t)e * n + col);
-    // slices (pair, gate, 0..splits-1) then (pair, up, 0..splits-1)
-    float sum[2][2];
-    sum_slices<2, 4>(part + (int64_t)pair * 2 * splits * n + col, (int64_t)splits * n, splits, n, sum);
-    float gv[2], uv[2];
-    for (int slot = 0; slot < 2; ++slot) {
-      float a = sum[slot][0], b = sum[slot][1];
-      fwht128_pair(a, b);
-      const uint32_t sv = slot == 0 ? sv0 : sv1;
-      a *= kInvSqrt128 * h2f((uint16_t)(sv & 0xFFFF));
-      b *= kInvSqrt128 * h2f((uint16_t)(sv >> 16));
-      if (slot == 0) { gv[0] = a; gv[1] = b; } else { uv[0] = a; uv[1] = b; }
+  // then the down projection's input transform (a .* suh_down) H.  Wave 0
+  // takes the gate, wave 1 the up projection; wave 0 finishes.
+  struct FinishPre {
+    uint32_t sv;  // svh of this wave's slot (waves 0, 1)
+    uint32_t su;  // suh of the down projection (wave 0)
+  };
+  __device__ FinishPre finish_prefetch(int u, int nb) const {
+    FinishPre f{0u, 0u};
+    const int wave = threadIdx.x >> 6;
+    if (wave < 2) {
+      const int e = ids[u >> 1];
+      const int col = nb * 128 + 2 * (int)lane_id();
+      f.sv = *reinterpret_cast<const uint32_t*>(svh + (int64_t)(e * 2 + wave) * n + col);
+      if (wave == 0) f.su = *reinterpret_cast<const uint32_t*>(suh_dn + (int64_t)e * n + col);
     }
-    float a = silu_f(gv[0]) * uv[0];
-    float b = silu_f(gv[1]) * uv[1];
-    a *= h2f((uint16_t)(su & 0xFFFF));
-    b *= h2f((uint16_t)(su >> 16));
+    return f;
+  }
+  __device__ void finish(int u, int nb, int, const FinishPre& f, unsigned char* smem) const {
+    const int wave = threadIdx.x >> 6;
+    const int pair = u >> 1;
+    const int col = nb * 128 + 2 * (int)lane_id();
+    float* up = reinterpret_cast<float*>(smem);  // [128]: the transformed up projection
+    float a = 0.f, b = 0.f;
+    if (wave < 2) {
+      // slices (pair, slot = wave, 0..splits-1)
+      float sum[1][2];
+      sum_slices<1, 4>(part + (int64_t)(pair * 2 + wave) * splits * n + col, 0, splits, n, sum);
+      a = sum[0][0];
+      b = sum[0][1];
+      fwht128_pair(a, b);
+      a *= kInvSqrt128 * h2f((uint16_t)(f.sv & 0xFFFF));
+      b *= kInvSqrt128 * h2f((uint16_t)(f.sv >> 16));
+      if (wave == 1) *reinterpret_cast<float2*>(up + 2 * lane_id()) = make_float2(a, b);
+    }
+    __syncthreads();
+    if (wave != 0) return;
+    const float2 uv = *reinterpret_cast<const float2*>(up + 2 * lane_id());
+    a = silu_f(a) * uv.x;
+    b = silu_f(b) * uv.y;
+    a *= h2f((uint16_t)(f.su & 0xFFFF));
+    b *= h2f((uint16_t)(f.su >> 16));
     fwht128_pair(a, b);
     a *= kInvSqrt128;
     b *= kInvSqrt128;
@@ -260,38 +274,58 @@ struct DnUnitRes {
   __device__ unsigned int* counter(int u, int nb) const { return ctr + (u / topk) * (n >> 7) + nb; }
   __device__ unsigned int arrivals(int) const { return (unsigned int)(topk * splits); }
   // y[token, block] = sum over slots in order of w * ((sum_s partial) H .* svh).
-  // The routing, svh and partial loads of kDnFinishSlots slots go out before
-  // their arithmetic.
-  __device__ void finish(int u, int nb, int) const {
-    if ((threadIdx.x >> 6) != 0) return;
-    const int tok = u / topk;
+  // Wave w takes slots w, w + 4, ...; each slot's weighted term goes through
+  // LDS and wave 0 adds them in slot order.
+  struct FinishPre {
+    uint32_t sv[kDnSlotsPerWave];  // svh of this wave's slots
+    float wt[kDnSlotsPerWave];     // their routing weights
+  };
+  __device__ FinishPre finish_prefetch(int u, int nb) const {
+    FinishPre f;
+    const int wave = threadIdx.x >> 6;
+    const int p0 = (u / topk) * topk;
     const int col = nb * 128 + 2 * (int)lane_id();
+#pragma unroll
+    for (int q = 0; q < kDnSlotsPerWave; ++q) {
+      const int s = wave + 4 * q;
+      f.sv[q] = 0u;
+      f.wt[q] = 0.f;
+      if (s < topk) {
+        const int e = ids[p0 + s];
+        f.sv[q] = *reinterpret_cast<const uint32_t*>(svh + (int64_t)e * n + col);
+        f.wt[q] = w[p0 + s];
+      }
+    }
+    return f;
+  }
+  __device__ void finish(int u, int nb, int, const FinishPre& f, unsigned char* smem) const {
+    const int wave = threadIdx.x >> 6;
+    const int tok = u / topk;
+    const int p0 = tok * topk;
+    const int col = nb * 128 + 2 * (int)lane_id();
+    float* terms = reinterpret_cast<float*>(smem);  // [topk][128]
+    const int mine = wave < topk ? (topk - wave + 3) / 4 : 0;  // slots of this wave
+    // slices (pair p0 + wave + 4 q, 0..splits-1)
+    float sum[kDnSlotsPerWave][2];
+    sum_slices<kDnSlotsPerWave, 2>(part + (int64_t)(p0 + wave) * splits * n + col, (int64_t)4 * splits * n,
+                                   splits, n, sum, mine);
+#pragma unroll
+    for (int q = 0; q < kDnSlotsPerWave; ++q) {
+      if (q < mine) {
+        float a = sum[q][0], b = sum[q][1];
+        fwht128_pair(a, b);
+        const float ta = f.wt[q] * (a * kInvSqrt128 * h2f((uint16_t)(f.sv[q] & 0xFFFF)));
+        const float tb = f.wt[q] * (b * kInvSqrt128 * h2f((uint16_t)(f.sv[q] >> 16)));
+        *reinterpret_cast<float2*>(terms + (wave + 4 * q) * 128 + 2 * lane_id()) = make_float2(ta, tb);
+      }
+    }
+    __syncthreads();
+    if (wave != 0) return;
     float ya = 0.f, yb = 0.f;
-    for (int p0 = tok * topk, pend = p0 + topk; p0 < pend; p0 += kDnFinishSlots) {
-      const int rows = pend - p0 < kDnFinishSlots ? pend - p0 : kDnFinishSlots;
-      uint32_t sv[kDnFinishSlots];
-      float wt[kDnFinishSlots];
-#pragma unroll
-      for (int s = 0; s < kDnFinishSlots; ++s) {
-        if (s < rows) {
-          const int e = ids[p0 + s];
-          sv[s] = *reinterpret_cast<const uint32_t*>(svh + (int64_t)e * n + col);
-          wt[s] = w[p0 + s];
-        }
-      }
-      // slices (pair p0 + s, 0..splits-1)
-      float sum[kDnFinishSlots][2];
-      sum_slices<kDnFinishSlots, 2>(part + (int64_t)p0 * splits * n + col, (int64_t)splits * n, splits, n,
-                                    sum, rows);
-#pragma unroll
-      for (int s = 0; s < kDnFinishSlots; ++s) {
-        if (s < rows) {
-          float a = sum[s][0], b = sum[s][1];
-          fwht128_pair(a, b);
-          ya += wt[s] * (a * kInvSqrt128 * h2f((uint16_t)(sv[s] & 0xFFFF)));
-          yb += wt[s] * (b * kInvSqrt128 * h2f((uint16_t)(sv[s] >> 16)));
-        }
-      }
+    for (int s = 0; s < topk; ++s) {
+      const float2 t = *reinterpret_cast<const float2*>(terms + s * 128 + 2 * lane_id());
+      ya += t.x;
+      yb += t.y;
     }
     *reinterpret_cast<float2*>(y + (int64_t)tok * n + col) = make_float2(ya, yb);
   }
