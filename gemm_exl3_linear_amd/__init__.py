@@ -316,8 +316,8 @@ def exl3_linear(x, w: Exl3Weight, out_dtype=None, out=None, workspace=None, stre
     cw = w._c()
     if workspace is None:  # a caller's workspace is checked against the size by the library
         need = int(lib().exl3_linear_workspace_size(ctypes.byref(cw), int(m)))
-        if need:
-            workspace = torch.zeros(need, dtype=torch.uint8, device=x.device)
+        if need:  # scratch only: no clearing needed
+            workspace = torch.empty(need, dtype=torch.uint8, device=x.device)
     wsb = 0 if workspace is None else workspace.numel() * workspace.element_size()
     _check(lib().exl3_linear(ctypes.byref(cw), _ptr(x), m, x.stride(0), _ptr(out), out.stride(0), ydt,
                              _ptr(workspace), wsb, _stream(stream)), "exl3_linear")
@@ -396,8 +396,8 @@ def exl3_linear_multi(x, ws, out_dtype=None, outs=None, workspace=None, stream=N
     arr, _recs = _weight_array(ws)
     if workspace is None:
         need = int(lib().exl3_linear_multi_workspace_size(arr, len(ws), int(m)))
-        if need:
-            workspace = torch.zeros(need, dtype=torch.uint8, device=x.device)
+        if need:  # scratch only: no clearing needed
+            workspace = torch.empty(need, dtype=torch.uint8, device=x.device)
     wsb = 0 if workspace is None else workspace.numel() * workspace.element_size()
     yp = (ctypes.c_void_p * len(outs))(*[_ptr(o) for o in outs])
     ld = (ctypes.c_int64 * len(outs))(*[o.stride(0) for o in outs])

@@ -75,15 +75,10 @@ struct DenseGemmRun {
   }
 };
 
-// The workspace starts with the same arrival-counter region as the decode
-// GEMV's (left untouched here, so it stays zero), followed by x' (fp16,
-// fragment-major, m rounded up to 16 rows).
-static size_t counter_region(int n) { return ((size_t)(n / 128) * 4 + 255) & ~(size_t)255; }
+// The workspace holds x' (fp16, fragment-major, m rounded up to 16 rows).
 static int64_t frag_rows(int64_t m) { return (m + 15) & ~(int64_t)15; }
 
-size_t gemm_workspace(int k, int n, int m) {
-  return counter_region(n) + (size_t)frag_rows(m) * k * sizeof(uint16_t);
-}
+size_t gemm_workspace(int k, int /*n*/, int m) { return (size_t)frag_rows(m) * k * sizeof(uint16_t); }
 
 int64_t gemm_max_workgroups(int k, int n, int64_t m) {
   const int64_t frag = (m + 15) / 16 * (k / 128);  // launch_input_frag
@@ -95,7 +90,7 @@ int64_t gemm_max_workgroups(int k, int n, int64_t m) {
 hipError_t launch_gemm(const uint16_t* trellis, const uint16_t* suh, const uint16_t* svh,
                        const uint16_t* bias, int k, int n, int bits, const uint16_t* x, int m,
                        int64_t ldx, void* y, int64_t ldy, bool y_f32, void* ws, hipStream_t s) {
-  uint16_t* xp = reinterpret_cast<uint16_t*>(static_cast<unsigned char*>(ws) + counter_region(n));
+  uint16_t* xp = static_cast<uint16_t*>(ws);
   hipError_t e = launch_input_frag(x, ldx, m, k, suh, xp, s);
   if (e != hipSuccess) return e;
   const int bm = choose_bm(m);

@@ -160,10 +160,10 @@ size_t exl3_linear_workspace_size(const exl3_weight* w, int64_t m);
  *   y      [m][ldy] of y_dtype (EXL3_F16 or EXL3_F32; fp32 outputs are the
  *          issue's "decodeF32/promptF32" contract), ldy >= n, multiple of 8
  *   ws     device workspace of at least exl3_linear_workspace_size(w, m)
- *          bytes (may be NULL when that size is 0).  It must be zero-filled
- *          before its first use: it holds arrival counters that every call
- *          leaves at zero again, so a workspace can be reused by later calls
- *          (of any size, on the same stream) without clearing it.
+ *          bytes (may be NULL when that size is 0): scratch of the call
+ *          (partial sums, the transformed activations).  Nothing is kept in
+ *          it between calls, so it needs no clearing and serves later calls
+ *          of any size on the same stream; calls that overlap on it race.
  * m == 0 returns EXL3_OK without enqueueing anything.  The kernel (decode
  * GEMV for m <= 16, MFMA GEMM above) is chosen internally from m.  Within
  * each of the ranges 1 <= m <= 16 and m > 16 a row's result does not depend
@@ -215,7 +215,7 @@ size_t exl3_linear_multi_workspace_size(const exl3_weight* const* w, int32_t cou
  *   y      host array of count device pointers, y[i] is [m][ldy[i]] of
  *          y_dtype with ldy[i] >= w[i]->n, multiple of 8
  *   ws     device workspace of at least exl3_linear_multi_workspace_size
- *          bytes, zero-filled before its first use (same rule as exl3_linear)
+ *          bytes, scratch of the call as for exl3_linear
  * m == 1 runs all tensors in one decode-GEMV launch and one finishing
  * launch (each tensor keeps its own split over a share of the waves, in
  * proportion to its trellis bytes, so its results agree with exl3_linear to
@@ -279,7 +279,8 @@ size_t exl3_grouped_experts_workspace_size(const exl3_expert_weights* gate_up,
  *                 Y[i] = sum over s in slot order of w[i][s] * down_e(a),
  *                 a = silu(gate_e(x_i)) * up_e(x_i), e = topk_ids[i][s]
  *   ws            device workspace of at least the queried size, zero-filled
- *                 before its first use (same counter rule as exl3_linear)
+ *                 before its first use; calls leave its arrival counts at
+ *                 zero, so it serves later calls without clearing
  * 1 <= topk <= EXL3_MAX_TOPK.  t == 0 returns EXL3_OK without work.
  * Out-of-range ids are a contract violation and are not checked by default.
  * With the environment variable EXL3_CHECK_IDS set (not "0"; read at every
@@ -290,11 +291,13 @@ size_t exl3_grouped_experts_workspace_size(const exl3_expert_weights* gate_up,
  * being captured returns EXL3_E_INVALID without enqueueing anything (the
  * capture stays valid).  The same holds for exl3_grouped_experts_mixed.
  * Small calls (t * topk <= 384) hand partial sums between workgroups planned
- * on one XCD; a workgroup that finds itself on another XCD takes a
- * device-scope release/acquire hand-off instead, so results never depend on
- * the dispatch order.  The environment variable EXL3_FORCE_DEVICE_SCOPE (not
- * "0"; read at every call) makes every workgroup take that hand-off: the
- * results are the same bits, only slower (a debug check of the guard).    */
+ * on one XCD (the XCD each group was finished on in the previous call, kept
+ * in the workspace's counters); a workgroup that finds itself on another XCD
+ * takes a device-scope release/acquire hand-off instead, so results never
+ * depend on the dispatch order.  The environment variable
+ * EXL3_FORCE_DEVICE_SCOPE (not "0"; read at every call) makes every
+ * workgroup take that hand-off: the results are the same bits, only slower
+ * (a debug check of the guard).                                            */
 exl3_status exl3_grouped_experts(const exl3_expert_weights* gate_up,
                                  const exl3_expert_weights* down, const void* x,
                                  const int32_t* topk_ids, const float* topk_weights, int64_t t,

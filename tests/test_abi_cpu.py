@@ -33,7 +33,7 @@ def test_workspace_queries_are_host_only():
     for m in (1, 4, 16):
         ws = L.exl3_linear_workspace_size(ctypes.byref(w), m)
         assert ws > 0 and ws % 4 == 0
-    assert L.exl3_linear_workspace_size(ctypes.byref(w), 4096) == 4096 * 5120 * 2 + 768
+    assert L.exl3_linear_workspace_size(ctypes.byref(w), 4096) == 4096 * 5120 * 2
     assert L.exl3_linear_workspace_size(ctypes.byref(_w(bits=9)), 1) == 0
     assert L.exl3_linear_workspace_size(ctypes.byref(_w(k=200)), 1) == 0
     gu = X._Arena(16, 16, 16, 256, 2, 2048, 512, 3, X.CODEBOOK_MUL1)
