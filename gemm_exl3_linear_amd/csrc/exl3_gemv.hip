@@ -116,7 +116,7 @@ static void sk_split_extent(const SkSplit& s, int64_t KT, int64_t NB, int64_t W,
 // m <= kMfLdsRows, one otherwise; then the transformed activations when
 // m > kMfLdsRows).  The plan depends on (k, n) only, so every m from 1 to 16
 // sums in the same order.  No device query.
-GemvPlan plan_gemv(int k, int n, int m) {
+static GemvPlan plan_gemv_new(int k, int n, int m) {
   GemvPlan p;
   const int64_t KT = k / 16, NB = n / 128, NP = (NB + 1) / 2, R = KT * NP;
   int64_t W = kMfWorkgroups;
@@ -126,11 +126,29 @@ GemvPlan plan_gemv(int k, int n, int m) {
                           kMfTierWeight2);
   p.splits = (int)W;
   sk_split_extent(p.split, KT, NP, W, p.slots, p.kc);
-  p.lds = 0;
-  p.ctr_bytes = 0;
   const size_t per_slot = (m <= kMfLdsRows ? 4 : 1) * (size_t)m * 256 * sizeof(float);  // wave or workgroup slots
   p.xprep_off = ((size_t)NP * p.slots * per_slot + 255) & ~(size_t)255;
   p.ws = p.xprep_off + (m > kMfLdsRows ? (size_t)m * k * sizeof(uint16_t) : 0);
+  return p;
+}
+
+// A plan depends on (k, n, m) only; each host thread keeps the last few it
+// made, so a call (which plans twice: the workspace check, then the launch)
+// costs a lookup instead of the split arithmetic.
+constexpr int kPlanMemo = 16;
+GemvPlan plan_gemv(int k, int n, int m) {
+  struct Entry {
+    int k, n, m;
+    GemvPlan p;
+  };
+  static thread_local Entry memo[kPlanMemo];
+  static thread_local int used = 0, next = 0;
+  for (int i = 0; i < used; ++i)
+    if (memo[i].k == k && memo[i].n == n && memo[i].m == m) return memo[i].p;
+  const GemvPlan p = plan_gemv_new(k, n, m);
+  memo[next] = Entry{k, n, m, p};
+  next = (next + 1) % kPlanMemo;
+  if (used < kPlanMemo) ++used;
   return p;
 }
 
@@ -187,7 +205,7 @@ hipError_t launch_gemv(const uint16_t* trellis, const uint16_t* suh, const uint1
   a.W = plan.splits;
   a.sp = plan.split;
   a.slots = plan.slots;
-  a.part = reinterpret_cast<float*>(base + plan.ctr_bytes);
+  a.part = reinterpret_cast<float*>(base);  // the partials start the workspace
   a.svh = svh;
   a.bias = bias;
   a.y = y;
@@ -205,7 +223,7 @@ hipError_t launch_gemv(const uint16_t* trellis, const uint16_t* suh, const uint1
 // launch's first round.  Partials of tensor i follow those of i - 1.
 static_assert(kMultiMax == kSkMaxMulti, "multi-tensor limits differ");
 
-MultiPlan plan_gemv_multi(const MultiTensor* t, int count, int k) {
+static MultiPlan plan_gemv_multi_new(const MultiTensor* t, int count, int k) {
   MultiPlan mp;
   mp.count = count;
   double total = 0;
@@ -240,6 +258,37 @@ MultiPlan plan_gemv_multi(const MultiTensor* t, int count, int k) {
   }
   mp.ws = off;
   return mp;
+}
+
+// Memo of the last few multi-tensor plans of this host thread, keyed by k
+// and the tensors' (n, bits) in order, as for plan_gemv.
+MultiPlan plan_gemv_multi(const MultiTensor* t, int count, int k) {
+  struct Entry {
+    int count, k;
+    int n[kMultiMax], bits[kMultiMax];
+    MultiPlan p;
+  };
+  static thread_local Entry memo[kPlanMemo];
+  static thread_local int used = 0, next = 0;
+  for (int i = 0; i < used; ++i) {
+    const Entry& e = memo[i];
+    if (e.count != count || e.k != k) continue;
+    bool same = true;
+    for (int j = 0; j < count && same; ++j) same = e.n[j] == t[j].n && e.bits[j] == t[j].bits;
+    if (same) return e.p;
+  }
+  Entry e;
+  e.count = count;
+  e.k = k;
+  for (int j = 0; j < count; ++j) {
+    e.n[j] = t[j].n;
+    e.bits[j] = t[j].bits;
+  }
+  e.p = plan_gemv_multi_new(t, count, k);
+  memo[next] = e;
+  next = (next + 1) % kPlanMemo;
+  if (used < kPlanMemo) ++used;
+  return e.p;
 }
 
 hipError_t launch_gemv_multi(const MultiTensor* t, int count, int k, const uint16_t* x, void* const* y,

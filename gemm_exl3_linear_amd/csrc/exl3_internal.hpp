@@ -47,8 +47,6 @@ struct GemvPlan {
   int splits;        // workgroups of the grid
   int kc;            // longest run of units
   int slots;         // partial-sum slots per 256-column pair
-  size_t lds;        // dynamic LDS bytes of the kernel
-  size_t ctr_bytes;  // bytes before the fp32 partials (0: no arrival counters)
   size_t xprep_off;  // offset of the transformed rows x' (m > 4)
   size_t ws;         // workspace bytes (partials + x')
 };
