@@ -538,20 +538,18 @@ __global__ __launch_bounds__(kBinThreads) void bin_scatter(const int32_t* __rest
 }
 
 // x'_slot[r] = (x[token(r)] .* suh[e(r)][slot]) H for both slots, one wave
-// per (token, slot) pair, written to its sorted row r.  Lane l holds 8 elements of block 4 pass + l / 16 (the
+// per sorted row.  Lane l holds 8 elements of block 4 pass + l / 16 (the
 // fwht128_x8 layout); the x and sign loads of up to kGuPasses passes
 // (16 blocks, 2048 elements) are all issued before the first transform.
 constexpr int kGuPasses = 4;
 
 __global__ __launch_bounds__(256) void gu_input_transform(
     const uint16_t* __restrict__ x, int topk, int64_t P, int hidden,
-    const int32_t* __restrict__ pos, const int32_t* __restrict__ ids,
+    const int32_t* __restrict__ sorted, const int32_t* __restrict__ ids,
     const uint16_t* __restrict__ suh_gu, uint16_t* __restrict__ xg) {
-  // waves in (token, slot) order: the topk waves of a token read its row of
-  // x together (from HBM once), and each writes its sorted row pos[pair]
-  const int64_t pair = (int64_t)blockIdx.x * 4 + (threadIdx.x >> 6);
-  if (pair >= P) return;
-  const int64_t r = pos[pair];
+  const int64_t r = (int64_t)blockIdx.x * 4 + (threadIdx.x >> 6);
+  if (r >= P) return;
+  const int pair = sorted[r];
   const int e = ids[pair];
   const int64_t tok = pair / topk;
   const int lane = (int)lane_id();
@@ -870,7 +868,7 @@ hipError_t launch_grouped(const ArenaDesc& gu, const ArenaDesc& dn, const uint16
   {
     const int64_t tasks = P;  // one wave each
     hipLaunchKernelGGL(gu_input_transform, dim3((unsigned)((tasks + 3) / 4)), dim3(256), 0, s, x,
-                       topk, P, hidden, pos, ids, gu.suh, xg);
+                       topk, P, hidden, sorted, ids, gu.suh, xg);
   }
   if ((e = hipGetLastError()) != hipSuccess) return e;
   GroupedGateUpRes rg{tiles, ntiles, xg, P, hidden, inter, gu.trellis, gu.svh, dn.suh,
