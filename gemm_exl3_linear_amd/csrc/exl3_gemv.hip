@@ -21,16 +21,16 @@ namespace exl3 {
 // ---------------------------------------------------------------------------
 // planning and launch (dense tensors)
 // ---------------------------------------------------------------------------
-size_t gemv_lds_bytes(int kc, int m) {
+size_t gemv_lds_bytes(int kc, int m, int nw) {
   const size_t xs = ((size_t)kc * m * 2 + 15) & ~(size_t)15;
-  const size_t tr = 4 * 64 * 20 * 4;
-  const size_t red = (size_t)4 * m * 128 * 4;
+  const size_t tr = (size_t)nw * 64 * 20 * 4;
+  const size_t red = (size_t)nw * m * 128 * 4;
   return xs + (tr > red ? tr : red);
 }
 
-int gemv_prefetch(int kc) {
-  const int cnt = kc / 64;  // k tiles per wave
-  return (cnt % 8 == 0) ? 8 : (cnt % 4 == 0) ? 4 : 2;
+int gemv_prefetch(int kc, int nw) {
+  const int cnt = kc / (16 * nw);  // k tiles per wave
+  return (cnt % 8 == 0) ? 8 : (cnt % 4 == 0) ? 4 : (cnt % 2 == 0) ? 2 : 1;
 }
 
 // Split of k into ranges of kc rows (kc a multiple of 128).  Preference: at

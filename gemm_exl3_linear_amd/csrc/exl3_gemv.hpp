@@ -6,7 +6,7 @@
 // output group runs (split-k sum in a fixed order, output transform, ...):
 // R::FinishPre holds what the finish reads that does not depend on the
 // partial sums, loaded by every workgroup during its k range
-// (finish_prefetch), and R::finish runs on all four waves of the finisher.
+// (finish_prefetch), and R::finish runs on all the finisher's waves.
 #pragma once
 
 #include "exl3_device.hpp"
@@ -25,23 +25,35 @@ struct GemvTask {
 };
 
 constexpr size_t kGemvMaxLds = 64 * 1024;
+// Waves of a workgroup (NW below): wave w takes the k tiles w, w + NW, ... of
+// its range.  A grid of at most kGemvWideGrid workgroups (two per CU) runs
+// eight waves, which halves each wave's serial chain of tiles (what a small
+// call waits for); larger grids run four, where eight cost occupancy.
+// Measured on MI355X, routed experts 256 x (2048 -> 2 x 512 -> 2048), K=3,
+// top-8 (both launches per call): T=1 20.9 us against 22.2 with four waves
+// everywhere, T=2 22.3 against 25.0, T=4 31.6 against 33.2; with eight waves
+// for every grid T=8 took 52.0 against 48.7 and T=48 220 against 194.
+constexpr int kGemvMaxWaves = 8;
+constexpr int kGemvWideGrid = 512;
+inline int gemv_waves(int grid) { return grid <= kGemvWideGrid ? 8 : 4; }
 constexpr int kGemvTargetWorkgroups = 256;
 constexpr int kGemvMaxKc = 1024;  // longest k range of one workgroup in small grids
 
-size_t gemv_lds_bytes(int kc, int m);
+size_t gemv_lds_bytes(int kc, int m, int nw = kGemvMaxWaves);
 int gemv_choose_splits(int k, int groups, int m, int target_wgs);
-int gemv_prefetch(int kc);
+int gemv_prefetch(int kc, int nw = 4);
 
 // ---------------------------------------------------------------------------
 // prologue: x' = (x .* suh) H over the workgroup's k range into LDS, layout
 // xs[kt][i][16] (k tile, activation row, 16 k values) as fp16.
 // ---------------------------------------------------------------------------
+template <int NW>
 __device__ __forceinline__ void gemv_prologue(const GemvTask& T, int k0, int kc, uint16_t* xs) {
   const int wave = threadIdx.x >> 6;
   const int lane = threadIdx.x & 63;
   const int kblocks = kc >> 7;
   const int m = T.m;
-  for (int task = wave; task < kblocks * m; task += 4) {
+  for (int task = wave; task < kblocks * m; task += NW) {
     const int i = task / kblocks;
     const int blk = task - i * kblocks;
     const int kk = k0 + blk * 128 + 2 * lane;
@@ -156,7 +168,7 @@ __device__ __forceinline__ void gemv_tile(const uint32_t (&D)[K], int kt, int m,
 // per lane; the per-wave trip count kc/64 must be a multiple of PF (the
 // planner guarantees it), so the loop has no tail and no branch around its
 // loads.
-template <int K, int PF, class R>
+template <int K, int PF, int NW, class R>
 __device__ __forceinline__ void gemv_unit(const R& r, const GemvTask& T, int unit, int split, int nb,
                                           int n, int kc, unsigned char* smem, int& last_flag,
                                           typename R::FinishPre& pre) {
@@ -175,11 +187,12 @@ __device__ __forceinline__ void gemv_unit(const R& r, const GemvTask& T, int uni
   uint32_t* tr = tr_all + wave * (64 * 20);
   uint32_t* my = tr + (t * 8 + p) * 20;
 
-  // wave w handles k tiles w, w+4, w+8, ... of the range; iteration it -> tile w + 4 it
+  // wave w handles k tiles w, w + NW, ... of the range; iteration it -> tile
+  // w + NW it
   const uint32_t* tbase = reinterpret_cast<const uint32_t*>(T.trellis) +
                           ((int64_t)((k0 >> 4) + wave) * nt + nb * 8 + t) * (8 * K) + K * p;
-  const int64_t it_stride = (int64_t)4 * nt * (8 * K);
-  const int cnt = kc >> 6;
+  const int64_t it_stride = (int64_t)NW * nt * (8 * K);
+  const int cnt = kc / (16 * NW);
 
   // the group's XCD record (constant during the call: arrivals change only
   // the count fields, and the finisher rewrites it after every arrival),
@@ -194,7 +207,7 @@ __device__ __forceinline__ void gemv_unit(const R& r, const GemvTask& T, int uni
 #pragma unroll
   for (int s = 0; s < PF; ++s) load_rowpair<K>(tbase + s * it_stride, ring[s]);
 
-  gemv_prologue(T, k0, kc, xs);
+  gemv_prologue<NW>(T, k0, kc, xs);
   __syncthreads();
   // what the finish needs besides the partial sums, in case this workgroup
   // arrives last: issued after the input transform (which waits for its own
@@ -209,7 +222,7 @@ __device__ __forceinline__ void gemv_unit(const R& r, const GemvTask& T, int uni
 #pragma unroll
     for (int s = 0; s < PF; ++s) {
       const int it = base + s;
-      gemv_tile<K>(ring[s], wave + 4 * it, m, xs, tr, my, g, j, acc);
+      gemv_tile<K>(ring[s], wave + NW * it, m, xs, tr, my, g, j, acc);
       // refill the slot just consumed (same registers, so no copy and no wait
       // at the loop edge); the last block re-reads the final tile, a cache
       // hit, instead of branching
@@ -218,7 +231,7 @@ __device__ __forceinline__ void gemv_unit(const R& r, const GemvTask& T, int uni
     }
   }
 
-  // fixed-order reduction of the four waves' partials
+  // fixed-order reduction of the waves' partials (wave order)
   __syncthreads();
 #pragma unroll
   for (int q = 0; q < 8; ++q) {
@@ -229,12 +242,11 @@ __device__ __forceinline__ void gemv_unit(const R& r, const GemvTask& T, int uni
     }
   }
   __syncthreads();
-  for (int idx = threadIdx.x; idx < m * 128; idx += 256) {
+  for (int idx = threadIdx.x; idx < m * 128; idx += 64 * NW) {
     const int i = idx >> 7, c = idx & 127;
     float s = red[i * 128 + c];
-    s += red[(m + i) * 128 + c];
-    s += red[(2 * m + i) * 128 + c];
-    s += red[(3 * m + i) * 128 + c];
+#pragma unroll
+    for (int w = 1; w < NW; ++w) s += red[(w * m + i) * 128 + c];
     __hip_atomic_store(T.partial + (int64_t)i * n + nb * 128 + c, s, __ATOMIC_RELAXED,
                        __HIP_MEMORY_SCOPE_AGENT);
   }
@@ -276,8 +288,8 @@ __device__ __forceinline__ void gemv_group_finish(const R& r, int unit, int nb, 
 
 // K = 1..8: every unit has that width.  K = 0: each unit has its own width
 // (T.bits, a width per expert), all of them in one launch.
-template <int K, int PF, class R>
-__global__ __launch_bounds__(256) void gemv_kernel(R r, int /*k*/, int n, int kc) {
+template <int K, int PF, int NW, class R>
+__global__ __launch_bounds__(64 * NW) void gemv_kernel(R r, int /*k*/, int n, int kc) {
   extern __shared__ __align__(16) unsigned char smem[];
   __shared__ int last_flag;
   typename R::FinishPre pre;
@@ -287,31 +299,41 @@ __global__ __launch_bounds__(256) void gemv_kernel(R r, int /*k*/, int n, int kc
   if (!T.valid) return;
   if constexpr (K == 0) {
     switch (T.bits) {
-      case 1: gemv_unit<1, PF>(r, T, unit, split, nb, n, kc, smem, last_flag, pre); break;
-      case 2: gemv_unit<2, PF>(r, T, unit, split, nb, n, kc, smem, last_flag, pre); break;
-      case 3: gemv_unit<3, PF>(r, T, unit, split, nb, n, kc, smem, last_flag, pre); break;
-      case 4: gemv_unit<4, PF>(r, T, unit, split, nb, n, kc, smem, last_flag, pre); break;
-      case 5: gemv_unit<5, PF>(r, T, unit, split, nb, n, kc, smem, last_flag, pre); break;
-      case 6: gemv_unit<6, PF>(r, T, unit, split, nb, n, kc, smem, last_flag, pre); break;
-      case 7: gemv_unit<7, PF>(r, T, unit, split, nb, n, kc, smem, last_flag, pre); break;
-      case 8: gemv_unit<8, PF>(r, T, unit, split, nb, n, kc, smem, last_flag, pre); break;
+      case 1: gemv_unit<1, PF, NW>(r, T, unit, split, nb, n, kc, smem, last_flag, pre); break;
+      case 2: gemv_unit<2, PF, NW>(r, T, unit, split, nb, n, kc, smem, last_flag, pre); break;
+      case 3: gemv_unit<3, PF, NW>(r, T, unit, split, nb, n, kc, smem, last_flag, pre); break;
+      case 4: gemv_unit<4, PF, NW>(r, T, unit, split, nb, n, kc, smem, last_flag, pre); break;
+      case 5: gemv_unit<5, PF, NW>(r, T, unit, split, nb, n, kc, smem, last_flag, pre); break;
+      case 6: gemv_unit<6, PF, NW>(r, T, unit, split, nb, n, kc, smem, last_flag, pre); break;
+      case 7: gemv_unit<7, PF, NW>(r, T, unit, split, nb, n, kc, smem, last_flag, pre); break;
+      case 8: gemv_unit<8, PF, NW>(r, T, unit, split, nb, n, kc, smem, last_flag, pre); break;
       default: return;  // a width outside 1..8: the unit is left out
     }
   } else {
-    gemv_unit<K, PF>(r, T, unit, split, nb, n, kc, smem, last_flag, pre);
+    gemv_unit<K, PF, NW>(r, T, unit, split, nb, n, kc, smem, last_flag, pre);
   }
   if (last_flag) gemv_group_finish(r, unit, nb, n, last_flag, pre, smem);
 }
 
-// Launch with the prefetch depth the k range allows.
-template <int K, class R>
-hipError_t launch_gemv_kernel(const R& r, dim3 grid, size_t lds, hipStream_t s, int k, int n,
-                              int kc) {
-  switch (gemv_prefetch(kc)) {
-    case 8: hipLaunchKernelGGL((gemv_kernel<K, 8, R>), grid, dim3(256), lds, s, r, k, n, kc); break;
-    case 4: hipLaunchKernelGGL((gemv_kernel<K, 4, R>), grid, dim3(256), lds, s, r, k, n, kc); break;
-    default: hipLaunchKernelGGL((gemv_kernel<K, 2, R>), grid, dim3(256), lds, s, r, k, n, kc); break;
+// Launch with the waves the grid size calls for and the prefetch depth the k
+// range allows.
+template <int K, int NW, class R>
+void launch_gemv_nw(const R& r, dim3 grid, int m, hipStream_t s, int k, int n, int kc) {
+  const dim3 block(64 * NW);
+  const size_t lds = gemv_lds_bytes(kc, m, NW);
+  switch (gemv_prefetch(kc, NW)) {
+    case 8: hipLaunchKernelGGL((gemv_kernel<K, 8, NW, R>), grid, block, lds, s, r, k, n, kc); break;
+    case 4: hipLaunchKernelGGL((gemv_kernel<K, 4, NW, R>), grid, block, lds, s, r, k, n, kc); break;
+    case 2: hipLaunchKernelGGL((gemv_kernel<K, 2, NW, R>), grid, block, lds, s, r, k, n, kc); break;
+    default: hipLaunchKernelGGL((gemv_kernel<K, 1, NW, R>), grid, block, lds, s, r, k, n, kc); break;
   }
+}
+template <int K, class R>
+hipError_t launch_gemv_kernel(const R& r, dim3 grid, int m, hipStream_t s, int k, int n, int kc) {
+  if (gemv_waves((int)grid.x) == 8)
+    launch_gemv_nw<K, 8>(r, grid, m, s, k, n, kc);
+  else
+    launch_gemv_nw<K, 4>(r, grid, m, s, k, n, kc);
   return hipGetLastError();
 }
 

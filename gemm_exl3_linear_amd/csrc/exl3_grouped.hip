@@ -131,7 +131,7 @@ __device__ __forceinline__ void sum_slices(const float* p, int64_t row_stride, i
   }
 }
 
-// Slots of one token per wave in a down finish (four waves, top-k <= 16).
+// Slots of one token per wave in a down finish (four or eight waves, top-k <= 16).
 constexpr int kDnSlotsPerWave = 4;
 
 struct GuUnitRes {
@@ -274,7 +274,7 @@ struct DnUnitRes {
   __device__ unsigned int* counter(int u, int nb) const { return ctr + (u / topk) * (n >> 7) + nb; }
   __device__ unsigned int arrivals(int) const { return (unsigned int)(topk * splits); }
   // y[token, block] = sum over slots in order of w * ((sum_s partial) H .* svh).
-  // Wave w takes slots w, w + 4, ...; each slot's weighted term goes through
+  // Wave w takes slots w, w + nw, ... (nw waves); each slot's weighted term goes through
   // LDS and wave 0 adds them in slot order.
   struct FinishPre {
     uint32_t sv[kDnSlotsPerWave];  // svh of this wave's slots
@@ -283,11 +283,12 @@ struct DnUnitRes {
   __device__ FinishPre finish_prefetch(int u, int nb) const {
     FinishPre f;
     const int wave = threadIdx.x >> 6;
+    const int nw = (int)(blockDim.x >> 6);
     const int p0 = (u / topk) * topk;
     const int col = nb * 128 + 2 * (int)lane_id();
 #pragma unroll
     for (int q = 0; q < kDnSlotsPerWave; ++q) {
-      const int s = wave + 4 * q;
+      const int s = wave + nw * q;
       f.sv[q] = 0u;
       f.wt[q] = 0.f;
       if (s < topk) {
@@ -300,14 +301,15 @@ struct DnUnitRes {
   }
   __device__ void finish(int u, int nb, int, const FinishPre& f, unsigned char* smem) const {
     const int wave = threadIdx.x >> 6;
+    const int nw = (int)(blockDim.x >> 6);
     const int tok = u / topk;
     const int p0 = tok * topk;
     const int col = nb * 128 + 2 * (int)lane_id();
     float* terms = reinterpret_cast<float*>(smem);  // [topk][128]
-    const int mine = wave < topk ? (topk - wave + 3) / 4 : 0;  // slots of this wave
+    const int mine = wave < topk ? (topk - wave + nw - 1) / nw : 0;  // slots of this wave
     // slices (pair p0 + wave + 4 q, 0..splits-1)
     float sum[kDnSlotsPerWave][2];
-    sum_slices<kDnSlotsPerWave, 2>(part + (int64_t)(p0 + wave) * splits * n + col, (int64_t)4 * splits * n,
+    sum_slices<kDnSlotsPerWave, 2>(part + (int64_t)(p0 + wave) * splits * n + col, (int64_t)nw * splits * n,
                                    splits, n, sum, mine);
 #pragma unroll
     for (int q = 0; q < kDnSlotsPerWave; ++q) {
@@ -316,7 +318,7 @@ struct DnUnitRes {
         fwht128_pair(a, b);
         const float ta = f.wt[q] * (a * kInvSqrt128 * h2f((uint16_t)(f.sv[q] & 0xFFFF)));
         const float tb = f.wt[q] * (b * kInvSqrt128 * h2f((uint16_t)(f.sv[q] >> 16)));
-        *reinterpret_cast<float2*>(terms + (wave + 4 * q) * 128 + 2 * lane_id()) = make_float2(ta, tb);
+        *reinterpret_cast<float2*>(terms + (wave + nw * q) * 128 + 2 * lane_id()) = make_float2(ta, tb);
       }
     }
     __syncthreads();
@@ -333,19 +335,17 @@ struct DnUnitRes {
 
 template <int K>
 struct GuUnitRun {
-  static hipError_t run(const GuUnitRes& r, int k, int n, int /*units*/, int kc, size_t lds,
-                        hipStream_t s) {
+  static hipError_t run(const GuUnitRes& r, int k, int n, int /*units*/, int kc, hipStream_t s) {
     const int grid = gemv_grid(r.pairs * (n / 128), 2 * r.splits);
-    return launch_gemv_kernel<K>(r, dim3(grid), lds, s, k, n, kc);
+    return launch_gemv_kernel<K>(r, dim3(grid), 1, s, k, n, kc);
   }
 };
 
 template <int K>
 struct DnUnitRun {
-  static hipError_t run(const DnUnitRes& r, int k, int n, int /*units*/, int kc, size_t lds,
-                        hipStream_t s) {
+  static hipError_t run(const DnUnitRes& r, int k, int n, int /*units*/, int kc, hipStream_t s) {
     const int grid = gemv_grid(r.tokens * (n / 128), r.topk * r.splits);
-    return launch_gemv_kernel<K>(r, dim3(grid), lds, s, k, n, kc);
+    return launch_gemv_kernel<K>(r, dim3(grid), 1, s, k, n, kc);
   }
 };
 
@@ -837,14 +837,14 @@ hipError_t launch_grouped(const ArenaDesc& gu, const ArenaDesc& dn, const uint16
     rg.ew = arena_widths(gu);
     rg.off_xcd_all = off_xcd_all ? 1 : 0;
     const int kc_g = hidden / L.s_gu;
-    e = run_widths<GuUnitRun>(gu, rg, hidden, inter, (int)(P * 2), kc_g, gemv_lds_bytes(kc_g, 1), s);
+    e = run_widths<GuUnitRun>(gu, rg, hidden, inter, (int)(P * 2), kc_g, s);
     if (e != hipSuccess) return e;
     DnUnitRes rd{dn.trellis, dn.svh, words_per_bit(dn) * dn.bits, inter, hidden, xd, ids, w, topk,
                  part_dn, L.s_dn, ctr_dn, y, (int)t};
     rd.ew = arena_widths(dn);
     rd.off_xcd_all = off_xcd_all ? 1 : 0;
     const int kc_d = inter / L.s_dn;
-    return run_widths<DnUnitRun>(dn, rd, inter, hidden, (int)P, kc_d, gemv_lds_bytes(kc_d, 1), s);
+    return run_widths<DnUnitRun>(dn, rd, inter, hidden, (int)P, kc_d, s);
   }
 
   const GemmLayout L = gemm_layout(gu, dn, P);
