@@ -33,12 +33,14 @@
 // waves never wait for each other); above, the four waves meet in LDS at each
 // segment end and the workgroup stores t (a quarter of the partial traffic).
 //
-// x': for m <= kMfLdsRows every wave transforms the k blocks its workgroup's
-// run touches into its own LDS region (the input transform is a small part
-// of a wave's work); above, one input-transform launch (gemv_xprep_kernel)
-// writes x' for all rows first and the A fragments are loaded with the
-// trellis.  Both compute x' with the same function (xform8), so a row's x'
-// is the same bits either way.
+// x': for m <= kMfLdsRows the four waves transform the k blocks the
+// workgroup's run touches into one LDS region of the workgroup, a round of
+// four blocks each, then meet at one workgroup barrier (a region per wave,
+// each wave transforming every block, made m = 2 and 4 calls 0.8 and 1.3 us
+// longer on 5120 x 17408); above, one input-transform launch
+// (gemv_xprep_kernel) writes x' for all rows first and the A fragments are
+// loaded with the trellis.  Both compute x' with the same function (xform8),
+// so a row's x' is the same bits either way.
 #pragma once
 
 #include "exl3_device.hpp"
@@ -53,9 +55,9 @@ constexpr int kMfRoundWorkgroups = 256;  // the first dispatch round: one per CU
 constexpr int kMfTierWeight1 = 13;
 constexpr int kMfTierWeight2 = 7;
 constexpr int kMfMaxRunWG = 80;    // longest run of units of a workgroup (bounds the LDS x' region)
-constexpr int kMfLdsRows = 4;      // rows whose x' each wave stages in LDS itself
+constexpr int kMfLdsRows = 4;      // rows whose x' the workgroup stages in LDS itself
 constexpr int kMfXBlocks = 12;     // k blocks a workgroup's run may touch
-constexpr int kMfXRowBytes = kMfXBlocks * 128 * 2;  // LDS x' bytes per row and wave
+constexpr int kMfXRowBytes = kMfXBlocks * 128 * 2;  // LDS x' bytes per row
 constexpr int kMfGroupBatch = 8;   // workgroup slots per lane loaded per batch in the finish
 
 // the x' positions read (one unit ahead of the last) stay inside the region
@@ -300,20 +302,21 @@ __device__ __forceinline__ void mf_finish(const MfArgs& a, int i, int nb) {
   }
 }
 
-// LDS of one workgroup: XR > 0, a region of XR rows of x' per wave; XR = 0,
-// the combine buffer (a row block of 256 floats per wave and row).
+// LDS of one workgroup: XR > 0, a region of XR rows of x' shared by the
+// waves; XR = 0, the combine buffer (a row block of 256 floats per wave and
+// row).
 template <int XR>
 struct MfLds {
-  static constexpr int kXBytes = 4 * XR * kMfXRowBytes;
+  static constexpr int kXBytes = XR * kMfXRowBytes;
   static constexpr int kCombineBytes = XR > 0 ? 0 : 4 * 16 * 256 * 4;
   static constexpr int kBytes = XR > 0 ? kXBytes : kCombineBytes;
 };
 
 // The work of workgroup `wg`: the units [r0, r0 + len) of its run, wave w
-// taking units r0 + w, r0 + w + 4, ...  XR = rows whose x' each wave stages
-// in LDS itself (1 or kMfLdsRows; the waves store their own slots), or 0: x'
-// comes from the input-transform launch and the workgroup combines its waves'
-// sums in LDS.
+// taking units r0 + w, r0 + w + 4, ...  XR = rows whose x' the workgroup
+// stages in LDS itself (1 or kMfLdsRows; the waves store their own slots), or
+// 0: x' comes from the input-transform launch and the workgroup combines its
+// waves' sums in LDS.
 template <int K, int XR>
 __device__ __forceinline__ void mf_wg(const MfArgs& a, int wg, unsigned char* smem) {
   constexpr bool LDSX = XR > 0;
@@ -326,7 +329,7 @@ __device__ __forceinline__ void mf_wg(const MfArgs& a, int wg, unsigned char* sm
   const int lane = threadIdx.x & 63;
   const int g = lane >> 4, T = lane & 15;  // decode: row quad, n tile of the pair
   const int j = lane & 15;                 // A operand: activation row
-  unsigned char* xl = smem + wave * XR * kMfXRowBytes;  // the wave's x' region
+  unsigned char* xl = smem;  // the workgroup's x' region
   float* cbuf = reinterpret_cast<float*>(smem);          // combine buffer (XR == 0)
 
   const int p_first = r0 / KT;
@@ -387,9 +390,10 @@ __device__ __forceinline__ void mf_wg(const MfArgs& a, int wg, unsigned char* sm
     if (pf_left > 0) --pf_left;
   };
 
-  // ---- x' of rows < m staged by each wave: block b of the run is
-  // (kt0 / 8 + b) mod k/128; lane (g, j) loads 8 elements of run block
-  // 4 rd + g in rounds rd = 0, 1, 2 (rounds past the run's blocks skipped).
+  // ---- x' of rows < m staged by the workgroup: block b of the run is
+  // (kt0 / 8 + b) mod k/128; wave rd takes round rd (rd = 0, 1, 2; wave 3
+  // none), whose lane (g, j) loads 8 elements of run block 4 rd + g (rounds
+  // past the run's blocks skipped).
   constexpr int XRD = kMfXBlocks / 4;
   const int nblk = ((kt0 & 7) + len + 7) >> 3;
   uint4 xv[LDSX ? XR : 1][LDSX ? XRD : 1], sv[LDSX ? XRD : 1];
@@ -397,7 +401,7 @@ __device__ __forceinline__ void mf_wg(const MfArgs& a, int wg, unsigned char* sm
     const int kb0 = kt0 >> 3, KBn = KT >> 3;
 #pragma unroll
     for (int rd = 0; rd < XRD; ++rd) {
-      if (4 * rd < nblk) {  // uniform
+      if (rd == wave && 4 * rd < nblk) {  // uniform
         const int b = 4 * rd + g;
         const int bb = b < nblk ? b : nblk - 1;
         const int kk = ((kb0 + bb) % KBn) * 128 + 8 * j;
@@ -425,7 +429,7 @@ __device__ __forceinline__ void mf_wg(const MfArgs& a, int wg, unsigned char* sm
         uint16_t* xs = reinterpret_cast<uint16_t*>(xl + i * kMfXRowBytes);
 #pragma unroll
         for (int rd = 0; rd < XRD; ++rd) {
-          if (4 * rd < nblk) {  // uniform
+          if (rd == wave && 4 * rd < nblk) {  // uniform
             const int b = 4 * rd + g;
             const uint4 o = xform8(xv[i][rd], sv[rd]);
             if (b < nblk) *reinterpret_cast<uint4*>(xs + b * 128 + 8 * j) = o;
@@ -433,10 +437,7 @@ __device__ __forceinline__ void mf_wg(const MfArgs& a, int wg, unsigned char* sm
         }
       }
     }
-    // the wave's own region: a wave-level barrier orders the writes
-    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront", "local");
-    __builtin_amdgcn_wave_barrier();
-    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront", "local");
+    __syncthreads();  // every round written before any wave reads
   }
 
   // ---- main loop
