@@ -15,7 +15,7 @@ struct DenseGemmRes {
   int m;
   int bm;
   int mt;   // row tiles
-  int nbt;  // 256-column tiles
+  int nbt;  // 128-column tiles
   const uint16_t* trellis;
   const uint16_t* svh;
   const uint16_t* bias;
