@@ -426,7 +426,8 @@ static GemmLayout gemm_layout(const ArenaDesc& gu, const ArenaDesc& dn, int64_t 
 // not fixed (LDS atomics), but every row is computed independently of its
 // position, so the output does not depend on it.
 constexpr int kBinChunk = 8192;  // experts per pass (32 KB of LDS)
-constexpr int kPlanThreads = 1024;
+constexpr int kPlanThreads = 256;
+constexpr int kCombineBatch = 8;  // slots whose loads the combine issues together
 
 __device__ __forceinline__ void bin_load_ids(const int32_t* __restrict__ ids, int64_t P,
                                              int (&ev)[kBinPerThread]) {
@@ -457,40 +458,67 @@ __global__ __launch_bounds__(kBinThreads) void bin_count(const int32_t* __restri
   }
 }
 
-__device__ __forceinline__ int block_exclusive_scan(int v, int* sh, int& total) {
-  const int tid = threadIdx.x;
-  sh[tid] = v;
-  __syncthreads();
-  for (int d = 1; d < kPlanThreads; d <<= 1) {
-    const int add = tid >= d ? sh[tid - d] : 0;
-    __syncthreads();
-    sh[tid] += add;
-    __syncthreads();
+// Exclusive scans of two values over the workgroup (in thread order) and
+// their totals: an inclusive scan inside each wave (lane shuffles), then the
+// wave totals through LDS.  Integer sums, so the result is exact.
+__device__ __forceinline__ void block_exclusive_scan2(int a, int b, int* sh, int& ea, int& eb, int& ta,
+                                                      int& tb) {
+  constexpr int NW = kPlanThreads / 64;
+  const int lane = (int)(threadIdx.x & 63), wave = (int)(threadIdx.x >> 6);
+  int ia = a, ib = b;
+#pragma unroll
+  for (int d = 1; d < 64; d <<= 1) {
+    const int xa = __shfl_up(ia, d), xb = __shfl_up(ib, d);
+    if (lane >= d) {
+      ia += xa;
+      ib += xb;
+    }
   }
-  const int incl = sh[tid];
-  total = sh[kPlanThreads - 1];
+  if (lane == 63) {
+    sh[wave] = ia;
+    sh[NW + wave] = ib;
+  }
   __syncthreads();
-  return incl - v;
+  int pa = 0, pb = 0, sa = 0, sb = 0;
+#pragma unroll
+  for (int w = 0; w < NW; ++w) {
+    const int va = sh[w], vb = sh[NW + w];
+    if (w < wave) {
+      pa += va;
+      pb += vb;
+    }
+    sa += va;
+    sb += vb;
+  }
+  __syncthreads();  // sh is written again by the next call
+  ea = pa + ia - a;
+  eb = pb + ib - b;
+  ta = sa;
+  tb = sb;
 }
 
 __global__ __launch_bounds__(kPlanThreads) void bin_plan(int32_t* __restrict__ hist, int chunks, int E,
                                                          int bm, int32_t* __restrict__ offsets,
                                                          int32_t* __restrict__ ntiles,
                                                          TileEntry* __restrict__ tiles) {
-  __shared__ int sh[kPlanThreads];
+  __shared__ int sh[2 * (kPlanThreads / 64)];
   int row_base = 0, tile_base = 0;
   for (int e0 = 0; e0 < E; e0 += kPlanThreads) {
     const int e = e0 + (int)threadIdx.x;
     int c = 0;
-    if (e < E)
+    if (e < E) {
+#pragma unroll 8
       for (int ch = 0; ch < chunks; ++ch) c += hist[(int64_t)ch * E + e];
+    }
     const int nt = (c + bm - 1) / bm;
-    int rows_total, tiles_total;
-    const int off = row_base + block_exclusive_scan(c, sh, rows_total);
-    const int toff = tile_base + block_exclusive_scan(nt, sh, tiles_total);
+    int rows_total, tiles_total, off, toff;
+    block_exclusive_scan2(c, nt, sh, off, toff, rows_total, tiles_total);
+    off += row_base;
+    toff += tile_base;
     if (e < E) {
       offsets[e] = off;
       int run = off;
+#pragma unroll 8
       for (int ch = 0; ch < chunks; ++ch) {
         const int64_t hi = (int64_t)ch * E + e;
         const int v = hist[hi];
@@ -613,14 +641,27 @@ __global__ __launch_bounds__(256) void combine_rows(const float* __restrict__ d,
   const int64_t tok = idx / q;
   const int c4 = (int)(idx - tok * q);
   float4 acc = make_float4(0.f, 0.f, 0.f, 0.f);
-  for (int s = 0; s < topk; ++s) {
-    const int64_t pr = tok * topk + s;
-    const float wt = w[pr];
-    const float4 v = reinterpret_cast<const float4*>(d + (int64_t)pos[pr] * hidden)[c4];
-    acc.x += wt * v.x;
-    acc.y += wt * v.y;
-    acc.z += wt * v.z;
-    acc.w += wt * v.w;
+  for (int s0 = 0; s0 < topk; s0 += kCombineBatch) {
+    // every load of the batch first, then the sums in slot order
+    float wt[kCombineBatch];
+    float4 v[kCombineBatch];
+#pragma unroll
+    for (int u = 0; u < kCombineBatch; ++u) {
+      if (s0 + u < topk) {
+        const int64_t pr = tok * topk + s0 + u;
+        wt[u] = w[pr];
+        v[u] = reinterpret_cast<const float4*>(d + (int64_t)pos[pr] * hidden)[c4];
+      }
+    }
+#pragma unroll
+    for (int u = 0; u < kCombineBatch; ++u) {
+      if (s0 + u < topk) {
+        acc.x += wt[u] * v[u].x;
+        acc.y += wt[u] * v[u].y;
+        acc.z += wt[u] * v[u].z;
+        acc.w += wt[u] * v[u].w;
+      }
+    }
   }
   reinterpret_cast<float4*>(y + tok * hidden)[c4] = acc;
 }
