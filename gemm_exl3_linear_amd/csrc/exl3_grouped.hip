@@ -566,10 +566,44 @@ __global__ __launch_bounds__(kBinThreads) void bin_scatter(const int32_t* __rest
 }
 
 // x'_slot[r] = (x[token(r)] .* suh[e(r)][slot]) H for both slots, one wave
-// per sorted row.  Lane l holds 8 elements of block 4 pass + l / 16 (the
-// fwht128_x8 layout); the x and sign loads of up to kGuPasses passes
-// (16 blocks, 2048 elements) are all issued before the first transform.
-constexpr int kGuPasses = 4;
+// per sorted row, 16 blocks of 128 elements per pass.  Lane l holds the 32
+// elements 32 i + 8 (l % 4) + e (i < 4, e < 8) of block l / 4: the strides 1,
+// 2, 4 (e) and 32, 64 (i) stay inside the lane and 8, 16 pair the lanes of a
+// quad (DPP moves).  The stages run in the order 1, 2, ..., 64 and each
+// butterfly is the same sum or difference as in fwht128_x8, so the result
+// has the same bits as that layout's.
+constexpr int kGuBlocks = 16;  // blocks per pass (four lanes each)
+
+__device__ __forceinline__ void fwht128_x32(float (&v)[32]) {
+#pragma unroll
+  for (int h = 1; h < 8; h <<= 1)
+#pragma unroll
+    for (int e = 0; e < 32; ++e)
+      if ((e & h) == 0) {
+        const float u = v[e], w = v[e + h];
+        v[e] = u + w;
+        v[e + h] = u - w;
+      }
+#pragma unroll
+  for (int mi = 0; mi < 2; ++mi) {
+    const int m = 1 << mi;
+    float pv[32];
+#pragma unroll
+    for (int e = 0; e < 32; ++e) pv[e] = mi == 0 ? xor_partner<1>(v[e]) : xor_partner<2>(v[e]);
+    const bool upper = (lane_id() & (uint32_t)m) != 0;
+#pragma unroll
+    for (int e = 0; e < 32; ++e) v[e] = bfly(v[e], pv[e], upper);
+  }
+#pragma unroll
+  for (int h = 8; h < 32; h <<= 1)
+#pragma unroll
+    for (int e = 0; e < 32; ++e)
+      if ((e & h) == 0) {
+        const float u = v[e], w = v[e + h];
+        v[e] = u + w;
+        v[e + h] = u - w;
+      }
+}
 
 __global__ __launch_bounds__(256) void gu_input_transform(
     const uint16_t* __restrict__ x, int topk, int64_t P, int hidden,
@@ -581,50 +615,53 @@ __global__ __launch_bounds__(256) void gu_input_transform(
   const int e = ids[pair];
   const int64_t tok = pair / topk;
   const int lane = (int)lane_id();
-  const int g = lane >> 4, j = lane & 15;
+  const int bq = lane >> 2, q = lane & 3;
   const int nblk = hidden >> 7;
   const uint16_t* xr = x + tok * hidden;
   const uint16_t* s0 = suh_gu + (int64_t)e * 2 * hidden;
   const uint16_t* s1 = s0 + hidden;
   uint16_t* d0 = xg + r * hidden;
   uint16_t* d1 = xg + (P + r) * hidden;
-  for (int b0 = 0; b0 < nblk; b0 += 4 * kGuPasses) {
-    uint4 xv[kGuPasses], sv0[kGuPasses], sv1[kGuPasses];
+  for (int b0 = 0; b0 < nblk; b0 += kGuBlocks) {
+    const int b = b0 + bq;
+    const int base = (b < nblk ? b : nblk - 1) * 128 + 8 * q;  // lanes past the last block repeat it (not stored)
+    uint4 xv[4], sv0[4], sv1[4];
 #pragma unroll
-    for (int q = 0; q < kGuPasses; ++q) {
-      const int b = b0 + 4 * q + g;
-      const int kk = (b < nblk ? b : nblk - 1) * 128 + 8 * j;
-      xv[q] = *reinterpret_cast<const uint4*>(xr + kk);
-      sv0[q] = *reinterpret_cast<const uint4*>(s0 + kk);
-      sv1[q] = *reinterpret_cast<const uint4*>(s1 + kk);
+    for (int i = 0; i < 4; ++i) {
+      xv[i] = *reinterpret_cast<const uint4*>(xr + base + 32 * i);
+      sv0[i] = *reinterpret_cast<const uint4*>(s0 + base + 32 * i);
+      sv1[i] = *reinterpret_cast<const uint4*>(s1 + base + 32 * i);
     }
+    float v0[32], v1[32];
 #pragma unroll
-    for (int q = 0; q < kGuPasses; ++q) {
-      const int b = b0 + 4 * q + g;
-      const int kk = b * 128 + 8 * j;
-      const uint32_t xw[4] = {xv[q].x, xv[q].y, xv[q].z, xv[q].w};
-      const uint32_t w0[4] = {sv0[q].x, sv0[q].y, sv0[q].z, sv0[q].w};
-      const uint32_t w1[4] = {sv1[q].x, sv1[q].y, sv1[q].z, sv1[q].w};
-      float v0[8], v1[8];
+    for (int i = 0; i < 4; ++i) {
+      const uint32_t xw[4] = {xv[i].x, xv[i].y, xv[i].z, xv[i].w};
+      const uint32_t w0[4] = {sv0[i].x, sv0[i].y, sv0[i].z, sv0[i].w};
+      const uint32_t w1[4] = {sv1[i].x, sv1[i].y, sv1[i].z, sv1[i].w};
 #pragma unroll
       for (int c = 0; c < 4; ++c) {
         const float xa = h2f((uint16_t)(xw[c] & 0xFFFF)), xb = h2f((uint16_t)(xw[c] >> 16));
-        v0[2 * c] = xa * h2f((uint16_t)(w0[c] & 0xFFFF));
-        v0[2 * c + 1] = xb * h2f((uint16_t)(w0[c] >> 16));
-        v1[2 * c] = xa * h2f((uint16_t)(w1[c] & 0xFFFF));
-        v1[2 * c + 1] = xb * h2f((uint16_t)(w1[c] >> 16));
+        v0[8 * i + 2 * c] = xa * h2f((uint16_t)(w0[c] & 0xFFFF));
+        v0[8 * i + 2 * c + 1] = xb * h2f((uint16_t)(w0[c] >> 16));
+        v1[8 * i + 2 * c] = xa * h2f((uint16_t)(w1[c] & 0xFFFF));
+        v1[8 * i + 2 * c + 1] = xb * h2f((uint16_t)(w1[c] >> 16));
       }
-      fwht128_x8(v0);
-      fwht128_x8(v1);
-      uint32_t o0[4], o1[4];
+    }
+    fwht128_x32(v0);
+    fwht128_x32(v1);
+    if (b < nblk) {
 #pragma unroll
-      for (int c = 0; c < 4; ++c) {
-        o0[c] = (uint32_t)f2h(v0[2 * c] * kInvSqrt128) | ((uint32_t)f2h(v0[2 * c + 1] * kInvSqrt128) << 16);
-        o1[c] = (uint32_t)f2h(v1[2 * c] * kInvSqrt128) | ((uint32_t)f2h(v1[2 * c + 1] * kInvSqrt128) << 16);
-      }
-      if (b < nblk) {
-        *reinterpret_cast<uint4*>(d0 + kk) = make_uint4(o0[0], o0[1], o0[2], o0[3]);
-        *reinterpret_cast<uint4*>(d1 + kk) = make_uint4(o1[0], o1[1], o1[2], o1[3]);
+      for (int i = 0; i < 4; ++i) {
+        uint32_t o0[4], o1[4];
+#pragma unroll
+        for (int c = 0; c < 4; ++c) {
+          o0[c] = (uint32_t)f2h(v0[8 * i + 2 * c] * kInvSqrt128) |
+                  ((uint32_t)f2h(v0[8 * i + 2 * c + 1] * kInvSqrt128) << 16);
+          o1[c] = (uint32_t)f2h(v1[8 * i + 2 * c] * kInvSqrt128) |
+                  ((uint32_t)f2h(v1[8 * i + 2 * c + 1] * kInvSqrt128) << 16);
+        }
+        *reinterpret_cast<uint4*>(d0 + base + 32 * i) = make_uint4(o0[0], o0[1], o0[2], o0[3]);
+        *reinterpret_cast<uint4*>(d1 + base + 32 * i) = make_uint4(o1[0], o1[1], o1[2], o1[3]);
       }
     }
   }
