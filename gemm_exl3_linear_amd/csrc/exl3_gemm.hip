@@ -81,7 +81,7 @@ static int64_t frag_rows(int64_t m) { return (m + 15) & ~(int64_t)15; }
 size_t gemm_workspace(int k, int /*n*/, int m) { return (size_t)frag_rows(m) * k * sizeof(uint16_t); }
 
 int64_t gemm_max_workgroups(int k, int n, int64_t m) {
-  const int64_t frag = (m + 15) / 16 * (k / 128);  // launch_input_frag
+  const int64_t frag = (m + 15) / 16 * (k / 128);  // launch_input_frag's grid at one block per workgroup (its largest)
   const int64_t bm = choose_bm(m > (1 << 30) ? (1 << 30) : (int)m);
   const int64_t gemm = (m + bm - 1) / bm * ((n + kGemmBN - 1) / kGemmBN);
   return frag > gemm ? frag : gemm;

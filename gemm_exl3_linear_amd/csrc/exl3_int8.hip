@@ -18,18 +18,20 @@ namespace exl3 {
 // ---------------------------------------------------------------------------
 // input transform with per-row int8 quantization
 // ---------------------------------------------------------------------------
-// Two launch shapes of one computation (the same per-element arithmetic and
+// Three launch shapes of one computation (the same per-element arithmetic and
 // the same maximum, so their outputs are identical):
 //   quant_groups_kernel (m >= kQuantGroupMinRows): one workgroup of 16 waves
 //     per 16-row group, wave w on row w of the group, so every 128-byte line
 //     of x_q (eight rows of one 16-k piece) is written by one CU into one L2;
+//   quant_groups_held_kernel: the same for rows of at most 4 kQuantHeldPasses
+//     blocks, holding the transformed row in registers;
 //   quant_rows_kernel (smaller m): one workgroup of four waves per row, four
 //     times the waves for batches too small to fill the GPU with groups.
 // A wave transforms four 128-element blocks at a time (lane l holds elements
 // 8 (l % 16) .. + 7 of block l / 16, the layout of fwht128_x8), with the
-// loads of the next four blocks in flight.  The row is transformed twice,
-// once for its maximum and once to quantize, instead of being held: k has no
-// upper bound here and the second pass reads the row from cache.
+// loads of the next four blocks in flight.  Except in the held kernel the row
+// is transformed twice, once for its maximum and once to quantize: k has no
+// upper bound there and the second pass reads the row from cache.
 // Measured on MI355X (k = 5120, n = 17408, K = 4, whole int8 linear): m = 4096
 // 0.498 ms by groups against 0.512 by rows; m = 1000 0.191 against 0.181.
 constexpr int kQuantGroupMinRows = 2048;
@@ -134,6 +136,63 @@ __global__ __launch_bounds__(kQuantGroupThreads) void quant_groups_kernel(
   quant_pass<true>(xr, suh, nb, 0, 4, a > 0.f ? 127.0f / a : 0.f, dst);
   if (lane == 0) scale[row] = a / 127.0f;
 }
+
+// quant_groups_kernel for rows of at most 4 NP blocks: the transformed row
+// stays in registers between the maximum and the codes (one transform instead
+// of two; the same per-element arithmetic, so the same codes and scale).
+template <int NP>
+__global__ __launch_bounds__(kQuantGroupThreads) void quant_groups_held_kernel(
+    const uint16_t* __restrict__ x, int64_t ldx, const uint16_t* __restrict__ suh, int k, int64_t m,
+    int8_t* __restrict__ xq, float* __restrict__ scale) {
+  const int wave = (int)(threadIdx.x >> 6), lane = (int)(threadIdx.x & 63);
+  const int64_t row = (int64_t)blockIdx.x * 16 + wave;
+  const int nb = k / 128;
+  const QuantDst dst(xq, row, k, lane);
+  if (row >= m) {  // padding row of the last 16-row group (uniform per wave)
+    quant_zero_row(nb, 0, 4, dst);
+    if (lane == 0) scale[row] = 0.f;
+    return;
+  }
+  const uint16_t* xr = x + row * ldx;
+  const int jj = lane & 15;
+  float v[NP][8];
+  float amax = 0.f;
+  uint4 xv, sv;
+  quant_load4(xr, suh, nb, lane >> 4, jj, xv, sv);
+#pragma unroll
+  for (int p = 0; p < NP; ++p) {
+    if (4 * p < nb) {  // uniform
+      uint4 xn, sn;
+      quant_load4(xr, suh, nb, 4 * p + 4 + (lane >> 4), jj, xn, sn);
+      quant_transform4(xv, sv, v[p]);
+      if (4 * p + (lane >> 4) < nb) {
+#pragma unroll
+        for (int e = 0; e < 8; ++e) amax = fmaxf(amax, fabsf(v[p][e]));
+      }
+      xv = xn;
+      sv = sn;
+    }
+  }
+#pragma unroll
+  for (int msk = 32; msk >= 1; msk >>= 1) amax = fmaxf(amax, shfl_xor_f(amax, msk));
+  const float a = amax;
+  const float inv = a > 0.f ? 127.0f / a : 0.f;
+#pragma unroll
+  for (int p = 0; p < NP; ++p) {
+    const int b = 4 * p + (lane >> 4);
+    if (4 * p < nb && b < nb) {
+      uint32_t w[2] = {0u, 0u};
+#pragma unroll
+      for (int e = 0; e < 8; ++e) {
+        const float qf = fminf(fmaxf(rintf(v[p][e] * inv), -127.f), 127.f);
+        w[e >> 2] |= ((uint32_t)(int32_t)qf & 0xFFu) << (8 * (e & 3));
+      }
+      *reinterpret_cast<uint2*>(dst.at(b)) = make_uint2(w[0], w[1]);
+    }
+  }
+  if (lane == 0) scale[row] = a / 127.0f;
+}
+constexpr int kQuantHeldPasses = 10;  // rows of up to 40 blocks (k <= 5120) held in registers
 
 __global__ __launch_bounds__(kQuantRowThreads) void quant_rows_kernel(
     const uint16_t* __restrict__ x, int64_t ldx, const uint16_t* __restrict__ suh, int k, int64_t m,
@@ -258,7 +317,10 @@ hipError_t launch_linear_int8(const uint16_t* trellis, const uint16_t* suh, cons
   unsigned char* base = static_cast<unsigned char*>(ws);
   int8_t* xq = reinterpret_cast<int8_t*>(base);
   float* sc = reinterpret_cast<float*>(base + i8_scale_offset(k, m));
-  if (m >= kQuantGroupMinRows)
+  if (m >= kQuantGroupMinRows && k <= 4 * 128 * kQuantHeldPasses)
+    hipLaunchKernelGGL(quant_groups_held_kernel<kQuantHeldPasses>, dim3((unsigned)(i8_rows(m) / 16)),
+                       dim3(kQuantGroupThreads), 0, s, x, ldx, suh, k, m, xq, sc);
+  else if (m >= kQuantGroupMinRows)
     hipLaunchKernelGGL(quant_groups_kernel, dim3((unsigned)(i8_rows(m) / 16)), dim3(kQuantGroupThreads), 0, s,
                        x, ldx, suh, k, m, xq, sc);
   else
