@@ -56,6 +56,17 @@ def test_random_routing_large_tiles(t):
     assert err < TOL, err
 
 
+# hidden widths past one pass of the gate/up input transform (16 blocks of
+# 128): 2176 takes a second pass with a single block, 4096 two full passes;
+# both paths (t = 8: unit path, t = 200: binned)
+@pytest.mark.parametrize("hidden", [2176, 4096])
+@pytest.mark.parametrize("t", [8, 200])
+def test_wide_hidden(t, hidden):
+    m = _small(t, hidden=hidden, seed=52)
+    err = O.rel_frobenius(_run(m), _ref(m))
+    assert err < TOL, err
+
+
 @pytest.mark.parametrize("t", [3, 40, 200, 700])
 def test_all_tokens_same_experts(t):
     m = _small(t)
