@@ -12,7 +12,7 @@ the same stream), timed per call with HIP events on the launch stream.  The
 float64 oracle is timed on the host on the same workload as the CPU baseline.
 
 python bench.py [--gpus 1] [--steps K] [--warmup W] [--no-cpu-baseline]
-                [--no-secondary] [--profile-pass [gemv|prefill|prefill_int8|moe4096]]
+                [--no-secondary] [--profile-pass [gemv|prefill|prefill_int8|moe4096|moe1|mixed1]]
 
 --profile-pass runs a short fixed sequence for counter collection instead of
 the benchmark: a plain 256 MiB device copy (the scale of the HBM byte
@@ -341,10 +341,11 @@ def main():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-secondary", action="store_true")
     ap.add_argument("--profile-pass", nargs="?", const="gemv", default=None,
-                    choices=["gemv", "prefill", "prefill_int8", "moe4096"],
+                    choices=["gemv", "prefill", "prefill_int8", "moe4096", "moe1", "mixed1"],
                     help="short run for counter collection: a plain copy of known size, then a few calls of "
                          "one leg (gemv: 50 M=1 calls; prefill / prefill_int8: 10 M=4096 calls; moe4096: 5 "
-                         "routed-expert calls at T=4096)")
+                         "routed-expert calls at T=4096; moe1: 64 at T=1, routing rotated over all experts; "
+                         "mixed1: the mixed-width layer's seven M=1 projections, 10 times in layer order)")
     args = ap.parse_args()
     world = int(os.environ.get("WORLD_SIZE", "1"))
     if args.gpus != 1 or world != 1:
@@ -407,6 +408,35 @@ def main():
             calls = 10
             for _ in range(calls):
                 fn()
+        elif kind == "moe1":
+            # one token, routing rotated over the disjoint id sets that cover
+            # all 256 experts (each call reads its experts from HBM)
+            mo = synth.moe_inputs(synth.SEED_MOE_256x2048x512, 1)
+            gu = X.Exl3Arena.from_numpy(mo["gate_up"], dev)
+            dn = X.Exl3Arena.from_numpy(mo["down"], dev)
+            xm = torch.from_numpy(mo["x"]).to(dev)
+            ids_list = moe_id_sets(mo["ids"], 256, torch, dev)
+            wt = torch.from_numpy(mo["weights"]).to(dev)
+            wsm = torch.zeros(X.exl3_grouped_experts_workspace_size(gu, dn, 1, 8), dtype=torch.uint8, device=dev)
+            ym = torch.empty((1, 2048), dtype=torch.float32, device=dev)
+            calls = 2 * len(ids_list)
+            for i in range(calls):
+                X.exl3_grouped_experts(xm, ids_list[i % len(ids_list)], wt, gu, dn, out=ym, workspace=wsm,
+                                       stream=stream)
+        elif kind == "mixed1":
+            # the mixed-width layer at M=1: the seven projections in layer order
+            d1 = synth.mixed_layer_inputs(synth.SEED_MIXED_LAYER, 1)
+            names = [nm for nm, _, _ in synth.MIXED_LAYER_SHAPES]
+            wl = {nm: X.Exl3Weight.from_numpy(d1[nm]["trellis"], d1[nm]["suh"], d1[nm]["svh"], d1[nm]["bits"],
+                                              device=dev) for nm in names}
+            xl = {nm: torch.from_numpy(d1[nm]["x"]).to(dev) for nm in names}
+            yl = {nm: torch.empty((1, d1[nm]["n"]), dtype=torch.float16, device=dev) for nm in names}
+            wsl = torch.zeros(max(X.exl3_linear_workspace_size(wl[nm], 1) for nm in names), dtype=torch.uint8,
+                              device=dev)
+            calls = 10
+            for _ in range(calls):
+                for nm in names:
+                    X.exl3_linear(xl[nm], wl[nm], out=yl[nm], workspace=wsl, stream=stream)
         else:
             mo = synth.moe_inputs(synth.SEED_MOE_256x2048x512, 4096)
             gu = X.Exl3Arena.from_numpy(mo["gate_up"], dev)
