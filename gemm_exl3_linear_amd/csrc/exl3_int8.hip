@@ -3,7 +3,7 @@
 // Hadamard, weights one static scale inside the decode, the product runs in
 // int8 with both scales applied and writes fp16).
 //
-//   quant_groups_kernel / quant_rows_kernel
+//   quant_groups_held_kernel / quant_pairs_kernel / quant_rows_kernel
 //                      x' = (x .* suh) H_k in fp32 per row, a = max |x'|,
 //                      x_q = RNE(127 x' / a) (int8, fragment-major) and a / 127.
 //   gemm_i8_kernel     decode to int8 + v_mfma_i32_16x16x64_i8, epilogue with
@@ -18,20 +18,22 @@ namespace exl3 {
 // ---------------------------------------------------------------------------
 // input transform with per-row int8 quantization
 // ---------------------------------------------------------------------------
-// Three launch shapes of one computation (the same per-element arithmetic and
-// the same maximum, so their outputs are identical):
-//   quant_groups_kernel (m >= kQuantGroupMinRows): one workgroup of 16 waves
-//     per 16-row group, wave w on row w of the group, so every 128-byte line
-//     of x_q (eight rows of one 16-k piece) is written by one CU into one L2;
-//   quant_groups_held_kernel: the same for rows of at most 4 kQuantHeldPasses
-//     blocks, holding the transformed row in registers;
+// Launch shapes of one computation (the same per-element arithmetic and the
+// same maximum, so their outputs are identical):
+//   quant_groups_held_kernel (m >= kQuantGroupMinRows, rows of at most
+//     4 kQuantHeldPasses blocks): one workgroup of 16 waves per 16-row group,
+//     wave w on row w of the group, so every 128-byte line of x_q (eight rows
+//     of one 16-k piece) is written by one CU into one L2; the transformed
+//     row stays in registers between its maximum and its codes;
+//   quant_pairs_kernel (m >= kQuantGroupMinRows, longer rows): two waves per
+//     row, eight rows per workgroup, each wave holding part of its half;
 //   quant_rows_kernel (smaller m): one workgroup of four waves per row, four
 //     times the waves for batches too small to fill the GPU with groups.
 // A wave transforms four 128-element blocks at a time (lane l holds elements
-// 8 (l % 16) .. + 7 of block l / 16, the layout of fwht128_x8), with the
-// loads of the next four blocks in flight.  Except in the held kernel the row
-// is transformed twice, once for its maximum and once to quantize: k has no
-// upper bound there and the second pass reads the row from cache.
+// 8 (l % 16) .. + 7 of block l / 16, the layout of fwht128_x8).  Where a row
+// is not held it is transformed twice, once for its maximum and once to
+// quantize: k has no upper bound and the second pass reads the row from
+// cache.
 // Measured on MI355X (k = 5120, n = 17408, K = 4, whole int8 linear): m = 4096
 // 0.498 ms by groups against 0.512 by rows; m = 1000 0.191 against 0.181.
 constexpr int kQuantGroupMinRows = 2048;
@@ -114,32 +116,11 @@ __device__ __forceinline__ void quant_zero_row(int nb, int first, int stride, co
   }
 }
 
-// Rows m .. m_pad - 1 (up to the next multiple of 16) are written as zeros
-// with scale 0, so every 16-row group of x_q is complete.
-__global__ __launch_bounds__(kQuantGroupThreads) void quant_groups_kernel(
-    const uint16_t* __restrict__ x, int64_t ldx, const uint16_t* __restrict__ suh, int k, int64_t m,
-    int8_t* __restrict__ xq, float* __restrict__ scale) {
-  const int wave = (int)(threadIdx.x >> 6), lane = (int)(threadIdx.x & 63);
-  const int64_t row = (int64_t)blockIdx.x * 16 + wave;
-  const int nb = k / 128;
-  const QuantDst dst(xq, row, k, lane);
-  if (row >= m) {  // padding row of the last 16-row group (uniform per wave)
-    quant_zero_row(nb, 0, 4, dst);
-    if (lane == 0) scale[row] = 0.f;
-    return;
-  }
-  const uint16_t* xr = x + row * ldx;
-  float amax = quant_pass<false>(xr, suh, nb, 0, 4, 0.f, dst);
-#pragma unroll
-  for (int msk = 32; msk >= 1; msk >>= 1) amax = fmaxf(amax, shfl_xor_f(amax, msk));
-  const float a = amax;
-  quant_pass<true>(xr, suh, nb, 0, 4, a > 0.f ? 127.0f / a : 0.f, dst);
-  if (lane == 0) scale[row] = a / 127.0f;
-}
+// In every shape, rows m .. m_pad - 1 (up to the next multiple of 16) are
+// written as zeros with scale 0, so every 16-row group of x_q is complete.
 
-// quant_groups_kernel for rows of at most 4 NP blocks: the transformed row
-// stays in registers between the maximum and the codes (one transform instead
-// of two; the same per-element arithmetic, so the same codes and scale).
+// Rows of at most 4 NP blocks, one wave per row of a 16-row group: the
+// transformed row stays in registers between the maximum and the codes.
 template <int NP>
 __global__ __launch_bounds__(kQuantGroupThreads) void quant_groups_held_kernel(
     const uint16_t* __restrict__ x, int64_t ldx, const uint16_t* __restrict__ suh, int k, int64_t m,
@@ -193,6 +174,87 @@ __global__ __launch_bounds__(kQuantGroupThreads) void quant_groups_held_kernel(
   if (lane == 0) scale[row] = a / 127.0f;
 }
 constexpr int kQuantHeldPasses = 10;  // rows of up to 40 blocks (k <= 5120) held in registers
+
+// Longer rows: two waves per row (wave h of a row takes the passes h, h + 2,
+// ...), eight rows per workgroup (a 128-byte line of x_q still comes from one
+// workgroup), each wave holding its first HP passes in registers and
+// transforming only the rest twice; the pair's maxima meet in LDS.
+template <int HP>
+__global__ __launch_bounds__(kQuantGroupThreads) void quant_pairs_kernel(
+    const uint16_t* __restrict__ x, int64_t ldx, const uint16_t* __restrict__ suh, int k, int64_t m,
+    int8_t* __restrict__ xq, float* __restrict__ scale) {
+  __shared__ float wmax[kQuantGroupThreads / 64];
+  const int wave = (int)(threadIdx.x >> 6), lane = (int)(threadIdx.x & 63);
+  const int64_t row = (int64_t)blockIdx.x * 8 + (wave >> 1);
+  const int h = wave & 1;
+  const int nb = k / 128;
+  const int np = (nb + 3) >> 2;  // four-block passes of the row
+  const int jj = lane & 15;
+  const QuantDst dst(xq, row, k, lane);
+  const bool pad = row >= m;  // padding row of the last 16-row group (uniform per wave)
+  const uint16_t* xr = x + (pad ? 0 : row) * ldx;
+  float v[HP][8];
+  float amax = 0.f;
+  if (!pad) {
+#pragma unroll
+    for (int i = 0; i < HP; ++i) {
+      const int p = h + 2 * i;
+      if (p < np) {  // uniform
+        uint4 xv, sv;
+        quant_load4(xr, suh, nb, 4 * p + (lane >> 4), jj, xv, sv);
+        quant_transform4(xv, sv, v[i]);
+        if (4 * p + (lane >> 4) < nb) {
+#pragma unroll
+          for (int e = 0; e < 8; ++e) amax = fmaxf(amax, fabsf(v[i][e]));
+        }
+      }
+    }
+    for (int p = h + 2 * HP; p < np; p += 2) {
+      uint4 xv, sv;
+      quant_load4(xr, suh, nb, 4 * p + (lane >> 4), jj, xv, sv);
+      float t[8];
+      quant_transform4(xv, sv, t);
+      if (4 * p + (lane >> 4) < nb) {
+#pragma unroll
+        for (int e = 0; e < 8; ++e) amax = fmaxf(amax, fabsf(t[e]));
+      }
+    }
+  }
+#pragma unroll
+  for (int msk = 32; msk >= 1; msk >>= 1) amax = fmaxf(amax, shfl_xor_f(amax, msk));
+  if (lane == 0) wmax[wave] = amax;
+  __syncthreads();
+  const float a = fmaxf(wmax[wave & ~1], wmax[wave | 1]);
+  if (pad) {
+    quant_zero_row(nb, 4 * h, 8, dst);
+    if (lane == 0 && h == 0) scale[row] = 0.f;
+    return;
+  }
+  const float inv = a > 0.f ? 127.0f / a : 0.f;
+  auto store = [&](const float (&t)[8], int b) {
+    uint32_t w[2] = {0u, 0u};
+#pragma unroll
+    for (int e = 0; e < 8; ++e) {
+      const float qf = fminf(fmaxf(rintf(t[e] * inv), -127.f), 127.f);
+      w[e >> 2] |= ((uint32_t)(int32_t)qf & 0xFFu) << (8 * (e & 3));
+    }
+    if (b < nb) *reinterpret_cast<uint2*>(dst.at(b)) = make_uint2(w[0], w[1]);
+  };
+#pragma unroll
+  for (int i = 0; i < HP; ++i) {
+    const int p = h + 2 * i;
+    if (p < np) store(v[i], 4 * p + (lane >> 4));
+  }
+  for (int p = h + 2 * HP; p < np; p += 2) {
+    uint4 xv, sv;
+    quant_load4(xr, suh, nb, 4 * p + (lane >> 4), jj, xv, sv);
+    float t[8];
+    quant_transform4(xv, sv, t);
+    store(t, 4 * p + (lane >> 4));
+  }
+  if (lane == 0 && h == 0) scale[row] = a / 127.0f;
+}
+constexpr int kQuantPairHeld = 10;  // passes each wave of a pair holds
 
 __global__ __launch_bounds__(kQuantRowThreads) void quant_rows_kernel(
     const uint16_t* __restrict__ x, int64_t ldx, const uint16_t* __restrict__ suh, int k, int64_t m,
@@ -303,8 +365,8 @@ size_t linear_int8_workspace(int k, int64_t m) {
 }
 
 int64_t linear_int8_max_workgroups(int k, int n, int64_t m) {
-  (void)k;
-  const int64_t quant = m >= kQuantGroupMinRows ? i8_rows(m) / 16 : i8_rows(m);
+  const int64_t quant = m < kQuantGroupMinRows ? i8_rows(m)
+                        : (k <= 4 * 128 * kQuantHeldPasses ? i8_rows(m) / 16 : i8_rows(m) / 8);
   const int64_t bm = choose_bm_i8(m);
   const int64_t gemm = (m + bm - 1) / bm * (n / kGemmBN);
   return quant > gemm ? quant : gemm;
@@ -321,8 +383,8 @@ hipError_t launch_linear_int8(const uint16_t* trellis, const uint16_t* suh, cons
     hipLaunchKernelGGL(quant_groups_held_kernel<kQuantHeldPasses>, dim3((unsigned)(i8_rows(m) / 16)),
                        dim3(kQuantGroupThreads), 0, s, x, ldx, suh, k, m, xq, sc);
   else if (m >= kQuantGroupMinRows)
-    hipLaunchKernelGGL(quant_groups_kernel, dim3((unsigned)(i8_rows(m) / 16)), dim3(kQuantGroupThreads), 0, s,
-                       x, ldx, suh, k, m, xq, sc);
+    hipLaunchKernelGGL(quant_pairs_kernel<kQuantPairHeld>, dim3((unsigned)(i8_rows(m) / 8)),
+                       dim3(kQuantGroupThreads), 0, s, x, ldx, suh, k, m, xq, sc);
   else
     hipLaunchKernelGGL(quant_rows_kernel, dim3((unsigned)i8_rows(m)), dim3(kQuantRowThreads), 0, s, x, ldx,
                        suh, k, m, xq, sc);

@@ -83,13 +83,13 @@ def test_linear_int8_rows_independent_bit_exact():
 
 @pytest.mark.parametrize("k", [512, 5120, 5248])
 def test_linear_int8_quant_shapes_agree(k):
-    # from 2048 rows on the activations are quantized one 16-row group per
-    # workgroup (rows of up to 40 blocks held in registers, longer ones
-    # transformed twice), below one row per workgroup; all do the same
-    # arithmetic, so the rows of a short batch equal those of a long one bit
-    # for bit, and the long batch (2050 rows: its last group is two rows)
-    # matches the oracle.  k = 5120 fills the held rows exactly, 5248 is the
-    # first width past them.
+    # from 2048 rows on the activations are quantized by 16-row groups (rows
+    # of up to 40 blocks held in registers, one wave per row; longer rows two
+    # waves each, eight rows per workgroup), below that one row per
+    # workgroup; all do the same arithmetic, so the rows of a short batch
+    # equal those of a long one bit for bit, and the long batch (2050 rows:
+    # its last group is two rows) matches the oracle.  k = 5120 fills the
+    # held rows exactly, 5248 is the first width past them.
     d = G.linear_case(826 + k // 128, 2050, k, 256, 3)
     full = _run8(d)
     np.testing.assert_array_equal(G.f16_bits(_run8(d, m=1000)), G.f16_bits(full)[:1000])
