@@ -176,13 +176,14 @@ def test_row_invariance_gemm():
 def test_input_transform_wide_grid_rows_agree():
     # from 8192 (16-row group, 128-column block) tasks on, the prefill input
     # transform gives each workgroup four blocks of its group; k = 640 has
-    # five blocks, so every group's second workgroup holds one.  Rows
-    # computed that way equal the rows of a short batch (one block per
-    # workgroup) bit for bit, and sampled rows match the oracle.
-    d = synth.linear_inputs(703, 26240, 640, 128, 3)
+    # five blocks, so every group's second workgroup holds one, and the last
+    # group holds three rows (26243 = 16 x 1640 + 3).  Rows computed that way
+    # equal the rows of a short batch (one block per workgroup) bit for bit,
+    # and sampled rows match the oracle.
+    d = synth.linear_inputs(703, 26243, 640, 128, 3)
     y = G.f16_bits(_run(d))
     np.testing.assert_array_equal(G.f16_bits(_run(d, m=2000)), y[:2000])
-    rows = np.r_[0:4, 13107:13111, 26236:26240]
+    rows = np.r_[0:4, 13107:13111, 26236:26243]
     d2 = dict(d); d2["x"] = d["x"][rows]
     got = y[rows].view(np.float16).astype(np.float64)
     assert O.rel_frobenius(got, _ref(d2)) < TOL
