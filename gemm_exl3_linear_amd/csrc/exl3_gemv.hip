@@ -108,7 +108,9 @@ static void sk_split_extent(const SkSplit& s, int64_t KT, int64_t NB, int64_t W,
 
 // Plan of the dense decode GEMV (exl3_gemv_mf.hpp): W workgroups
 // (kMfWorkgroups = two per CU of the 256-CU MI355X, all resident at once;
-// more when runs would exceed kMfMaxRunWG units, fewer for small tensors),
+// one per CU for tensors of at most kMfRoundWorkgroups x kMfSmallRun units,
+// which then have half the partial slots and no CU shared by two workgroups;
+// more when runs would exceed kMfMaxRunWG units, fewer for tiny tensors),
 // their runs over the units (k tile x 256-column pair) in two tiers (the
 // kMfRoundWorkgroups dispatched first take runs kMfTierWeight1 /
 // kMfTierWeight2 longer), the number of partial slots a pair can receive,
@@ -119,7 +121,7 @@ static void sk_split_extent(const SkSplit& s, int64_t KT, int64_t NB, int64_t W,
 static GemvPlan plan_gemv_new(int k, int n, int m) {
   GemvPlan p;
   const int64_t KT = k / 16, NB = n / 128, NP = (NB + 1) / 2, R = KT * NP;
-  int64_t W = kMfWorkgroups;
+  int64_t W = R <= (int64_t)kMfRoundWorkgroups * kMfSmallRun ? kMfRoundWorkgroups : kMfWorkgroups;
   if (W < (R + kMfMaxRunWG - 1) / kMfMaxRunWG) W = (R + kMfMaxRunWG - 1) / kMfMaxRunWG;
   if (W > R) W = R;  // runs of at least one unit
   p.split = make_sk_split(R, W, W > kMfRoundWorkgroups ? kMfRoundWorkgroups : W, kMfMaxRunWG, kMfTierWeight1,

@@ -50,6 +50,9 @@ namespace exl3 {
 
 constexpr int kMfWorkgroups = 512;  // two workgroups of four waves per CU of the 256-CU MI355X
 constexpr int kMfRoundWorkgroups = 256;  // the first dispatch round: one per CU
+// Tensors of at most kMfRoundWorkgroups x kMfSmallRun units take one
+// workgroup per CU (kMfRoundWorkgroups, one tier) instead of kMfWorkgroups.
+constexpr int kMfSmallRun = 50;
 // Relative run lengths of the first-round workgroups (the older of the two on
 // a CU, which wins the instruction arbiter) and the others.
 constexpr int kMfTierWeight1 = 13;
