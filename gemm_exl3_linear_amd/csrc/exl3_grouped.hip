@@ -12,7 +12,7 @@
 // Two regimes, chosen on the host from the number of (token, slot) pairs
 // P = t * topk (no device data is read back):
 //
-// Small P (P <= 384: decode, token-parallel verify, short prompts): every pair is an independent M=1
+// Small P (P <= 224: decode, token-parallel verify, short prompts): every pair is an independent M=1
 // unit (the README's "per-unit x stride" idea).
 //   1. gemv_kernel over units (pair, gate|up); the last workgroup to arrive on
 //      a (pair, 128 columns) group sums the k slices of gate and up, applies
@@ -41,10 +41,11 @@
 namespace exl3 {
 
 // P at or below this uses the unit path: measured on MI355X for 256 experts x
-// (2048 -> 2 x 512 -> 2048), K=3, top-8, the unit path is faster up to T = 32
-// (P = 256: 129 us against 155 us for the binned path), even at T = 48 (181
-// against 180 us) and slower from T = 64 (236 against 190 us).
-constexpr int kGroupedUnitMaxPairs = 384;
+// (2048 -> 2 x 512 -> 2048), K=3, top-8, random routing, the unit path is
+// faster up to T = 24 (P = 192: 119-122 us against 132 us for the binned
+// path), about even at T = 28 and slower from T = 29 (144-149 against
+// 138 us) on (T = 32: 153-157 against 143 us; T = 48: 230 against 179 us).
+constexpr int kGroupedUnitMaxPairs = 224;
 // Rows per tile of the grouped GEMM: 256 when the experts average at least
 // 96 rows (one tile per expert instead of two, so each expert's weights are
 // decoded once per column block), else 128.  A wave runs MFMAs only for its

@@ -290,7 +290,7 @@ size_t exl3_grouped_experts_workspace_size(const exl3_expert_weights* gate_up,
  * if there is any.  With EXL3_CHECK_IDS set, a call on a stream that is
  * being captured returns EXL3_E_INVALID without enqueueing anything (the
  * capture stays valid).  The same holds for exl3_grouped_experts_mixed.
- * Small calls (t * topk <= 384) hand partial sums between workgroups planned
+ * Small calls (t * topk <= 224) hand partial sums between workgroups planned
  * on one XCD (the XCD each group was finished on in the previous call, kept
  * in the workspace's counters); a workgroup that finds itself on another XCD
  * takes a device-scope release/acquire hand-off instead, so results never

@@ -37,9 +37,9 @@ def _small(t, experts=16, topk=4, hidden=256, inter=128, bits=3, seed=40):
     return synth.moe_inputs(seed + t, t, experts=experts, topk=topk, hidden=hidden, inter=inter, bits=bits)
 
 
-# The unit path serves t * topk <= 384 (token, slot) pairs, the binned grouped
+# The unit path serves t * topk <= 224 (token, slot) pairs, the binned grouped
 # GEMM path larger calls; sizes on both sides of the threshold (topk = 4 here).
-@pytest.mark.parametrize("t", [1, 2, 4, 16, 64, 96, 97, 128, 300])
+@pytest.mark.parametrize("t", [1, 2, 4, 16, 56, 57, 64, 96, 128, 300])
 def test_random_routing(t):
     m = _small(t)
     err = O.rel_frobenius(_run(m), _ref(m))
@@ -144,7 +144,7 @@ def test_moe_256x2048x512_k3_t4096_sampled_tokens():
 # through its L2; any workgroup found elsewhere takes a device-scope
 # release/acquire hand-off.  Forcing that hand-off everywhere must give the
 # same bits (and it is the path another dispatch order would take).
-@pytest.mark.parametrize("t", [1, 4, 48])
+@pytest.mark.parametrize("t", [1, 4, 28])  # 28 x 8 = 224: the largest unit-path call
 def test_forced_device_scope_hand_off_same_bits(t, monkeypatch):
     import gemm_exl3_linear_amd as X
     m = synth.moe_inputs(synth.SEED_MOE_256x2048x512, t)
@@ -161,18 +161,18 @@ def test_forced_device_scope_hand_off_same_bits(t, monkeypatch):
 
 # The XCD a group's workgroups are expected on is learned from the previous
 # call: its finisher stores 1 + its XCD in bits 28..31 of the group's arrival
-# counter (count fields zero).  The counter region starts the workspace: 384
-# pairs x (intermediate / 128) gate/up groups, then 384 x (hidden / 128) down
+# counter (count fields zero).  The counter region starts the workspace: 224
+# pairs x (intermediate / 128) gate/up groups, then 224 x (hidden / 128) down
 # groups, one uint32 each.  Records that name the wrong XCD (planted here from
 # the host), or work run on a second stream (which has been seen to rotate the
 # dispatch of later launches by one XCD), change which hand-off the groups
 # take, never the bits; after every call the count fields are zero again.
 def _counter_words(ws, m):
-    n = 384 * (m["gate_up"]["n"] // 128 + m["down"]["n"] // 128)
+    n = 224 * (m["gate_up"]["n"] // 128 + m["down"]["n"] // 128)
     return ws[:4 * n].view(dtype=__import__("torch").int32)
 
 
-@pytest.mark.parametrize("t", [1, 4, 48])
+@pytest.mark.parametrize("t", [1, 4, 28])
 def test_xcd_records_only_change_the_hand_off(t):
     import torch
     import gemm_exl3_linear_amd as X
