@@ -219,7 +219,8 @@ hipError_t launch_gemv(const uint16_t* trellis, const uint16_t* suh, const uint1
 // ---------------------------------------------------------------------------
 // several tensors sharing one activation row (m == 1), one launch pair
 // ---------------------------------------------------------------------------
-// Waves per tensor: kGemvSkWaves in proportion to the tensors' trellis bytes,
+// Waves per tensor: kGemvSkWaves (kGemvRoundWaves, one per SIMD, for calls
+// of at most 16384 units) in proportion to the tensors' trellis bytes,
 // each at least ceil(R_i / kSkMaxRun) and at most R_i, rounded up to a
 // multiple of 4; each tensor's waves split their runs in two tiers by the
 // launch's first round.  Partials of tensor i follow those of i - 1.
@@ -231,10 +232,13 @@ static MultiPlan plan_gemv_multi_new(const MultiTensor* t, int count, int k) {
   double total = 0;
   for (int i = 0; i < count; ++i) total += (double)t[i].n * t[i].bits;
   const int64_t KT = k / 16;
+  int64_t units = 0;
+  for (int i = 0; i < count; ++i) units += KT * (t[i].n / 128);
+  const int waves_total = units <= 16384 ? kGemvRoundWaves : kGemvSkWaves;
   int64_t wsum = 0, tasks = 0;
   for (int i = 0; i < count; ++i) {
     const int64_t NB = t[i].n / 128, R = KT * NB;
-    int64_t W = (int64_t)((double)kGemvSkWaves * t[i].n * t[i].bits / total + 0.5);
+    int64_t W = (int64_t)((double)waves_total * t[i].n * t[i].bits / total + 0.5);
     if (W < (R + kSkMaxRun - 1) / kSkMaxRun) W = (R + kSkMaxRun - 1) / kSkMaxRun;
     W = (W + 3) / 4 * 4;
     if (W > R) W = (R + 3) / 4 * 4;
