@@ -334,7 +334,18 @@ struct DenseGemmI8Res {
 // still faster than the 128-row tile.  (An eight-wave 512-row tile, which
 // halves the decode per MFMA, measured 1-18 % slower than this once the
 // activations were fragment-major.)
-static int choose_bm_i8(int64_t m) { return m > 128 ? 256 : (m > 64 ? 128 : 64); }
+// Tile height by the rule of the fp16 GEMM (256 rows unless the grid would
+// have fewer than kGemmI8MinGrid workgroups).  Measured on MI355X (K=4):
+// 5120x5120 at m = 200 / 500 took 49 / 57 us against 68 / 73 with the
+// m-only choice, 17408x5120 at m = 200 148 against 203 us, 5120x17408 at
+// m = 300 84 against 106 us.
+constexpr int64_t kGemmI8MinGrid = 128;
+static int choose_bm_i8(int64_t m, int64_t nbt) {
+  if (m <= 64) return 64;
+  const int64_t t256 = (m + 255) / 256, t128 = (m + 127) / 128;
+  if (t256 * nbt >= kGemmI8MinGrid) return (t256 <= 2 && t128 * 128 < t256 * 256) ? 128 : 256;
+  return t128 * nbt >= kGemmI8MinGrid ? 128 : 64;
+}
 
 template <int K>
 struct DenseGemmI8Run {
@@ -367,7 +378,7 @@ size_t linear_int8_workspace(int k, int64_t m) {
 int64_t linear_int8_max_workgroups(int k, int n, int64_t m) {
   const int64_t quant = m < kQuantGroupMinRows ? i8_rows(m)
                         : (k <= 4 * 128 * kQuantHeldPasses ? i8_rows(m) / 16 : i8_rows(m) / 8);
-  const int64_t bm = choose_bm_i8(m);
+  const int64_t bm = choose_bm_i8(m, n / kGemmBN);
   const int64_t gemm = (m + bm - 1) / bm * (n / kGemmBN);
   return quant > gemm ? quant : gemm;
 }
@@ -390,7 +401,7 @@ hipError_t launch_linear_int8(const uint16_t* trellis, const uint16_t* suh, cons
                        suh, k, m, xq, sc);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
-  const int bm = choose_bm_i8(m);
+  const int bm = choose_bm_i8(m, n / kGemmBN);
   DenseGemmI8Res r{xq, sc, (int64_t)16 * k, (int)m, bm, (int)((m + bm - 1) / bm), n / kGemmBN, trellis,
                    svh, bias, y, ldy, y_f32};
   return dispatch_bits<DenseGemmI8Run>(bits, r, k, n, s);
