@@ -73,16 +73,19 @@ constexpr int kGemmThreads = 256;   // four waves, each BM/4 rows x 128 columns
 constexpr int kGemmFragBytes = 1024;
 
 // Decoded-weight stage: 128 columns x 32 k (fp16) as 512 chunks of 16 bytes
-// (four k-pairs of one column each).  Each group of four columns G = col / 4
-// owns 16 consecutive chunks (256 bytes, one pass over 64 LDS banks); inside
-// it, chunk gc of column cl = col % 4 sits at 4 (cl ^ (G / 4 % 4)) +
-// (gc ^ (G % 4)).  The MFMA fragment reads (16 lanes: sixteen consecutive
-// columns, one chunk each) and the decoder's 4-byte writes (64 lanes: eight
-// k-pairs of two k tiles and four n tiles, one column each) then each touch
-// distinct banks.
+// (four k-pairs of one column each).  Chunk gc of the 16 columns q = col / 16
+// fill the 16 consecutive chunks 16 (4 q + gc) .. + 15 (256 bytes, one pass
+// over 64 LDS banks), column col % 16 at position (col % 16) ^ (gc + 4 (q % 4)).
+// The MFMA fragment reads (sixteen consecutive columns of one gc) then cover
+// all 16 positions, and each half of them (eight columns) the eight positions
+// of one 128-byte line of 32 banks, so a 16-byte read is conflict free in
+// passes of 16 lanes over 64 banks and of 8 lanes over 32; the decoder's
+// 4-byte writes (64 lanes: the four gc of four column groups q, one column)
+// touch 16 distinct positions, and each 32 lanes (two column groups) eight
+// distinct positions modulo 8.
 __device__ __forceinline__ int gemm_b_chunk(int col, int gc) {
-  const int G = col >> 2, cl = col & 3;
-  return 16 * G + 4 * (cl ^ ((G >> 2) & 3)) + (gc ^ (G & 3));
+  const int q = col >> 4;
+  return 16 * (4 * q + gc) + ((col & 15) ^ (gc | ((q & 3) << 2)));
 }
 
 // The 128-point transform across a wave's 128 columns: v[q] holds column
