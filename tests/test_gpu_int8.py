@@ -51,15 +51,28 @@ def test_reconstruct_int8_bit_exact(bits):
 @pytest.mark.parametrize("bits", [1, 2, 3, 4, 5, 6, 7, 8])
 @pytest.mark.parametrize("m", [1, 70, 300, 700, 1030])
 def test_linear_int8_parity(bits, m):
-    # several 128-column blocks, k of several 64-row steps, ragged row tiles
-    # of every tile height (64, 128 and 256 rows) and a last 16-row group of
-    # the fragment-major activations that is only partly filled
+    # several 128-column blocks, k of several 64-row steps, ragged 64-row
+    # tiles (three column tiles make too small a grid for taller ones) and a
+    # last 16-row group of the fragment-major activations that is only
+    # partly filled
     d = G.linear_case(810 + bits, 1030, 512, 384, bits)
     y = _run8(d, m=m).double().cpu().numpy()
     ref = O.linear_int8(d["x"][:m], d["trellis"], d["suh"], d["svh"], bits, wq=_wq(810 + bits, 1030, 512, 384, bits))
     assert O.rel_frobenius(y, ref) < TOL8
     ref16 = O.linear(d["x"][:m], d["trellis"], d["suh"], d["svh"], bits)
     assert O.rel_frobenius(y, ref16) < TOL_VS_FP16
+
+
+# 128 column tiles: m = 100 and 300 take 128-row tiles (one or three), m =
+# 600 256-row tiles (three, the last ragged); 64-row tiles are the narrow
+# tensors' above
+@pytest.mark.parametrize("bits", range(1, 9))
+@pytest.mark.parametrize("m", [100, 300, 600])
+def test_linear_int8_each_tile_height(bits, m):
+    d = G.linear_case(830 + bits, m, 256, 16384, bits)
+    y = _run8(d, m=m).double().cpu().numpy()
+    ref = O.linear_int8(d["x"], d["trellis"], d["suh"], d["svh"], bits, wq=_wq(830 + bits, m, 256, 16384, bits))
+    assert O.rel_frobenius(y, ref) < TOL8
 
 
 def test_linear_int8_fp32_output_and_bias():

@@ -42,10 +42,22 @@ def test_gemv_all_widths(bits, m):
     assert err < TOL, err
 
 
-@pytest.mark.parametrize("bits", [2, 3, 4, 8])
+@pytest.mark.parametrize("bits", range(1, 9))
 @pytest.mark.parametrize("m", [17, 64, 100, 300])
 def test_gemm_ragged_rows(bits, m):
     d = synth.linear_inputs(300 + bits, m, 512, 256, bits)
+    y = _run(d)
+    err = O.rel_frobenius(y.double().cpu().numpy(), _ref(d))
+    assert err < TOL, err
+
+
+# 128 column tiles: m = 100 and 300 take 128-row tiles (one or three), m =
+# 600 256-row tiles (three, the last ragged); 64-row tiles are the narrow
+# tensors' above
+@pytest.mark.parametrize("bits", range(1, 9))
+@pytest.mark.parametrize("m", [100, 300, 600])
+def test_gemm_each_tile_height(bits, m):
+    d = synth.linear_inputs(320 + bits, m, 256, 16384, bits)
     y = _run(d)
     err = O.rel_frobenius(y.double().cpu().numpy(), _ref(d))
     assert err < TOL, err
